@@ -1,0 +1,138 @@
+/*
+ * sqa.h - C ABI of libsqa, the Sparse Query Attention forward pass on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation is defined in "Sparse Query Attention (SQA): A Computationally
+ * Efficient Attention Mechanism with Query Heads Reduction" (arXiv 2510.01817,
+ * abstract) and in the ReactiveAI/GQA-Ref-Micro and ReactiveAI/xSMQAT-m model
+ * cards (descriptions). SQA is grouped-query attention with fewer query heads:
+ *
+ *   Q = X Wq  (H_q heads)   K = X Wk, V = X Wv  (H_kv heads), y = x W
+ *   query head i reads key/value head floor(i / (H_q / H_kv))
+ *   A_i = softmax(Q_i K^T / sqrt(d_head) [+ causal mask]) V     per head
+ *   A = [A_0 | A_1 | ... | A_{H_q-1}]  (head-major columns)
+ *   Y = A Wo
+ *
+ * d_head = d_model / H. H is the head count of the equally shaped MHA model,
+ * and H_q <= H of those heads are used (the cards' "d/heads"). Causal means
+ * that key c is visible to query r iff c <= r.
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer is a device pointer the caller owns. The buffers are
+ *     contiguous, row-major and 16-byte aligned, with element type `dtype`
+ *     (fp32 or bf16; one dtype for inputs, intermediates and output).
+ *   - Work is enqueued on `stream` and runs asynchronously. The caller keeps
+ *     the buffers alive until the stream has passed the call. The library
+ *     retains no pointer after it returns.
+ *   - Arguments are validated on the host before any HIP call. An invalid
+ *     call returns a status, enqueues nothing and writes no buffer.
+ *     sqa_last_error_message() names the failed check. Nothing is printed and
+ *     no C++ exception crosses the ABI.
+ *   - A kernel fault after a successful launch surfaces at the caller's next
+ *     synchronisation, as for any HIP call.
+ *   - Supported: d_head in {32, 64}; 1 <= H_kv <= H_q <= H; H_q % H_kv == 0;
+ *     1 <= N <= SQA_MAX_N. A call with B*N == 0 is a no-op that returns SQA_OK.
+ *   - Arithmetic: matrix products on the MFMA units with fp32 accumulation,
+ *     softmax in fp32. Q, K, V, A and Y are each rounded once (to nearest,
+ *     ties to even) to `dtype` when stored.
+ *   - Calls on different streams may run concurrently. The library keeps only
+ *     one stream-ordered memory pool per device (see sqa_forward).
+ */
+#ifndef SQA_H
+#define SQA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SQA_OK = 0,
+  SQA_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, inconsistent shape, aliasing */
+  SQA_ERR_UNSUPPORTED = 2,   /* valid but not built: d_head not 32/64, unknown dtype, N too large */
+  SQA_ERR_HIP = 3,           /* a HIP call failed (launch, pool, device query) */
+  SQA_ERR_OUT_OF_MEMORY = 4  /* the workspace could not be allocated */
+} sqa_status;
+
+typedef enum { SQA_DTYPE_FP32 = 0, SQA_DTYPE_BF16 = 1 } sqa_dtype;
+
+/* Largest sequence length accepted (keeps per-head offsets in 32 bits). */
+#define SQA_MAX_N (1 << 24)
+
+/*
+ * sqa_forward - the whole SQA forward pass: projection, attention core and
+ * output projection (the three steps of the definition above).
+ *
+ *   x   [B, N, d_model]        input tokens
+ *   Wq  [d_model, H_q*d_head]  query projection, narrowed to the H_q used heads
+ *   Wk  [d_model, H_kv*d_head] key projection
+ *   Wv  [d_model, H_kv*d_head] value projection
+ *   Wo  [H_q*d_head, d_model]  output projection, narrowed likewise
+ *   out [B, N, d_model]        result Y; must not overlap any input
+ *   causal: 0 or 1.
+ *
+ * Workspace: Q, K, V^T and A intermediates,
+ * elem_size * (B*Np*d_head*(H_q + 2*H_kv) + B*N*H_q*d_head) bytes with
+ * Np = sqa_padded_length(N). It is taken from a per-device stream-ordered
+ * memory pool (hipMallocFromPoolAsync) and returned to it (hipFreeAsync) on
+ * `stream`. The pool keeps freed memory for reuse until the process ends.
+ * Returns SQA_ERR_OUT_OF_MEMORY if the pool cannot supply the workspace.
+ */
+sqa_status sqa_forward(const void* x, const void* Wq, const void* Wk, const void* Wv,
+                       const void* Wo, void* out, int64_t B, int64_t N, int64_t d_model,
+                       int64_t H, int64_t H_q, int64_t H_kv, int64_t d_head, int causal,
+                       sqa_dtype dtype, hipStream_t stream);
+
+/*
+ * sqa_padded_length - Np, the sequence length of the Q/K/V^T layouts below:
+ * N rounded up to a multiple of 256. Returns -1 for N < 0.
+ */
+int64_t sqa_padded_length(int64_t N);
+
+/*
+ * sqa_qkv_projection - step 1, Q = X Wq, K = X Wk, V = X Wv, written in the
+ * layouts the attention step reads (Np = sqa_padded_length(N)):
+ *   q  [B, H_q,  Np, d_head]   head-major; column h*d_head + c of X Wq is q[b, h, t, c]
+ *   k  [B, H_kv, Np, d_head]
+ *   vt [B, H_kv, d_head, Np]   V transposed per head: vt[b, h, c, t] = V[b, t, h*d_head + c]
+ * Rows t in [N, Np) are written as zeros. x and the weights are as in sqa_forward.
+ */
+sqa_status sqa_qkv_projection(const void* x, const void* Wq, const void* Wk, const void* Wv,
+                              void* q, void* k, void* vt, int64_t B, int64_t N,
+                              int64_t d_model, int64_t H, int64_t H_q, int64_t H_kv,
+                              int64_t d_head, sqa_dtype dtype, hipStream_t stream);
+
+/*
+ * sqa_attention - step 2, the attention core of every query head:
+ *   a[b*N + t, i*d_head + c] = sum_s softmax_s(q_i[t] . k_j[s] / sqrt(d_head)) vt_j[c, s]
+ * with j = floor(i / (H_q/H_kv)), s over 0..N-1 (0..t if causal), in the q/k/vt
+ * layouts of sqa_qkv_projection. Rows t in [N, Np) of q/k/vt must be finite
+ * (sqa_qkv_projection writes zeros there). The output a is [B*N, H_q*d_head].
+ */
+sqa_status sqa_attention(const void* q, const void* k, const void* vt, void* a, int64_t B,
+                         int64_t N, int64_t H_q, int64_t H_kv, int64_t d_head, int causal,
+                         sqa_dtype dtype, hipStream_t stream);
+
+/*
+ * sqa_output_projection - step 3, out[M, d_model] = a[M, K] Wo[K, d_model].
+ * K must be a multiple of 32 and d_model a multiple of 8; out must not
+ * overlap a or Wo.
+ */
+sqa_status sqa_output_projection(const void* a, const void* Wo, void* out, int64_t M,
+                                 int64_t K, int64_t d_model, sqa_dtype dtype,
+                                 hipStream_t stream);
+
+/* Static description of a status code. Never NULL. */
+const char* sqa_status_string(sqa_status s);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char* sqa_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SQA_H */

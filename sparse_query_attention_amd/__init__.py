@@ -1,0 +1,137 @@
+"""Sparse Query Attention (SQA) forward pass on AMD MI355X (gfx950).
+
+SQA ("Sparse Query Attention (SQA): A Computationally Efficient Attention
+Mechanism with Query Heads Reduction", arXiv 2510.01817, abstract) is
+grouped-query attention with only H_q < H query heads, so its score FLOPs
+scale with H_q. Query head i reads key/value head floor(i / (H_q/H_kv)), and
+the query and output projections are narrowed to the H_q used heads
+(ReactiveAI/xSMQAT-m model card, description).
+
+This package is a thin binding of ``libsqa.so`` (C ABI in include/sqa.h).
+Tensors are torch device tensors, used only for memory and streams. Every
+arithmetic step runs in the library's HIP kernels. There is no CPU fallback:
+if the library is missing, importing the functions still works but calling
+them raises.
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+from . import _lib
+from ._lib import SQAError
+
+__all__ = ["forward", "qkv_projection", "attention", "output_projection", "padded_length",
+           "SQAError", "library_path"]
+
+library_path = _lib.LIB_PATH
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return _lib.SQA_DTYPE_FP32
+    if t.dtype == torch.bfloat16:
+        return _lib.SQA_DTYPE_BF16
+    raise NotImplementedError(f"dtype {t.dtype} is not supported (float32 or bfloat16)")
+
+
+def _check_tensor(name: str, t, shape, dtype, device) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device) -> int:
+    return _torch().cuda.current_stream(device).cuda_stream
+
+
+def padded_length(N: int) -> int:
+    """Sequence length Np of the q/k/vt layouts (N rounded up to 256)."""
+    return int(_lib.load().sqa_padded_length(N))
+
+
+def forward(x, Wq, Wk, Wv, Wo, *, H: int, H_q: int, H_kv: int, causal: bool = False, out=None):
+    """Y = SQA(x) for x [B, N, d_model]; weights stored [in, out] (y = x W):
+    Wq [d_model, H_q*d], Wk/Wv [d_model, H_kv*d], Wo [H_q*d, d_model], with
+    d = d_model / H. Runs on the current stream of x's device."""
+    lib = _lib.load()
+    if x.dim() != 3:
+        raise ValueError("x must be [B, N, d_model]")
+    B, N, D = x.shape
+    if H <= 0 or D % H:
+        raise ValueError("d_model must be a multiple of H")
+    d = D // H
+    if out is None:
+        out = _torch().empty_like(x)
+    for name, t, shp in (("x", x, (B, N, D)), ("Wq", Wq, (D, H_q * d)), ("Wk", Wk, (D, H_kv * d)),
+                         ("Wv", Wv, (D, H_kv * d)), ("Wo", Wo, (H_q * d, D)), ("out", out, (B, N, D))):
+        _check_tensor(name, t, shp, x.dtype, x.device)
+    _lib.check(lib.sqa_forward(x.data_ptr(), Wq.data_ptr(), Wk.data_ptr(), Wv.data_ptr(),
+                               Wo.data_ptr(), out.data_ptr(), B, N, D, H, H_q, H_kv, d,
+                               int(bool(causal)), _dtype_code(x), _stream(x.device)))
+    return out
+
+
+def qkv_projection(x, Wq, Wk, Wv, *, H: int, H_q: int, H_kv: int, q=None, k=None, vt=None
+                   ) -> Tuple[object, object, object]:
+    """Step 1: returns q [B,H_q,Np,d], k [B,H_kv,Np,d], vt [B,H_kv,d,Np]
+    (Np = padded_length(N); padded rows are zero)."""
+    lib = _lib.load()
+    torch = _torch()
+    B, N, D = x.shape
+    d = D // H
+    Np = padded_length(N)
+    q = torch.empty((B, H_q, Np, d), dtype=x.dtype, device=x.device) if q is None else q
+    k = torch.empty((B, H_kv, Np, d), dtype=x.dtype, device=x.device) if k is None else k
+    vt = torch.empty((B, H_kv, d, Np), dtype=x.dtype, device=x.device) if vt is None else vt
+    for name, t, shp in (("x", x, (B, N, D)), ("Wq", Wq, (D, H_q * d)), ("Wk", Wk, (D, H_kv * d)),
+                         ("Wv", Wv, (D, H_kv * d)), ("q", q, (B, H_q, Np, d)),
+                         ("k", k, (B, H_kv, Np, d)), ("vt", vt, (B, H_kv, d, Np))):
+        _check_tensor(name, t, shp, x.dtype, x.device)
+    _lib.check(lib.sqa_qkv_projection(x.data_ptr(), Wq.data_ptr(), Wk.data_ptr(), Wv.data_ptr(),
+                                      q.data_ptr(), k.data_ptr(), vt.data_ptr(), B, N, D, H, H_q,
+                                      H_kv, d, _dtype_code(x), _stream(x.device)))
+    return q, k, vt
+
+
+def attention(q, k, vt, *, N: int, causal: bool = False, a=None):
+    """Step 2: a [B*N, H_q*d] from the step-1 layouts."""
+    lib = _lib.load()
+    torch = _torch()
+    B, H_q, Np, d = q.shape
+    H_kv = k.shape[1]
+    if Np != padded_length(N):
+        raise ValueError(f"q has {Np} rows per head, expected padded_length(N)={padded_length(N)}")
+    a = torch.empty((B * N, H_q * d), dtype=q.dtype, device=q.device) if a is None else a
+    for name, t, shp in (("k", k, (B, H_kv, Np, d)), ("vt", vt, (B, H_kv, d, Np)),
+                         ("a", a, (B * N, H_q * d)), ("q", q, (B, H_q, Np, d))):
+        _check_tensor(name, t, shp, q.dtype, q.device)
+    _lib.check(lib.sqa_attention(q.data_ptr(), k.data_ptr(), vt.data_ptr(), a.data_ptr(), B, N,
+                                 H_q, H_kv, d, int(bool(causal)), _dtype_code(q),
+                                 _stream(q.device)))
+    return a
+
+
+def output_projection(a, Wo, out=None):
+    """Step 3: out [M, d_model] = a [M, K] @ Wo [K, d_model]."""
+    lib = _lib.load()
+    M, K = a.shape
+    D = Wo.shape[1]
+    out = _torch().empty((M, D), dtype=a.dtype, device=a.device) if out is None else out
+    for name, t, shp in (("a", a, (M, K)), ("Wo", Wo, (K, D)), ("out", out, (M, D))):
+        _check_tensor(name, t, shp, a.dtype, a.device)
+    _lib.check(lib.sqa_output_projection(a.data_ptr(), Wo.data_ptr(), out.data_ptr(), M, K, D,
+                                         _dtype_code(a), _stream(a.device)))
+    return out

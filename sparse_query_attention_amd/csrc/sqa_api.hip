@@ -1,0 +1,292 @@
+// C ABI of libsqa (declared in include/sqa.h): argument validation on the
+// host, the stream-ordered workspace of sqa_forward, and dispatch to the three
+// gfx950 kernels (projection, attention core, output projection).
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "sqa.h"
+#include "sqa_internal.h"
+
+namespace {
+
+thread_local char g_err[256] = "";
+
+sqa_status fail(sqa_status s, const char* msg) {
+  snprintf(g_err, sizeof(g_err), "%s", msg);
+  return s;
+}
+
+sqa_status fail_hip(hipError_t e, const char* where) {
+  snprintf(g_err, sizeof(g_err), "%s: %s", where, hipGetErrorString(e));
+  return e == hipErrorOutOfMemory ? SQA_ERR_OUT_OF_MEMORY : SQA_ERR_HIP;
+}
+
+sqa_status ok() {
+  g_err[0] = '\0';
+  return SQA_OK;
+}
+
+size_t elem_size(sqa_dtype dt) { return dt == SQA_DTYPE_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// a*b without overflow into out; false on overflow or negative factors.
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+struct Shape {
+  int64_t B, N, d_model, H, H_q, H_kv, d;
+};
+
+// Shared checks of the head configuration (pure host, no HIP call).
+sqa_status check_heads(const Shape& s, bool need_h) {
+  if (s.B < 0 || s.N < 0) return fail(SQA_ERR_INVALID_ARG, "B and N must be >= 0");
+  if (s.N > SQA_MAX_N) return fail(SQA_ERR_UNSUPPORTED, "N exceeds SQA_MAX_N");
+  if (s.B > (int64_t)1 << 20) return fail(SQA_ERR_UNSUPPORTED, "B exceeds 2^20");
+  if (s.H_kv < 1 || s.H_q < s.H_kv) return fail(SQA_ERR_INVALID_ARG, "need 1 <= H_kv <= H_q");
+  if (s.H_q % s.H_kv != 0) return fail(SQA_ERR_INVALID_ARG, "H_q must be a multiple of H_kv");
+  if (s.H_q > 1024) return fail(SQA_ERR_UNSUPPORTED, "H_q exceeds 1024");
+  if (need_h) {
+    if (s.H < s.H_q) return fail(SQA_ERR_INVALID_ARG, "need H_q <= H");
+    int64_t dm;
+    if (!mul_ok(s.H, s.d, &dm) || dm != s.d_model)
+      return fail(SQA_ERR_INVALID_ARG, "d_model must equal H * d_head");
+  }
+  if (s.d != 32 && s.d != 64) return fail(SQA_ERR_UNSUPPORTED, "d_head must be 32 or 64");
+  return SQA_OK;
+}
+
+sqa_status check_dtype(sqa_dtype dt) {
+  if (dt != SQA_DTYPE_FP32 && dt != SQA_DTYPE_BF16)
+    return fail(SQA_ERR_UNSUPPORTED, "dtype must be SQA_DTYPE_FP32 or SQA_DTYPE_BF16");
+  return SQA_OK;
+}
+
+sqa_status check_ptr(const void* p, const char* msg_null, const char* msg_align) {
+  if (!p) return fail(SQA_ERR_INVALID_ARG, msg_null);
+  if (!aligned16(p)) return fail(SQA_ERR_INVALID_ARG, msg_align);
+  return SQA_OK;
+}
+
+#define SQA_TRY(expr)            \
+  do {                           \
+    sqa_status _s = (expr);      \
+    if (_s != SQA_OK) return _s; \
+  } while (0)
+
+// Byte sizes of the intermediates, with overflow checks.
+struct Sizes {
+  int64_t Np, q, kv, a;  // bytes of q, of k (= of vt), of a
+};
+
+sqa_status sizes_for(const Shape& s, sqa_dtype dt, Sizes* out) {
+  out->Np = sqa::padded_length(s.N);
+  int64_t t, es = (int64_t)elem_size(dt);
+  if (!mul_ok(s.B, out->Np, &t) || !mul_ok(t, s.d * es, &t)) return fail(SQA_ERR_UNSUPPORTED, "size overflow");
+  int64_t qb, kb;
+  if (!mul_ok(t, s.H_q, &qb) || !mul_ok(t, s.H_kv, &kb)) return fail(SQA_ERR_UNSUPPORTED, "size overflow");
+  int64_t ab;
+  if (!mul_ok(s.B, s.N, &ab) || !mul_ok(ab, s.H_q * s.d * es, &ab))
+    return fail(SQA_ERR_UNSUPPORTED, "size overflow");
+  out->q = qb; out->kv = kb; out->a = ab;
+  return SQA_OK;
+}
+
+int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
+
+// One stream-ordered pool per device. Freed workspace stays in the pool for
+// reuse (release threshold = max) instead of going back to the driver.
+constexpr int kMaxDevices = 64;
+std::mutex g_pool_mu;
+hipMemPool_t g_pools[kMaxDevices] = {};
+
+sqa_status pool_for(hipStream_t stream, hipMemPool_t* out) {
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e, "device of stream");
+  if (dev < 0 || dev >= kMaxDevices) return fail(SQA_ERR_UNSUPPORTED, "device index too large");
+  std::lock_guard<std::mutex> lock(g_pool_mu);
+  if (!g_pools[dev]) {
+    hipMemPoolProps props;
+    memset(&props, 0, sizeof(props));
+    props.allocType = hipMemAllocationTypePinned;
+    props.handleTypes = hipMemHandleTypeNone;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t pool;
+    e = hipMemPoolCreate(&pool, &props);
+    if (e != hipSuccess) return fail_hip(e, "hipMemPoolCreate");
+    uint64_t thr = UINT64_MAX;
+    e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr);
+    if (e != hipSuccess) {
+      (void)hipMemPoolDestroy(pool);
+      return fail_hip(e, "hipMemPoolSetAttribute");
+    }
+    g_pools[dev] = pool;
+  }
+  *out = g_pools[dev];
+  return SQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sqa_status_string(sqa_status s) {
+  switch (s) {
+    case SQA_OK: return "SQA_OK";
+    case SQA_ERR_INVALID_ARG: return "SQA_ERR_INVALID_ARG: invalid argument";
+    case SQA_ERR_UNSUPPORTED: return "SQA_ERR_UNSUPPORTED: configuration not supported";
+    case SQA_ERR_HIP: return "SQA_ERR_HIP: a HIP runtime call failed";
+    case SQA_ERR_OUT_OF_MEMORY: return "SQA_ERR_OUT_OF_MEMORY: workspace allocation failed";
+  }
+  return "unknown sqa_status";
+}
+
+const char* sqa_last_error_message(void) { return g_err; }
+
+int64_t sqa_padded_length(int64_t N) { return N < 0 ? -1 : sqa::padded_length(N); }
+
+sqa_status sqa_qkv_projection(const void* x, const void* Wq, const void* Wk, const void* Wv,
+                              void* q, void* k, void* vt, int64_t B, int64_t N, int64_t d_model,
+                              int64_t H, int64_t H_q, int64_t H_kv, int64_t d_head,
+                              sqa_dtype dtype, hipStream_t stream) {
+  const Shape s{B, N, d_model, H, H_q, H_kv, d_head};
+  SQA_TRY(check_dtype(dtype));
+  SQA_TRY(check_heads(s, true));
+  if (B * N == 0) return ok();
+  SQA_TRY(check_ptr(x, "x is null", "x is not 16-byte aligned"));
+  SQA_TRY(check_ptr(Wq, "Wq is null", "Wq is not 16-byte aligned"));
+  SQA_TRY(check_ptr(Wk, "Wk is null", "Wk is not 16-byte aligned"));
+  SQA_TRY(check_ptr(Wv, "Wv is null", "Wv is not 16-byte aligned"));
+  SQA_TRY(check_ptr(q, "q is null", "q is not 16-byte aligned"));
+  SQA_TRY(check_ptr(k, "k is null", "k is not 16-byte aligned"));
+  SQA_TRY(check_ptr(vt, "vt is null", "vt is not 16-byte aligned"));
+  Sizes z;
+  SQA_TRY(sizes_for(s, dtype, &z));
+  const size_t es = elem_size(dtype);
+  const size_t xb = (size_t)(B * N * d_model) * es;
+  const size_t wqb = (size_t)(d_model * H_q * d_head) * es, wkb = (size_t)(d_model * H_kv * d_head) * es;
+  const void* ins[4] = {x, Wq, Wk, Wv};
+  const size_t inb[4] = {xb, wqb, wkb, wkb};
+  void* outs[3] = {q, k, vt};
+  const size_t outb[3] = {(size_t)z.q, (size_t)z.kv, (size_t)z.kv};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 4; ++j)
+      if (overlap(outs[i], outb[i], ins[j], inb[j]))
+        return fail(SQA_ERR_INVALID_ARG, "an output of the projection overlaps an input");
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outb[i], outs[j], outb[j]))
+        return fail(SQA_ERR_INVALID_ARG, "q, k and vt must not overlap");
+  }
+  hipError_t e = sqa::launch_qkv_projection(dtype, x, Wq, Wk, Wv, q, k, vt, B, N, z.Np, d_model,
+                                            H_q, H_kv, d_head, stream);
+  if (e != hipSuccess) return fail_hip(e, "qkv projection launch");
+  return ok();
+}
+
+sqa_status sqa_attention(const void* q, const void* k, const void* vt, void* a, int64_t B,
+                         int64_t N, int64_t H_q, int64_t H_kv, int64_t d_head, int causal,
+                         sqa_dtype dtype, hipStream_t stream) {
+  const Shape s{B, N, H_q * d_head, H_q, H_q, H_kv, d_head};
+  SQA_TRY(check_dtype(dtype));
+  SQA_TRY(check_heads(s, false));
+  if (causal != 0 && causal != 1) return fail(SQA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (B * N == 0) return ok();
+  SQA_TRY(check_ptr(q, "q is null", "q is not 16-byte aligned"));
+  SQA_TRY(check_ptr(k, "k is null", "k is not 16-byte aligned"));
+  SQA_TRY(check_ptr(vt, "vt is null", "vt is not 16-byte aligned"));
+  SQA_TRY(check_ptr(a, "a is null", "a is not 16-byte aligned"));
+  Sizes z;
+  SQA_TRY(sizes_for(s, dtype, &z));
+  if (overlap(a, z.a, q, z.q) || overlap(a, z.a, k, z.kv) || overlap(a, z.a, vt, z.kv))
+    return fail(SQA_ERR_INVALID_ARG, "a overlaps q, k or vt");
+  hipError_t e = sqa::launch_attention(dtype, q, k, vt, a, B, N, z.Np, H_q, H_kv, d_head,
+                                       causal != 0, stream);
+  if (e != hipSuccess) return fail_hip(e, "attention launch");
+  return ok();
+}
+
+sqa_status sqa_output_projection(const void* a, const void* Wo, void* out, int64_t M, int64_t K,
+                                 int64_t d_model, sqa_dtype dtype, hipStream_t stream) {
+  SQA_TRY(check_dtype(dtype));
+  if (M < 0) return fail(SQA_ERR_INVALID_ARG, "M must be >= 0");
+  if (K < 32 || K % 32 != 0) return fail(SQA_ERR_UNSUPPORTED, "K must be a positive multiple of 32");
+  if (d_model < 8 || d_model % 8 != 0)
+    return fail(SQA_ERR_UNSUPPORTED, "d_model must be a positive multiple of 8");
+  if (K > 65536 || d_model > 65536) return fail(SQA_ERR_UNSUPPORTED, "K or d_model exceeds 65536");
+  if (M > ((int64_t)1 << 40)) return fail(SQA_ERR_UNSUPPORTED, "M too large");
+  if (M == 0) return ok();
+  SQA_TRY(check_ptr(a, "a is null", "a is not 16-byte aligned"));
+  SQA_TRY(check_ptr(Wo, "Wo is null", "Wo is not 16-byte aligned"));
+  SQA_TRY(check_ptr(out, "out is null", "out is not 16-byte aligned"));
+  const size_t es = elem_size(dtype);
+  if (overlap(out, (size_t)(M * d_model) * es, a, (size_t)(M * K) * es) ||
+      overlap(out, (size_t)(M * d_model) * es, Wo, (size_t)(K * d_model) * es))
+    return fail(SQA_ERR_INVALID_ARG, "out overlaps a or Wo");
+  hipError_t e = sqa::launch_output_projection(dtype, a, Wo, out, M, K, d_model, stream);
+  if (e != hipSuccess) return fail_hip(e, "output projection launch");
+  return ok();
+}
+
+sqa_status sqa_forward(const void* x, const void* Wq, const void* Wk, const void* Wv,
+                       const void* Wo, void* out, int64_t B, int64_t N, int64_t d_model,
+                       int64_t H, int64_t H_q, int64_t H_kv, int64_t d_head, int causal,
+                       sqa_dtype dtype, hipStream_t stream) {
+  const Shape s{B, N, d_model, H, H_q, H_kv, d_head};
+  SQA_TRY(check_dtype(dtype));
+  SQA_TRY(check_heads(s, true));
+  if (causal != 0 && causal != 1) return fail(SQA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (B * N == 0) return ok();
+  SQA_TRY(check_ptr(x, "x is null", "x is not 16-byte aligned"));
+  SQA_TRY(check_ptr(Wq, "Wq is null", "Wq is not 16-byte aligned"));
+  SQA_TRY(check_ptr(Wk, "Wk is null", "Wk is not 16-byte aligned"));
+  SQA_TRY(check_ptr(Wv, "Wv is null", "Wv is not 16-byte aligned"));
+  SQA_TRY(check_ptr(Wo, "Wo is null", "Wo is not 16-byte aligned"));
+  SQA_TRY(check_ptr(out, "out is null", "out is not 16-byte aligned"));
+  Sizes z;
+  SQA_TRY(sizes_for(s, dtype, &z));
+  const size_t es = elem_size(dtype);
+  const size_t yb = (size_t)(B * N * d_model) * es;
+  const size_t wqb = (size_t)(d_model * H_q * d_head) * es, wkb = (size_t)(d_model * H_kv * d_head) * es;
+  const void* ins[5] = {x, Wq, Wk, Wv, Wo};
+  const size_t inb[5] = {yb, wqb, wkb, wkb, wqb};
+  for (int j = 0; j < 5; ++j)
+    if (overlap(out, yb, ins[j], inb[j])) return fail(SQA_ERR_INVALID_ARG, "out overlaps an input");
+
+  const int64_t off_k = round256(z.q), off_v = off_k + round256(z.kv);
+  const int64_t off_a = off_v + round256(z.kv), total = off_a + round256(z.a);
+  hipMemPool_t pool;
+  SQA_TRY(pool_for(stream, &pool));
+  void* ws = nullptr;
+  hipError_t e = hipMallocFromPoolAsync(&ws, (size_t)total, pool, stream);
+  if (e != hipSuccess) return fail_hip(e, "workspace allocation");
+  char* base = (char*)ws;
+  void *q = base, *k = base + off_k, *vt = base + off_v, *a = base + off_a;
+
+  e = sqa::launch_qkv_projection(dtype, x, Wq, Wk, Wv, q, k, vt, B, N, z.Np, d_model, H_q, H_kv,
+                                 d_head, stream);
+  if (e == hipSuccess)
+    e = sqa::launch_attention(dtype, q, k, vt, a, B, N, z.Np, H_q, H_kv, d_head, causal != 0, stream);
+  if (e == hipSuccess)
+    e = sqa::launch_output_projection(dtype, a, Wo, out, B * N, H_q * d_head, d_model, stream);
+  const hipError_t ef = hipFreeAsync(ws, stream);
+  if (e != hipSuccess) return fail_hip(e, "kernel launch");
+  if (ef != hipSuccess) return fail_hip(ef, "workspace release");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,58 @@
+// Device-side building blocks shared by the gfx950 kernels: element types,
+// the MFMA instructions each dtype uses, and the operand layouts they share.
+//
+// A 32x32 MFMA tile (v_mfma_f32_32x32x16_bf16 / v_mfma_f32_32x32x2_f32)
+// computes C[32][32] += A[32][K] * B[K][32] across one wave of 64 lanes:
+//   A operand: lane l supplies row (l % 32), k-group (l / 32), E values
+//   B operand: lane l supplies column (l % 32), k-group (l / 32), E values
+//   C/D:       lane l holds column (l % 32), rows 8*(r/4) + 4*(l/32) + (r%4)
+//              for its 16 accumulator registers r = 0..15
+// The k-group split only has to agree between A and B, so every operand below
+// is loaded with "k-group g holds the E consecutive k at g*E of each step".
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sqa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T> struct Mfma;
+
+// bf16 inputs, fp32 accumulation: 32x32x16, 8 bf16 (16 bytes) per lane and operand.
+template <> struct Mfma<bf16> {
+  static constexpr int E = 8;
+  static constexpr int KS = 16;
+  typedef bf16x8 Frag;
+  __device__ static inline f32x16 run(Frag a, Frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+// fp32 inputs and accumulation: 32x32x2, one float per lane and operand.
+template <> struct Mfma<float> {
+  static constexpr int E = 1;
+  static constexpr int KS = 2;
+  typedef float Frag;
+  __device__ static inline f32x16 run(Frag a, Frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+};
+
+// Round-to-nearest-even conversion from fp32 (v_cvt_pk_bf16_f32 on gfx950).
+template <typename T> __device__ inline T from_f32(float x);
+template <> __device__ inline float from_f32<float>(float x) { return x; }
+template <> __device__ inline bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+// 16-byte vector of T, the unit of every global<->LDS copy.
+struct alignas(16) Chunk { uint32_t w[4]; };
+
+__device__ inline Chunk zero_chunk() { Chunk c; c.w[0] = c.w[1] = c.w[2] = c.w[3] = 0u; return c; }
+
+}  // namespace sqa

@@ -1,0 +1,34 @@
+// Host-side launchers of the gfx950 kernels. The C ABI (include/sqa.h)
+// validates every argument before it calls these; they assume valid shapes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sqa.h"
+
+namespace sqa {
+
+// Sequence padding granule of the Q/K/V^T layouts: a multiple of every query
+// tile and key tile the attention kernel uses.
+constexpr int64_t kSeqPad = 256;
+
+inline int64_t padded_length(int64_t n) { return (n + kSeqPad - 1) / kSeqPad * kSeqPad; }
+
+// Step 1: X [B*N, d_model] times [Wq | Wk | Wv] into q [B,H_q,Np,d], k [B,H_kv,Np,d],
+// vt [B,H_kv,d,Np].
+hipError_t launch_qkv_projection(sqa_dtype dt, const void* x, const void* wq, const void* wk,
+                                 const void* wv, void* q, void* k, void* vt, int64_t B, int64_t N,
+                                 int64_t Np, int64_t d_model, int64_t H_q, int64_t H_kv,
+                                 int64_t d_head, hipStream_t stream);
+
+// Step 2: attention core into a [B*N, H_q*d].
+hipError_t launch_attention(sqa_dtype dt, const void* q, const void* k, const void* vt, void* a,
+                            int64_t B, int64_t N, int64_t Np, int64_t H_q, int64_t H_kv,
+                            int64_t d_head, bool causal, hipStream_t stream);
+
+// Step 3: out [M, d_model] = a [M, K] * wo [K, d_model].
+hipError_t launch_output_projection(sqa_dtype dt, const void* a, const void* wo, void* out,
+                                    int64_t M, int64_t K, int64_t d_model, hipStream_t stream);
+
+}  // namespace sqa

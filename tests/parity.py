@@ -1,0 +1,88 @@
+"""Helpers of the GPU parity tests: run the HIP path through the C ABI, run the
+oracle on the same seeded inputs, and compare to the tolerances of the
+workload's dtype.
+
+Tolerances:
+  fp32: max |Y - Y_ref| <= 1e-4.
+  bf16: ||Y - Y_ref|| / ||Y_ref|| <= 1e-2 over all compared elements, and
+        |Y - Y_ref| <= 2e-2 * max(1, |Y_ref|) elementwise.
+Y_ref is the float64 oracle with bf16 rounding at the Q/K/V/A/Y boundaries
+for bf16 runs, and no rounding for fp32 runs.
+"""
+from __future__ import annotations
+
+import sys
+from dataclasses import dataclass
+from typing import Dict, Optional
+
+import numpy as np
+
+import workloads as wl
+
+
+@dataclass
+class Report:
+    max_abs: float
+    rel_l2: float
+    worst_scaled: float      # max |err| / max(1, |ref|)
+    ok: bool
+
+    def __str__(self):
+        return (f"max_abs={self.max_abs:.3e} rel_l2={self.rel_l2:.3e} "
+                f"worst_scaled={self.worst_scaled:.3e} {'OK' if self.ok else 'FAIL'}")
+
+
+def compare(got: np.ndarray, ref: np.ndarray, dtype: str) -> Report:
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    if not np.isfinite(got).all():
+        return Report(float("inf"), float("inf"), float("inf"), False)
+    err = np.abs(got - ref)
+    max_abs = float(err.max()) if err.size else 0.0
+    nref = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(got - ref) / nref) if nref > 0 else float(np.linalg.norm(got - ref))
+    scaled = float((err / np.maximum(1.0, np.abs(ref))).max()) if err.size else 0.0
+    if dtype == "fp32":
+        ok = max_abs <= 1e-4
+    else:
+        ok = rel <= 1e-2 and scaled <= 2e-2
+    return Report(max_abs, rel, scaled, ok)
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def device_inputs(w: wl.Workload, device):
+    """Seeded inputs rounded to the dtype: (host torch tensors, device tensors)."""
+    host = wl.to_device_dtype(wl.draw(w), w.dtype)
+    dev = {k: v.to(device) for k, v in host.items()}
+    return host, dev
+
+
+def oracle_inputs(host) -> Dict[str, np.ndarray]:
+    return {k: wl.widen(v) for k, v in host.items()}
+
+
+def sample_rows(w: wl.Workload, n_random: int = 96, seed: int = 0) -> np.ndarray:
+    """Flat token rows for full-size parity: both ends of every sequence, rows
+    around key/query tile boundaries, outlier rows, and random rows."""
+    N, B = w.N, w.B
+    rows = set()
+    for b in (0, B - 1):
+        base = b * N
+        rows.update(base + t for t in range(min(N, 16)))
+        rows.update(base + t for t in range(max(0, N - 16), N))
+        for edge in (32, 64, 128, 256, N // 2, N - 257, N - 65):
+            for t in (edge - 1, edge, edge + 1):
+                if 0 <= t < N:
+                    rows.add(base + t)
+    out = wl.outlier_rows(w)
+    if out.size:
+        rng = np.random.default_rng(seed + 1)
+        rows.update(rng.choice(out, size=min(48, out.size), replace=False).tolist())
+    rng = np.random.default_rng(seed)
+    rows.update(rng.integers(0, B * N, size=n_random).tolist())
+    return np.array(sorted(rows), dtype=np.int64)

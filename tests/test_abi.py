@@ -1,0 +1,112 @@
+"""The C ABI (CPU only): libsqa.so loads, exports every function include/sqa.h
+declares, and rejects invalid arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_query_attention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sqa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
+                                reason="libsqa.so not built (run __graft_entry__.build())")
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sqa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(_lib.SIGNATURES)
+
+
+def test_library_exports_every_declared_function():
+    lib = _lib.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    lib = _lib.load()
+    for s in range(5):
+        assert lib.sqa_status_string(s)
+    assert b"unknown" in lib.sqa_status_string(99)
+    assert lib.sqa_padded_length(1) == 256 and lib.sqa_padded_length(256) == 256
+    assert lib.sqa_padded_length(257) == 512 and lib.sqa_padded_length(200000) == 200192
+    assert lib.sqa_padded_length(0) == 0 and lib.sqa_padded_length(-1) == -1
+
+
+def _fwd(**kw):
+    a = dict(x=FAKE, Wq=FAKE + 0x1000000, Wk=FAKE + 0x2000000, Wv=FAKE + 0x3000000,
+             Wo=FAKE + 0x4000000, out=FAKE + 0x5000000, B=1, N=256, d_model=256, H=8, H_q=4,
+             H_kv=2, d_head=32, causal=0, dtype=_lib.SQA_DTYPE_BF16)
+    a.update(kw)
+    lib = _lib.load()
+    st = lib.sqa_forward(a["x"], a["Wq"], a["Wk"], a["Wv"], a["Wo"], a["out"], a["B"], a["N"],
+                         a["d_model"], a["H"], a["H_q"], a["H_kv"], a["d_head"], a["causal"],
+                         a["dtype"], None)
+    return st, lib.sqa_last_error_message().decode()
+
+
+@pytest.mark.parametrize("kw,status,words", [
+    (dict(x=0), _lib.SQA_ERR_INVALID_ARG, "x is null"),
+    (dict(Wo=0), _lib.SQA_ERR_INVALID_ARG, "Wo is null"),
+    (dict(Wq=FAKE + 0x1000008), _lib.SQA_ERR_INVALID_ARG, "aligned"),
+    (dict(out=FAKE + 8), _lib.SQA_ERR_INVALID_ARG, "aligned"),
+    (dict(out=FAKE), _lib.SQA_ERR_INVALID_ARG, "overlaps"),
+    (dict(H_kv=3), _lib.SQA_ERR_INVALID_ARG, "multiple of H_kv"),
+    (dict(H_kv=0), _lib.SQA_ERR_INVALID_ARG, "H_kv"),
+    (dict(H_q=2, H_kv=4), _lib.SQA_ERR_INVALID_ARG, "H_kv <= H_q"),
+    (dict(H_q=16, H_kv=2), _lib.SQA_ERR_INVALID_ARG, "H_q <= H"),
+    (dict(d_model=512), _lib.SQA_ERR_INVALID_ARG, "H * d_head"),
+    (dict(B=-1), _lib.SQA_ERR_INVALID_ARG, ">= 0"),
+    (dict(causal=2), _lib.SQA_ERR_INVALID_ARG, "causal"),
+    (dict(d_model=128, H=8, d_head=16), _lib.SQA_ERR_UNSUPPORTED, "d_head"),
+    (dict(dtype=7), _lib.SQA_ERR_UNSUPPORTED, "dtype"),
+    (dict(N=(1 << 24) + 1), _lib.SQA_ERR_UNSUPPORTED, "SQA_MAX_N"),
+])
+def test_forward_rejects_invalid_arguments(kw, status, words):
+    st, msg = _fwd(**kw)
+    assert st == status, msg
+    assert words in msg
+
+
+def test_empty_problem_is_a_no_op():
+    # B*N == 0: nothing to compute, no device call, pointers unused
+    assert _fwd(B=0, x=0, out=0)[0] == _lib.SQA_OK
+    assert _fwd(N=0)[0] == _lib.SQA_OK
+
+
+def test_stage_entry_points_validate():
+    lib = _lib.load()
+    st = lib.sqa_attention(FAKE, FAKE + 0x100000, FAKE + 0x200000, 0, 1, 10, 4, 2, 64, 0,
+                           _lib.SQA_DTYPE_BF16, None)
+    assert st == _lib.SQA_ERR_INVALID_ARG and b"a is null" in lib.sqa_last_error_message()
+    st = lib.sqa_attention(FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE, 1, 10, 4, 2, 64, 0,
+                           _lib.SQA_DTYPE_BF16, None)
+    assert st == _lib.SQA_ERR_INVALID_ARG and b"overlaps" in lib.sqa_last_error_message()
+    st = lib.sqa_output_projection(FAKE, FAKE + 0x100000, FAKE + 0x200000, 10, 48, 64,
+                                   _lib.SQA_DTYPE_BF16, None)
+    assert st == _lib.SQA_ERR_UNSUPPORTED
+    st = lib.sqa_qkv_projection(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 256, 8, 4, 2, 32,
+                                _lib.SQA_DTYPE_FP32, None)
+    assert st == _lib.SQA_ERR_INVALID_ARG and b"overlaps" in lib.sqa_last_error_message()
+
+
+def test_python_binding_maps_statuses_to_exceptions():
+    with pytest.raises(ValueError):
+        _lib.check(_lib.SQA_ERR_INVALID_ARG)
+    with pytest.raises(NotImplementedError):
+        _lib.check(_lib.SQA_ERR_UNSUPPORTED)
+    with pytest.raises(_lib.SQAError):
+        _lib.check(_lib.SQA_ERR_HIP)
+    with pytest.raises(_lib.SQAError):
+        _lib.check(_lib.SQA_ERR_OUT_OF_MEMORY)
+    _lib.check(_lib.SQA_OK)

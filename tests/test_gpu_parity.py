@@ -1,0 +1,193 @@
+"""Parity of the HIP path (through the C ABI) with the float64 CPU oracle.
+
+Small shapes are compared element by element over the whole output. They
+span several key/query tiles plus a ragged tail, every query-group size, both
+head widths, both dtypes and both masks. The five full workloads run at their
+real sizes in the launch configuration the benchmark times. Their outputs are
+compared on sampled rows that the oracle computes one by one.
+"""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_query_attention_amd as sqa
+import workloads as wl
+from parity import compare, device_inputs, log, oracle_inputs, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    sqa._lib.load()   # the HIP library, never a stand-in
+    return torch.device("cuda:0")
+
+
+def run_forward(w, d):
+    return sqa.forward(d["X"], d["Wq"], d["Wk"], d["Wv"], d["Wo"], H=w.H, H_q=w.H_q, H_kv=w.H_kv,
+                       causal=w.causal)
+
+
+def full_check(w, dev, stages=False):
+    log(f"case {w.name}: B={w.B} N={w.N} d_model={w.d_model} H={w.H} H_q={w.H_q} H_kv={w.H_kv} "
+        f"causal={w.causal} dtype={w.dtype}")
+    host, d = device_inputs(w, dev)
+    y = run_forward(w, d)
+    torch.cuda.synchronize()
+    o = oracle_inputs(host)
+    ref = oracle.sqa_forward(o["X"], o["Wq"], o["Wk"], o["Wv"], o["Wo"], w.H_q, w.H_kv, w.d_head,
+                             w.causal, bf16=(w.dtype == "bf16"))
+    rep = compare(wl.widen(y.cpu()), ref["Y"], w.dtype)
+    log(f"  Y: {rep}")
+    assert rep.ok, f"{w.name}: {rep}"
+    if stages:
+        check_stages(w, d, ref)
+    return y
+
+
+def check_stages(w, d, ref):
+    """Each C-ABI step against the oracle's intermediate of the same name."""
+    q, k, vt = sqa.qkv_projection(d["X"], d["Wq"], d["Wk"], d["Wv"], H=w.H, H_q=w.H_q, H_kv=w.H_kv)
+    a = sqa.attention(q, k, vt, N=w.N, causal=w.causal)
+    y = sqa.output_projection(a, d["Wo"])
+    torch.cuda.synchronize()
+    B, N, dh = w.B, w.N, w.d_head
+    Np = sqa.padded_length(N)
+    qh = wl.widen(q.cpu())
+    kh = wl.widen(k.cpu())
+    vh = wl.widen(vt.cpu())
+    # padded rows are zeros (the attention step relies on finite padding)
+    assert not qh[:, :, N:].any() and not kh[:, :, N:].any() and not vh[..., N:].any()
+    Q = ref["Q"].reshape(B, N, w.H_q, dh).transpose(0, 2, 1, 3)
+    K = ref["K"].reshape(B, N, w.H_kv, dh).transpose(0, 2, 1, 3)
+    V = ref["V"].reshape(B, N, w.H_kv, dh).transpose(0, 2, 3, 1)
+    # projections: fp32 accumulation rounded once; bf16 may differ by one
+    # rounding of a near-tie, so allow one bf16 ulp.
+    for name, got, want in (("Q", qh[:, :, :N], Q), ("K", kh[:, :, :N], K), ("V^T", vh[..., :N], V)):
+        if w.dtype == "bf16":
+            ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(want), 1e-30))) - 7)
+            bad = np.abs(got - want) > ulp * 1.0001
+            exact = float((got == want).mean())
+            log(f"  {name}: exact={exact:.5f} beyond_1ulp={int(bad.sum())}")
+            assert not bad.any() and exact > 0.99, name
+        else:
+            err = float(np.abs(got - want).max())
+            log(f"  {name}: max_abs={err:.3e}")
+            assert err <= 1e-4, name
+    rep_a = compare(wl.widen(a.cpu()).reshape(B, N, -1), ref["A"], w.dtype)
+    log(f"  A: {rep_a}")
+    assert rep_a.ok
+    rep_y = compare(wl.widen(y.cpu()).reshape(B, N, -1), ref["Y"], w.dtype)
+    log(f"  Y (staged): {rep_y}")
+    assert rep_y.ok
+
+
+# ----------------------------------------------------------------------------------------------
+# small shapes: whole outputs
+
+HEADS = [  # (H, d_head, H_q, H_kv): g = 1, 2, 16, 2, 8, 3
+    (16, 64, 4, 4), (16, 64, 8, 4), (16, 64, 16, 1), (8, 32, 4, 2), (16, 32, 16, 2), (8, 32, 6, 2),
+]
+LENGTHS = [(1, False), (2, True), (17, False), (63, True), (64, False), (65, True), (127, False),
+           (255, True), (257, False), (1000, True)]
+
+
+def _small_cases():
+    cases = []
+    for dtype in ("bf16", "fp32"):
+        for i, (N, causal) in enumerate(LENGTHS):
+            H, dh, H_q, H_kv = HEADS[(i + (dtype == "fp32")) % len(HEADS)]
+            B = 3 if i % 3 == 0 else 1
+            cases.append(wl.Workload(f"small_{dtype}_N{N}_{'c' if causal else 'nc'}_g{H_q // H_kv}",
+                                     B=B, N=N, d_model=H * dh, H=H, H_q=H_q, H_kv=H_kv,
+                                     causal=causal, dtype=dtype, seed=500 + i))
+    return cases
+
+
+@pytest.mark.parametrize("w", _small_cases(), ids=lambda w: w.name)
+def test_small_shapes_match_oracle(dev, w):
+    full_check(w, dev)
+
+
+@pytest.mark.parametrize("H,dh,H_q,H_kv", HEADS, ids=lambda v: str(v))
+@pytest.mark.parametrize("dtype,causal", [("bf16", True), ("fp32", False)])
+def test_every_stage_matches_oracle(dev, H, dh, H_q, H_kv, dtype, causal):
+    w = wl.Workload(f"stages_{dtype}_{H_q}_{H_kv}_{dh}", B=2, N=333, d_model=H * dh, H=H, H_q=H_q,
+                    H_kv=H_kv, causal=causal, dtype=dtype, seed=77)
+    full_check(w, dev, stages=True)
+
+
+def test_tiny_fp32_workload(dev):
+    full_check(wl.TINY_SQA_FP32, dev, stages=True)
+
+
+def test_ssqa_1k_causal_workload_and_gqa_baseline(dev):
+    full_check(wl.SSQA_1K_CAUSAL, dev, stages=True)
+    full_check(wl.SSQA_1K_CAUSAL.baseline(), dev)
+
+
+# ----------------------------------------------------------------------------------------------
+# full sizes: sampled rows
+
+LONG = [wl.XSQA_32K, wl.SQA_131K_CAUSAL, wl.XSMQA_200K]
+
+
+@pytest.mark.parametrize("w", LONG + [x.baseline() for x in LONG], ids=lambda w: w.name)
+def test_long_workloads_on_sampled_rows(dev, w):
+    log(f"case {w.name}: B={w.B} N={w.N} H_q={w.H_q} H_kv={w.H_kv} causal={w.causal}")
+    host, d = device_inputs(w, dev)
+    y = run_forward(w, d)
+    torch.cuda.synchronize()
+    rows = sample_rows(w, n_random=64 if w.H_q > 8 else 96)
+    yg = wl.widen(y.reshape(-1, w.d_model)[torch.from_numpy(rows).to(dev)].cpu())
+    del d, y
+    o = oracle_inputs(host)
+    ref = oracle.sqa_forward_rows(o["X"], o["Wq"], o["Wk"], o["Wv"], o["Wo"], w.H_q, w.H_kv,
+                                  w.d_head, w.causal, bf16=True, rows=rows)["Y_rows"]
+    rep = compare(yg, ref, w.dtype)
+    log(f"  {rows.size} rows: {rep}")
+    assert rep.ok, f"{w.name}: {rep}"
+
+
+# ----------------------------------------------------------------------------------------------
+# determinism and edge cases
+
+def test_bitwise_deterministic_across_calls_and_streams(dev):
+    w = wl.Workload("determinism", B=2, N=777, d_model=1024, H=16, H_q=8, H_kv=2, causal=True,
+                    dtype="bf16", seed=5)
+    _, d = device_inputs(w, dev)
+    y1 = run_forward(w, d)
+    y2 = run_forward(w, d)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        y3 = run_forward(w, d)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(y1, y3)
+
+
+def test_single_token_returns_projected_value(dev):
+    """N = 1: softmax over one key is 1, so A = V and Y = V Wo per head."""
+    w = wl.Workload("one_token", B=4, N=1, d_model=512, H=8, H_q=4, H_kv=2, causal=False,
+                    dtype="fp32", seed=9)
+    host, d = device_inputs(w, dev)
+    y = run_forward(w, d)
+    o = oracle_inputs(host)
+    V = o["X"] @ o["Wv"]
+    A = np.concatenate([V[..., 0:64], V[..., 0:64], V[..., 64:128], V[..., 64:128]], axis=-1)
+    rep = compare(wl.widen(y.cpu()), A @ o["Wo"], "fp32")
+    log(f"  {rep}")
+    assert rep.ok
+
+
+def test_empty_batch_is_a_no_op(dev):
+    x = torch.empty((0, 5, 256), dtype=torch.bfloat16, device=dev)
+    W = {k: torch.zeros(s, dtype=torch.bfloat16, device=dev)
+         for k, s in (("q", (256, 128)), ("k", (256, 64)), ("v", (256, 64)), ("o", (128, 256)))}
+    y = sqa.forward(x, W["q"], W["k"], W["v"], W["o"], H=8, H_q=4, H_kv=2)
+    assert y.shape == (0, 5, 256)
