@@ -1,0 +1,301 @@
+#!/usr/bin/env python3
+"""Benchmark of the SQA forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one whole SQA forward (query/key/value projection, attention core,
+output projection) through the C ABI (sqa_forward), on synthetic inputs
+already resident in HBM. The headline workload is standard SQA at 131072
+tokens, causal (H=16, H_q=8, H_kv=4, d_head=64, bf16). This is the middle of the
+32k-200k range that the SQA paper's abstract benchmarks. The other long
+workloads and their equally shaped MHA/GQA/MQA baselines are timed as well and
+reported under "variants".
+
+Prints ONE JSON line. FLOPs use the closed form: attention core
+4*B*H_q*N^2*d_head (halved when causal) plus the projections
+2*B*N*d_model*d_head*(2*H_q + 2*H_kv).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as wl  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X published dense bf16 MFMA peak
+PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X published fp32 matrix peak
+HBM_PEAK_GBS = 8000.0
+HEADLINE = wl.SQA_131K_CAUSAL.name
+ATTN_SRC = os.path.join(ROOT, "sparse_query_attention_amd", "csrc", "sqa_attention.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_hbm_traffic_{}.txt")
+
+
+def core_flops(w: wl.Workload) -> float:
+    f = 4.0 * w.B * w.H_q * float(w.N) ** 2 * w.d_head
+    return f / 2 if w.causal else f
+
+
+def proj_flops(w: wl.Workload) -> float:
+    return 2.0 * w.B * w.N * w.d_model * w.d_head * (2 * w.H_q + 2 * w.H_kv)
+
+
+def attention_bytes(w: wl.Workload) -> int:
+    """Algorithmic HBM bytes of one attention launch: read Q, K, V once, write A once."""
+    es = 2 if w.dtype == "bf16" else 4
+    return es * w.B * w.N * w.d_head * (2 * w.H_q + 2 * w.H_kv)
+
+
+def proj_bytes(w: wl.Workload):
+    """Algorithmic HBM bytes of the two projection launches: (read X and the
+    three weights, write Q/K/V) and (read A and Wo, write Y)."""
+    es = 2 if w.dtype == "bf16" else 4
+    M, D, d = w.B * w.N, w.d_model, w.d_head
+    qkv = es * (M * D + D * d * (w.H_q + 2 * w.H_kv) + M * d * (w.H_q + 2 * w.H_kv))
+    out = es * (M * w.H_q * d + w.H_q * d * D + M * D)
+    return qkv, out
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(w: wl.Workload):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    path = TRAFFIC_FILE.format(w.name)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+class Timer:
+    """HIP events recorded on the stream the library launches on."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+
+    def event(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record(self.stream)
+        return e
+
+
+def run_workload(w: wl.Workload, steps: int, warmup: int, torch, sqa, dev, stage_timing: bool):
+    host = wl.to_device_dtype(wl.draw(w), w.dtype)
+    d = {k: v.to(dev) for k, v in host.items()}
+    del host
+    out = torch.empty_like(d["X"])
+    stream = torch.cuda.current_stream(dev)
+    tm = Timer(torch, stream)
+
+    def step():
+        sqa.forward(d["X"], d["Wq"], d["Wk"], d["Wv"], d["Wo"], H=w.H, H_q=w.H_q, H_kv=w.H_kv,
+                    causal=w.causal, out=out)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0 = tm.event()
+    for _ in range(steps):
+        step()
+    e1 = tm.event()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    ms = e0.elapsed_time(e1) / steps
+    res = {"ms_per_step": ms, "wall_ms_per_step": wall_ms}
+
+    if stage_timing:
+        # The same three kernels through the per-step entry points, with events
+        # between them on the launch stream: per-kernel average durations.
+        q, k, vt = sqa.qkv_projection(d["X"], d["Wq"], d["Wk"], d["Wv"], H=w.H, H_q=w.H_q,
+                                      H_kv=w.H_kv)
+        a = sqa.attention(q, k, vt, N=w.N, causal=w.causal)
+        y = sqa.output_projection(a, d["Wo"])
+        torch.cuda.synchronize()
+        tot = {"qkv_projection": 0.0, "attention": 0.0, "output_projection": 0.0}
+        for _ in range(steps):
+            ev = [tm.event()]
+            sqa.qkv_projection(d["X"], d["Wq"], d["Wk"], d["Wv"], H=w.H, H_q=w.H_q, H_kv=w.H_kv,
+                               q=q, k=k, vt=vt)
+            ev.append(tm.event())
+            sqa.attention(q, k, vt, N=w.N, causal=w.causal, a=a)
+            ev.append(tm.event())
+            sqa.output_projection(a, d["Wo"], out=y)
+            ev.append(tm.event())
+            torch.cuda.synchronize()
+            for i, name in enumerate(tot):
+                tot[name] += ev[i].elapsed_time(ev[i + 1])
+        res["kernel_ms"] = {k: v / steps for k, v in tot.items()}
+        del q, k, vt, a, y
+    del d, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(w: wl.Workload, rows_sample: int = 24576):
+    """The float64 oracle on a bounded sample: every key/value projection of the
+    workload, plus the whole forward of `rows_sample` evenly spaced query rows.
+    The time is extrapolated linearly to all B*N rows."""
+    import numpy as np
+    import oracle
+    host = wl.to_device_dtype(wl.draw(w), w.dtype)
+    o = {k: wl.widen(v) for k, v in host.items()}
+    del host
+    cores = len(os.sched_getaffinity(0))
+    rows = ((np.arange(rows_sample) + 0.5) * (w.B * w.N) / rows_sample).astype(np.int64)
+    cache = {}
+    t0 = time.perf_counter()
+    oracle.sqa_forward_rows(o["X"], o["Wq"], o["Wk"], o["Wv"], o["Wo"], w.H_q, w.H_kv, w.d_head,
+                            w.causal, bf16=(w.dtype == "bf16"), rows=rows[:1], kv_cache=cache,
+                            workers=cores)
+    t_kv = time.perf_counter() - t0          # key/value projection of every token (+ one row)
+    t1 = time.perf_counter()
+    oracle.sqa_forward_rows(o["X"], o["Wq"], o["Wk"], o["Wv"], o["Wo"], w.H_q, w.H_kv, w.d_head,
+                            w.causal, bf16=(w.dtype == "bf16"), rows=rows, kv_cache=cache,
+                            workers=cores)
+    t_rows = time.perf_counter() - t1
+    full_s = t_kv + t_rows * (w.B * w.N) / rows_sample
+    return {"value": (w.B * w.N) / full_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": (f"float64 oracle: key/value projection of all {w.B * w.N} tokens "
+                       f"({t_kv:.1f} s) + full forward of {rows_sample} evenly spaced query rows "
+                       f"({t_rows:.1f} s), extrapolated linearly to {w.B * w.N} rows "
+                       f"= {full_s:.0f} s per step"),
+            "seconds_measured": round(t_kv + t_rows, 2)}
+
+
+def calibrate_copy(torch, dev, nbytes: int = 1 << 30, reps: int = 3):
+    """A plain device copy of known size, for scaling rocprofv3 FETCH_SIZE and
+    WRITE_SIZE readings to bytes."""
+    x = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(wl.WORKLOADS))
+    ap.add_argument("--no-variants", action="store_true", help="time only the headline workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=24576)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 1 GiB device copy (rocprofv3 counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this SQA forward path has no multi-GPU mode "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_query_attention_amd as sqa
+    sqa._lib.load()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        calibrate_copy(torch, dev)
+        return
+
+    w = wl.WORKLOADS[args.workload]
+    main_res = run_workload(w, args.steps, args.warmup, torch, sqa, dev, stage_timing=True)
+    ms = main_res["ms_per_step"]
+    tokens_s = w.tokens / (ms / 1e3)
+    cf, pf = core_flops(w), proj_flops(w)
+    attn_ms = main_res["kernel_ms"]["attention"]
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS
+    achieved = cf / (attn_ms / 1e3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": measured_traffic(w),
+                "kernel": "attn_kernel (attention core)",
+                "algorithmic_flop_per_launch": cf, "algorithmic_bytes_per_launch": attention_bytes(w),
+                "avg_launch_ms": round(attn_ms, 4)}
+
+    variants = {}
+    if not args.no_variants:
+        vsteps, vwarm = max(3, args.steps // 2), max(1, args.warmup)
+        for v in (wl.XSQA_32K, wl.XSQA_32K.baseline(), wl.SQA_131K_CAUSAL.baseline(),
+                  wl.XSMQA_200K, wl.XSMQA_200K.baseline()):
+            if v.name == w.name:
+                continue
+            r = run_workload(v, vsteps, vwarm, torch, sqa, dev, stage_timing=True)
+            am = r["kernel_ms"]["attention"]
+            variants[v.name] = {
+                "H_q": v.H_q, "H_kv": v.H_kv, "N": v.N, "causal": v.causal,
+                "ms_per_step": round(r["ms_per_step"], 4),
+                "tokens_per_s": round(v.tokens / (r["ms_per_step"] / 1e3), 1),
+                "attention_ms": round(am, 4),
+                "attention_tflops": round(core_flops(v) / (am / 1e3) / 1e12, 2),
+                "total_tflops": round((core_flops(v) + proj_flops(v)) / (r["ms_per_step"] / 1e3) / 1e12, 2)}
+        for v in (wl.XSQA_32K, wl.SQA_131K_CAUSAL, wl.XSMQA_200K):
+            b = v.baseline()
+            sv = variants.get(v.name) or ({"attention_ms": attn_ms, "ms_per_step": ms}
+                                          if v.name == w.name else None)
+            sb = variants.get(b.name)
+            if sv and sb:
+                key = v.name + "_speedup_vs_baseline"
+                variants[key] = {"attention": round(sb["attention_ms"] / sv["attention_ms"], 3),
+                                 "whole_forward": round(sb["ms_per_step"] / sv["ms_per_step"], 3),
+                                 "ideal_H_over_H_q": b.H_q / v.H_q}
+
+    line = {
+        "metric": "SQA fwd tokens/s + TFLOP/s (% bf16 MFMA peak) at N=32k-200k, 1 GPU",
+        "value": round(tokens_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) tokens, N(0,1/d_model) weights)",
+        "config": {"workload": w.name, "B": w.B, "N": w.N, "d_model": w.d_model, "H": w.H,
+                   "H_q": w.H_q, "H_kv": w.H_kv, "d_head": w.d_head, "causal": w.causal,
+                   "global_batch": w.B, "seq_len": w.N, "parallelism": "single GPU"},
+        "tflops_total": round((cf + pf) / (ms / 1e3) / 1e12, 2),
+        "tflops_attention": round(achieved, 2),
+        "pct_bf16_peak_attention": round(100 * achieved / peak, 2),
+        "kernel_ms": {k: round(v, 4) for k, v in main_res["kernel_ms"].items()},
+        "projection_gbs": {
+            "qkv_projection": round(proj_bytes(w)[0] / (main_res["kernel_ms"]["qkv_projection"] / 1e3) / 1e9, 1),
+            "output_projection": round(proj_bytes(w)[1] / (main_res["kernel_ms"]["output_projection"] / 1e3) / 1e9, 1)},
+        "roofline": roofline,
+        "variants": variants,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

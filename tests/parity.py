@@ -5,7 +5,13 @@ workload's dtype.
 Tolerances:
   fp32: max |Y - Y_ref| <= 1e-4.
   bf16: ||Y - Y_ref|| / ||Y_ref|| <= 1e-2 over all compared elements, and
-        |Y - Y_ref| <= 2e-2 * max(1, |Y_ref|) elementwise.
+        |Y[r, c] - Y_ref[r, c]| <= 2e-2 * max(1, max_c' |Y_ref[r, c']|)
+        for every output row r.
+The elementwise bound scales with the row, not the element. Y[r, c] is a dot
+product of the attention row A[r, :] with a column of Wo. Rounding A to bf16
+(relative 2^-9 per element) therefore moves every element of the row by an
+amount proportional to the row's magnitude, whatever that element's own
+value is.
 Y_ref is the float64 oracle with bf16 rounding at the Q/K/V/A/Y boundaries
 for bf16 runs, and no rounding for fp32 runs.
 """
@@ -24,30 +30,40 @@ import workloads as wl
 class Report:
     max_abs: float
     rel_l2: float
-    worst_scaled: float      # max |err| / max(1, |ref|)
+    worst_scaled: float      # max over rows of max_c |err[r, c]| / max(1, max_c |ref[r, c]|)
+    worst_row_rel: float     # max over rows of ||err[r]|| / ||ref[r]||
     ok: bool
 
     def __str__(self):
         return (f"max_abs={self.max_abs:.3e} rel_l2={self.rel_l2:.3e} "
-                f"worst_scaled={self.worst_scaled:.3e} {'OK' if self.ok else 'FAIL'}")
+                f"worst_scaled={self.worst_scaled:.3e} worst_row_rel={self.worst_row_rel:.3e} "
+                f"{'OK' if self.ok else 'FAIL'}")
 
 
 def compare(got: np.ndarray, ref: np.ndarray, dtype: str) -> Report:
+    """Compare outputs whose last axis is one output row (d_model wide)."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (got.shape, ref.shape)
     if not np.isfinite(got).all():
-        return Report(float("inf"), float("inf"), float("inf"), False)
-    err = np.abs(got - ref)
-    max_abs = float(err.max()) if err.size else 0.0
-    nref = float(np.linalg.norm(ref))
-    rel = float(np.linalg.norm(got - ref) / nref) if nref > 0 else float(np.linalg.norm(got - ref))
-    scaled = float((err / np.maximum(1.0, np.abs(ref))).max()) if err.size else 0.0
+        return Report(float("inf"), float("inf"), float("inf"), float("inf"), False)
+    if got.size == 0:
+        return Report(0.0, 0.0, 0.0, 0.0, True)
+    g2 = got.reshape(-1, got.shape[-1])
+    r2 = ref.reshape(-1, ref.shape[-1])
+    err = np.abs(g2 - r2)
+    max_abs = float(err.max())
+    nref = float(np.linalg.norm(r2))
+    rel = float(np.linalg.norm(g2 - r2) / nref) if nref > 0 else float(np.linalg.norm(g2 - r2))
+    row_scale = np.maximum(1.0, np.abs(r2).max(axis=1))
+    scaled = float((err.max(axis=1) / row_scale).max())
+    rn = np.linalg.norm(r2, axis=1)
+    row_rel = float((np.linalg.norm(g2 - r2, axis=1) / np.where(rn > 0, rn, 1.0)).max())
     if dtype == "fp32":
         ok = max_abs <= 1e-4
     else:
         ok = rel <= 1e-2 and scaled <= 2e-2
-    return Report(max_abs, rel, scaled, ok)
+    return Report(max_abs, rel, scaled, row_rel, ok)
 
 
 def log(msg: str) -> None:

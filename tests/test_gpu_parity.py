@@ -46,11 +46,11 @@ def full_check(w, dev, stages=False):
     log(f"  Y: {rep}")
     assert rep.ok, f"{w.name}: {rep}"
     if stages:
-        check_stages(w, d, ref)
+        check_stages(w, d, ref, o)
     return y
 
 
-def check_stages(w, d, ref):
+def check_stages(w, d, ref, o):
     """Each C-ABI step against the oracle's intermediate of the same name."""
     q, k, vt = sqa.qkv_projection(d["X"], d["Wq"], d["Wk"], d["Wv"], H=w.H, H_q=w.H_q, H_kv=w.H_kv)
     a = sqa.attention(q, k, vt, N=w.N, causal=w.causal)
@@ -66,19 +66,30 @@ def check_stages(w, d, ref):
     Q = ref["Q"].reshape(B, N, w.H_q, dh).transpose(0, 2, 1, 3)
     K = ref["K"].reshape(B, N, w.H_kv, dh).transpose(0, 2, 1, 3)
     V = ref["V"].reshape(B, N, w.H_kv, dh).transpose(0, 2, 3, 1)
-    # projections: fp32 accumulation rounded once; bf16 may differ by one
-    # rounding of a near-tie, so allow one bf16 ulp.
-    for name, got, want in (("Q", qh[:, :, :N], Q), ("K", kh[:, :, :N], K), ("V^T", vh[..., :N], V)):
+    # Projections: the GPU sums K = d_model products in fp32 and rounds once.
+    # It may miss the exactly rounded value by one bf16 ulp plus the fp32
+    # summation error bound K * 2^-24 * sum_k |x_k w_k|; the latter dominates
+    # for results near zero that come from cancelling terms.
+    def heads(M, n, t):
+        return M.reshape(B, N, n, dh).transpose(*t)
+    absx = np.abs(o["X"])
+    bounds = {nm: w.d_model * 2.0 ** -24 * (absx @ np.abs(o[wn]))
+              for nm, wn in (("Q", "Wq"), ("K", "Wk"), ("V^T", "Wv"))}
+    for name, got, want, n, t in (("Q", qh[:, :, :N], Q, w.H_q, (0, 2, 1, 3)),
+                                  ("K", kh[:, :, :N], K, w.H_kv, (0, 2, 1, 3)),
+                                  ("V^T", vh[..., :N], V, w.H_kv, (0, 2, 3, 1))):
+        bound = heads(bounds[name], n, t)
+        diff = np.abs(got - want)
         if w.dtype == "bf16":
             ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(want), 1e-30))) - 7)
-            bad = np.abs(got - want) > ulp * 1.0001
-            exact = float((got == want).mean())
-            log(f"  {name}: exact={exact:.5f} beyond_1ulp={int(bad.sum())}")
+            bad = diff > ulp * 1.0001 + bound
+            exact = float((diff == 0).mean())
+            log(f"  {name}: exact={exact:.5f} beyond_bound={int(bad.sum())}")
             assert not bad.any() and exact > 0.99, name
         else:
-            err = float(np.abs(got - want).max())
-            log(f"  {name}: max_abs={err:.3e}")
-            assert err <= 1e-4, name
+            bad = diff > 2.0 ** -24 * np.abs(want) + bound
+            log(f"  {name}: max_abs={float(diff.max()):.3e} beyond_bound={int(bad.sum())}")
+            assert not bad.any(), name
     rep_a = compare(wl.widen(a.cpu()).reshape(B, N, -1), ref["A"], w.dtype)
     log(f"  A: {rep_a}")
     assert rep_a.ok
