@@ -38,15 +38,18 @@
 namespace sqa {
 namespace {
 
-constexpr int KT = 64;       // keys per LDS tile (two 32-key MFMA blocks)
+constexpr int KT = 64;       // keys per LDS tile (two 32-key blocks)
+constexpr int NBUF = 4;      // LDS tile ring: one in use, one visible next, two in flight
 constexpr int WAVES = 4;
 constexpr int QB = 2;        // 32-query MFMA column blocks per wave
 constexpr int QW = 32 * QB;  // query rows per wave
 constexpr int THREADS = 64 * WAVES;
-// Lazy rescaling: exponentials are taken against a reference max that may lag
-// the true running max by up to 2^TAU_LOG2 in the exp2 domain (so p <= 256);
-// the O accumulators are rescaled only when a row's max outgrows that margin.
-constexpr float TAU_LOG2 = 8.0f;
+// Exponentials are taken against a reference max m_ref that may lag the true
+// running max. A lane's block sum above SUM_LIMIT (or inf/NaN) means the
+// reference is too low for that block; only then is the block's exact max
+// computed, O and l rescaled and the block's exponentials redone.
+constexpr float SUM_LIMIT = 256.0f;
+constexpr float M_INIT = -1e30f;   // finite, so masked scores give exp2(-inf) = 0
 
 struct AttnParams {
   const void* q; const void* k; const void* vt; void* a;
@@ -54,39 +57,44 @@ struct AttnParams {
   float c;  // log2(e) / sqrt(d_head)
 };
 
-template <typename T, int D> struct AttnCfg {
-  static constexpr int EPC = 16 / sizeof(T);
-  static constexpr int KLD = D + EPC;         // LDS K row (one key), 16-byte pad
-  static constexpr int VLD = KT + EPC;        // LDS V^T row (one head dim), 16-byte pad
-  static constexpr int K_PER = KT * D / EPC / THREADS;
-  static constexpr int V_PER = D * KT / EPC / THREADS;
-  static_assert(K_PER * THREADS * EPC == KT * D, "K tile split");
-  static_assert(V_PER * THREADS * EPC == KT * D, "V tile split");
-};
+// XOR swizzle of 16-byte chunks within an LDS row of CPR chunks. It spreads
+// the rows that one ds_read_b128 touches over distinct banks.
+template <int CPR> __device__ inline int swz(int r);
+template <> __device__ inline int swz<16>(int r) { return r & 15; }
+template <> __device__ inline int swz<8>(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+template <> __device__ inline int swz<4>(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
 
 // In-tile key index <-> LDS row: swap bits 2 and 3 (an involution).
 __device__ inline int swap23(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
 
 __device__ inline float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
-// Row sum of 8 bf16 probabilities with two v_dot2_f32_bf16 chains.
-__device__ inline float sum8(bf16x8 p, float acc) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
-  float a0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p[0], p[1]}, one, acc, false);
-  float a1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p[2], p[3]}, one, 0.f, false);
-  a0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p[4], p[5]}, one, a0, false);
-  a1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p[6], p[7]}, one, a1, false);
-  return a0 + a1;
+// Wait until at most N of this wave's vector-memory operations are outstanding
+// (N < 16). The encoding leaves the other counters unconstrained.
+template <int N> __device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(N | (0x7 << 4) | (0xF << 8));
 }
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// Exponentiated scores of one 32-key block, as the PV MFMA consumes them.
+template <typename T> struct PBlock;
+template <> struct PBlock<bf16> { bf16x8 v[QB][2]; };
+template <> struct PBlock<float> { f32x16 v[QB]; };
 
 template <typename T, int D>
 __global__ __launch_bounds__(THREADS, 2) void attn_kernel(AttnParams p) {
-  using Cfg = AttnCfg<T, D>;
   using MF = Mfma<T>;
   using Frag = typename MF::Frag;
-  __shared__ __align__(16) T Ks[2][KT * Cfg::KLD];
-  __shared__ __align__(16) T Vs[2][D * Cfg::VLD];
+  constexpr int EPC = 16 / sizeof(T);          // elements per 16-byte chunk
+  constexpr int KCPR = D / EPC, VCPR = KT / EPC;
+  constexpr int K_ELEMS = KT * D;              // elements of one tile's K (and of its V^T)
+  constexpr int TILE = 2 * K_ELEMS;
+  constexpr int INS = K_ELEMS / (64 * EPC) / WAVES;  // 1 KB direct loads per wave, K or V^T
+  constexpr int VM_PER_TILE = 2 * INS;
+  static_assert(INS * WAVES * 64 * EPC == K_ELEMS, "tile split");
+  __shared__ __align__(16) T smem[NBUF * TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, grp = lane >> 5;
@@ -116,38 +124,53 @@ __global__ __launch_bounds__(THREADS, 2) void attn_kernel(AttnParams p) {
       qf[qb][s] = *reinterpret_cast<const Frag*>(Qh + (int64_t)(qw + 32 * qb + col) * D +
                                                  s * MF::KS + grp * MF::E);
 
+  // All waves of the workgroup walk the same key range; rows past a wave's own
+  // causal horizon are masked to zero weight.
   const int kv_len = p.causal ? min(p.N, q0 + p.q_per_wg) : p.N;
+  const int nblk = (kv_len + 31) / 32;
   const int n_tiles = (kv_len + KT - 1) / KT;
 
-  Chunk kreg[Cfg::K_PER], vreg[Cfg::V_PER];
-  auto load = [&](int kt) {
-    const int k0 = kt * KT;
+  // Direct global->LDS loads of tile t into ring slot t % NBUF. Lane L of a
+  // load lands at 16*L bytes past the load's LDS base, so the source address
+  // chosen per lane realises the key permutation and the chunk swizzle.
+  auto issue = [&](int t) {
+    if (t >= n_tiles) return;
+    T* kb = smem + (t % NBUF) * TILE;
+    T* vb = kb + K_ELEMS;
+    const int k0 = t * KT;
 #pragma unroll
-    for (int i = 0; i < Cfg::K_PER; ++i) {
-      const int c = tid + i * THREADS;
-      const int key = c / (D / Cfg::EPC), cc = c % (D / Cfg::EPC);
-      kreg[i] = *reinterpret_cast<const Chunk*>(Kh + (int64_t)(k0 + key) * D + cc * Cfg::EPC);
+    for (int i = 0; i < INS; ++i) {
+      const int ins = wave * INS + i;
+      const int pos = ins * 64 + lane;
+      const int r = pos / KCPR, slot = pos % KCPR;
+      const T* src = Kh + (int64_t)(k0 + swap23(r)) * D + (slot ^ swz<KCPR>(r)) * EPC;
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)(kb + ins * 64 * EPC), 16, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < Cfg::V_PER; ++i) {
-      const int c = tid + i * THREADS;
-      const int row = c / (KT / Cfg::EPC), cc = c % (KT / Cfg::EPC);
-      vreg[i] = *reinterpret_cast<const Chunk*>(Vh + (int64_t)row * p.Np + k0 + cc * Cfg::EPC);
+    for (int i = 0; i < INS; ++i) {
+      const int ins = wave * INS + i;
+      const int pos = ins * 64 + lane;
+      const int r = pos / VCPR, slot = pos % VCPR;
+      const T* src = Vh + (int64_t)r * p.Np + k0 + (slot ^ swz<VCPR>(r)) * EPC;
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)(vb + ins * 64 * EPC), 16, 0, 0);
     }
   };
-  auto stash = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < Cfg::K_PER; ++i) {
-      const int c = tid + i * THREADS;
-      const int key = c / (D / Cfg::EPC), cc = c % (D / Cfg::EPC);
-      *reinterpret_cast<Chunk*>(&Ks[buf][swap23(key) * Cfg::KLD + cc * Cfg::EPC]) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < Cfg::V_PER; ++i) {
-      const int c = tid + i * THREADS;
-      const int row = c / (KT / Cfg::EPC), cc = c % (KT / Cfg::EPC);
-      *reinterpret_cast<Chunk*>(&Vs[buf][row * Cfg::VLD + cc * Cfg::EPC]) = vreg[i];
-    }
+
+  // K fragment (A operand of S^T) of global 32-key block j, k-step st.
+  auto kfrag = [&](int j, int st) -> Frag {
+    const int r = (j & 1) * 32 + col;
+    const int e = st * MF::KS + grp * MF::E;
+    const int off = ((j >> 1) % NBUF) * TILE + r * D + (((e / EPC) ^ swz<KCPR>(r)) * EPC) + e % EPC;
+    return *reinterpret_cast<const Frag*>(&smem[off]);
+  };
+  // V^T fragment (A operand of O^T) of block j: head dims 32*nb + col,
+  // keys kk.. of the block (8 consecutive for bf16, one for fp32).
+  auto vfrag = [&](int j, int nb, int kk) -> Frag {
+    const int r = nb * 32 + col;
+    const int key = (j & 1) * 32 + kk;
+    const int off = ((j >> 1) % NBUF) * TILE + K_ELEMS + r * KT +
+                    (((key / EPC) ^ swz<VCPR>(r)) * EPC) + key % EPC;
+    return *reinterpret_cast<const Frag*>(&smem[off]);
   };
 
   f32x16 o[QB][D / 32];
@@ -157,25 +180,83 @@ __global__ __launch_bounds__(THREADS, 2) void attn_kernel(AttnParams p) {
     for (int nb = 0; nb < D / 32; ++nb) o[qb][nb] = f32x16{};
   float m_ref[QB], l_run[QB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) { m_ref[qb] = -INFINITY; l_run[qb] = 0.f; }
+  for (int qb = 0; qb < QB; ++qb) { m_ref[qb] = M_INIT; l_run[qb] = 0.f; }
   const float c = p.c;
 
-  // S^T of one 32-key block for both query blocks. Register r of lane group
-  // grp holds key 32*kb + 16*(r/8) + 8*grp + r%8 (after the LDS row swap).
-  auto scores = [&](const T* ks, f32x16 (&s)[QB]) {
+  // S^T of block j for both query blocks. Register r of lane group grp holds
+  // key 32*j + 16*(r/8) + 8*grp + r%8 (after the LDS row swap).
+  auto qk = [&](int j, f32x16 (&s)[QB]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) s[qb] = f32x16{};
 #pragma unroll
     for (int st = 0; st < D / MF::KS; ++st) {
-      const Frag a = *reinterpret_cast<const Frag*>(&ks[col * Cfg::KLD + st * MF::KS + grp * MF::E]);
+      const Frag a = kfrag(j, st);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) s[qb] = MF::run(a, qf[qb][st], s[qb]);
     }
   };
 
-  // Online softmax of one 32-key block (first key k0b) followed by
-  // O^T += V^T P^T. vs points at the block's first key column of V^T.
-  auto softmax_pv = [&](f32x16 (&s)[QB], int k0b, const T* vs) {
+  // O^T += V^T P^T for block j.
+  auto pv = [&](int j, const PBlock<T>& P) {
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb) {
+          const Frag a = vfrag(j, nb, half * 16 + grp * 8);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) o[qb][nb] = MF::run(a, P.v[qb][half], o[qb][nb]);
+        }
+    } else {
+#pragma unroll
+      for (int st = 0; st < 16; ++st)
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb) {
+          const Frag a = vfrag(j, nb, 16 * (st >> 3) + 8 * grp + (st & 7));
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) o[qb][nb] = MF::run(a, P.v[qb][st], o[qb][nb]);
+        }
+    }
+  };
+
+  // p = exp2(s*c - m_ref) into P, and each lane's block sums.
+  auto exponentiate = [&](const f32x16 (&s)[QB], PBlock<T>& P, float (&bsum)[QB]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float mb = m_ref[qb];
+      if constexpr (sizeof(T) == 2) {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+        float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            P.v[qb][half][e] = from_f32<T>(__builtin_amdgcn_exp2f(fmaf(s[qb][8 * half + e], c, -mb)));
+#pragma unroll
+          for (int e = 0; e < 8; e += 4) {
+            acc0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{P.v[qb][half][e], P.v[qb][half][e + 1]}, one, acc0, false);
+            acc1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{P.v[qb][half][e + 2], P.v[qb][half][e + 3]}, one, acc1, false);
+          }
+        }
+        bsum[qb] = acc0 + acc1;
+      } else {
+        float acc = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          P.v[qb][r] = __builtin_amdgcn_exp2f(fmaf(s[qb][r], c, -mb));
+          acc += P.v[qb][r];
+        }
+        bsum[qb] = acc;
+      }
+    }
+  };
+
+  // Online softmax of block j: mask if the block crosses the diagonal or the
+  // sequence end, exponentiate against m_ref, and fall back to an exact
+  // rescale when a block sum shows m_ref was too low.
+  auto softmax = [&](f32x16 (&s)[QB], int j, PBlock<T>& P) {
+    const int k0b = j * 32;
     if (k0b + 32 > p.N || (p.causal && k0b + 31 > qw)) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
@@ -187,93 +268,62 @@ __global__ __launch_bounds__(THREADS, 2) void attn_kernel(AttnParams p) {
         }
       }
     }
-    float mx[QB];
-    bool grow = false;
+    float bsum[QB];
+    exponentiate(s, P, bsum);
+    bool redo = false;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float m = max3(s[qb][0], s[qb][1], s[qb][2]);
-#pragma unroll
-      for (int r = 3; r < 15; r += 2) m = max3(m, s[qb][r], s[qb][r + 1]);
-      m = fmaxf(m, s[qb][15]);
-      m = fmaxf(m, __shfl_xor(m, 32)) * c;
-      mx[qb] = m;
-      grow |= m > m_ref[qb] + TAU_LOG2;
-    }
-    if (__any(grow)) {
+    for (int qb = 0; qb < QB; ++qb) redo |= !(bsum[qb] <= SUM_LIMIT);
+    if (__any(redo)) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const float m_new = fmaxf(m_ref[qb], mx[qb]);
+        float m = max3(s[qb][0], s[qb][1], s[qb][2]);
+#pragma unroll
+        for (int r = 3; r < 15; r += 2) m = max3(m, s[qb][r], s[qb][r + 1]);
+        m = fmaxf(m, s[qb][15]);
+        m = fmaxf(m, __shfl_xor(m, 32));
+        const float m_new = fmaxf(m_ref[qb], m * c);
         const float alpha = __builtin_amdgcn_exp2f(m_ref[qb] - m_new);
         l_run[qb] *= alpha;
 #pragma unroll
         for (int nb = 0; nb < D / 32; ++nb) o[qb][nb] *= alpha;
         m_ref[qb] = m_new;
       }
+      exponentiate(s, P, bsum);
     }
-    if constexpr (sizeof(T) == 2) {
-      Frag pf[QB][2];
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        // a row with no visible key yet keeps m_ref = -inf; use 0 so that its
-        // masked scores give exp2(-inf) = 0 rather than NaN
-        const float mb = m_ref[qb] == -INFINITY ? 0.f : m_ref[qb];
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            pf[qb][half][e] = from_f32<T>(__builtin_amdgcn_exp2f(fmaf(s[qb][8 * half + e], c, -mb)));
-          l_run[qb] = sum8(pf[qb][half], l_run[qb]);
-        }
-      }
-#pragma unroll
-      for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int nb = 0; nb < D / 32; ++nb) {
-          const Frag a = *reinterpret_cast<const Frag*>(
-              &vs[(nb * 32 + col) * Cfg::VLD + half * 16 + grp * 8]);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) o[qb][nb] = MF::run(a, pf[qb][half], o[qb][nb]);
-        }
-    } else {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const float mb = m_ref[qb] == -INFINITY ? 0.f : m_ref[qb];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s[qb][r] = __builtin_amdgcn_exp2f(fmaf(s[qb][r], c, -mb));
-          l_run[qb] += s[qb][r];
-        }
-      }
-#pragma unroll
-      for (int st = 0; st < 16; ++st)
-#pragma unroll
-        for (int nb = 0; nb < D / 32; ++nb) {
-          const Frag a = *reinterpret_cast<const Frag*>(
-              &vs[(nb * 32 + col) * Cfg::VLD + 16 * (st >> 3) + 8 * grp + (st & 7)]);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) o[qb][nb] = MF::run(a, s[qb][st], o[qb][nb]);
-        }
-    }
+    for (int qb = 0; qb < QB; ++qb) l_run[qb] += bsum[qb];
   };
 
-  load(0);
-  stash(0);
+  // Prologue: tiles 0..2 in flight, tile 0 visible, S of block 0.
+  issue(0);
+  issue(1);
+  issue(2);
+  wait_vmcnt<0>();
   __syncthreads();
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < n_tiles) load(kt + 1);
-    const int k0 = kt * KT;
-    // a 32-key block is skipped by a wave whose last query precedes its first key
-    const bool act0 = !p.causal || k0 <= qw + QW - 1;
-    const bool act1 = !p.causal || k0 + 32 <= qw + QW - 1;
-    f32x16 s0[QB], s1[QB];
-    if (act0) scores(&Ks[buf][0], s0);
-    if (act1) scores(&Ks[buf][32 * Cfg::KLD], s1);
-    if (act0) softmax_pv(s0, k0, &Vs[buf][0]);
-    if (act1) softmax_pv(s1, k0 + 32, &Vs[buf][32]);
-    if (kt + 1 < n_tiles) stash(buf ^ 1);
-    __syncthreads();
+
+  f32x16 sA[QB], sB[QB];
+  PBlock<T> pA, pB;
+  qk(0, sA);
+  // Block pipeline: while block j's softmax runs on the VALU, the MFMAs of
+  // S(j+1) = K Q^T and of O += V^T P(j-1) are independent of it. PV(j-1) is
+  // issued first: a rescale inside softmax(j) must see O including block j-1,
+  // whose P used the previous reference max.
+  for (int j = 0; j < nblk; j += 2) {
+    if (j + 1 < nblk) qk(j + 1, sB);
+    if (j > 0) pv(j - 1, pB);
+    softmax(sA, j, pA);
+    if (j + 1 < nblk) {
+      // Odd block 2t+1: tile t+1 must be visible, tile t-1 is no longer read.
+      const int t = j >> 1;
+      if (t + 2 < n_tiles) wait_vmcnt<VM_PER_TILE>(); else wait_vmcnt<0>();
+      __syncthreads();
+      issue(t + 3);
+      if (j + 2 < nblk) qk(j + 2, sA);
+      pv(j, pA);
+      softmax(sB, j + 1, pB);
+    }
   }
+  if (nblk & 1) pv(nblk - 1, pA); else pv(nblk - 1, pB);
 
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
