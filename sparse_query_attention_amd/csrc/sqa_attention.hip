@@ -32,6 +32,8 @@
 //    heaviest query tiles are dispatched first.
 #include <math.h>
 
+#include <type_traits>
+
 #include "sqa_device.h"
 #include "sqa_internal.h"
 
@@ -77,11 +79,6 @@ template <int N> __device__ inline void wait_vmcnt() {
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
-
-// Exponentiated scores of one 32-key block, as the PV MFMA consumes them.
-template <typename T> struct PBlock;
-template <> struct PBlock<bf16> { bf16x8 v[QB][2]; };
-template <> struct PBlock<float> { f32x16 v[QB]; };
 
 template <typename T, int D>
 __global__ __launch_bounds__(THREADS, 2) void attn_kernel(AttnParams p) {
@@ -196,8 +193,21 @@ __global__ __launch_bounds__(THREADS, 2) void attn_kernel(AttnParams p) {
     }
   };
 
-  // O^T += V^T P^T for block j.
-  auto pv = [&](int j, const PBlock<T>& P) {
+  // After softmax, a block's probabilities live in its own S registers: bf16
+  // pairs packed into the first 8 fp32 slots of each query block (fp32 runs
+  // keep all 16 values). PV reads them there, before QK of a later block
+  // overwrites the registers.
+  auto pfrag = [&](const f32x16& sp, int half) -> Frag {
+    if constexpr (sizeof(T) == 2) {
+      const f32x4 v = {sp[4 * half], sp[4 * half + 1], sp[4 * half + 2], sp[4 * half + 3]};
+      return __builtin_bit_cast(Frag, v);
+    } else {
+      return sp[half];
+    }
+  };
+
+  // O^T += V^T P^T for block j, with P in sp.
+  auto pv = [&](int j, const f32x16 (&sp)[QB]) {
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
       for (int half = 0; half < 2; ++half)
@@ -205,7 +215,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_kernel(AttnParams p) {
         for (int nb = 0; nb < D / 32; ++nb) {
           const Frag a = vfrag(j, nb, half * 16 + grp * 8);
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) o[qb][nb] = MF::run(a, P.v[qb][half], o[qb][nb]);
+          for (int qb = 0; qb < QB; ++qb) o[qb][nb] = MF::run(a, pfrag(sp[qb], half), o[qb][nb]);
         }
     } else {
 #pragma unroll
@@ -214,82 +224,166 @@ __global__ __launch_bounds__(THREADS, 2) void attn_kernel(AttnParams p) {
         for (int nb = 0; nb < D / 32; ++nb) {
           const Frag a = vfrag(j, nb, 16 * (st >> 3) + 8 * grp + (st & 7));
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) o[qb][nb] = MF::run(a, P.v[qb][st], o[qb][nb]);
+          for (int qb = 0; qb < QB; ++qb) o[qb][nb] = MF::run(a, pfrag(sp[qb], st), o[qb][nb]);
         }
     }
   };
 
-  // p = exp2(s*c - m_ref) into P, and each lane's block sums.
-  auto exponentiate = [&](const f32x16 (&s)[QB], PBlock<T>& P, float (&bsum)[QB]) {
+  // p = exp2(s*c - m_ref) in place, packed as PV consumes it, and each lane's
+  // block sums (taken on the rounded bf16 values that PV multiplies).
+  auto exponentiate = [&](f32x16 (&s)[QB], float (&bsum)[QB]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const float mb = m_ref[qb];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[qb][r] = __builtin_amdgcn_exp2f(fmaf(s[qb][r], c, -mb));
       if constexpr (sizeof(T) == 2) {
         typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
         const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+        float packed[8];
         float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            P.v[qb][half][e] = from_f32<T>(__builtin_amdgcn_exp2f(fmaf(s[qb][8 * half + e], c, -mb)));
-#pragma unroll
-          for (int e = 0; e < 8; e += 4) {
-            acc0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{P.v[qb][half][e], P.v[qb][half][e + 1]}, one, acc0, false);
-            acc1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{P.v[qb][half][e + 2], P.v[qb][half][e + 3]}, one, acc1, false);
-          }
+        for (int e = 0; e < 8; ++e) {
+          const bf16x2 pr = __builtin_convertvector(f32x2{s[qb][2 * e], s[qb][2 * e + 1]}, bf16x2);
+          packed[e] = __builtin_bit_cast(float, pr);
+          if (e & 1) acc1 = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc1, false);
+          else acc0 = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc0, false);
         }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[qb][e] = packed[e];
         bsum[qb] = acc0 + acc1;
       } else {
         float acc = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          P.v[qb][r] = __builtin_amdgcn_exp2f(fmaf(s[qb][r], c, -mb));
-          acc += P.v[qb][r];
-        }
+        for (int r = 0; r < 16; ++r) acc += s[qb][r];
         bsum[qb] = acc;
       }
     }
   };
 
-  // Online softmax of block j: mask if the block crosses the diagonal or the
-  // sequence end, exponentiate against m_ref, and fall back to an exact
-  // rescale when a block sum shows m_ref was too low.
-  auto softmax = [&](f32x16 (&s)[QB], int j, PBlock<T>& P) {
+  auto mask = [&](f32x16 (&s)[QB], int j) {
     const int k0b = j * 32;
-    if (k0b + 32 > p.N || (p.causal && k0b + 31 > qw)) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const int qi = qw + 32 * qb + col;
+    for (int qb = 0; qb < QB; ++qb) {
+      const int qi = qw + 32 * qb + col;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0b + 16 * (r >> 3) + 8 * grp + (r & 7);
-          if (key >= p.N || (p.causal && key > qi)) s[qb][r] = -INFINITY;
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0b + 16 * (r >> 3) + 8 * grp + (r & 7);
+        if (key >= p.N || (p.causal && key > qi)) s[qb][r] = -INFINITY;
       }
     }
+  };
+
+  // The exact-rescale fallback of block j's softmax, used only when a block
+  // sum showed that m_ref was too low for it. Block j's keys are still in
+  // the LDS ring, so its scores are recomputed rather than kept.
+  auto rescale = [&](int j, f32x16 (&s)[QB], float (&bsum)[QB], bool masked) {
+    qk(j, s);
+    if (masked) mask(s, j);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float m = max3(s[qb][0], s[qb][1], s[qb][2]);
+#pragma unroll
+      for (int r = 3; r < 15; r += 2) m = max3(m, s[qb][r], s[qb][r + 1]);
+      m = fmaxf(m, s[qb][15]);
+      m = fmaxf(m, __shfl_xor(m, 32));
+      const float m_new = fmaxf(m_ref[qb], m * c);
+      const float alpha = __builtin_amdgcn_exp2f(m_ref[qb] - m_new);
+      l_run[qb] *= alpha;
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb) o[qb][nb] *= alpha;
+      m_ref[qb] = m_new;
+    }
+    exponentiate(s, bsum);
+  };
+
+  // One pipeline step for block j. s_cur holds S(j); s_next holds P(j-1).
+  // The MFMAs of O += V^T P(j-1), then of S(j+1) = K Q^T (into s_next, once
+  // PV has read it), are independent of block j's softmax. The step is laid
+  // out as one group per MFMA, each carrying the VALU work of one pair of
+  // scores (the exponentials of the next pair and the bf16 packing and row
+  // sum of the current one) and, every other group, the LDS fragment read for
+  // the MFMA four groups ahead. sched_barrier keeps this order, so the MFMA
+  // pipe and the VALU stay busy together and the register set stays what the
+  // layout implies. S(j+1) of the last block and P(-1) = 0 are padding that
+  // keeps each step straight-line.
+  auto step_interleaved = [&](int j, f32x16 (&sc)[QB], f32x16 (&sn)[QB], float (&bsum)[QB]) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    constexpr int NB = D / 32, NST = D / MF::KS;
+    constexpr int N_PV = 2 * NB * QB, N_QK = NST * QB, NG = N_PV + N_QK;
+    constexpr int PAIRS = QB * 8, PPG = PAIRS / NG > 0 ? PAIRS / NG : 1;   // score pairs per group
+    static_assert(sizeof(T) != 2 || PPG * NG == PAIRS, "pairs per group");
+    const int jp = j > 0 ? j - 1 : 0;
+    const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+    Frag vf[2][NB], kf[NST];
+    // fragment first used by MFMA group u (even u only)
+    auto fetch = [&](int u) {
+      if (u < N_PV) {
+        const int half = u / (NB * QB), nb = (u % (NB * QB)) / QB;
+        vf[half][nb] = vfrag(jp, nb, half * 16 + grp * 8);
+      } else if (u < NG) {
+        const int st = (u - N_PV) / QB;
+        kf[st] = kfrag(j + 1, st);
+      }
+    };
+    float acc[QB][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) acc[qb][0] = acc[qb][1] = 0.f;
+    float x[2 * PPG];   // exponentials of the pairs packed in the next group
+    auto expo = [&](int pr, float* dst) {   // pair pr: scores 2e, 2e+1 of query block qb
+      const int qb = pr / 8, e = pr % 8;
+      dst[0] = __builtin_amdgcn_exp2f(fmaf(sc[qb][2 * e], c, -m_ref[qb]));
+      dst[1] = __builtin_amdgcn_exp2f(fmaf(sc[qb][2 * e + 1], c, -m_ref[qb]));
+    };
+    fetch(0);
+    fetch(2);
+#pragma unroll
+    for (int k = 0; k < PPG; ++k) expo(k, &x[2 * k]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      if ((g & 1) == 0) fetch(g + 4);
+      if (g < N_PV) {
+        const int half = g / (NB * QB), nb = (g % (NB * QB)) / QB, qb = g % QB;
+        o[qb][nb] = MF::run(vf[half][nb], pfrag(sn[qb], half), o[qb][nb]);
+      } else {
+        const int st = (g - N_PV) / QB, qb = g % QB;
+        sn[qb] = MF::run(kf[st], qf[qb][st], st == 0 ? f32x16{} : sn[qb]);
+      }
+#pragma unroll
+      for (int k = 0; k < PPG; ++k) {
+        const int pr = g * PPG + k, qb = pr / 8, e = pr % 8;
+        const bf16x2 pk = __builtin_convertvector(f32x2{x[2 * k], x[2 * k + 1]}, bf16x2);
+        acc[qb][e & 1] = __builtin_amdgcn_fdot2_f32_bf16(pk, one, acc[qb][e & 1], false);
+        sc[qb][e] = __builtin_bit_cast(float, pk);   // slot e: its own scores are already used
+        if (pr + PPG < PAIRS) expo(pr + PPG, &x[2 * k]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) bsum[qb] = acc[qb][0] + acc[qb][1];
+  };
+
+  // Masking touches only S(j), so it stays a small branch in front of the one
+  // copy of the step body (two copies of the body would double its register
+  // footprint at their merge).
+  auto run_step = [&](int j, f32x16 (&s_cur)[QB], f32x16 (&s_next)[QB]) {
+    const bool masked = j * 32 + 32 > p.N || (p.causal && j * 32 + 31 > qw);
+    if (masked) mask(s_cur, j);
     float bsum[QB];
-    exponentiate(s, P, bsum);
+    if constexpr (sizeof(T) == 2) {
+      step_interleaved(j, s_cur, s_next, bsum);
+    } else {
+      pv(j > 0 ? j - 1 : 0, s_next);
+      qk(j + 1, s_next);
+      exponentiate(s_cur, bsum);
+    }
     bool redo = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) redo |= !(bsum[qb] <= SUM_LIMIT);
-    if (__any(redo)) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float m = max3(s[qb][0], s[qb][1], s[qb][2]);
-#pragma unroll
-        for (int r = 3; r < 15; r += 2) m = max3(m, s[qb][r], s[qb][r + 1]);
-        m = fmaxf(m, s[qb][15]);
-        m = fmaxf(m, __shfl_xor(m, 32));
-        const float m_new = fmaxf(m_ref[qb], m * c);
-        const float alpha = __builtin_amdgcn_exp2f(m_ref[qb] - m_new);
-        l_run[qb] *= alpha;
-#pragma unroll
-        for (int nb = 0; nb < D / 32; ++nb) o[qb][nb] *= alpha;
-        m_ref[qb] = m_new;
-      }
-      exponentiate(s, P, bsum);
-    }
+    if (__any(redo)) rescale(j, s_cur, bsum, masked);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) l_run[qb] += bsum[qb];
   };
@@ -302,28 +396,21 @@ __global__ __launch_bounds__(THREADS, 2) void attn_kernel(AttnParams p) {
   __syncthreads();
 
   f32x16 sA[QB], sB[QB];
-  PBlock<T> pA, pB;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) sB[qb] = f32x16{};   // P(-1) = 0
   qk(0, sA);
-  // Block pipeline: while block j's softmax runs on the VALU, the MFMAs of
-  // S(j+1) = K Q^T and of O += V^T P(j-1) are independent of it. PV(j-1) is
-  // issued first: a rescale inside softmax(j) must see O including block j-1,
-  // whose P used the previous reference max.
   for (int j = 0; j < nblk; j += 2) {
-    if (j + 1 < nblk) qk(j + 1, sB);
-    if (j > 0) pv(j - 1, pB);
-    softmax(sA, j, pA);
+    run_step(j, sA, sB);
     if (j + 1 < nblk) {
       // Odd block 2t+1: tile t+1 must be visible, tile t-1 is no longer read.
       const int t = j >> 1;
       if (t + 2 < n_tiles) wait_vmcnt<VM_PER_TILE>(); else wait_vmcnt<0>();
       __syncthreads();
       issue(t + 3);
-      if (j + 2 < nblk) qk(j + 2, sA);
-      pv(j, pA);
-      softmax(sB, j + 1, pB);
+      run_step(j + 1, sB, sA);
     }
   }
-  if (nblk & 1) pv(nblk - 1, pA); else pv(nblk - 1, pB);
+  if (nblk & 1) pv(nblk - 1, sA); else pv(nblk - 1, sB);
 
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
