@@ -43,7 +43,9 @@ namespace {
 constexpr int KT = 64;       // keys per LDS tile (two 32-key blocks)
 constexpr int NBUF = 4;      // LDS tile ring: one in use, one visible next, two in flight
 constexpr int WAVES = 4;
-constexpr int QB = 2;        // 32-query MFMA column blocks per wave
+constexpr int QB = 2;             // 32-query MFMA column blocks per wave
+constexpr int FETCH_AHEAD = 2;    // LDS fragments read ahead of their first MFMA
+constexpr int OCCUPANCY = 2;      // waves per SIMD: two workgroups per CU
 constexpr int QW = 32 * QB;  // query rows per wave
 constexpr int THREADS = 64 * WAVES;
 // Exponentials are taken against a reference max m_ref that may lag the true
@@ -81,16 +83,17 @@ template <int N> __device__ inline void wait_vmcnt() {
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
 template <typename T, int D>
-__global__ __launch_bounds__(THREADS, 2) void attn_kernel(AttnParams p) {
+__global__ __launch_bounds__(THREADS, OCCUPANCY) void attn_kernel(AttnParams p) {
   using MF = Mfma<T>;
   using Frag = typename MF::Frag;
   constexpr int EPC = 16 / sizeof(T);          // elements per 16-byte chunk
   constexpr int KCPR = D / EPC, VCPR = KT / EPC;
   constexpr int K_ELEMS = KT * D;              // elements of one tile's K (and of its V^T)
   constexpr int TILE = 2 * K_ELEMS;
-  constexpr int INS = K_ELEMS / (64 * EPC) / WAVES;  // 1 KB direct loads per wave, K or V^T
-  constexpr int VM_PER_TILE = 2 * INS;
-  static_assert(INS * WAVES * 64 * EPC == K_ELEMS, "tile split");
+  constexpr int K_INS = K_ELEMS / (64 * EPC);      // 1 KB direct loads of a tile's K (and of V^T)
+  constexpr int INS = 2 * K_INS / WAVES;           // loads per wave per tile
+  constexpr int VM_PER_TILE = INS;
+  static_assert(INS * WAVES == 2 * K_INS && K_INS * 64 * EPC == K_ELEMS, "tile split");
   __shared__ __align__(16) T smem[NBUF * TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -129,27 +132,27 @@ __global__ __launch_bounds__(THREADS, 2) void attn_kernel(AttnParams p) {
 
   // Direct global->LDS loads of tile t into ring slot t % NBUF. Lane L of a
   // load lands at 16*L bytes past the load's LDS base, so the source address
-  // chosen per lane realises the key permutation and the chunk swizzle.
+  // chosen per lane realises the key permutation and the chunk swizzle. The
+  // tile's 1 KB loads (K first, then V^T) are split evenly over the waves.
   auto issue = [&](int t) {
     if (t >= n_tiles) return;
     T* kb = smem + (t % NBUF) * TILE;
-    T* vb = kb + K_ELEMS;
     const int k0 = t * KT;
 #pragma unroll
     for (int i = 0; i < INS; ++i) {
-      const int ins = wave * INS + i;
-      const int pos = ins * 64 + lane;
-      const int r = pos / KCPR, slot = pos % KCPR;
-      const T* src = Kh + (int64_t)(k0 + swap23(r)) * D + (slot ^ swz<KCPR>(r)) * EPC;
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)(kb + ins * 64 * EPC), 16, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < INS; ++i) {
-      const int ins = wave * INS + i;
-      const int pos = ins * 64 + lane;
-      const int r = pos / VCPR, slot = pos % VCPR;
-      const T* src = Vh + (int64_t)r * p.Np + k0 + (slot ^ swz<VCPR>(r)) * EPC;
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)(vb + ins * 64 * EPC), 16, 0, 0);
+      const int ins = wave * INS + i;            // 0 .. 2*K_INS-1
+      if (ins < K_INS) {
+        const int pos = ins * 64 + lane;
+        const int r = pos / KCPR, slot = pos % KCPR;
+        const T* src = Kh + (int64_t)(k0 + swap23(r)) * D + (slot ^ swz<KCPR>(r)) * EPC;
+        __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)(kb + ins * 64 * EPC), 16, 0, 0);
+      } else {
+        const int vi = ins - K_INS;
+        const int pos = vi * 64 + lane;
+        const int r = pos / VCPR, slot = pos % VCPR;
+        const T* src = Vh + (int64_t)r * p.Np + k0 + (slot ^ swz<VCPR>(r)) * EPC;
+        __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)(kb + K_ELEMS + vi * 64 * EPC), 16, 0, 0);
+      }
     }
   };
 
@@ -318,7 +321,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_kernel(AttnParams p) {
     const int jp = j > 0 ? j - 1 : 0;
     const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
     Frag vf[2][NB], kf[NST];
-    // fragment first used by MFMA group u (even u only)
+    // the fragment whose first use is MFMA group u (u % QB == 0)
     auto fetch = [&](int u) {
       if (u < N_PV) {
         const int half = u / (NB * QB), nb = (u % (NB * QB)) / QB;
@@ -337,14 +340,14 @@ __global__ __launch_bounds__(THREADS, 2) void attn_kernel(AttnParams p) {
       dst[0] = __builtin_amdgcn_exp2f(fmaf(sc[qb][2 * e], c, -m_ref[qb]));
       dst[1] = __builtin_amdgcn_exp2f(fmaf(sc[qb][2 * e + 1], c, -m_ref[qb]));
     };
-    fetch(0);
-    fetch(2);
+#pragma unroll
+    for (int u = 0; u < FETCH_AHEAD * QB; u += QB) fetch(u);
 #pragma unroll
     for (int k = 0; k < PPG; ++k) expo(k, &x[2 * k]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-      if ((g & 1) == 0) fetch(g + 4);
+      if (g % QB == 0) fetch(g + FETCH_AHEAD * QB);
       if (g < N_PV) {
         const int half = g / (NB * QB), nb = (g % (NB * QB)) / QB, qb = g % QB;
         o[qb][nb] = MF::run(vf[half][nb], pfrag(sn[qb], half), o[qb][nb]);
@@ -452,7 +455,8 @@ hipError_t launch_attention(sqa_dtype dt, const void* q, const void* k, const vo
   p.q = q; p.k = k; p.vt = vt; p.a = a;
   p.N = (int)N; p.Np = (int)Np; p.H_q = (int)H_q; p.H_kv = (int)H_kv;
   p.g = (int)(H_q / H_kv);
-  p.G = p.g % 4 == 0 ? 4 : (p.g % 2 == 0 ? 2 : 1);   // heads per workgroup
+  p.G = 1;   // heads per workgroup: the largest power of two <= WAVES dividing g
+  while (p.G * 2 <= WAVES && p.g % (p.G * 2) == 0) p.G *= 2;
   p.n_sub = p.g / p.G;
   p.q_per_wg = QW * (WAVES / p.G);
   p.n_qt = (int)((N + p.q_per_wg - 1) / p.q_per_wg);
