@@ -32,6 +32,7 @@
 //    heaviest query tiles are dispatched first.
 #include <math.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "sqa_device.h"
@@ -41,13 +42,10 @@ namespace sqa {
 namespace {
 
 constexpr int KT = 64;       // keys per LDS tile (two 32-key blocks)
-constexpr int NBUF = 4;      // LDS tile ring: one in use, one visible next, two in flight
-constexpr int WAVES = 4;
+constexpr int NBUF = 4;      // LDS tile ring: in use, visible next, NBUF-2 in flight
 constexpr int QB = 2;             // 32-query MFMA column blocks per wave
 constexpr int FETCH_AHEAD = 2;    // LDS fragments read ahead of their first MFMA
-constexpr int OCCUPANCY = 2;      // waves per SIMD: two workgroups per CU
-constexpr int QW = 32 * QB;  // query rows per wave
-constexpr int THREADS = 64 * WAVES;
+constexpr int QW = 32 * QB;       // query rows per wave
 // Exponentials are taken against a reference max m_ref that may lag the true
 // running max. A lane's block sum above SUM_LIMIT (or inf/NaN) means the
 // reference is too low for that block; only then is the block's exact max
@@ -74,16 +72,26 @@ __device__ inline int swap23(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 
 __device__ inline float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
 // Wait until at most N of this wave's vector-memory operations are outstanding
-// (N < 16). The encoding leaves the other counters unconstrained.
+// (N < 64: vmcnt bits [3:0] and [15:14]). The other counters are left unconstrained.
 template <int N> __device__ inline void wait_vmcnt() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(N | (0x7 << 4) | (0xF << 8));
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// wait_vmcnt<n * PER>() for a runtime n in [0, MAXN].
+template <int PER, int MAXN> __device__ inline void wait_vmcnt_tiles(int n) {
+  if constexpr (MAXN > 0) {
+    if (n >= MAXN) { wait_vmcnt<MAXN * PER>(); return; }
+    wait_vmcnt_tiles<PER, MAXN - 1>(n);
+  } else {
+    wait_vmcnt<0>();
+  }
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
-template <typename T, int D>
-__global__ __launch_bounds__(THREADS, OCCUPANCY) void attn_kernel(AttnParams p) {
+template <typename T, int D, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
   using MF = Mfma<T>;
   using Frag = typename MF::Frag;
   constexpr int EPC = 16 / sizeof(T);          // elements per 16-byte chunk
@@ -391,10 +399,9 @@ __global__ __launch_bounds__(THREADS, OCCUPANCY) void attn_kernel(AttnParams p) 
     for (int qb = 0; qb < QB; ++qb) l_run[qb] += bsum[qb];
   };
 
-  // Prologue: tiles 0..2 in flight, tile 0 visible, S of block 0.
-  issue(0);
-  issue(1);
-  issue(2);
+  // Prologue: tiles 0..NBUF-2 in flight, tile 0 visible, S of block 0.
+#pragma unroll
+  for (int t = 0; t < NBUF - 1; ++t) issue(t);
   wait_vmcnt<0>();
   __syncthreads();
 
@@ -405,11 +412,13 @@ __global__ __launch_bounds__(THREADS, OCCUPANCY) void attn_kernel(AttnParams p) 
   for (int j = 0; j < nblk; j += 2) {
     run_step(j, sA, sB);
     if (j + 1 < nblk) {
-      // Odd block 2t+1: tile t+1 must be visible, tile t-1 is no longer read.
+      // Odd block 2t+1: tile t+1 must be visible (loads of tiles t+2.. may
+      // still be in flight), and tile t-1 is no longer read, so its slot
+      // takes tile t+NBUF-1.
       const int t = j >> 1;
-      if (t + 2 < n_tiles) wait_vmcnt<VM_PER_TILE>(); else wait_vmcnt<0>();
+      wait_vmcnt_tiles<VM_PER_TILE, NBUF - 3>(min(NBUF - 3, max(0, n_tiles - (t + 2))));
       __syncthreads();
-      issue(t + 3);
+      issue(t + NBUF - 1);
       run_step(j + 1, sB, sA);
     }
   }
@@ -440,14 +449,57 @@ __global__ __launch_bounds__(THREADS, OCCUPANCY) void attn_kernel(AttnParams p) 
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, int WAVES>
 hipError_t run(const AttnParams& p, unsigned grid, hipStream_t stream) {
-  attn_kernel<T, D><<<grid, THREADS, 0, stream>>>(p);
+  attn_kernel<T, D, WAVES><<<grid, 64 * WAVES, 0, stream>>>(p);
   return hipGetLastError();
+}
+
+template <int WAVES>
+int64_t plan(AttnParams& p, int64_t B, int64_t H_kv) {
+  p.G = 1;   // heads per workgroup: the largest power of two <= WAVES dividing g
+  while (p.G * 2 <= WAVES && p.g % (p.G * 2) == 0) p.G *= 2;
+  p.n_sub = p.g / p.G;
+  p.q_per_wg = QW * (WAVES / p.G);
+  p.n_qt = (p.N + p.q_per_wg - 1) / p.q_per_wg;
+  return (int64_t)p.n_qt * p.n_sub * H_kv * B;
+}
+
+template <int WAVES>
+hipError_t dispatch(sqa_dtype dt, int64_t d_head, const AttnParams& p, int64_t grid,
+                    hipStream_t stream) {
+  if (grid <= 0 || grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  if (dt == SQA_DTYPE_BF16)
+    return d_head == 64 ? run<bf16, 64, WAVES>(p, (unsigned)grid, stream)
+                        : run<bf16, 32, WAVES>(p, (unsigned)grid, stream);
+  return d_head == 64 ? run<float, 64, WAVES>(p, (unsigned)grid, stream)
+                      : run<float, 32, WAVES>(p, (unsigned)grid, stream);
+}
+
+// Compute units of the stream's device (cached per device).
+int cu_count(hipStream_t stream) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if ((stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev)) != hipSuccess || dev < 0 ||
+      dev >= 64)
+    return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
 }
 
 }  // namespace
 
+// Workgroup shape: 8 waves (one workgroup per CU, 512 query rows sharing each
+// K/V tile) by default. A non-causal grid whose last dispatch round would be
+// under half full runs with 4-wave workgroups instead (two per CU): every
+// workgroup of a non-causal grid costs the same, and the smaller ones pack
+// that tail round over more CUs. Causal grids, dispatched heaviest first,
+// fill their tail with short workgroups.
 hipError_t launch_attention(sqa_dtype dt, const void* q, const void* k, const void* vt, void* a,
                             int64_t B, int64_t N, int64_t Np, int64_t H_q, int64_t H_kv,
                             int64_t d_head, bool causal, hipStream_t stream) {
@@ -455,20 +507,17 @@ hipError_t launch_attention(sqa_dtype dt, const void* q, const void* k, const vo
   p.q = q; p.k = k; p.vt = vt; p.a = a;
   p.N = (int)N; p.Np = (int)Np; p.H_q = (int)H_q; p.H_kv = (int)H_kv;
   p.g = (int)(H_q / H_kv);
-  p.G = 1;   // heads per workgroup: the largest power of two <= WAVES dividing g
-  while (p.G * 2 <= WAVES && p.g % (p.G * 2) == 0) p.G *= 2;
-  p.n_sub = p.g / p.G;
-  p.q_per_wg = QW * (WAVES / p.G);
-  p.n_qt = (int)((N + p.q_per_wg - 1) / p.q_per_wg);
   p.causal = causal ? 1 : 0;
   p.c = (float)(1.4426950408889634 / sqrt((double)d_head));
-  const int64_t grid = (int64_t)p.n_qt * p.n_sub * H_kv * B;
-  if (grid <= 0 || grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  if (dt == SQA_DTYPE_BF16)
-    return d_head == 64 ? run<bf16, 64>(p, (unsigned)grid, stream)
-                        : run<bf16, 32>(p, (unsigned)grid, stream);
-  return d_head == 64 ? run<float, 64>(p, (unsigned)grid, stream)
-                      : run<float, 32>(p, (unsigned)grid, stream);
+  AttnParams p8 = p;
+  const int64_t grid8 = plan<8>(p8, B, H_kv);
+  const int64_t cus = cu_count(stream);
+  const int64_t tail = grid8 % cus;
+  if (!causal && tail != 0 && 2 * tail <= cus) {
+    const int64_t grid4 = plan<4>(p, B, H_kv);
+    return dispatch<4>(dt, d_head, p, grid4, stream);
+  }
+  return dispatch<8>(dt, d_head, p8, grid8, stream);
 }
 
 }  // namespace sqa
