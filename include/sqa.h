@@ -74,11 +74,12 @@ typedef enum { SQA_DTYPE_FP32 = 0, SQA_DTYPE_BF16 = 1 } sqa_dtype;
  *   out [B, N, d_model]        result Y; must not overlap any input
  *   causal: 0 or 1.
  *
- * Workspace: Q, K, V^T and A intermediates,
- * elem_size * (B*Np*d_head*(H_q + 2*H_kv) + B*N*H_q*d_head) bytes with
- * Np = sqa_padded_length(N). It is taken from a per-device stream-ordered
- * memory pool (hipMallocFromPoolAsync) and returned to it (hipFreeAsync) on
- * `stream`. The pool keeps freed memory for reuse until the process ends.
+ * Workspace: Q, K, V^T and A intermediates plus the two weight matrices
+ * transposed, about elem_size * (B*Np*d_head*(H_q + 2*H_kv) + B*N*H_q*d_head
+ * + d_model*d_head*(2*H_q + 2*H_kv)) bytes with Np = sqa_padded_length(N).
+ * It is taken from a per-device stream-ordered memory pool
+ * (hipMallocFromPoolAsync) and returned to it (hipFreeAsync) on `stream`.
+ * The pool keeps freed memory for reuse until the process ends.
  * Returns SQA_ERR_OUT_OF_MEMORY if the pool cannot supply the workspace.
  */
 sqa_status sqa_forward(const void* x, const void* Wq, const void* Wk, const void* Wv,
@@ -99,6 +100,8 @@ int64_t sqa_padded_length(int64_t N);
  *   k  [B, H_kv, Np, d_head]
  *   vt [B, H_kv, d_head, Np]   V transposed per head: vt[b, h, c, t] = V[b, t, h*d_head + c]
  * Rows t in [N, Np) are written as zeros. x and the weights are as in sqa_forward.
+ * Scratch for the transposed weights (elem_size * d_model*d_head*(H_q + 2*H_kv)
+ * bytes) comes from the same stream-ordered pool as sqa_forward's workspace.
  */
 sqa_status sqa_qkv_projection(const void* x, const void* Wq, const void* Wk, const void* Wv,
                               void* q, void* k, void* vt, int64_t B, int64_t N,
@@ -118,8 +121,9 @@ sqa_status sqa_attention(const void* q, const void* k, const void* vt, void* a, 
 
 /*
  * sqa_output_projection - step 3, out[M, d_model] = a[M, K] Wo[K, d_model].
- * K must be a multiple of 32 and d_model a multiple of 8; out must not
- * overlap a or Wo.
+ * K and d_model must be multiples of 32; out must not overlap a or Wo.
+ * Scratch for Wo transposed (elem_size * K * d_model bytes) comes from the
+ * stream-ordered pool.
  */
 sqa_status sqa_output_projection(const void* a, const void* Wo, void* out, int64_t M,
                                  int64_t K, int64_t d_model, sqa_dtype dtype,

@@ -141,6 +141,26 @@ sqa_status pool_for(hipStream_t stream, hipMemPool_t* out) {
   return SQA_OK;
 }
 
+// Stream-ordered scratch from the device's pool, released on the same stream.
+struct PoolScratch {
+  void* ptr = nullptr;
+  hipStream_t stream = nullptr;
+  sqa_status acquire(size_t bytes, hipStream_t s) {
+    hipMemPool_t pool;
+    SQA_TRY(pool_for(s, &pool));
+    const hipError_t e = hipMallocFromPoolAsync(&ptr, bytes, pool, s);
+    if (e != hipSuccess) { ptr = nullptr; return fail_hip(e, "scratch allocation"); }
+    stream = s;
+    return SQA_OK;
+  }
+  hipError_t release() {
+    if (!ptr) return hipSuccess;
+    const hipError_t e = hipFreeAsync(ptr, stream);
+    ptr = nullptr;
+    return e;
+  }
+};
+
 }  // namespace
 
 extern "C" {
@@ -192,9 +212,13 @@ sqa_status sqa_qkv_projection(const void* x, const void* Wq, const void* Wk, con
       if (overlap(outs[i], outb[i], outs[j], outb[j]))
         return fail(SQA_ERR_INVALID_ARG, "q, k and vt must not overlap");
   }
-  hipError_t e = sqa::launch_qkv_projection(dtype, x, Wq, Wk, Wv, q, k, vt, B, N, z.Np, d_model,
-                                            H_q, H_kv, d_head, stream);
+  PoolScratch wt;
+  SQA_TRY(wt.acquire(sqa::qkv_wt_bytes(dtype, d_model, H_q, H_kv, d_head), stream));
+  hipError_t e = sqa::launch_qkv_projection(dtype, x, Wq, Wk, Wv, wt.ptr, q, k, vt, B, N, z.Np,
+                                            d_model, H_q, H_kv, d_head, stream);
+  const hipError_t ef = wt.release();
   if (e != hipSuccess) return fail_hip(e, "qkv projection launch");
+  if (ef != hipSuccess) return fail_hip(ef, "scratch release");
   return ok();
 }
 
@@ -225,8 +249,8 @@ sqa_status sqa_output_projection(const void* a, const void* Wo, void* out, int64
   SQA_TRY(check_dtype(dtype));
   if (M < 0) return fail(SQA_ERR_INVALID_ARG, "M must be >= 0");
   if (K < 32 || K % 32 != 0) return fail(SQA_ERR_UNSUPPORTED, "K must be a positive multiple of 32");
-  if (d_model < 8 || d_model % 8 != 0)
-    return fail(SQA_ERR_UNSUPPORTED, "d_model must be a positive multiple of 8");
+  if (d_model < 32 || d_model % 32 != 0)
+    return fail(SQA_ERR_UNSUPPORTED, "d_model must be a positive multiple of 32");
   if (K > 65536 || d_model > 65536) return fail(SQA_ERR_UNSUPPORTED, "K or d_model exceeds 65536");
   if (M > ((int64_t)1 << 40)) return fail(SQA_ERR_UNSUPPORTED, "M too large");
   if (M == 0) return ok();
@@ -237,8 +261,12 @@ sqa_status sqa_output_projection(const void* a, const void* Wo, void* out, int64
   if (overlap(out, (size_t)(M * d_model) * es, a, (size_t)(M * K) * es) ||
       overlap(out, (size_t)(M * d_model) * es, Wo, (size_t)(K * d_model) * es))
     return fail(SQA_ERR_INVALID_ARG, "out overlaps a or Wo");
-  hipError_t e = sqa::launch_output_projection(dtype, a, Wo, out, M, K, d_model, stream);
+  PoolScratch wt;
+  SQA_TRY(wt.acquire(sqa::out_wt_bytes(dtype, K, d_model), stream));
+  hipError_t e = sqa::launch_output_projection(dtype, a, Wo, wt.ptr, out, M, K, d_model, stream);
+  const hipError_t ef = wt.release();
   if (e != hipSuccess) return fail_hip(e, "output projection launch");
+  if (ef != hipSuccess) return fail_hip(ef, "scratch release");
   return ok();
 }
 
@@ -268,7 +296,9 @@ sqa_status sqa_forward(const void* x, const void* Wq, const void* Wk, const void
     if (overlap(out, yb, ins[j], inb[j])) return fail(SQA_ERR_INVALID_ARG, "out overlaps an input");
 
   const int64_t off_k = round256(z.q), off_v = off_k + round256(z.kv);
-  const int64_t off_a = off_v + round256(z.kv), total = off_a + round256(z.a);
+  const int64_t off_a = off_v + round256(z.kv), off_w1 = off_a + round256(z.a);
+  const int64_t off_w3 = off_w1 + round256((int64_t)sqa::qkv_wt_bytes(dtype, d_model, H_q, H_kv, d_head));
+  const int64_t total = off_w3 + round256((int64_t)sqa::out_wt_bytes(dtype, H_q * d_head, d_model));
   hipMemPool_t pool;
   SQA_TRY(pool_for(stream, &pool));
   void* ws = nullptr;
@@ -276,13 +306,14 @@ sqa_status sqa_forward(const void* x, const void* Wq, const void* Wk, const void
   if (e != hipSuccess) return fail_hip(e, "workspace allocation");
   char* base = (char*)ws;
   void *q = base, *k = base + off_k, *vt = base + off_v, *a = base + off_a;
+  void *w1 = base + off_w1, *w3 = base + off_w3;
 
-  e = sqa::launch_qkv_projection(dtype, x, Wq, Wk, Wv, q, k, vt, B, N, z.Np, d_model, H_q, H_kv,
-                                 d_head, stream);
+  e = sqa::launch_qkv_projection(dtype, x, Wq, Wk, Wv, w1, q, k, vt, B, N, z.Np, d_model, H_q,
+                                 H_kv, d_head, stream);
   if (e == hipSuccess)
     e = sqa::launch_attention(dtype, q, k, vt, a, B, N, z.Np, H_q, H_kv, d_head, causal != 0, stream);
   if (e == hipSuccess)
-    e = sqa::launch_output_projection(dtype, a, Wo, out, B * N, H_q * d_head, d_model, stream);
+    e = sqa::launch_output_projection(dtype, a, Wo, w3, out, B * N, H_q * d_head, d_model, stream);
   const hipError_t ef = hipFreeAsync(ws, stream);
   if (e != hipSuccess) return fail_hip(e, "kernel launch");
   if (ef != hipSuccess) return fail_hip(ef, "workspace release");

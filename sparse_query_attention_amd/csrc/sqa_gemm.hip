@@ -7,86 +7,96 @@
 // One kernel template serves both steps. Only where rows come from and where
 // results go differ.
 //
-// Tiling: a 256-thread workgroup owns a 128x128 tile of C. Its four waves
-// each own a 64x64 sub-tile, i.e. 2x2 MFMA 32x32 tiles. K advances in
-// steps of 32 through double-buffered LDS; the next step's global loads are
-// in flight while the current one feeds the MFMAs. W is stored transposed in
-// LDS ([n][k]) so that both MFMA operands read k-contiguous 16-byte
-// fragments.
+// Design:
+//  * W is first transposed to W^T [Ncols, K] (a few MB, once per call), so both
+//    MFMA operands are k-contiguous rows.
+//  * A 256-thread workgroup owns a 128x128 tile of C. Each of its four waves
+//    owns 64x64, i.e. 2x2 v_mfma_f32_32x32x16 tiles.
+//  * K advances in steps of 32 through a 4-stage LDS ring filled by direct
+//    global->LDS loads (global_load_lds_dwordx4), three stages ahead, with one
+//    barrier per step. Each load lands lane-contiguously, so 16-byte chunks are
+//    XOR-swizzled per row against LDS bank conflicts.
+//  * Workgroups are dispatched round-robin over the 8 XCDs, each with its own
+//    L2. The 1-D grid is remapped so that every column tile of a row block
+//    runs on one XCD, and that row block of A is fetched from memory once.
+//  * Rows past the end of A are loaded from a clamped, valid row and never
+//    stored as computed: step 1 writes zeros there (the padded rows of the
+//    Q/K/V^T layouts), step 3 skips them.
 #include "sqa_device.h"
 #include "sqa_internal.h"
 
 namespace sqa {
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 32, THREADS = 256;
+constexpr int BM = 128, BN = 128, BK = 32, THREADS = 256, WAVES = 4;
+constexpr int NST = 4;   // LDS ring stages
+constexpr int XCDS = 8;
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+template <int CPR> __device__ inline int swz(int r);
+template <> __device__ inline int swz<8>(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+template <> __device__ inline int swz<4>(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+
+template <int N> __device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+template <int PER, int MAXN> __device__ inline void wait_vmcnt_stages(int n) {
+  if constexpr (MAXN > 0) {
+    if (n >= MAXN) { wait_vmcnt<MAXN * PER>(); return; }
+    wait_vmcnt_stages<PER, MAXN - 1>(n);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
 
 template <typename T> struct GemmCfg {
-  static constexpr int EPC = 16 / sizeof(T);            // elements per 16-byte chunk
-  static constexpr int LD = BK + EPC;                    // LDS row length, 16-byte pad
-  static constexpr int CPR = BK / EPC;                   // chunks per A-tile row
-  static constexpr int A_PER = BM * CPR / THREADS;       // A chunks per thread
-  static constexpr int RPT = sizeof(T) == 2 ? 2 : 1;     // W rows per task (fills 32-bit LDS words)
-  static constexpr int B_TASKS = (BK / RPT) * (BN / EPC);
-  static constexpr int B_PER = B_TASKS / THREADS;        // W tasks per thread
-  static_assert(B_PER * THREADS == B_TASKS, "W tile split");
-  static_assert(A_PER * THREADS == BM * CPR, "A tile split");
+  static constexpr int EPC = 16 / sizeof(T);          // elements per 16-byte chunk
+  static constexpr int CPR = BK / EPC;                 // chunks per tile row (4 bf16, 8 fp32)
+  static constexpr int A_ELEMS = BM * BK, B_ELEMS = BN * BK, STAGE = A_ELEMS + B_ELEMS;
+  static constexpr int A_INS = A_ELEMS / (64 * EPC) / WAVES;   // 1 KB loads per wave
+  static constexpr int B_INS = B_ELEMS / (64 * EPC) / WAVES;
+  static constexpr int VM = A_INS + B_INS;                     // loads per wave per stage
+  static_assert(A_INS * WAVES * 64 * EPC == A_ELEMS && B_INS * WAVES * 64 * EPC == B_ELEMS, "split");
 };
 
-// Rows of X for step 1: output row gr = b*Np + t reads X row b*N + t when t < N,
-// and zeros otherwise (the padded rows of the Q/K/V^T layouts).
+// Rows of X for step 1: output row gr = b*Np + t is X row b*N + t when t < N
+// (padded rows load the sequence's last row and are stored as zeros).
 template <typename T> struct PaddedRows {
   const T* x; int64_t N, Np; int K;
   __device__ const T* row(int64_t gr) const {
     const int64_t b = gr / Np, t = gr - b * Np;
-    return t < N ? x + (b * N + t) * K : nullptr;
+    return x + (b * N + (t < N ? t : N - 1)) * K;
   }
 };
 
-// Rows of A for step 3: plain [M, K] with a ragged last tile.
+// Rows of A for step 3: plain [M, K]; rows past M load row M-1 and are not stored.
 template <typename T> struct DenseRows {
   const T* a; int64_t M; int K;
-  __device__ const T* row(int64_t gr) const { return gr < M ? a + gr * K : nullptr; }
-};
-
-// Columns of [Wq | Wk | Wv] (widths wq, wkv, wkv). A 16-byte chunk never
-// straddles two matrices because every width is a multiple of d_head >= 32.
-template <typename T> struct QkvCols {
-  const T* wq; const T* wk; const T* wv; int wq_w, wkv_w;
-  __device__ const T* col(int n, int& ld) const {
-    if (n < wq_w) { ld = wq_w; return wq + n; }
-    n -= wq_w;
-    if (n < wkv_w) { ld = wkv_w; return wk + n; }
-    n -= wkv_w;
-    if (n < wkv_w) { ld = wkv_w; return wv + n; }
-    ld = 0; return nullptr;
-  }
-};
-
-template <typename T> struct DenseCols {
-  const T* w; int ncols;
-  __device__ const T* col(int n, int& ld) const {
-    ld = ncols; return n < ncols ? w + n : nullptr;
-  }
+  __device__ const T* row(int64_t gr) const { return a + (gr < M ? gr : M - 1) * K; }
 };
 
 // Step 1 epilogue: route column n to q, k or vt and row gr to (b, t).
 template <typename T> struct QkvStore {
-  T* q; T* k; T* vt; int64_t Np; int H_q, H_kv, D, wq_w, wkv_w;
-  // v[i] is C[gr + i][n] for i = 0..3 (four consecutive rows, one column).
+  T* q; T* k; T* vt; int64_t N, Np; int H_q, H_kv, D, wq_w, wkv_w;
+  // v[i] is C[gr + i][n] for i = 0..3 (four consecutive rows of one batch, one column).
   __device__ void operator()(int64_t gr, int n, const float v[4]) const {
     const int64_t b = gr / Np, t = gr - b * Np;
+    float w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = t + i < N ? v[i] : 0.f;
     if (n < wq_w) {
       T* p = q + ((b * H_q + n / D) * Np + t) * D + n % D;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[(int64_t)i * D] = from_f32<T>(v[i]);
+      for (int i = 0; i < 4; ++i) p[(int64_t)i * D] = from_f32<T>(w[i]);
       return;
     }
     n -= wq_w;
     if (n < wkv_w) {
       T* p = k + ((b * H_kv + n / D) * Np + t) * D + n % D;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[(int64_t)i * D] = from_f32<T>(v[i]);
+      for (int i = 0; i < 4; ++i) p[(int64_t)i * D] = from_f32<T>(w[i]);
       return;
     }
     n -= wkv_w;
@@ -94,10 +104,10 @@ template <typename T> struct QkvStore {
       // V^T: the four rows are four consecutive t, contiguous in vt.
       T* p = vt + ((b * H_kv + n / D) * (int64_t)D + n % D) * Np + t;
       if constexpr (sizeof(T) == 2) {
-        bf16x4 w = {from_f32<T>(v[0]), from_f32<T>(v[1]), from_f32<T>(v[2]), from_f32<T>(v[3])};
-        *reinterpret_cast<bf16x4*>(p) = w;
+        *reinterpret_cast<bf16x4*>(p) =
+            bf16x4{from_f32<T>(w[0]), from_f32<T>(w[1]), from_f32<T>(w[2]), from_f32<T>(w[3])};
       } else {
-        *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<f32x4*>(p) = f32x4{w[0], w[1], w[2], w[3]};
       }
     }
   }
@@ -106,119 +116,96 @@ template <typename T> struct QkvStore {
 template <typename T> struct DenseStore {
   T* out; int64_t M; int ncols;
   __device__ void operator()(int64_t gr, int n, const float v[4]) const {
-    if (n >= ncols) return;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (gr + i < M) out[(gr + i) * ncols + n] = from_f32<T>(v[i]);
   }
 };
 
-template <typename T, class Rows, class Cols, class Store>
-__global__ __launch_bounds__(THREADS) void gemm_kernel(Rows rows, Cols cols, Store store, int K) {
+// C = A * W with W given transposed (wt [ncols, K]); see the file header.
+template <typename T, class Rows, class Store>
+__global__ __launch_bounds__(THREADS) void gemm_kernel(Rows rows, const T* wt, int ncols,
+                                                       Store store, int K, int n_rb, int n_ct) {
   using C = GemmCfg<T>;
   using MF = Mfma<T>;
   using Frag = typename MF::Frag;
-  __shared__ __align__(16) T As[2][BM * C::LD];
-  __shared__ __align__(16) T Bs[2][BN * C::LD];
+  __shared__ __align__(16) T smem[NST * C::STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t m0 = (int64_t)blockIdx.x * BM;
-  const int n0 = blockIdx.y * BN;
+  const int col = lane & 31, grp = lane >> 5;
+  // block L runs on XCD L % 8; XCD x owns row blocks x, x+8, ... in turn
+  const int L = blockIdx.x, xcd = L % XCDS, k_in_xcd = L / XCDS;
+  const int rb = (k_in_xcd / n_ct) * XCDS + xcd, ct = k_in_xcd % n_ct;
+  if (rb >= n_rb) return;
+  const int64_t m0 = (int64_t)rb * BM;
+  const int n0 = ct * BN;
 
-  // Fixed per-thread source pointers of the A tile chunks and W tile tasks.
-  const T* a_src[C::A_PER];
+  // Per-thread sources of its direct loads (fixed rows, chunk swizzled per row).
+  const T* a_src[C::A_INS];
+  const T* b_src[C::B_INS];
 #pragma unroll
-  for (int i = 0; i < C::A_PER; ++i) {
-    const int c = tid + i * THREADS;
-    const T* r = rows.row(m0 + c / C::CPR);
-    a_src[i] = r ? r + (c % C::CPR) * C::EPC : nullptr;
+  for (int i = 0; i < C::A_INS; ++i) {
+    const int pos = (wave * C::A_INS + i) * 64 + lane;
+    const int r = pos / C::CPR, slot = pos % C::CPR;
+    a_src[i] = rows.row(m0 + r) + (slot ^ swz<C::CPR>(r)) * C::EPC;
   }
-  const T* b_src[C::B_PER];
-  int b_ld[C::B_PER];
 #pragma unroll
-  for (int i = 0; i < C::B_PER; ++i) {
-    const int task = tid + i * THREADS;
-    const int kp = task / (BN / C::EPC), nc = task % (BN / C::EPC);
-    const T* p = cols.col(n0 + nc * C::EPC, b_ld[i]);
-    b_src[i] = p ? p + (int64_t)kp * C::RPT * b_ld[i] : nullptr;
+  for (int i = 0; i < C::B_INS; ++i) {
+    const int pos = (wave * C::B_INS + i) * 64 + lane;
+    const int r = pos / C::CPR, slot = pos % C::CPR;
+    const int n = min(n0 + r, ncols - 1);
+    b_src[i] = wt + (int64_t)n * K + (slot ^ swz<C::CPR>(r)) * C::EPC;
   }
-
-  Chunk areg[C::A_PER];
-  Chunk breg[C::B_PER][C::RPT];
-
-  auto load = [&](int kt) {
+  const int nk = K / BK;
+  auto issue = [&](int kt) {
+    if (kt >= nk) return;
+    T* st = smem + (kt % NST) * C::STAGE;
 #pragma unroll
-    for (int i = 0; i < C::A_PER; ++i)
-      areg[i] = a_src[i] ? *reinterpret_cast<const Chunk*>(a_src[i] + kt * BK) : zero_chunk();
+    for (int i = 0; i < C::A_INS; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(a_src[i] + kt * BK),
+                                       (lds_ptr)(st + (wave * C::A_INS + i) * 64 * C::EPC), 16, 0, 0);
 #pragma unroll
-    for (int i = 0; i < C::B_PER; ++i)
-#pragma unroll
-      for (int j = 0; j < C::RPT; ++j)
-        breg[i][j] = b_src[i]
-            ? *reinterpret_cast<const Chunk*>(b_src[i] + ((int64_t)kt * BK + j) * b_ld[i])
-            : zero_chunk();
+    for (int i = 0; i < C::B_INS; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(b_src[i] + kt * BK),
+                                       (lds_ptr)(st + C::A_ELEMS + (wave * C::B_INS + i) * 64 * C::EPC),
+                                       16, 0, 0);
   };
-
-  auto stash = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < C::A_PER; ++i) {
-      const int c = tid + i * THREADS;
-      *reinterpret_cast<Chunk*>(&As[buf][(c / C::CPR) * C::LD + (c % C::CPR) * C::EPC]) = areg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < C::B_PER; ++i) {
-      const int task = tid + i * THREADS;
-      const int kp = task / (BN / C::EPC), nc = task % (BN / C::EPC);
-      uint32_t* dst = reinterpret_cast<uint32_t*>(&Bs[buf][(nc * C::EPC) * C::LD + kp * C::RPT]);
-      constexpr int WSTRIDE = C::LD * sizeof(T) / 4;  // one LDS row in 32-bit words
-#pragma unroll
-      for (int e = 0; e < C::EPC; ++e) {
-        uint32_t w;
-        if constexpr (sizeof(T) == 2) {
-          const uint32_t lo = (breg[i][0].w[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-          const uint32_t hi = (breg[i][1].w[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-          w = lo | (hi << 16);
-        } else {
-          w = breg[i][0].w[e];
-        }
-        dst[e * WSTRIDE] = w;
-      }
-    }
+  // MFMA fragment of tile row r (A or B part of a stage), k-step s.
+  auto frag = [&](const T* part, int r, int s) -> Frag {
+    const int e = s * MF::KS + grp * MF::E;
+    return *reinterpret_cast<const Frag*>(
+        &part[r * BK + (((e / C::EPC) ^ swz<C::CPR>(r)) * C::EPC) + e % C::EPC]);
   };
 
   const int wm = wave >> 1, wn = wave & 1;
-  const int col = lane & 31, grp = lane >> 5;
   f32x16 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-  const int nk = K / BK;
-  load(0);
-  stash(0);
-  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s) issue(s);
+  wait_vmcnt_stages<C::VM, NST - 2>(min(NST - 2, nk - 1));
   for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load(kt + 1);
+    // stage kt is visible to every wave; stage kt-1's slot is free
+    __syncthreads();
+    issue(kt + NST - 1);
+    const T* st = smem + (kt % NST) * C::STAGE;
 #pragma unroll
     for (int s = 0; s < BK / MF::KS; ++s) {
       Frag a[2], b[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = *reinterpret_cast<const Frag*>(
-            &As[buf][(wm * 64 + i * 32 + col) * C::LD + s * MF::KS + grp * MF::E]);
+      for (int i = 0; i < 2; ++i) a[i] = frag(st, wm * 64 + i * 32 + col, s);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        b[j] = *reinterpret_cast<const Frag*>(
-            &Bs[buf][(wn * 64 + j * 32 + col) * C::LD + s * MF::KS + grp * MF::E]);
+      for (int j = 0; j < 2; ++j) b[j] = frag(st + C::A_ELEMS, wn * 64 + j * 32 + col, s);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = MF::run(a[i], b[j], acc[i][j]);
     }
-    if (kt + 1 < nk) stash(buf ^ 1);
-    __syncthreads();
+    // this wave's loads of stage kt+1 are complete (later stages may be in flight)
+    wait_vmcnt_stages<C::VM, NST - 2>(min(NST - 2, max(0, nk - 2 - kt)));
   }
 
 #pragma unroll
@@ -229,50 +216,109 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Rows rows, Cols cols, Sto
       for (int rq = 0; rq < 4; ++rq) {
         const float v[4] = {acc[i][j][4 * rq], acc[i][j][4 * rq + 1], acc[i][j][4 * rq + 2],
                             acc[i][j][4 * rq + 3]};
-        store(m0 + wm * 64 + i * 32 + 8 * rq + 4 * grp, n0 + wn * 64 + j * 32 + col, v);
+        const int n = n0 + wn * 64 + j * 32 + col;
+        if (n < ncols) store(m0 + wm * 64 + i * 32 + 8 * rq + 4 * grp, n, v);
       }
 }
 
+// W^T [ncols, K] from W = [W0 | W1 | W2] ([K, w0], [K, w1], [K, w2] row-major;
+// w1, w2 may be 0). One 32x32 tile per workgroup through LDS.
 template <typename T>
-hipError_t qkv_impl(const void* x, const void* wq, const void* wk, const void* wv, void* q,
-                    void* k, void* vt, int64_t B, int64_t N, int64_t Np, int64_t d_model,
-                    int64_t H_q, int64_t H_kv, int64_t d, hipStream_t stream) {
-  const int wq_w = (int)(H_q * d), wkv_w = (int)(H_kv * d);
-  const int ncols = wq_w + 2 * wkv_w;
-  PaddedRows<T> rows{(const T*)x, N, Np, (int)d_model};
-  QkvCols<T> cols{(const T*)wq, (const T*)wk, (const T*)wv, wq_w, wkv_w};
-  QkvStore<T> st{(T*)q, (T*)k, (T*)vt, Np, (int)H_q, (int)H_kv, (int)d, wq_w, wkv_w};
-  dim3 grid((unsigned)(B * Np / BM), (unsigned)((ncols + BN - 1) / BN));
-  gemm_kernel<T><<<grid, THREADS, 0, stream>>>(rows, cols, st, (int)d_model);
+__global__ __launch_bounds__(256) void transpose_weights(const T* w0, int w0n, const T* w1, int w1n,
+                                                         const T* w2, int w2n, T* wt, int K) {
+  __shared__ T tile[32][33];
+  const int n0 = blockIdx.x * 32, k0 = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // 32 x 8
+#pragma unroll
+  for (int r = 0; r < 32; r += 8) {
+    int n = n0 + tx;
+    const T* src;
+    int ld;
+    if (n < w0n) { src = w0; ld = w0n; }
+    else if ((n -= w0n) < w1n) { src = w1; ld = w1n; }
+    else { n -= w1n; src = w2; ld = w2n; }
+    tile[ty + r][tx] = src[(int64_t)(k0 + ty + r) * ld + n];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 32; r += 8)
+    wt[(int64_t)(n0 + ty + r) * K + k0 + tx] = tile[tx][ty + r];
+}
+
+// Blocks for n_rb row blocks x n_ct column tiles under the XCD remap (row
+// blocks rounded up to a multiple of 8; the extra blocks exit at once).
+int64_t grid_size(int64_t n_rb, int64_t n_ct) { return (n_rb + XCDS - 1) / XCDS * XCDS * n_ct; }
+
+bool grid_ok(int64_t n_rb, int64_t n_ct) {
+  return n_rb > 0 && n_ct > 0 && grid_size(n_rb, n_ct) <= 0x7FFFFFFF;
+}
+
+template <typename T>
+hipError_t transpose(const T* w0, int w0n, const T* w1, int w1n, const T* w2, int w2n, T* wt,
+                     int K, hipStream_t stream) {
+  const int ncols = w0n + w1n + w2n;
+  dim3 grid((unsigned)(ncols / 32), (unsigned)(K / 32));
+  transpose_weights<T><<<grid, 256, 0, stream>>>(w0, w0n, w1, w1n, w2, w2n, wt, K);
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t out_impl(const void* a, const void* wo, void* out, int64_t M, int64_t K,
+hipError_t qkv_impl(const void* x, const void* wq, const void* wk, const void* wv, void* wt,
+                    void* q, void* k, void* vt, int64_t B, int64_t N, int64_t Np, int64_t d_model,
+                    int64_t H_q, int64_t H_kv, int64_t d, hipStream_t stream) {
+  const int wq_w = (int)(H_q * d), wkv_w = (int)(H_kv * d);
+  const int ncols = wq_w + 2 * wkv_w;
+  const int64_t n_rb = B * Np / BM, n_ct = (ncols + BN - 1) / BN;
+  if (!grid_ok(n_rb, n_ct)) return hipErrorInvalidConfiguration;
+  hipError_t e = transpose<T>((const T*)wq, wq_w, (const T*)wk, wkv_w, (const T*)wv, wkv_w, (T*)wt,
+                              (int)d_model, stream);
+  if (e != hipSuccess) return e;
+  PaddedRows<T> rows{(const T*)x, N, Np, (int)d_model};
+  QkvStore<T> st{(T*)q, (T*)k, (T*)vt, N, Np, (int)H_q, (int)H_kv, (int)d, wq_w, wkv_w};
+  gemm_kernel<T><<<(unsigned)grid_size(n_rb, n_ct), THREADS, 0, stream>>>(
+      rows, (const T*)wt, ncols, st, (int)d_model, (int)n_rb, (int)n_ct);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t out_impl(const void* a, const void* wo, void* wt, void* out, int64_t M, int64_t K,
                     int64_t d_model, hipStream_t stream) {
+  const int64_t n_rb = (M + BM - 1) / BM, n_ct = (d_model + BN - 1) / BN;
+  if (!grid_ok(n_rb, n_ct)) return hipErrorInvalidConfiguration;
+  hipError_t e = transpose<T>((const T*)wo, (int)d_model, nullptr, 0, nullptr, 0, (T*)wt, (int)K,
+                              stream);
+  if (e != hipSuccess) return e;
   DenseRows<T> rows{(const T*)a, M, (int)K};
-  DenseCols<T> cols{(const T*)wo, (int)d_model};
   DenseStore<T> st{(T*)out, M, (int)d_model};
-  dim3 grid((unsigned)((M + BM - 1) / BM), (unsigned)((d_model + BN - 1) / BN));
-  gemm_kernel<T><<<grid, THREADS, 0, stream>>>(rows, cols, st, (int)K);
+  gemm_kernel<T><<<(unsigned)grid_size(n_rb, n_ct), THREADS, 0, stream>>>(
+      rows, (const T*)wt, (int)d_model, st, (int)K, (int)n_rb, (int)n_ct);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_qkv_projection(sqa_dtype dt, const void* x, const void* wq, const void* wk,
-                                 const void* wv, void* q, void* k, void* vt, int64_t B, int64_t N,
-                                 int64_t Np, int64_t d_model, int64_t H_q, int64_t H_kv,
-                                 int64_t d_head, hipStream_t stream) {
-  if (dt == SQA_DTYPE_BF16)
-    return qkv_impl<bf16>(x, wq, wk, wv, q, k, vt, B, N, Np, d_model, H_q, H_kv, d_head, stream);
-  return qkv_impl<float>(x, wq, wk, wv, q, k, vt, B, N, Np, d_model, H_q, H_kv, d_head, stream);
+size_t qkv_wt_bytes(sqa_dtype dt, int64_t d_model, int64_t H_q, int64_t H_kv, int64_t d_head) {
+  return (size_t)(d_model * (H_q + 2 * H_kv) * d_head) * (dt == SQA_DTYPE_BF16 ? 2 : 4);
 }
 
-hipError_t launch_output_projection(sqa_dtype dt, const void* a, const void* wo, void* out,
-                                    int64_t M, int64_t K, int64_t d_model, hipStream_t stream) {
-  if (dt == SQA_DTYPE_BF16) return out_impl<bf16>(a, wo, out, M, K, d_model, stream);
-  return out_impl<float>(a, wo, out, M, K, d_model, stream);
+size_t out_wt_bytes(sqa_dtype dt, int64_t K, int64_t d_model) {
+  return (size_t)(K * d_model) * (dt == SQA_DTYPE_BF16 ? 2 : 4);
+}
+
+hipError_t launch_qkv_projection(sqa_dtype dt, const void* x, const void* wq, const void* wk,
+                                 const void* wv, void* wt, void* q, void* k, void* vt, int64_t B,
+                                 int64_t N, int64_t Np, int64_t d_model, int64_t H_q, int64_t H_kv,
+                                 int64_t d_head, hipStream_t stream) {
+  if (dt == SQA_DTYPE_BF16)
+    return qkv_impl<bf16>(x, wq, wk, wv, wt, q, k, vt, B, N, Np, d_model, H_q, H_kv, d_head, stream);
+  return qkv_impl<float>(x, wq, wk, wv, wt, q, k, vt, B, N, Np, d_model, H_q, H_kv, d_head, stream);
+}
+
+hipError_t launch_output_projection(sqa_dtype dt, const void* a, const void* wo, void* wt,
+                                    void* out, int64_t M, int64_t K, int64_t d_model,
+                                    hipStream_t stream) {
+  if (dt == SQA_DTYPE_BF16) return out_impl<bf16>(a, wo, wt, out, M, K, d_model, stream);
+  return out_impl<float>(a, wo, wt, out, M, K, d_model, stream);
 }
 
 }  // namespace sqa
