@@ -56,8 +56,12 @@ constexpr float M_INIT = -1e30f;   // finite, so masked scores give exp2(-inf) =
 struct AttnParams {
   const void* q; const void* k; const void* vt; void* a;
   int N, Np, H_q, H_kv, g, G, n_sub, q_per_wg, n_qt, causal;
+  int chunk, remap_end;   // XCD-aware workgroup order (see the kernel's block decode)
   float c;  // log2(e) / sqrt(d_head)
 };
+
+// The dispatcher hands workgroup i to XCD i % XCDS, and each XCD has its own L2.
+constexpr int XCDS = 8;
 
 // XOR swizzle of 16-byte chunks within an LDS row of CPR chunks. It spreads
 // the rows that one ds_read_b128 touches over distinct banks.
@@ -107,7 +111,19 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, grp = lane >> 5;
 
+  // Renumber the workgroups so that each XCD runs logical chunks of `chunk`
+  // consecutive query tiles of one K/V stream, as many as the XCD holds at
+  // once. The chunk's workgroups start together and walk the same K/V rows
+  // within a few thousand keys of each other, so all but the first read of
+  // each K/V tile hit that XCD's L2. In round r the XCDs take chunks 8r..8r+7,
+  // in reverse order on odd rounds: the assignment to XCDs is static, and with
+  // causal work falling linearly along the chunks this gives every XCD the same
+  // total. Blocks from remap_end on keep their index.
   int blk = blockIdx.x;
+  if (blk < p.remap_end) {
+    const int xcd = blk % XCDS, s = blk / XCDS, r = s / p.chunk;
+    blk = (r * XCDS + ((r & 1) ? XCDS - 1 - xcd : xcd)) * p.chunk + s % p.chunk;
+  }
   int qt = blk % p.n_qt;
   blk /= p.n_qt;
   if (p.causal) qt = p.n_qt - 1 - qt;   // heaviest query tiles first
@@ -465,10 +481,22 @@ int64_t plan(AttnParams& p, int64_t B, int64_t H_kv) {
   return (int64_t)p.n_qt * p.n_sub * H_kv * B;
 }
 
+// Chunks of the XCD-aware order: one chunk is what an XCD holds at once
+// (two waves per SIMD: 8 / WAVES workgroups per CU). No renumbering when the
+// CU count does not split evenly over the XCDs.
 template <int WAVES>
-hipError_t dispatch(sqa_dtype dt, int64_t d_head, const AttnParams& p, int64_t grid,
+void plan_order(AttnParams& p, int64_t grid, int64_t cus) {
+  p.chunk = (int)(cus / XCDS) * (8 / WAVES);
+  p.remap_end = 0;
+  if (cus % XCDS == 0 && p.chunk > 0)
+    p.remap_end = (int)(grid / ((int64_t)XCDS * p.chunk) * XCDS * p.chunk);
+}
+
+template <int WAVES>
+hipError_t dispatch(sqa_dtype dt, int64_t d_head, AttnParams& p, int64_t grid, int64_t cus,
                     hipStream_t stream) {
   if (grid <= 0 || grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  plan_order<WAVES>(p, grid, cus);
   if (dt == SQA_DTYPE_BF16)
     return d_head == 64 ? run<bf16, 64, WAVES>(p, (unsigned)grid, stream)
                         : run<bf16, 32, WAVES>(p, (unsigned)grid, stream);
@@ -515,9 +543,9 @@ hipError_t launch_attention(sqa_dtype dt, const void* q, const void* k, const vo
   const int64_t tail = grid8 % cus;
   if (!causal && tail != 0 && 2 * tail <= cus) {
     const int64_t grid4 = plan<4>(p, B, H_kv);
-    return dispatch<4>(dt, d_head, p, grid4, stream);
+    return dispatch<4>(dt, d_head, p, grid4, cus, stream);
   }
-  return dispatch<8>(dt, d_head, p8, grid8, stream);
+  return dispatch<8>(dt, d_head, p8, grid8, cus, stream);
 }
 
 }  // namespace sqa
