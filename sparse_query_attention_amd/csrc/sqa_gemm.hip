@@ -19,9 +19,13 @@
 //  * Workgroups are dispatched round-robin over the 8 XCDs, each with its own
 //    L2. The 1-D grid is remapped so that every column tile of a row block
 //    runs on one XCD, and that row block of A is fetched from memory once.
+//  * LDS fragments are read one k-step of 16 ahead of the MFMAs that use them,
+//    across the stage boundary too, so LDS latency overlaps the MFMAs.
 //  * Rows past the end of A are loaded from a clamped, valid row and never
 //    stored as computed: step 1 writes zeros there (the padded rows of the
 //    Q/K/V^T layouts), step 3 skips them.
+//  * The epilogue stages the C tile in LDS and writes it in 16-byte chunks that
+//    run along contiguous memory: rows of Q, K and Y, sequence runs of V^T.
 #include "sqa_device.h"
 #include "sqa_internal.h"
 
@@ -77,49 +81,61 @@ template <typename T> struct DenseRows {
   __device__ const T* row(int64_t gr) const { return a + (gr < M ? gr : M - 1) * K; }
 };
 
-// Step 1 epilogue: route column n to q, k or vt and row gr to (b, t).
+// Epilogue interface. The workgroup's C tile reaches memory in 16-byte chunks
+// from LDS, one 32x32 block at a time. store.col_major(n) says whether the
+// block whose first column is n is staged column by column (its chunks run
+// along rows) or row by row (chunks run along columns). store.tile(m0) gives
+// the tile whose rows start at m0, with rows r counted from m0:
+//  * zero_row(r): row r is stored as zeros (padding of the Q/K/V^T layouts);
+//  * row_chunk(r, n, c): C[r][n .. n+E-1]; col_chunk(r, n, c): C[r .. r+E-1][n],
+//    with E = 16 / sizeof(T).
+
+// Step 1: column n goes to q, k or vt, row to (b, t). A 128-row tile lies in
+// one batch (Np is a multiple of 256). V^T blocks are column-major so that
+// their chunks are runs of t, contiguous in vt.
 template <typename T> struct QkvStore {
-  T* q; T* k; T* vt; int64_t N, Np; int H_q, H_kv, D, wq_w, wkv_w;
-  // v[i] is C[gr + i][n] for i = 0..3 (four consecutive rows of one batch, one column).
-  __device__ void operator()(int64_t gr, int n, const float v[4]) const {
-    const int64_t b = gr / Np, t = gr - b * Np;
-    float w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = t + i < N ? v[i] : 0.f;
-    if (n < wq_w) {
-      T* p = q + ((b * H_q + n / D) * Np + t) * D + n % D;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) p[(int64_t)i * D] = from_f32<T>(w[i]);
-      return;
-    }
-    n -= wq_w;
-    if (n < wkv_w) {
-      T* p = k + ((b * H_kv + n / D) * Np + t) * D + n % D;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) p[(int64_t)i * D] = from_f32<T>(w[i]);
-      return;
-    }
-    n -= wkv_w;
-    if (n < wkv_w) {
-      // V^T: the four rows are four consecutive t, contiguous in vt.
-      T* p = vt + ((b * H_kv + n / D) * (int64_t)D + n % D) * Np + t;
-      if constexpr (sizeof(T) == 2) {
-        *reinterpret_cast<bf16x4*>(p) =
-            bf16x4{from_f32<T>(w[0]), from_f32<T>(w[1]), from_f32<T>(w[2]), from_f32<T>(w[3])};
-      } else {
-        *reinterpret_cast<f32x4*>(p) = f32x4{w[0], w[1], w[2], w[3]};
+  T* q; T* k; T* vt; int64_t N, Np; int H_q, H_kv, dsh, wq_w, wkv_w;   // d_head = 1 << dsh
+  __device__ bool col_major(int n) const { return n >= wq_w + wkv_w; }
+  struct Tile {
+    T* q; T* k; T* vt;   // batch b's slices, row t0
+    int t0, n_valid, dsh, wq_w, wkv_w; int64_t Np;
+    __device__ bool zero_row(int r) const { return t0 + r >= n_valid; }
+    __device__ void row_chunk(int r, int n, const Chunk& c) const {
+      const int64_t t = t0 + r;
+      T* p;
+      if (n < wq_w) p = q + ((int64_t)(n >> dsh) * Np + t) * (1 << dsh) + (n & ((1 << dsh) - 1));
+      else {
+        n -= wq_w;
+        p = k + ((int64_t)(n >> dsh) * Np + t) * (1 << dsh) + (n & ((1 << dsh) - 1));
       }
+      *reinterpret_cast<Chunk*>(p) = c;
     }
+    __device__ void col_chunk(int r, int n, const Chunk& c) const {
+      n -= wq_w + wkv_w;   // V^T row (head n >> dsh, dim n & mask) is row n of batch b's block
+      *reinterpret_cast<Chunk*>(vt + (int64_t)n * Np + t0 + r) = c;
+    }
+  };
+  __device__ Tile tile(int64_t m0) const {
+    const int64_t b = m0 / Np, t0 = m0 - b * Np;
+    const int64_t d = (int64_t)1 << dsh;
+    return Tile{q + b * H_q * Np * d, k + b * H_kv * Np * d, vt + b * H_kv * d * Np,
+                (int)t0, (int)N, dsh, wq_w, wkv_w, Np};
   }
 };
 
+// Step 3: plain row-major out [M, ncols]; rows past M are not stored.
 template <typename T> struct DenseStore {
   T* out; int64_t M; int ncols;
-  __device__ void operator()(int64_t gr, int n, const float v[4]) const {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (gr + i < M) out[(gr + i) * ncols + n] = from_f32<T>(v[i]);
-  }
+  __device__ bool col_major(int) const { return false; }
+  struct Tile {
+    T* out; int64_t rows_left; int ncols;   // rows from m0 on
+    __device__ bool zero_row(int) const { return false; }
+    __device__ void row_chunk(int r, int n, const Chunk& c) const {
+      if (r < rows_left) *reinterpret_cast<Chunk*>(out + (int64_t)r * ncols + n) = c;
+    }
+    __device__ void col_chunk(int, int, const Chunk&) const {}
+  };
+  __device__ Tile tile(int64_t m0) const { return Tile{out + m0 * ncols, M - m0, ncols}; }
 };
 
 // C = A * W with W given transposed (wt [ncols, K]); see the file header.
@@ -184,41 +200,104 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Rows rows, const T* wt, i
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-#pragma unroll
-  for (int s = 0; s < NST - 1; ++s) issue(s);
-  wait_vmcnt_stages<C::VM, NST - 2>(min(NST - 2, nk - 1));
-  for (int kt = 0; kt < nk; ++kt) {
-    // stage kt is visible to every wave; stage kt-1's slot is free
-    __syncthreads();
-    issue(kt + NST - 1);
+  // Fragments of stage kt, k-step s, for this wave's 2x2 MFMA tiles.
+  constexpr int SUB = BK / MF::KS;
+  auto read = [&](int kt, int s, Frag (&a)[2], Frag (&b)[2]) {
     const T* st = smem + (kt % NST) * C::STAGE;
 #pragma unroll
-    for (int s = 0; s < BK / MF::KS; ++s) {
-      Frag a[2], b[2];
+    for (int i = 0; i < 2; ++i) a[i] = frag(st, wm * 64 + i * 32 + col, s);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) a[i] = frag(st, wm * 64 + i * 32 + col, s);
+    for (int j = 0; j < 2; ++j) b[j] = frag(st + C::A_ELEMS, wn * 64 + j * 32 + col, s);
+  };
+
+  // All NST stages in flight; stage 0 visible; its first fragments read.
 #pragma unroll
-      for (int j = 0; j < 2; ++j) b[j] = frag(st + C::A_ELEMS, wn * 64 + j * 32 + col, s);
+  for (int s = 0; s < NST; ++s) issue(s);
+  wait_vmcnt_stages<C::VM, NST - 1>(min(NST - 1, nk - 1));
+  __syncthreads();
+  Frag ca[2], cb[2];
+  read(0, 0, ca, cb);
+  for (int kt = 0; kt < nk; ++kt) {
+#pragma unroll
+    for (int s = 0; s < SUB; ++s) {
+      Frag na[2], nb[2];
+      if (s + 1 < SUB) {
+        read(kt, s + 1, na, nb);
+      } else if (kt + 1 < nk) {
+        // Stage kt+1 complete for this wave (later stages may be in flight),
+        // then visible to all; every wave's reads of stage kt are done, so its
+        // slot takes stage kt+NST.
+        wait_vmcnt_stages<C::VM, NST - 2>(min(NST - 2, max(0, nk - 2 - kt)));
+        __syncthreads();
+        issue(kt + NST);
+        read(kt + 1, 0, na, nb);
+      }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = MF::run(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < 2; ++j) acc[i][j] = MF::run(ca[i], cb[j], acc[i][j]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) { ca[i] = na[i]; cb[i] = nb[i]; }
     }
-    // this wave's loads of stage kt+1 are complete (later stages may be in flight)
-    wait_vmcnt_stages<C::VM, NST - 2>(min(NST - 2, max(0, nk - 2 - kt)));
   }
 
+  // Epilogue through LDS (the ring is free once every wave has passed this
+  // barrier). Block (bi, bj) is the 32x32 sub-tile at rows 32*bi, columns
+  // 32*bj; each is staged row- or column-major as the store asks, in lines of
+  // 32 elements with a 16-byte pad against bank conflicts. Then all threads
+  // write 16-byte chunks, four (bf16) or eight (fp32) per line.
+  constexpr int LINE = 32 * (int)sizeof(T) + 16;   // bytes per staged line
+  constexpr int BLOCK = 32 * LINE;
+  constexpr int EPC = 16 / (int)sizeof(T);
+  static_assert(16 * BLOCK <= NST * C::STAGE * (int)sizeof(T), "epilogue fits the ring");
+  char* ep = reinterpret_cast<char*>(smem);
+  const auto tile = store.tile(m0);
+  __syncthreads();
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 2; ++j) {
+      const int bi = wm * 2 + i, bj = wn * 2 + j;
+      char* blk = ep + (bi * 4 + bj) * BLOCK;
+      // accumulator register r of this lane: row 8*(r/4) + 4*grp + r%4, column col
+      if (store.col_major(n0 + 32 * bj)) {
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const float v[4] = {acc[i][j][4 * rq], acc[i][j][4 * rq + 1], acc[i][j][4 * rq + 2],
-                            acc[i][j][4 * rq + 3]};
-        const int n = n0 + wn * 64 + j * 32 + col;
-        if (n < ncols) store(m0 + wm * 64 + i * 32 + 8 * rq + 4 * grp, n, v);
+        for (int rq = 0; rq < 4; ++rq) {
+          const int r0 = 8 * rq + 4 * grp;
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            v[e] = tile.zero_row(32 * bi + r0 + e) ? 0.f : acc[i][j][4 * rq + e];
+          T* dst = reinterpret_cast<T*>(blk + col * LINE) + r0;
+          if constexpr (sizeof(T) == 2) {
+            *reinterpret_cast<bf16x4*>(dst) =
+                bf16x4{from_f32<T>(v[0]), from_f32<T>(v[1]), from_f32<T>(v[2]), from_f32<T>(v[3])};
+          } else {
+            *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+          }
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 8 * (r / 4) + 4 * grp + r % 4;
+          const bool z = tile.zero_row(32 * bi + row);
+          reinterpret_cast<T*>(blk + row * LINE)[col] = from_f32<T>(z ? 0.f : acc[i][j][r]);
+        }
       }
+    }
+  __syncthreads();
+  constexpr int CPL = 32 / EPC;                  // chunks per line
+  constexpr int CHUNKS = 16 * 32 * CPL;
+#pragma unroll
+  for (int cidx = tid; cidx < CHUNKS; cidx += THREADS) {
+    const int blkid = cidx / (32 * CPL), line = (cidx / CPL) % 32, qc = cidx % CPL;
+    const int bi = blkid / 4, bj = blkid % 4;
+    const int n_b = n0 + 32 * bj;
+    if (n_b >= ncols) continue;
+    const Chunk c = *reinterpret_cast<const Chunk*>(ep + blkid * BLOCK + line * LINE + qc * 16);
+    if (store.col_major(n_b)) tile.col_chunk(32 * bi + qc * EPC, n_b + line, c);
+    else tile.row_chunk(32 * bi + line, n_b + qc * EPC, c);
+  }
 }
 
 // W^T [ncols, K] from W = [W0 | W1 | W2] ([K, w0], [K, w1], [K, w2] row-major;
@@ -274,7 +353,8 @@ hipError_t qkv_impl(const void* x, const void* wq, const void* wk, const void* w
                               (int)d_model, stream);
   if (e != hipSuccess) return e;
   PaddedRows<T> rows{(const T*)x, N, Np, (int)d_model};
-  QkvStore<T> st{(T*)q, (T*)k, (T*)vt, N, Np, (int)H_q, (int)H_kv, (int)d, wq_w, wkv_w};
+  const int dsh = d == 64 ? 6 : 5;   // d_head is 32 or 64 (checked by the caller)
+  QkvStore<T> st{(T*)q, (T*)k, (T*)vt, N, Np, (int)H_q, (int)H_kv, dsh, wq_w, wkv_w};
   gemm_kernel<T><<<(unsigned)grid_size(n_rb, n_ct), THREADS, 0, stream>>>(
       rows, (const T*)wt, ncols, st, (int)d_model, (int)n_rb, (int)n_ct);
   return hipGetLastError();
