@@ -26,6 +26,8 @@
 //    Q/K/V^T layouts), step 3 skips them.
 //  * The epilogue stages the C tile in LDS and writes it in 16-byte chunks that
 //    run along contiguous memory: rows of Q, K and Y, sequence runs of V^T.
+#include <type_traits>
+
 #include "sqa_device.h"
 #include "sqa_internal.h"
 
@@ -210,36 +212,50 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Rows rows, const T* wt, i
     for (int j = 0; j < 2; ++j) b[j] = frag(st + C::A_ELEMS, wn * 64 + j * 32 + col, s);
   };
 
-  // All NST stages in flight; stage 0 visible; its first fragments read.
+  // The MFMA operand order fixes which way the accumulator's runs of four go:
+  // A*B gives runs along rows, B*A (the tile transposed) runs along columns.
+  // A workgroup whose blocks are all staged row-major takes B*A, so that it
+  // stages four consecutive columns per write.
+  bool rows_all = true;
 #pragma unroll
-  for (int s = 0; s < NST; ++s) issue(s);
-  wait_vmcnt_stages<C::VM, NST - 1>(min(NST - 1, nk - 1));
-  __syncthreads();
-  Frag ca[2], cb[2];
-  read(0, 0, ca, cb);
-  for (int kt = 0; kt < nk; ++kt) {
+  for (int bj = 0; bj < 4; ++bj) rows_all &= n0 + 32 * bj >= ncols || !store.col_major(n0 + 32 * bj);
+
+  auto main_loop = [&](auto transposed) {
+    constexpr bool TR = decltype(transposed)::value;
+    // All NST stages in flight; stage 0 visible; its first fragments read.
 #pragma unroll
-    for (int s = 0; s < SUB; ++s) {
-      Frag na[2], nb[2];
-      if (s + 1 < SUB) {
-        read(kt, s + 1, na, nb);
-      } else if (kt + 1 < nk) {
-        // Stage kt+1 complete for this wave (later stages may be in flight),
-        // then visible to all; every wave's reads of stage kt are done, so its
-        // slot takes stage kt+NST.
-        wait_vmcnt_stages<C::VM, NST - 2>(min(NST - 2, max(0, nk - 2 - kt)));
-        __syncthreads();
-        issue(kt + NST);
-        read(kt + 1, 0, na, nb);
+    for (int s = 0; s < NST; ++s) issue(s);
+    wait_vmcnt_stages<C::VM, NST - 1>(min(NST - 1, nk - 1));
+    __syncthreads();
+    Frag ca[2], cb[2];
+    read(0, 0, ca, cb);
+    for (int kt = 0; kt < nk; ++kt) {
+#pragma unroll
+      for (int s = 0; s < SUB; ++s) {
+        Frag na[2], nb[2];
+        if (s + 1 < SUB) {
+          read(kt, s + 1, na, nb);
+        } else if (kt + 1 < nk) {
+          // Stage kt+1 complete for this wave (later stages may be in flight),
+          // then visible to all; every wave's reads of stage kt are done, so
+          // its slot takes stage kt+NST.
+          wait_vmcnt_stages<C::VM, NST - 2>(min(NST - 2, max(0, nk - 2 - kt)));
+          __syncthreads();
+          issue(kt + NST);
+          read(kt + 1, 0, na, nb);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = TR ? MF::run(cb[j], ca[i], acc[i][j]) : MF::run(ca[i], cb[j], acc[i][j]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) { ca[i] = na[i]; cb[i] = nb[i]; }
       }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = MF::run(ca[i], cb[j], acc[i][j]);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) { ca[i] = na[i]; cb[i] = nb[i]; }
     }
-  }
+  };
+  if (rows_all) main_loop(std::true_type{});
+  else main_loop(std::false_type{});
 
   // Epilogue through LDS (the ring is free once every wave has passed this
   // barrier). Block (bi, bj) is the 32x32 sub-tile at rows 32*bi, columns
@@ -259,8 +275,24 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Rows rows, const T* wt, i
     for (int j = 0; j < 2; ++j) {
       const int bi = wm * 2 + i, bj = wn * 2 + j;
       char* blk = ep + (bi * 4 + bj) * BLOCK;
-      // accumulator register r of this lane: row 8*(r/4) + 4*grp + r%4, column col
-      if (store.col_major(n0 + 32 * bj)) {
+      if (rows_all) {
+        // transposed: register r holds row col, column 8*(r/4) + 4*grp + r%4
+        const bool z = tile.zero_row(32 * bi + col);
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = z ? 0.f : acc[i][j][4 * rq + e];
+          T* dst = reinterpret_cast<T*>(blk + col * LINE) + 8 * rq + 4 * grp;
+          if constexpr (sizeof(T) == 2) {
+            *reinterpret_cast<bf16x4*>(dst) =
+                bf16x4{from_f32<T>(v[0]), from_f32<T>(v[1]), from_f32<T>(v[2]), from_f32<T>(v[3])};
+          } else {
+            *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+          }
+        }
+      } else if (store.col_major(n0 + 32 * bj)) {
+        // register r of this lane: row 8*(r/4) + 4*grp + r%4, column col
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
           const int r0 = 8 * rq + 4 * grp;
