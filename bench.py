@@ -9,7 +9,8 @@ already resident in HBM. The headline workload is standard SQA at 131072
 tokens, causal (H=16, H_q=8, H_kv=4, d_head=64, bf16). This is the middle of the
 32k-200k range that the SQA paper's abstract benchmarks. The other long
 workloads and their equally shaped MHA/GQA/MQA baselines are timed as well and
-reported under "variants".
+reported under "variants", with a sweep of H_kv at fixed H_q (attention time
+should not depend on H_kv).
 
 Prints ONE JSON line. FLOPs use the closed form: attention core
 4*B*H_q*N^2*d_head (halved when causal) plus the projections
@@ -263,6 +264,19 @@ def main():
                 variants[key] = {"attention": round(sb["attention_ms"] / sv["attention_ms"], 3),
                                  "whole_forward": round(sb["ms_per_step"] / sv["ms_per_step"], 3),
                                  "ideal_H_over_H_q": b.H_q / v.H_q}
+        # Attention time at fixed H_q = 4 as H_kv shrinks 4 -> 2 -> 1. Score FLOPs
+        # depend on H_q alone, so fewer key/value heads should not cut the core
+        # time (ReactiveAI/xSMQAT-m model card, description and conclusion: xSMQA
+        # trains no faster than xSQA).
+        sweep = {}
+        for hkv in (4, 2, 1):
+            v = wl.XSQA_32K.with_(name=f"xsqa_bf16_n32768_hkv{hkv}", H_kv=hkv,
+                                  baseline_H_q=None, baseline_H_kv=None)
+            r = run_workload(v, vsteps, vwarm, torch, sqa, dev, stage_timing=True)
+            sweep[f"H_kv={hkv}"] = round(r["kernel_ms"]["attention"], 4)
+        times = list(sweep.values())
+        variants["hkv_sweep_n32768_hq4_attention_ms"] = dict(
+            sweep, max_over_min=round(max(times) / min(times), 3))
 
     line = {
         "metric": "SQA fwd tokens/s + TFLOP/s (% bf16 MFMA peak) at N=32k-200k, 1 GPU",

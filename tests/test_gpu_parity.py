@@ -146,9 +146,12 @@ def test_ssqa_1k_causal_workload_and_gqa_baseline(dev):
 # full sizes: sampled rows
 
 LONG = [wl.XSQA_32K, wl.SQA_131K_CAUSAL, wl.XSMQA_200K]
+# fixed H_q = 4 at 32k tokens with fewer key/value heads (the bench's H_kv sweep)
+HKV_SWEEP = [wl.XSQA_32K.with_(name=f"xsqa_bf16_n32768_hkv{h}", H_kv=h, baseline_H_q=None,
+                               baseline_H_kv=None) for h in (2, 1)]
 
 
-@pytest.mark.parametrize("w", LONG + [x.baseline() for x in LONG], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", LONG + [x.baseline() for x in LONG] + HKV_SWEEP, ids=lambda w: w.name)
 def test_long_workloads_on_sampled_rows(dev, w):
     log(f"case {w.name}: B={w.B} N={w.N} H_q={w.H_q} H_kv={w.H_kv} causal={w.causal}")
     host, d = device_inputs(w, dev)
@@ -163,6 +166,29 @@ def test_long_workloads_on_sampled_rows(dev, w):
     rep = compare(yg, ref, w.dtype)
     log(f"  {rows.size} rows: {rep}")
     assert rep.ok, f"{w.name}: {rep}"
+
+
+@pytest.mark.parametrize("w", LONG, ids=lambda w: w.name)
+def test_long_workloads_write_every_element(dev, w):
+    """Every output element of every step is written, at the full sizes and
+    launch shapes that the bench times (work-unit order, tails, padding): the
+    buffers start as NaN and must come back finite."""
+    log(f"case {w.name}: every element written")
+    _, d = device_inputs(w, dev)
+    Np = sqa.padded_length(w.N)
+    nan = float("nan")
+    q = torch.full((w.B, w.H_q, Np, w.d_head), nan, dtype=torch.bfloat16, device=dev)
+    k = torch.full((w.B, w.H_kv, Np, w.d_head), nan, dtype=torch.bfloat16, device=dev)
+    vt = torch.full((w.B, w.H_kv, w.d_head, Np), nan, dtype=torch.bfloat16, device=dev)
+    sqa.qkv_projection(d["X"], d["Wq"], d["Wk"], d["Wv"], H=w.H, H_q=w.H_q, H_kv=w.H_kv, q=q, k=k, vt=vt)
+    a = torch.full((w.B * w.N, w.H_q * w.d_head), nan, dtype=torch.bfloat16, device=dev)
+    sqa.attention(q, k, vt, N=w.N, causal=w.causal, a=a)
+    y = torch.full((w.B * w.N, w.d_model), nan, dtype=torch.bfloat16, device=dev)
+    sqa.output_projection(a, d["Wo"], out=y)
+    torch.cuda.synchronize()
+    for name, t in (("q", q), ("k", k), ("vt", vt), ("a", a), ("y", y)):
+        assert bool(torch.isfinite(t).all()), f"{w.name}: {name} has unwritten elements"
+    assert not bool(q[:, :, w.N:].any()) and not bool(vt[..., w.N:].any()), "padding rows not zero"
 
 
 # ----------------------------------------------------------------------------------------------
