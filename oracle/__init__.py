@@ -4,8 +4,9 @@ Only tests/, __graft_entry__.smoke() and bench.py's CPU-baseline leg may import
 this package. The HIP library and its Python binding never do.
 """
 from .sqa_oracle import (round_bf16, kv_head_for, split_heads, softmax_probs, attention_rows,
-                         sqa_forward, sqa_forward_rows)
+                         sqa_forward, sqa_forward_rows, sqa_forward_varlen, sqa_forward_varlen_rows)
 from .bruteforce import sqa_forward_bruteforce
 
 __all__ = ["round_bf16", "kv_head_for", "split_heads", "softmax_probs", "attention_rows",
-           "sqa_forward", "sqa_forward_rows", "sqa_forward_bruteforce"]
+           "sqa_forward", "sqa_forward_rows", "sqa_forward_varlen", "sqa_forward_varlen_rows",
+           "sqa_forward_bruteforce"]

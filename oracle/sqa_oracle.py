@@ -210,3 +210,56 @@ def sqa_forward_rows(X, Wq, Wk, Wv, Wo, H_q: int, H_kv: int, d_head: int, causal
     A_rows = _maybe_round(A_rows, bf16)
     Y_rows = _maybe_round(A_rows @ Wo, bf16)
     return {"A_rows": A_rows, "Y_rows": Y_rows}
+
+
+def check_lens(lens, B: int, N: int) -> np.ndarray:
+    lens = np.asarray(lens, dtype=np.int64).reshape(-1)
+    if lens.size != B or (lens.size and (lens.min() < 0 or lens.max() > N)):
+        raise ValueError("lens must hold B lengths in [0, N]")
+    return lens
+
+
+def sqa_forward_varlen(X, Wq, Wk, Wv, Wo, lens, H_q: int, H_kv: int, d_head: int, causal: bool,
+                       bf16: bool, workers: Optional[int] = None) -> np.ndarray:
+    """SQA forward over a batch of sequences padded to a common length N.
+
+    The model cards' training examples build their datasets with a maximum
+    sequence length (ReactiveAI/xSMQAT-m and ReactiveAI/GQA-Ref-Micro, training
+    example), so a batch holds sequences of up to N tokens. Sequence b is the
+    first lens[b] rows of X[b]; it is one SQA forward over those tokens alone
+    (its keys end at lens[b], whatever the padding rows hold). The pages define
+    no output at padding positions; those rows of Y are zero.
+    Returns Y [B, N, d_model] as float64.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    B, N, D = check_shapes(X, Wq, Wk, Wv, Wo, H_q, H_kv, d_head)
+    lens = check_lens(lens, B, N)
+    Y = np.zeros((B, N, D), dtype=np.float64)
+    for b in range(B):
+        L = int(lens[b])
+        if L:
+            Y[b, :L] = sqa_forward(X[b:b + 1, :L], Wq, Wk, Wv, Wo, H_q, H_kv, d_head, causal, bf16,
+                                   workers=workers)["Y"][0]
+    return Y
+
+
+def sqa_forward_varlen_rows(X, Wq, Wk, Wv, Wo, lens, H_q: int, H_kv: int, d_head: int,
+                            causal: bool, bf16: bool, rows: Iterable[int],
+                            workers: Optional[int] = None) -> np.ndarray:
+    """sqa_forward_varlen evaluated only at the flat rows ``rows`` (row = b*N + t).
+    Returns Y_rows [R, d_model] in the order of ``rows``."""
+    X = np.asarray(X, dtype=np.float64)
+    B, N, D = check_shapes(X, Wq, Wk, Wv, Wo, H_q, H_kv, d_head)
+    lens = check_lens(lens, B, N)
+    rows = np.asarray(list(rows), dtype=np.int64)
+    if rows.size and (rows.min() < 0 or rows.max() >= B * N):
+        raise ValueError("row index out of range")
+    Y_rows = np.zeros((rows.size, D), dtype=np.float64)
+    for b in np.unique(rows // N):
+        b = int(b)
+        L = int(lens[b])
+        sel = np.nonzero((rows // N == b) & (rows % N < L))[0]
+        if sel.size:
+            Y_rows[sel] = sqa_forward_rows(X[b:b + 1, :L], Wq, Wk, Wv, Wo, H_q, H_kv, d_head, causal,
+                                           bf16, rows=rows[sel] % N, workers=workers)["Y_rows"]
+    return Y_rows

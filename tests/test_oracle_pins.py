@@ -320,3 +320,102 @@ def test_planted_transposed_head_split_is_caught(monkeypatch):
     y_bf, _ = sqa_forward_bruteforce(X, Wq, Wk, Wv, Wo, 4, 2, 2, False, False)
     y = oracle.sqa_forward(X, Wq, Wk, Wv, Wo, 4, 2, 2, False, False)["Y"]
     assert not np.allclose(y, np.array(y_bf), rtol=1e-9, atol=1e-9)
+
+
+# ----------------------------------------------------------------------------------------------
+# variable-length batches (sequences padded to a common N)
+
+def test_varlen_with_full_lengths_is_the_plain_forward():
+    X, Wq, Wk, Wv, Wo = _rand_problem(61, B=3, N=40, H=4, d_head=8, H_q=2, H_kv=1)
+    for causal in (False, True):
+        y = oracle.sqa_forward_varlen(X, Wq, Wk, Wv, Wo, [40, 40, 40], 2, 1, 8, causal, True)
+        ref = oracle.sqa_forward(X, Wq, Wk, Wv, Wo, 2, 1, 8, causal, True)["Y"]
+        np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_matches_bruteforce_per_sequence(causal):
+    """Each sequence against the independent scalar-loop forward run on that
+    sequence's own tokens; padding rows are zero."""
+    X, Wq, Wk, Wv, Wo = _rand_problem(62, B=4, N=7, H=4, d_head=2, H_q=2, H_kv=1)
+    lens = [7, 3, 0, 1]
+    y = oracle.sqa_forward_varlen(X, Wq, Wk, Wv, Wo, lens, 2, 1, 2, causal, False)
+    for b, L in enumerate(lens):
+        if L:
+            yb, _ = sqa_forward_bruteforce(X[b:b + 1, :L], Wq, Wk, Wv, Wo, 2, 1, 2, causal, False)
+            np.testing.assert_allclose(y[b, :L], np.array(yb)[0], rtol=1e-12, atol=1e-14)
+        assert not y[b, L:].any()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_ignores_padding_and_other_sequences(causal):
+    X, Wq, Wk, Wv, Wo = _rand_problem(63, B=3, N=33, H=4, d_head=8, H_q=4, H_kv=2)
+    lens = [20, 33, 5]
+    y0 = oracle.sqa_forward_varlen(X, Wq, Wk, Wv, Wo, lens, 4, 2, 8, causal, True)
+    X2 = X.copy()
+    X2[0, 20:] = np.nan                 # padding of sequence 0
+    X2[2, 5:] = 1e30                    # padding of sequence 2
+    y1 = oracle.sqa_forward_varlen(X2, Wq, Wk, Wv, Wo, lens, 4, 2, 8, causal, True)
+    np.testing.assert_array_equal(y0, y1)
+    X3 = X.copy()
+    X3[1] *= -3.0                       # a different sequence 1 leaves 0 and 2 alone
+    y2 = oracle.sqa_forward_varlen(X3, Wq, Wk, Wv, Wo, lens, 4, 2, 8, causal, True)
+    np.testing.assert_array_equal(y0[[0, 2]], y2[[0, 2]])
+    assert not np.array_equal(y0[1], y2[1])
+
+
+def test_varlen_causal_prefix_equals_full_run():
+    """Causal row t sees keys <= t only, so cutting a sequence at L leaves its
+    first L rows as in the uncut run."""
+    X, Wq, Wk, Wv, Wo = _rand_problem(64, B=2, N=50, H=4, d_head=8, H_q=2, H_kv=2)
+    full = oracle.sqa_forward(X, Wq, Wk, Wv, Wo, 2, 2, 8, True, True)["Y"]
+    y = oracle.sqa_forward_varlen(X, Wq, Wk, Wv, Wo, [50, 17], 2, 2, 8, True, True)
+    np.testing.assert_allclose(y[0], full[0], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(y[1, :17], full[1, :17], rtol=1e-12, atol=1e-14)
+    # without the causal mask the cut changes the kept rows (keys past 17 matter)
+    nc = oracle.sqa_forward(X, Wq, Wk, Wv, Wo, 2, 2, 8, False, True)["Y"]
+    ync = oracle.sqa_forward_varlen(X, Wq, Wk, Wv, Wo, [50, 17], 2, 2, 8, False, True)
+    assert not np.allclose(ync[1, :17], nc[1, :17])
+
+
+def test_varlen_rows_match_full_varlen():
+    X, Wq, Wk, Wv, Wo = _rand_problem(65, B=3, N=30, H=4, d_head=8, H_q=2, H_kv=1)
+    lens = [30, 0, 11]
+    for causal in (False, True):
+        y = oracle.sqa_forward_varlen(X, Wq, Wk, Wv, Wo, lens, 2, 1, 8, causal, True)
+        rows = [0, 29, 30, 45, 60, 70, 71, 89]
+        yr = oracle.sqa_forward_varlen_rows(X, Wq, Wk, Wv, Wo, lens, 2, 1, 8, causal, True, rows)
+        np.testing.assert_allclose(yr, y.reshape(-1, 32)[rows], rtol=1e-12, atol=1e-14)
+
+
+def test_varlen_rejects_bad_lengths():
+    X, Wq, Wk, Wv, Wo = _rand_problem(66, B=2, N=8, H=4, d_head=2, H_q=2, H_kv=1)
+    for lens in ([9, 1], [-1, 1], [1]):
+        with pytest.raises(ValueError):
+            oracle.sqa_forward_varlen(X, Wq, Wk, Wv, Wo, lens, 2, 1, 2, False, False)
+
+
+def _bad_varlen_full_keys(X, Wq, Wk, Wv, Wo, lens, H_q, H_kv, d_head, causal, bf16, workers=None):
+    """Planted: queries stop at lens[b] but every padded key is still attended."""
+    Y = oracle.sqa_forward(X, Wq, Wk, Wv, Wo, H_q, H_kv, d_head, causal, bf16)["Y"]
+    for b, L in enumerate(lens):
+        Y[b, L:] = 0.0
+    return Y
+
+
+def _bad_varlen_unzeroed_padding(X, Wq, Wk, Wv, Wo, lens, H_q, H_kv, d_head, causal, bf16, workers=None):
+    """Planted: right valid rows, but padding rows keep computed values."""
+    X = np.asarray(X, dtype=np.float64)
+    Y = oracle.sqa_forward(X, Wq, Wk, Wv, Wo, H_q, H_kv, d_head, causal, bf16)["Y"]
+    for b, L in enumerate(lens):
+        if L:
+            Y[b, :L] = oracle.sqa_forward(X[b:b + 1, :L], Wq, Wk, Wv, Wo, H_q, H_kv, d_head, causal,
+                                          bf16)["Y"][0]
+    return Y
+
+
+@pytest.mark.parametrize("bad", [_bad_varlen_full_keys, _bad_varlen_unzeroed_padding])
+def test_planted_varlen_mistakes_are_caught(monkeypatch, bad):
+    monkeypatch.setattr(oracle, "sqa_forward_varlen", bad)
+    with pytest.raises(AssertionError):
+        test_varlen_matches_bruteforce_per_sequence(False)
