@@ -10,7 +10,8 @@ tokens, causal (H=16, H_q=8, H_kv=4, d_head=64, bf16). This is the middle of the
 32k-200k range that the SQA paper's abstract benchmarks. The other long
 workloads and their equally shaped MHA/GQA/MQA baselines are timed as well and
 reported under "variants", with a sweep of H_kv at fixed H_q (attention time
-should not depend on H_kv).
+should not depend on H_kv) and a padded batch of sequences of mixed length
+(sqa_forward_varlen).
 
 Prints ONE JSON line. FLOPs use the closed form: attention core
 4*B*H_q*N^2*d_head (halved when causal) plus the projections
@@ -27,6 +28,8 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
 
 import workloads as wl  # noqa: E402
 
@@ -146,6 +149,56 @@ def run_workload(w: wl.Workload, steps: int, warmup: int, torch, sqa, dev, stage
                 tot[name] += ev[i].elapsed_time(ev[i + 1])
         res["kernel_ms"] = {k: v / steps for k, v in tot.items()}
         del q, k, vt, a, y
+    del d, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_varlen(w: wl.Workload, steps: int, warmup: int, torch, sqa, dev):
+    """sqa_forward_varlen on a padded batch with w's length mix, against
+    sqa_forward on the same padded batch (every row treated as a token), timed
+    with events on the stream. Rates count the work each call does for real
+    tokens: the tokens of each sequence and the causal (or full) query-key
+    pairs within it."""
+    host = wl.to_device_dtype(wl.draw(w), w.dtype)
+    d = {k: v.to(dev) for k, v in host.items()}
+    del host
+    lens = wl.draw_lens(w)
+    stream = torch.cuda.current_stream(dev)
+    tm = Timer(torch, stream)
+    out = torch.empty_like(d["X"])
+    res = {}
+    for label, ln in (("varlen", lens), ("padded_dense", np.full(w.B, w.N, dtype=np.int32))):
+        lt = torch.from_numpy(ln).to(dev)
+
+        def step():
+            if label == "varlen":
+                sqa.forward_varlen(d["X"], d["Wq"], d["Wk"], d["Wv"], d["Wo"], lt, H=w.H,
+                                   H_q=w.H_q, H_kv=w.H_kv, causal=w.causal, out=out)
+            else:
+                sqa.forward(d["X"], d["Wq"], d["Wk"], d["Wv"], d["Wo"], H=w.H, H_q=w.H_q,
+                            H_kv=w.H_kv, causal=w.causal, out=out)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        e0 = tm.event()
+        for _ in range(steps):
+            step()
+        e1 = tm.event()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        L = ln.astype(np.float64)
+        pairs = float((L * (L + 1) / 2).sum() if w.causal else (L * L).sum())
+        core = 4.0 * w.H_q * w.d_head * pairs
+        proj = 2.0 * float(L.sum()) * w.d_model * w.d_head * (2 * w.H_q + 2 * w.H_kv)
+        res[label] = {"ms_per_step": round(ms, 4),
+                      "valid_tokens": int(L.sum()),
+                      "tokens_per_s": round(float(L.sum()) / (ms / 1e3), 1),
+                      "tflops_valid_work": round((core + proj) / (ms / 1e3) / 1e12, 2)}
+    res["lens"] = lens.tolist()
+    res["time_vs_padded_dense"] = round(res["varlen"]["ms_per_step"] /
+                                        res["padded_dense"]["ms_per_step"], 3)
     del d, out
     torch.cuda.empty_cache()
     return res
@@ -277,6 +330,9 @@ def main():
         times = list(sweep.values())
         variants["hkv_sweep_n32768_hq4_attention_ms"] = dict(
             sweep, max_over_min=round(max(times) / min(times), 3))
+        # A padded batch of sequences of mixed length (sqa_forward_varlen).
+        variants[wl.SQA_VARLEN_32K.name] = run_varlen(wl.SQA_VARLEN_32K, vsteps, vwarm, torch, sqa,
+                                                      dev)
 
     line = {
         "metric": "SQA fwd tokens/s + TFLOP/s (% bf16 MFMA peak) at N=32k-200k, 1 GPU",

@@ -88,6 +88,26 @@ sqa_status sqa_forward(const void* x, const void* Wq, const void* Wk, const void
                        sqa_dtype dtype, hipStream_t stream);
 
 /*
+ * sqa_forward_varlen - sqa_forward over a batch of sequences of different
+ * lengths, padded to a common N, as a training batch cut at a maximum sequence
+ * length holds them (ReactiveAI/xSMQAT-m and ReactiveAI/GQA-Ref-Micro model
+ * cards, training example).
+ *
+ *   lens  device array of B int32 values: sequence b is rows 0 .. lens[b]-1 of
+ *         x[b]. Values outside [0, N] are clamped into it.
+ *
+ * Each sequence is one SQA forward over its own tokens: its keys end at
+ * lens[b] (causal or not), whatever the padding rows of x hold. Rows t >= lens[b]
+ * of out are written as zeros. Everything else (layouts, workspace, errors) is
+ * as in sqa_forward. lens must be 4-byte aligned and must not overlap out;
+ * SQA_ERR_INVALID_ARG if it is null (unless B*N == 0).
+ */
+sqa_status sqa_forward_varlen(const void* x, const void* Wq, const void* Wk, const void* Wv,
+                              const void* Wo, void* out, const int32_t* lens, int64_t B, int64_t N,
+                              int64_t d_model, int64_t H, int64_t H_q, int64_t H_kv,
+                              int64_t d_head, int causal, sqa_dtype dtype, hipStream_t stream);
+
+/*
  * sqa_padded_length - Np, the sequence length of the Q/K/V^T layouts below:
  * N rounded up to a multiple of 256. Returns -1 for N < 0.
  */

@@ -20,7 +20,7 @@ from typing import Optional, Tuple
 from . import _lib
 from ._lib import SQAError
 
-__all__ = ["forward", "qkv_projection", "attention", "output_projection", "padded_length",
+__all__ = ["forward_varlen", "forward", "qkv_projection", "attention", "output_projection", "padded_length",
            "SQAError", "library_path"]
 
 library_path = _lib.LIB_PATH
@@ -81,6 +81,34 @@ def forward(x, Wq, Wk, Wv, Wo, *, H: int, H_q: int, H_kv: int, causal: bool = Fa
     _lib.check(lib.sqa_forward(x.data_ptr(), Wq.data_ptr(), Wk.data_ptr(), Wv.data_ptr(),
                                Wo.data_ptr(), out.data_ptr(), B, N, D, H, H_q, H_kv, d,
                                int(bool(causal)), _dtype_code(x), _stream(x.device)))
+    return out
+
+
+def forward_varlen(x, Wq, Wk, Wv, Wo, lens, *, H: int, H_q: int, H_kv: int, causal: bool = False,
+                   out=None):
+    """forward() over sequences padded to N: lens is an int32 tensor [B] on x's
+    device, sequence b being rows 0 .. lens[b]-1 of x[b]. Rows past a sequence's
+    length come back as zeros."""
+    lib = _lib.load()
+    if x.dim() != 3:
+        raise ValueError("x must be [B, N, d_model]")
+    B, N, D = x.shape
+    if H <= 0 or D % H:
+        raise ValueError("d_model must be a multiple of H")
+    d = D // H
+    torch = _torch()
+    if lens.dtype != torch.int32 or tuple(lens.shape) != (B,) or lens.device != x.device \
+            or not lens.is_contiguous():
+        raise ValueError("lens must be a contiguous int32 tensor [B] on x's device")
+    if out is None:
+        out = torch.empty_like(x)
+    for name, t, shp in (("x", x, (B, N, D)), ("Wq", Wq, (D, H_q * d)), ("Wk", Wk, (D, H_kv * d)),
+                         ("Wv", Wv, (D, H_kv * d)), ("Wo", Wo, (H_q * d, D)), ("out", out, (B, N, D))):
+        _check_tensor(name, t, shp, x.dtype, x.device)
+    _lib.check(lib.sqa_forward_varlen(x.data_ptr(), Wq.data_ptr(), Wk.data_ptr(), Wv.data_ptr(),
+                                      Wo.data_ptr(), out.data_ptr(), lens.data_ptr(), B, N, D, H,
+                                      H_q, H_kv, d, int(bool(causal)), _dtype_code(x),
+                                      _stream(x.device)))
     return out
 
 

@@ -161,6 +161,68 @@ struct PoolScratch {
   }
 };
 
+// sqa_forward (varlen false, lens unused) and sqa_forward_varlen.
+sqa_status forward_impl(const void* x, const void* Wq, const void* Wk, const void* Wv,
+                        const void* Wo, void* out, bool varlen, const int32_t* lens, int64_t B, int64_t N,
+                        int64_t d_model, int64_t H, int64_t H_q, int64_t H_kv, int64_t d_head,
+                        int causal, sqa_dtype dtype, hipStream_t stream) {
+  const Shape s{B, N, d_model, H, H_q, H_kv, d_head};
+  SQA_TRY(check_dtype(dtype));
+  SQA_TRY(check_heads(s, true));
+  if (causal != 0 && causal != 1) return fail(SQA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (B * N == 0) return ok();
+  SQA_TRY(check_ptr(x, "x is null", "x is not 16-byte aligned"));
+  SQA_TRY(check_ptr(Wq, "Wq is null", "Wq is not 16-byte aligned"));
+  SQA_TRY(check_ptr(Wk, "Wk is null", "Wk is not 16-byte aligned"));
+  SQA_TRY(check_ptr(Wv, "Wv is null", "Wv is not 16-byte aligned"));
+  SQA_TRY(check_ptr(Wo, "Wo is null", "Wo is not 16-byte aligned"));
+  SQA_TRY(check_ptr(out, "out is null", "out is not 16-byte aligned"));
+  if (!varlen) {
+    lens = nullptr;
+  } else if (lens == nullptr) {
+    return fail(SQA_ERR_INVALID_ARG, "lens is null");
+  } else if (reinterpret_cast<uintptr_t>(lens) & 3u) {
+    return fail(SQA_ERR_INVALID_ARG, "lens is not 4-byte aligned");
+  }
+  Sizes z;
+  SQA_TRY(sizes_for(s, dtype, &z));
+  const size_t es = elem_size(dtype);
+  const size_t yb = (size_t)(B * N * d_model) * es;
+  const size_t wqb = (size_t)(d_model * H_q * d_head) * es, wkb = (size_t)(d_model * H_kv * d_head) * es;
+  const void* ins[5] = {x, Wq, Wk, Wv, Wo};
+  const size_t inb[5] = {yb, wqb, wkb, wkb, wqb};
+  for (int j = 0; j < 5; ++j)
+    if (overlap(out, yb, ins[j], inb[j])) return fail(SQA_ERR_INVALID_ARG, "out overlaps an input");
+  if (lens && overlap(out, yb, lens, (size_t)B * sizeof(int32_t)))
+    return fail(SQA_ERR_INVALID_ARG, "out overlaps lens");
+
+  const int64_t off_k = round256(z.q), off_v = off_k + round256(z.kv);
+  const int64_t off_a = off_v + round256(z.kv), off_w1 = off_a + round256(z.a);
+  const int64_t off_w3 = off_w1 + round256((int64_t)sqa::qkv_wt_bytes(dtype, d_model, H_q, H_kv, d_head));
+  const int64_t total = off_w3 + round256((int64_t)sqa::out_wt_bytes(dtype, H_q * d_head, d_model));
+  hipMemPool_t pool;
+  SQA_TRY(pool_for(stream, &pool));
+  void* ws = nullptr;
+  hipError_t e = hipMallocFromPoolAsync(&ws, (size_t)total, pool, stream);
+  if (e != hipSuccess) return fail_hip(e, "workspace allocation");
+  char* base = (char*)ws;
+  void *q = base, *k = base + off_k, *vt = base + off_v, *a = base + off_a;
+  void *w1 = base + off_w1, *w3 = base + off_w3;
+
+  e = sqa::launch_qkv_projection(dtype, x, Wq, Wk, Wv, w1, q, k, vt, B, N, z.Np, d_model, H_q,
+                                 H_kv, d_head, lens, stream);
+  if (e == hipSuccess)
+    e = sqa::launch_attention(dtype, q, k, vt, a, B, N, z.Np, H_q, H_kv, d_head, causal != 0, lens,
+                              stream);
+  if (e == hipSuccess)
+    e = sqa::launch_output_projection(dtype, a, Wo, w3, out, B * N, H_q * d_head, d_model, lens, N,
+                                      stream);
+  const hipError_t ef = hipFreeAsync(ws, stream);
+  if (e != hipSuccess) return fail_hip(e, "kernel launch");
+  if (ef != hipSuccess) return fail_hip(ef, "workspace release");
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -215,7 +277,7 @@ sqa_status sqa_qkv_projection(const void* x, const void* Wq, const void* Wk, con
   PoolScratch wt;
   SQA_TRY(wt.acquire(sqa::qkv_wt_bytes(dtype, d_model, H_q, H_kv, d_head), stream));
   hipError_t e = sqa::launch_qkv_projection(dtype, x, Wq, Wk, Wv, wt.ptr, q, k, vt, B, N, z.Np,
-                                            d_model, H_q, H_kv, d_head, stream);
+                                            d_model, H_q, H_kv, d_head, nullptr, stream);
   const hipError_t ef = wt.release();
   if (e != hipSuccess) return fail_hip(e, "qkv projection launch");
   if (ef != hipSuccess) return fail_hip(ef, "scratch release");
@@ -239,7 +301,7 @@ sqa_status sqa_attention(const void* q, const void* k, const void* vt, void* a, 
   if (overlap(a, z.a, q, z.q) || overlap(a, z.a, k, z.kv) || overlap(a, z.a, vt, z.kv))
     return fail(SQA_ERR_INVALID_ARG, "a overlaps q, k or vt");
   hipError_t e = sqa::launch_attention(dtype, q, k, vt, a, B, N, z.Np, H_q, H_kv, d_head,
-                                       causal != 0, stream);
+                                       causal != 0, nullptr, stream);
   if (e != hipSuccess) return fail_hip(e, "attention launch");
   return ok();
 }
@@ -263,7 +325,8 @@ sqa_status sqa_output_projection(const void* a, const void* Wo, void* out, int64
     return fail(SQA_ERR_INVALID_ARG, "out overlaps a or Wo");
   PoolScratch wt;
   SQA_TRY(wt.acquire(sqa::out_wt_bytes(dtype, K, d_model), stream));
-  hipError_t e = sqa::launch_output_projection(dtype, a, Wo, wt.ptr, out, M, K, d_model, stream);
+  hipError_t e = sqa::launch_output_projection(dtype, a, Wo, wt.ptr, out, M, K, d_model, nullptr, 1,
+                                               stream);
   const hipError_t ef = wt.release();
   if (e != hipSuccess) return fail_hip(e, "output projection launch");
   if (ef != hipSuccess) return fail_hip(ef, "scratch release");
@@ -274,50 +337,16 @@ sqa_status sqa_forward(const void* x, const void* Wq, const void* Wk, const void
                        const void* Wo, void* out, int64_t B, int64_t N, int64_t d_model,
                        int64_t H, int64_t H_q, int64_t H_kv, int64_t d_head, int causal,
                        sqa_dtype dtype, hipStream_t stream) {
-  const Shape s{B, N, d_model, H, H_q, H_kv, d_head};
-  SQA_TRY(check_dtype(dtype));
-  SQA_TRY(check_heads(s, true));
-  if (causal != 0 && causal != 1) return fail(SQA_ERR_INVALID_ARG, "causal must be 0 or 1");
-  if (B * N == 0) return ok();
-  SQA_TRY(check_ptr(x, "x is null", "x is not 16-byte aligned"));
-  SQA_TRY(check_ptr(Wq, "Wq is null", "Wq is not 16-byte aligned"));
-  SQA_TRY(check_ptr(Wk, "Wk is null", "Wk is not 16-byte aligned"));
-  SQA_TRY(check_ptr(Wv, "Wv is null", "Wv is not 16-byte aligned"));
-  SQA_TRY(check_ptr(Wo, "Wo is null", "Wo is not 16-byte aligned"));
-  SQA_TRY(check_ptr(out, "out is null", "out is not 16-byte aligned"));
-  Sizes z;
-  SQA_TRY(sizes_for(s, dtype, &z));
-  const size_t es = elem_size(dtype);
-  const size_t yb = (size_t)(B * N * d_model) * es;
-  const size_t wqb = (size_t)(d_model * H_q * d_head) * es, wkb = (size_t)(d_model * H_kv * d_head) * es;
-  const void* ins[5] = {x, Wq, Wk, Wv, Wo};
-  const size_t inb[5] = {yb, wqb, wkb, wkb, wqb};
-  for (int j = 0; j < 5; ++j)
-    if (overlap(out, yb, ins[j], inb[j])) return fail(SQA_ERR_INVALID_ARG, "out overlaps an input");
+  return forward_impl(x, Wq, Wk, Wv, Wo, out, false, nullptr, B, N, d_model, H, H_q, H_kv, d_head, causal,
+                      dtype, stream);
+}
 
-  const int64_t off_k = round256(z.q), off_v = off_k + round256(z.kv);
-  const int64_t off_a = off_v + round256(z.kv), off_w1 = off_a + round256(z.a);
-  const int64_t off_w3 = off_w1 + round256((int64_t)sqa::qkv_wt_bytes(dtype, d_model, H_q, H_kv, d_head));
-  const int64_t total = off_w3 + round256((int64_t)sqa::out_wt_bytes(dtype, H_q * d_head, d_model));
-  hipMemPool_t pool;
-  SQA_TRY(pool_for(stream, &pool));
-  void* ws = nullptr;
-  hipError_t e = hipMallocFromPoolAsync(&ws, (size_t)total, pool, stream);
-  if (e != hipSuccess) return fail_hip(e, "workspace allocation");
-  char* base = (char*)ws;
-  void *q = base, *k = base + off_k, *vt = base + off_v, *a = base + off_a;
-  void *w1 = base + off_w1, *w3 = base + off_w3;
-
-  e = sqa::launch_qkv_projection(dtype, x, Wq, Wk, Wv, w1, q, k, vt, B, N, z.Np, d_model, H_q,
-                                 H_kv, d_head, stream);
-  if (e == hipSuccess)
-    e = sqa::launch_attention(dtype, q, k, vt, a, B, N, z.Np, H_q, H_kv, d_head, causal != 0, stream);
-  if (e == hipSuccess)
-    e = sqa::launch_output_projection(dtype, a, Wo, w3, out, B * N, H_q * d_head, d_model, stream);
-  const hipError_t ef = hipFreeAsync(ws, stream);
-  if (e != hipSuccess) return fail_hip(e, "kernel launch");
-  if (ef != hipSuccess) return fail_hip(ef, "workspace release");
-  return ok();
+sqa_status sqa_forward_varlen(const void* x, const void* Wq, const void* Wk, const void* Wv,
+                              const void* Wo, void* out, const int32_t* lens, int64_t B, int64_t N,
+                              int64_t d_model, int64_t H, int64_t H_q, int64_t H_kv,
+                              int64_t d_head, int causal, sqa_dtype dtype, hipStream_t stream) {
+  return forward_impl(x, Wq, Wk, Wv, Wo, out, true, lens, B, N, d_model, H, H_q, H_kv, d_head, causal,
+                      dtype, stream);
 }
 
 }  // extern "C"

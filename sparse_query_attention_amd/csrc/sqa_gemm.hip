@@ -88,6 +88,8 @@ template <typename T> struct DenseRows {
 // block whose first column is n is staged column by column (its chunks run
 // along rows) or row by row (chunks run along columns). store.tile(m0) gives
 // the tile whose rows start at m0, with rows r counted from m0:
+//  * all_zero(): every row of the tile is stored as zeros (padding of its
+//    sequence), so its products are not computed;
 //  * zero_row(r): row r is stored as zeros (padding of the Q/K/V^T layouts);
 //  * row_chunk(r, n, c): C[r][n .. n+E-1]; col_chunk(r, n, c): C[r .. r+E-1][n],
 //    with E = 16 / sizeof(T).
@@ -97,10 +99,12 @@ template <typename T> struct DenseRows {
 // their chunks are runs of t, contiguous in vt.
 template <typename T> struct QkvStore {
   T* q; T* k; T* vt; int64_t N, Np; int H_q, H_kv, dsh, wq_w, wkv_w;   // d_head = 1 << dsh
+  const int32_t* lens;   // null, or each sequence's length (clamped into [0, N])
   __device__ bool col_major(int n) const { return n >= wq_w + wkv_w; }
   struct Tile {
     T* q; T* k; T* vt;   // batch b's slices, row t0
     int t0, n_valid, dsh, wq_w, wkv_w; int64_t Np;
+    __device__ bool all_zero() const { return t0 >= n_valid; }
     __device__ bool zero_row(int r) const { return t0 + r >= n_valid; }
     __device__ void row_chunk(int r, int n, const Chunk& c) const {
       const int64_t t = t0 + r;
@@ -120,24 +124,37 @@ template <typename T> struct QkvStore {
   __device__ Tile tile(int64_t m0) const {
     const int64_t b = m0 / Np, t0 = m0 - b * Np;
     const int64_t d = (int64_t)1 << dsh;
+    const int n_valid = lens ? min(max(lens[b], 0), (int)N) : (int)N;
     return Tile{q + b * H_q * Np * d, k + b * H_kv * Np * d, vt + b * H_kv * d * Np,
-                (int)t0, (int)N, dsh, wq_w, wkv_w, Np};
+                (int)t0, n_valid, dsh, wq_w, wkv_w, Np};
   }
 };
 
-// Step 3: plain row-major out [M, ncols]; rows past M are not stored.
+// Step 3: plain row-major out [M, ncols]; rows past M are not stored. With
+// lens, row m is token m % seq_n of sequence m / seq_n, and a tile that lies in
+// one sequence's padding is stored as zeros without computing it.
 template <typename T> struct DenseStore {
   T* out; int64_t M; int ncols;
+  const int32_t* lens; int64_t seq_n;
   __device__ bool col_major(int) const { return false; }
   struct Tile {
-    T* out; int64_t rows_left; int ncols;   // rows from m0 on
-    __device__ bool zero_row(int) const { return false; }
+    T* out; int64_t rows_left; int ncols; bool pad;   // rows from m0 on
+    __device__ bool all_zero() const { return pad; }
+    __device__ bool zero_row(int) const { return pad; }
     __device__ void row_chunk(int r, int n, const Chunk& c) const {
       if (r < rows_left) *reinterpret_cast<Chunk*>(out + (int64_t)r * ncols + n) = c;
     }
     __device__ void col_chunk(int, int, const Chunk&) const {}
   };
-  __device__ Tile tile(int64_t m0) const { return Tile{out + m0 * ncols, M - m0, ncols}; }
+  __device__ Tile tile(int64_t m0) const {
+    bool pad = false;
+    if (lens) {
+      const int64_t b = m0 / seq_n, t0 = m0 - b * seq_n;
+      const int64_t L = min(max((int64_t)lens[b], (int64_t)0), seq_n);
+      pad = t0 >= L && t0 + BM <= seq_n;   // the whole tile is padding of sequence b
+    }
+    return Tile{out + m0 * ncols, M - m0, ncols, pad};
+  }
 };
 
 // C = A * W with W given transposed (wt [ncols, K]); see the file header.
@@ -254,8 +271,14 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Rows rows, const T* wt, i
       }
     }
   };
-  if (rows_all) main_loop(std::true_type{});
-  else main_loop(std::false_type{});
+  // A tile wholly in the padding of its sequence keeps zero accumulators.
+  const auto tile = store.tile(m0);
+  if (tile.all_zero()) {
+  } else if (rows_all) {
+    main_loop(std::true_type{});
+  } else {
+    main_loop(std::false_type{});
+  }
 
   // Epilogue through LDS (the ring is free once every wave has passed this
   // barrier). Block (bi, bj) is the 32x32 sub-tile at rows 32*bi, columns
@@ -267,7 +290,6 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Rows rows, const T* wt, i
   constexpr int EPC = 16 / (int)sizeof(T);
   static_assert(16 * BLOCK <= NST * C::STAGE * (int)sizeof(T), "epilogue fits the ring");
   char* ep = reinterpret_cast<char*>(smem);
-  const auto tile = store.tile(m0);
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -376,7 +398,8 @@ hipError_t transpose(const T* w0, int w0n, const T* w1, int w1n, const T* w2, in
 template <typename T>
 hipError_t qkv_impl(const void* x, const void* wq, const void* wk, const void* wv, void* wt,
                     void* q, void* k, void* vt, int64_t B, int64_t N, int64_t Np, int64_t d_model,
-                    int64_t H_q, int64_t H_kv, int64_t d, hipStream_t stream) {
+                    int64_t H_q, int64_t H_kv, int64_t d, const int32_t* lens,
+                    hipStream_t stream) {
   const int wq_w = (int)(H_q * d), wkv_w = (int)(H_kv * d);
   const int ncols = wq_w + 2 * wkv_w;
   const int64_t n_rb = B * Np / BM, n_ct = (ncols + BN - 1) / BN;
@@ -386,7 +409,7 @@ hipError_t qkv_impl(const void* x, const void* wq, const void* wk, const void* w
   if (e != hipSuccess) return e;
   PaddedRows<T> rows{(const T*)x, N, Np, (int)d_model};
   const int dsh = d == 64 ? 6 : 5;   // d_head is 32 or 64 (checked by the caller)
-  QkvStore<T> st{(T*)q, (T*)k, (T*)vt, N, Np, (int)H_q, (int)H_kv, dsh, wq_w, wkv_w};
+  QkvStore<T> st{(T*)q, (T*)k, (T*)vt, N, Np, (int)H_q, (int)H_kv, dsh, wq_w, wkv_w, lens};
   gemm_kernel<T><<<(unsigned)grid_size(n_rb, n_ct), THREADS, 0, stream>>>(
       rows, (const T*)wt, ncols, st, (int)d_model, (int)n_rb, (int)n_ct);
   return hipGetLastError();
@@ -394,14 +417,14 @@ hipError_t qkv_impl(const void* x, const void* wq, const void* wk, const void* w
 
 template <typename T>
 hipError_t out_impl(const void* a, const void* wo, void* wt, void* out, int64_t M, int64_t K,
-                    int64_t d_model, hipStream_t stream) {
+                    int64_t d_model, const int32_t* lens, int64_t seq_n, hipStream_t stream) {
   const int64_t n_rb = (M + BM - 1) / BM, n_ct = (d_model + BN - 1) / BN;
   if (!grid_ok(n_rb, n_ct)) return hipErrorInvalidConfiguration;
   hipError_t e = transpose<T>((const T*)wo, (int)d_model, nullptr, 0, nullptr, 0, (T*)wt, (int)K,
                               stream);
   if (e != hipSuccess) return e;
   DenseRows<T> rows{(const T*)a, M, (int)K};
-  DenseStore<T> st{(T*)out, M, (int)d_model};
+  DenseStore<T> st{(T*)out, M, (int)d_model, lens, seq_n};
   gemm_kernel<T><<<(unsigned)grid_size(n_rb, n_ct), THREADS, 0, stream>>>(
       rows, (const T*)wt, (int)d_model, st, (int)K, (int)n_rb, (int)n_ct);
   return hipGetLastError();
@@ -420,17 +443,20 @@ size_t out_wt_bytes(sqa_dtype dt, int64_t K, int64_t d_model) {
 hipError_t launch_qkv_projection(sqa_dtype dt, const void* x, const void* wq, const void* wk,
                                  const void* wv, void* wt, void* q, void* k, void* vt, int64_t B,
                                  int64_t N, int64_t Np, int64_t d_model, int64_t H_q, int64_t H_kv,
-                                 int64_t d_head, hipStream_t stream) {
+                                 int64_t d_head, const int32_t* lens, hipStream_t stream) {
   if (dt == SQA_DTYPE_BF16)
-    return qkv_impl<bf16>(x, wq, wk, wv, wt, q, k, vt, B, N, Np, d_model, H_q, H_kv, d_head, stream);
-  return qkv_impl<float>(x, wq, wk, wv, wt, q, k, vt, B, N, Np, d_model, H_q, H_kv, d_head, stream);
+    return qkv_impl<bf16>(x, wq, wk, wv, wt, q, k, vt, B, N, Np, d_model, H_q, H_kv, d_head, lens,
+                          stream);
+  return qkv_impl<float>(x, wq, wk, wv, wt, q, k, vt, B, N, Np, d_model, H_q, H_kv, d_head, lens,
+                         stream);
 }
 
 hipError_t launch_output_projection(sqa_dtype dt, const void* a, const void* wo, void* wt,
                                     void* out, int64_t M, int64_t K, int64_t d_model,
-                                    hipStream_t stream) {
-  if (dt == SQA_DTYPE_BF16) return out_impl<bf16>(a, wo, wt, out, M, K, d_model, stream);
-  return out_impl<float>(a, wo, wt, out, M, K, d_model, stream);
+                                    const int32_t* lens, int64_t seq_n, hipStream_t stream) {
+  if (dt == SQA_DTYPE_BF16)
+    return out_impl<bf16>(a, wo, wt, out, M, K, d_model, lens, seq_n, stream);
+  return out_impl<float>(a, wo, wt, out, M, K, d_model, lens, seq_n, stream);
 }
 
 }  // namespace sqa

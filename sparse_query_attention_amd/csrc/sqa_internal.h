@@ -15,24 +15,31 @@ constexpr int64_t kSeqPad = 256;
 
 inline int64_t padded_length(int64_t n) { return (n + kSeqPad - 1) / kSeqPad * kSeqPad; }
 
+// Sequence lengths of a padded batch: lens is null (every sequence has N tokens)
+// or a device array of B lengths, each clamped into [0, N] where it is read.
+
 // Step 1: X [B*N, d_model] times [Wq | Wk | Wv] into q [B,H_q,Np,d], k [B,H_kv,Np,d],
-// vt [B,H_kv,d,Np]. wt is device scratch of qkv_wt_bytes() for the transposed weights.
+// vt [B,H_kv,d,Np]; rows at or past a sequence's length are zero. wt is device
+// scratch of qkv_wt_bytes() for the transposed weights.
 size_t qkv_wt_bytes(sqa_dtype dt, int64_t d_model, int64_t H_q, int64_t H_kv, int64_t d_head);
 hipError_t launch_qkv_projection(sqa_dtype dt, const void* x, const void* wq, const void* wk,
                                  const void* wv, void* wt, void* q, void* k, void* vt, int64_t B,
                                  int64_t N, int64_t Np, int64_t d_model, int64_t H_q, int64_t H_kv,
-                                 int64_t d_head, hipStream_t stream);
+                                 int64_t d_head, const int32_t* lens, hipStream_t stream);
 
-// Step 2: attention core into a [B*N, H_q*d].
+// Step 2: attention core into a [B*N, H_q*d]; keys end at each sequence's
+// length, and rows at or past it are zero.
 hipError_t launch_attention(sqa_dtype dt, const void* q, const void* k, const void* vt, void* a,
                             int64_t B, int64_t N, int64_t Np, int64_t H_q, int64_t H_kv,
-                            int64_t d_head, bool causal, hipStream_t stream);
+                            int64_t d_head, bool causal, const int32_t* lens, hipStream_t stream);
 
 // Step 3: out [M, d_model] = a [M, K] * wo [K, d_model]. wt is device scratch of
-// out_wt_bytes() for the transposed weights.
+// out_wt_bytes() for the transposed weights. With lens, row m is token m % seq_n
+// of sequence m / seq_n, and rows in a sequence's padding may be stored as zeros
+// without being computed (they are zero when a is).
 size_t out_wt_bytes(sqa_dtype dt, int64_t K, int64_t d_model);
 hipError_t launch_output_projection(sqa_dtype dt, const void* a, const void* wo, void* wt,
                                     void* out, int64_t M, int64_t K, int64_t d_model,
-                                    hipStream_t stream);
+                                    const int32_t* lens, int64_t seq_n, hipStream_t stream);
 
 }  // namespace sqa

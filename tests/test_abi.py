@@ -110,3 +110,33 @@ def test_python_binding_maps_statuses_to_exceptions():
     with pytest.raises(_lib.SQAError):
         _lib.check(_lib.SQA_ERR_OUT_OF_MEMORY)
     _lib.check(_lib.SQA_OK)
+
+
+def _fwd_varlen(lens, **kw):
+    a = dict(x=FAKE, Wq=FAKE + 0x1000000, Wk=FAKE + 0x2000000, Wv=FAKE + 0x3000000,
+             Wo=FAKE + 0x4000000, out=FAKE + 0x5000000, B=2, N=256, d_model=256, H=8, H_q=4,
+             H_kv=2, d_head=32, causal=1, dtype=_lib.SQA_DTYPE_BF16)
+    a.update(kw)
+    lib = _lib.load()
+    st = lib.sqa_forward_varlen(a["x"], a["Wq"], a["Wk"], a["Wv"], a["Wo"], a["out"], lens, a["B"],
+                                a["N"], a["d_model"], a["H"], a["H_q"], a["H_kv"], a["d_head"],
+                                a["causal"], a["dtype"], None)
+    return st, lib.sqa_last_error_message().decode()
+
+
+@pytest.mark.parametrize("lens,kw,status,words", [
+    (0, {}, _lib.SQA_ERR_INVALID_ARG, "lens is null"),
+    (FAKE + 0x6000002, {}, _lib.SQA_ERR_INVALID_ARG, "4-byte aligned"),
+    (FAKE + 0x5000040, {}, _lib.SQA_ERR_INVALID_ARG, "overlaps lens"),
+    (FAKE + 0x6000000, dict(x=0), _lib.SQA_ERR_INVALID_ARG, "x is null"),
+    (FAKE + 0x6000000, dict(H_kv=3), _lib.SQA_ERR_INVALID_ARG, "multiple of H_kv"),
+    (FAKE + 0x6000000, dict(d_model=128, H=8, d_head=16), _lib.SQA_ERR_UNSUPPORTED, "d_head"),
+])
+def test_forward_varlen_rejects_invalid_arguments(lens, kw, status, words):
+    st, msg = _fwd_varlen(lens, **kw)
+    assert st == status, msg
+    assert words in msg
+
+
+def test_forward_varlen_empty_batch_is_a_no_op():
+    assert _fwd_varlen(0, B=0)[0] == _lib.SQA_OK

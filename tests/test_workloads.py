@@ -6,11 +6,12 @@ import workloads as wl
 
 
 def test_all_five_workloads_have_the_stated_shapes():
-    w = wl.WORKLOADS
-    assert [x.N for x in w.values()] == [256, 1024, 32768, 131072, 200000]
-    assert [x.d_head for x in w.values()] == [32, 32, 64, 64, 64]
-    assert [(x.H_q, x.H_kv) for x in w.values()] == [(4, 2), (8, 8), (4, 4), (8, 4), (4, 1)]
-    assert [(x.baseline().H_q, x.baseline().H_kv) for x in list(w.values())[1:]] == \
+    w = [wl.TINY_SQA_FP32, wl.SSQA_1K_CAUSAL, wl.XSQA_32K, wl.SQA_131K_CAUSAL, wl.XSMQA_200K]
+    assert all(wl.WORKLOADS[x.name] is x for x in w)
+    assert [x.N for x in w] == [256, 1024, 32768, 131072, 200000]
+    assert [x.d_head for x in w] == [32, 32, 64, 64, 64]
+    assert [(x.H_q, x.H_kv) for x in w] == [(4, 2), (8, 8), (4, 4), (8, 4), (4, 1)]
+    assert [(x.baseline().H_q, x.baseline().H_kv) for x in w[1:]] == \
         [(16, 4), (16, 16), (16, 4), (16, 1)]
     with pytest.raises(ValueError):
         wl.TINY_SQA_FP32.baseline()
@@ -54,3 +55,13 @@ def test_device_dtype_rounding_is_exact_to_widen():
     x = wl.widen(t["X"])
     assert x.dtype == np.float64
     assert np.array_equal(wl.widen(torch.from_numpy(x).to(torch.bfloat16)), x)
+
+
+def test_varlen_lengths_are_seeded_and_in_range():
+    w = wl.SQA_VARLEN_32K
+    a, b = wl.draw_lens(w), wl.draw_lens(w)
+    assert a.dtype == np.int32 and a.shape == (w.B,)
+    np.testing.assert_array_equal(a, b)
+    assert a.min() >= w.varlen_min and a.max() <= w.N
+    assert len(set(a.tolist())) > 1          # a real length mix
+    np.testing.assert_array_equal(wl.draw_lens(wl.XSQA_32K), [wl.XSQA_32K.N])

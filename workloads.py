@@ -21,6 +21,9 @@ Draw recipe (the same everywhere):
     values to float64, and the GPU receives the same rounded values.
   * A baseline run (MHA/GQA/MQA of the same shape) reuses X and draws its own
     weights, at its own widths, from the same streams.
+  * A variable-length batch (sequences padded to N, as a training batch cut at
+    a maximum sequence length holds them: model cards' training example) draws
+    its lengths from stream 6, uniform integers in [varlen_min, N].
 """
 from __future__ import annotations
 
@@ -29,7 +32,7 @@ from typing import Dict, Optional
 
 import numpy as np
 
-STREAM_X, STREAM_WQ, STREAM_WK, STREAM_WV, STREAM_WO, STREAM_OUTLIERS = range(6)
+STREAM_X, STREAM_WQ, STREAM_WK, STREAM_WV, STREAM_WO, STREAM_OUTLIERS, STREAM_LENS = range(7)
 
 
 @dataclass(frozen=True)
@@ -51,6 +54,7 @@ class Workload:
     outlier_scale: float = 20.0
     baseline_H_q: Optional[int] = None
     baseline_H_kv: Optional[int] = None
+    varlen_min: Optional[int] = None   # variable-length batch: shortest sequence length
 
     @property
     def d_head(self) -> int:
@@ -86,9 +90,13 @@ XSMQA_200K = Workload("xsmqa_bf16_n200000_outliers", B=1, N=200000, d_model=1024
                       H_kv=1, causal=False, dtype="bf16", seed=1004, outlier_frac=0.01,
                       baseline_H_q=16, baseline_H_kv=1)
 
+# Standard SQA, causal, 8 sequences of 4096..32768 tokens padded to 32768.
+SQA_VARLEN_32K = Workload("sqa_bf16_causal_varlen_b8_n32768", B=8, N=32768, d_model=1024, H=16,
+                          H_q=8, H_kv=4, causal=True, dtype="bf16", seed=1005, varlen_min=4096)
+
 WORKLOADS: Dict[str, Workload] = {w.name: w for w in
                                   (TINY_SQA_FP32, SSQA_1K_CAUSAL, XSQA_32K, SQA_131K_CAUSAL,
-                                   XSMQA_200K)}
+                                   XSMQA_200K, SQA_VARLEN_32K)}
 
 
 def _rng(seed: int, stream: int) -> np.random.Generator:
@@ -125,6 +133,13 @@ def draw_weights(w: Workload) -> Dict[str, np.ndarray]:
               "Wo": (STREAM_WO, (w.H_q * d, w.d_model))}
     return {k: _rng(w.seed, s).standard_normal(shp, dtype=np.float32) * std
             for k, (s, shp) in shapes.items()}
+
+
+def draw_lens(w: Workload) -> np.ndarray:
+    """Sequence lengths [B] int32 of a variable-length batch (all N otherwise)."""
+    if w.varlen_min is None:
+        return np.full(w.B, w.N, dtype=np.int32)
+    return _rng(w.seed, STREAM_LENS).integers(w.varlen_min, w.N + 1, size=w.B).astype(np.int32)
 
 
 def draw(w: Workload) -> Dict[str, np.ndarray]:
