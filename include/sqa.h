@@ -108,6 +108,44 @@ sqa_status sqa_forward_varlen(const void* x, const void* Wq, const void* Wk, con
                               int64_t d_head, int causal, sqa_dtype dtype, hipStream_t stream);
 
 /*
+ * Autoregressive inference with a key/value cache. The model cards generate
+ * text token by token (ReactiveAI/xSMQAT-m and ReactiveAI/GQA-Ref-Micro,
+ * inference example). The caches are caller-owned device buffers
+ *   k_cache, v_cache [B, H_kv, N_max, d_head]  (dtype; row t = token t)
+ * with 1 <= N_max <= SQA_MAX_N. They must not overlap each other, the inputs
+ * or out.
+ *
+ * sqa_prefill - sqa_forward with causal = 1 over x [B, N, d_model]
+ * (N <= N_max), which also writes the keys and values of tokens 0..N-1 to rows
+ * 0..N-1 of the caches. Rows N.. are not touched.
+ */
+sqa_status sqa_prefill(const void* x, const void* Wq, const void* Wk, const void* Wv,
+                       const void* Wo, void* out, void* k_cache, void* v_cache, int64_t B,
+                       int64_t N, int64_t N_max, int64_t d_model, int64_t H, int64_t H_q,
+                       int64_t H_kv, int64_t d_head, sqa_dtype dtype, hipStream_t stream);
+
+/*
+ * sqa_decode_step - one new token per sequence.
+ *   x_new [B, d_model]  the tokens
+ *   pos   device array of B int32: token b's position in sequence b, i.e. the
+ *         number of tokens already cached (clamped into [0, N_max-1])
+ *   out   [B, d_model]
+ * Projects the tokens and writes key and value of token b to cache row pos[b].
+ * Query head i then attends over cache rows 0..pos[b] of key/value head
+ * floor(i / (H_q/H_kv)), and out[b] = A Wo. The result is row pos[b] of
+ * sqa_forward(causal = 1) over the sequence's first pos[b]+1 tokens, provided
+ * that rows 0..pos[b]-1 of the caches hold those tokens' keys and values (from
+ * sqa_prefill or earlier steps). Attention is split over key chunks, with
+ * partial results in the workspace (stream-ordered pool, as in sqa_forward).
+ * 1 <= B <= 65535; pos must be 4-byte aligned.
+ */
+sqa_status sqa_decode_step(const void* x_new, const void* Wq, const void* Wk, const void* Wv,
+                           const void* Wo, void* out, void* k_cache, void* v_cache,
+                           const int32_t* pos, int64_t B, int64_t N_max, int64_t d_model,
+                           int64_t H, int64_t H_q, int64_t H_kv, int64_t d_head, sqa_dtype dtype,
+                           hipStream_t stream);
+
+/*
  * sqa_padded_length - Np, the sequence length of the Q/K/V^T layouts below:
  * N rounded up to a multiple of 256. Returns -1 for N < 0.
  */

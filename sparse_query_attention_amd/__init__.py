@@ -20,7 +20,7 @@ from typing import Optional, Tuple
 from . import _lib
 from ._lib import SQAError
 
-__all__ = ["forward_varlen", "forward", "qkv_projection", "attention", "output_projection", "padded_length",
+__all__ = ["forward_varlen", "prefill", "decode_step", "forward", "qkv_projection", "attention", "output_projection", "padded_length",
            "SQAError", "library_path"]
 
 library_path = _lib.LIB_PATH
@@ -109,6 +109,59 @@ def forward_varlen(x, Wq, Wk, Wv, Wo, lens, *, H: int, H_q: int, H_kv: int, caus
                                       Wo.data_ptr(), out.data_ptr(), lens.data_ptr(), B, N, D, H,
                                       H_q, H_kv, d, int(bool(causal)), _dtype_code(x),
                                       _stream(x.device)))
+    return out
+
+
+def _check_caches(k_cache, v_cache, B, H_kv, d, x):
+    if k_cache.dim() != 4 or tuple(k_cache.shape[:2]) != (B, H_kv) or k_cache.shape[3] != d:
+        raise ValueError("k_cache must be [B, H_kv, N_max, d_head]")
+    shp = tuple(k_cache.shape)
+    _check_tensor("k_cache", k_cache, shp, x.dtype, x.device)
+    _check_tensor("v_cache", v_cache, shp, x.dtype, x.device)
+    return shp[2]
+
+
+def prefill(x, Wq, Wk, Wv, Wo, k_cache, v_cache, *, H: int, H_q: int, H_kv: int, out=None):
+    """Causal forward over x [B, N, d_model] that also writes the keys and values
+    of tokens 0..N-1 to rows 0..N-1 of k_cache / v_cache [B, H_kv, N_max, d]."""
+    lib = _lib.load()
+    B, N, D = x.shape
+    d = D // H
+    N_max = _check_caches(k_cache, v_cache, B, H_kv, d, x)
+    out = _torch().empty_like(x) if out is None else out
+    for name, t, shp in (("x", x, (B, N, D)), ("Wq", Wq, (D, H_q * d)), ("Wk", Wk, (D, H_kv * d)),
+                         ("Wv", Wv, (D, H_kv * d)), ("Wo", Wo, (H_q * d, D)), ("out", out, (B, N, D))):
+        _check_tensor(name, t, shp, x.dtype, x.device)
+    _lib.check(lib.sqa_prefill(x.data_ptr(), Wq.data_ptr(), Wk.data_ptr(), Wv.data_ptr(),
+                               Wo.data_ptr(), out.data_ptr(), k_cache.data_ptr(),
+                               v_cache.data_ptr(), B, N, N_max, D, H, H_q, H_kv, d, _dtype_code(x),
+                               _stream(x.device)))
+    return out
+
+
+def decode_step(x_new, Wq, Wk, Wv, Wo, k_cache, v_cache, pos, *, H: int, H_q: int, H_kv: int,
+                out=None):
+    """One token per sequence: x_new [B, d_model], pos int32 [B] (tokens already
+    cached). Writes the tokens' keys/values to cache row pos[b] and returns
+    out [B, d_model], row pos[b] of the causal forward."""
+    lib = _lib.load()
+    torch = _torch()
+    if x_new.dim() != 2:
+        raise ValueError("x_new must be [B, d_model]")
+    B, D = x_new.shape
+    d = D // H
+    N_max = _check_caches(k_cache, v_cache, B, H_kv, d, x_new)
+    if pos.dtype != torch.int32 or tuple(pos.shape) != (B,) or pos.device != x_new.device \
+            or not pos.is_contiguous():
+        raise ValueError("pos must be a contiguous int32 tensor [B] on x_new's device")
+    out = torch.empty_like(x_new) if out is None else out
+    for name, t, shp in (("x_new", x_new, (B, D)), ("Wq", Wq, (D, H_q * d)), ("Wk", Wk, (D, H_kv * d)),
+                         ("Wv", Wv, (D, H_kv * d)), ("Wo", Wo, (H_q * d, D)), ("out", out, (B, D))):
+        _check_tensor(name, t, shp, x_new.dtype, x_new.device)
+    _lib.check(lib.sqa_decode_step(x_new.data_ptr(), Wq.data_ptr(), Wk.data_ptr(), Wv.data_ptr(),
+                                   Wo.data_ptr(), out.data_ptr(), k_cache.data_ptr(),
+                                   v_cache.data_ptr(), pos.data_ptr(), B, N_max, D, H, H_q, H_kv,
+                                   d, _dtype_code(x_new), _stream(x_new.device)))
     return out
 
 

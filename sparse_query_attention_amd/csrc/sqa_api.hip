@@ -161,11 +161,13 @@ struct PoolScratch {
   }
 };
 
-// sqa_forward (varlen false, lens unused) and sqa_forward_varlen.
+// sqa_forward (varlen false, lens unused), sqa_forward_varlen, and sqa_prefill
+// (kc, vc non-null: the caches [B, H_kv, N_max, d_head] receive K and V).
 sqa_status forward_impl(const void* x, const void* Wq, const void* Wk, const void* Wv,
-                        const void* Wo, void* out, bool varlen, const int32_t* lens, int64_t B, int64_t N,
-                        int64_t d_model, int64_t H, int64_t H_q, int64_t H_kv, int64_t d_head,
-                        int causal, sqa_dtype dtype, hipStream_t stream) {
+                        const void* Wo, void* out, bool varlen, const int32_t* lens, void* kc,
+                        void* vc, int64_t N_max, int64_t B, int64_t N, int64_t d_model, int64_t H,
+                        int64_t H_q, int64_t H_kv, int64_t d_head, int causal, sqa_dtype dtype,
+                        hipStream_t stream) {
   const Shape s{B, N, d_model, H, H_q, H_kv, d_head};
   SQA_TRY(check_dtype(dtype));
   SQA_TRY(check_heads(s, true));
@@ -195,6 +197,18 @@ sqa_status forward_impl(const void* x, const void* Wq, const void* Wk, const voi
     if (overlap(out, yb, ins[j], inb[j])) return fail(SQA_ERR_INVALID_ARG, "out overlaps an input");
   if (lens && overlap(out, yb, lens, (size_t)B * sizeof(int32_t)))
     return fail(SQA_ERR_INVALID_ARG, "out overlaps lens");
+  if (kc) {
+    if (N > N_max) return fail(SQA_ERR_INVALID_ARG, "N exceeds N_max");
+    int64_t cb;
+    if (!mul_ok(B * H_kv, N_max, &cb) || !mul_ok(cb, d_head * (int64_t)es, &cb))
+      return fail(SQA_ERR_UNSUPPORTED, "size overflow");
+    if (overlap(kc, (size_t)cb, vc, (size_t)cb)) return fail(SQA_ERR_INVALID_ARG, "k_cache overlaps v_cache");
+    for (void* c : {kc, vc}) {
+      if (overlap(c, (size_t)cb, out, yb)) return fail(SQA_ERR_INVALID_ARG, "a cache overlaps out");
+      for (int j = 0; j < 5; ++j)
+        if (overlap(c, (size_t)cb, ins[j], inb[j])) return fail(SQA_ERR_INVALID_ARG, "a cache overlaps an input");
+    }
+  }
 
   const int64_t off_k = round256(z.q), off_v = off_k + round256(z.kv);
   const int64_t off_a = off_v + round256(z.kv), off_w1 = off_a + round256(z.a);
@@ -211,6 +225,8 @@ sqa_status forward_impl(const void* x, const void* Wq, const void* Wk, const voi
 
   e = sqa::launch_qkv_projection(dtype, x, Wq, Wk, Wv, w1, q, k, vt, B, N, z.Np, d_model, H_q,
                                  H_kv, d_head, lens, stream);
+  if (e == hipSuccess && kc)
+    e = sqa::launch_fill_cache(dtype, k, vt, kc, vc, B, H_kv, N, z.Np, N_max, d_head, stream);
   if (e == hipSuccess)
     e = sqa::launch_attention(dtype, q, k, vt, a, B, N, z.Np, H_q, H_kv, d_head, causal != 0, lens,
                               stream);
@@ -337,7 +353,7 @@ sqa_status sqa_forward(const void* x, const void* Wq, const void* Wk, const void
                        const void* Wo, void* out, int64_t B, int64_t N, int64_t d_model,
                        int64_t H, int64_t H_q, int64_t H_kv, int64_t d_head, int causal,
                        sqa_dtype dtype, hipStream_t stream) {
-  return forward_impl(x, Wq, Wk, Wv, Wo, out, false, nullptr, B, N, d_model, H, H_q, H_kv, d_head, causal,
+  return forward_impl(x, Wq, Wk, Wv, Wo, out, false, nullptr, nullptr, nullptr, 0, B, N, d_model, H, H_q, H_kv, d_head, causal,
                       dtype, stream);
 }
 
@@ -345,8 +361,92 @@ sqa_status sqa_forward_varlen(const void* x, const void* Wq, const void* Wk, con
                               const void* Wo, void* out, const int32_t* lens, int64_t B, int64_t N,
                               int64_t d_model, int64_t H, int64_t H_q, int64_t H_kv,
                               int64_t d_head, int causal, sqa_dtype dtype, hipStream_t stream) {
-  return forward_impl(x, Wq, Wk, Wv, Wo, out, true, lens, B, N, d_model, H, H_q, H_kv, d_head, causal,
+  return forward_impl(x, Wq, Wk, Wv, Wo, out, true, lens, nullptr, nullptr, 0, B, N, d_model, H, H_q, H_kv, d_head, causal,
                       dtype, stream);
+}
+
+sqa_status sqa_prefill(const void* x, const void* Wq, const void* Wk, const void* Wv,
+                       const void* Wo, void* out, void* k_cache, void* v_cache, int64_t B,
+                       int64_t N, int64_t N_max, int64_t d_model, int64_t H, int64_t H_q,
+                       int64_t H_kv, int64_t d_head, sqa_dtype dtype, hipStream_t stream) {
+  if (N_max < 1 || N_max > SQA_MAX_N) return fail(SQA_ERR_UNSUPPORTED, "N_max must be in [1, SQA_MAX_N]");
+  if (B * N != 0) {
+    SQA_TRY(check_ptr(k_cache, "k_cache is null", "k_cache is not 16-byte aligned"));
+    SQA_TRY(check_ptr(v_cache, "v_cache is null", "v_cache is not 16-byte aligned"));
+  }
+  return forward_impl(x, Wq, Wk, Wv, Wo, out, false, nullptr, k_cache, v_cache, N_max, B, N,
+                      d_model, H, H_q, H_kv, d_head, 1, dtype, stream);
+}
+
+sqa_status sqa_decode_step(const void* x_new, const void* Wq, const void* Wk, const void* Wv,
+                           const void* Wo, void* out, void* k_cache, void* v_cache,
+                           const int32_t* pos, int64_t B, int64_t N_max, int64_t d_model,
+                           int64_t H, int64_t H_q, int64_t H_kv, int64_t d_head, sqa_dtype dtype,
+                           hipStream_t stream) {
+  // The B new tokens go through step 1 as one sequence of B tokens.
+  const Shape s{1, B, d_model, H, H_q, H_kv, d_head};
+  SQA_TRY(check_dtype(dtype));
+  SQA_TRY(check_heads(s, true));
+  if (N_max < 1 || N_max > SQA_MAX_N) return fail(SQA_ERR_UNSUPPORTED, "N_max must be in [1, SQA_MAX_N]");
+  if (B > 65535) return fail(SQA_ERR_UNSUPPORTED, "B exceeds 65535 for a decode step");
+  if (B == 0) return ok();
+  SQA_TRY(check_ptr(x_new, "x_new is null", "x_new is not 16-byte aligned"));
+  SQA_TRY(check_ptr(Wq, "Wq is null", "Wq is not 16-byte aligned"));
+  SQA_TRY(check_ptr(Wk, "Wk is null", "Wk is not 16-byte aligned"));
+  SQA_TRY(check_ptr(Wv, "Wv is null", "Wv is not 16-byte aligned"));
+  SQA_TRY(check_ptr(Wo, "Wo is null", "Wo is not 16-byte aligned"));
+  SQA_TRY(check_ptr(out, "out is null", "out is not 16-byte aligned"));
+  SQA_TRY(check_ptr(k_cache, "k_cache is null", "k_cache is not 16-byte aligned"));
+  SQA_TRY(check_ptr(v_cache, "v_cache is null", "v_cache is not 16-byte aligned"));
+  if (!pos) return fail(SQA_ERR_INVALID_ARG, "pos is null");
+  if (reinterpret_cast<uintptr_t>(pos) & 3u) return fail(SQA_ERR_INVALID_ARG, "pos is not 4-byte aligned");
+  Sizes z;
+  SQA_TRY(sizes_for(s, dtype, &z));
+  const size_t es = elem_size(dtype);
+  int64_t cb;
+  if (!mul_ok(B * H_kv, N_max, &cb) || !mul_ok(cb, d_head * (int64_t)es, &cb))
+    return fail(SQA_ERR_UNSUPPORTED, "size overflow");
+  const size_t yb = (size_t)(B * d_model) * es;
+  const size_t wqb = (size_t)(d_model * H_q * d_head) * es, wkb = (size_t)(d_model * H_kv * d_head) * es;
+  const void* ins[6] = {x_new, Wq, Wk, Wv, Wo, pos};
+  const size_t inb[6] = {yb, wqb, wkb, wkb, wqb, (size_t)B * sizeof(int32_t)};
+  for (int j = 0; j < 6; ++j) {
+    if (overlap(out, yb, ins[j], inb[j])) return fail(SQA_ERR_INVALID_ARG, "out overlaps an input");
+    if (overlap(k_cache, (size_t)cb, ins[j], inb[j]) || overlap(v_cache, (size_t)cb, ins[j], inb[j]))
+      return fail(SQA_ERR_INVALID_ARG, "a cache overlaps an input");
+  }
+  if (overlap(k_cache, (size_t)cb, v_cache, (size_t)cb)) return fail(SQA_ERR_INVALID_ARG, "k_cache overlaps v_cache");
+  if (overlap(out, yb, k_cache, (size_t)cb) || overlap(out, yb, v_cache, (size_t)cb))
+    return fail(SQA_ERR_INVALID_ARG, "out overlaps a cache");
+
+  const int64_t part_b = (int64_t)sqa::decode_partial_bytes(B, H_q, H_kv, N_max, d_head);
+  const int64_t off_k = round256(z.q), off_v = off_k + round256(z.kv);
+  const int64_t off_a = off_v + round256(z.kv), off_p = off_a + round256(z.a);
+  const int64_t off_w1 = off_p + round256(part_b);
+  const int64_t off_w3 = off_w1 + round256((int64_t)sqa::qkv_wt_bytes(dtype, d_model, H_q, H_kv, d_head));
+  const int64_t total = off_w3 + round256((int64_t)sqa::out_wt_bytes(dtype, H_q * d_head, d_model));
+  hipMemPool_t pool;
+  SQA_TRY(pool_for(stream, &pool));
+  void* ws = nullptr;
+  hipError_t e = hipMallocFromPoolAsync(&ws, (size_t)total, pool, stream);
+  if (e != hipSuccess) return fail_hip(e, "workspace allocation");
+  char* base = (char*)ws;
+  void *q = base, *k = base + off_k, *vt = base + off_v, *a = base + off_a, *part = base + off_p;
+  void *w1 = base + off_w1, *w3 = base + off_w3;
+  e = sqa::launch_qkv_projection(dtype, x_new, Wq, Wk, Wv, w1, q, k, vt, 1, B, z.Np, d_model, H_q,
+                                 H_kv, d_head, nullptr, stream);
+  if (e == hipSuccess)
+    e = sqa::launch_append_kv(dtype, k, vt, k_cache, v_cache, pos, B, H_kv, d_head, z.Np, N_max, stream);
+  if (e == hipSuccess)
+    e = sqa::launch_decode_attention(dtype, q, k_cache, v_cache, pos, a, part, B, z.Np, N_max, H_q,
+                                     H_kv, d_head, stream);
+  if (e == hipSuccess)
+    e = sqa::launch_output_projection(dtype, a, Wo, w3, out, B, H_q * d_head, d_model, nullptr, 1,
+                                      stream);
+  const hipError_t ef = hipFreeAsync(ws, stream);
+  if (e != hipSuccess) return fail_hip(e, "kernel launch");
+  if (ef != hipSuccess) return fail_hip(ef, "workspace release");
+  return ok();
 }
 
 }  // extern "C"

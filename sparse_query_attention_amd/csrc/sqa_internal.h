@@ -42,4 +42,23 @@ hipError_t launch_output_projection(sqa_dtype dt, const void* a, const void* wo,
                                     void* out, int64_t M, int64_t K, int64_t d_model,
                                     const int32_t* lens, int64_t seq_n, hipStream_t stream);
 
+// Key/value caches [B, H_kv, N_max, d]: rows 0..N-1 from the step-1 layouts k and vt.
+hipError_t launch_fill_cache(sqa_dtype dt, const void* k, const void* vt, void* kc, void* vc,
+                             int64_t B, int64_t H_kv, int64_t N, int64_t Np, int64_t N_max,
+                             int64_t d_head, hipStream_t stream);
+
+// Decode step. q, k, vt are step-1 layouts of the B new tokens taken as one
+// sequence (Npb = padded_length(B)): token b is row b. append writes token b's
+// key and value to cache row pos[b] (clamped into [0, N_max-1]); the attention
+// writes a [B, H_q*d] over cache rows 0..pos[b], with part as scratch of
+// decode_partial_bytes().
+hipError_t launch_append_kv(sqa_dtype dt, const void* k, const void* vt, void* kc, void* vc,
+                            const int32_t* pos, int64_t B, int64_t H_kv, int64_t d_head,
+                            int64_t Npb, int64_t N_max, hipStream_t stream);
+size_t decode_partial_bytes(int64_t B, int64_t H_q, int64_t H_kv, int64_t N_max, int64_t d_head);
+hipError_t launch_decode_attention(sqa_dtype dt, const void* q, const void* kc, const void* vc,
+                                   const int32_t* pos, void* a, void* part, int64_t B, int64_t Npb,
+                                   int64_t N_max, int64_t H_q, int64_t H_kv, int64_t d_head,
+                                   hipStream_t stream);
+
 }  // namespace sqa

@@ -140,3 +140,52 @@ def test_forward_varlen_rejects_invalid_arguments(lens, kw, status, words):
 
 def test_forward_varlen_empty_batch_is_a_no_op():
     assert _fwd_varlen(0, B=0)[0] == _lib.SQA_OK
+
+
+def _decode(**kw):
+    a = dict(x=FAKE, Wq=FAKE + 0x1000000, Wk=FAKE + 0x2000000, Wv=FAKE + 0x3000000,
+             Wo=FAKE + 0x4000000, out=FAKE + 0x5000000, kc=FAKE + 0x6000000, vc=FAKE + 0x7000000,
+             pos=FAKE + 0x8000000, B=2, N_max=1024, d_model=256, H=8, H_q=4, H_kv=2, d_head=32,
+             dtype=_lib.SQA_DTYPE_BF16)
+    a.update(kw)
+    lib = _lib.load()
+    st = lib.sqa_decode_step(a["x"], a["Wq"], a["Wk"], a["Wv"], a["Wo"], a["out"], a["kc"], a["vc"],
+                             a["pos"], a["B"], a["N_max"], a["d_model"], a["H"], a["H_q"], a["H_kv"],
+                             a["d_head"], a["dtype"], None)
+    return st, lib.sqa_last_error_message().decode()
+
+
+@pytest.mark.parametrize("kw,status,words", [
+    (dict(pos=0), _lib.SQA_ERR_INVALID_ARG, "pos is null"),
+    (dict(pos=FAKE + 0x8000002), _lib.SQA_ERR_INVALID_ARG, "4-byte aligned"),
+    (dict(kc=0), _lib.SQA_ERR_INVALID_ARG, "k_cache is null"),
+    (dict(vc=FAKE + 0x6000100), _lib.SQA_ERR_INVALID_ARG, "k_cache overlaps v_cache"),
+    (dict(out=FAKE + 0x6000000), _lib.SQA_ERR_INVALID_ARG, "overlaps"),
+    (dict(pos=FAKE + 0x6000040), _lib.SQA_ERR_INVALID_ARG, "cache overlaps an input"),
+    (dict(N_max=0), _lib.SQA_ERR_UNSUPPORTED, "N_max"),
+    (dict(B=70000), _lib.SQA_ERR_UNSUPPORTED, "65535"),
+    (dict(H_kv=3), _lib.SQA_ERR_INVALID_ARG, "multiple of H_kv"),
+    (dict(d_model=128, H=8, d_head=16), _lib.SQA_ERR_UNSUPPORTED, "d_head"),
+])
+def test_decode_step_rejects_invalid_arguments(kw, status, words):
+    st, msg = _decode(**kw)
+    assert st == status, msg
+    assert words in msg
+
+
+def test_decode_step_with_no_tokens_is_a_no_op():
+    assert _decode(B=0, x=0, pos=0)[0] == _lib.SQA_OK
+
+
+def test_prefill_validates_the_caches():
+    lib = _lib.load()
+    args = lambda kc, vc, N, N_max: (FAKE, FAKE + 0x1000000, FAKE + 0x2000000, FAKE + 0x3000000,
+                                     FAKE + 0x4000000, FAKE + 0x5000000, kc, vc, 2, N, N_max, 256,
+                                     8, 4, 2, 32, _lib.SQA_DTYPE_BF16, None)
+    assert lib.sqa_prefill(*args(0, FAKE + 0x7000000, 64, 128)) == _lib.SQA_ERR_INVALID_ARG
+    assert b"k_cache is null" in lib.sqa_last_error_message()
+    assert lib.sqa_prefill(*args(FAKE + 0x6000000, FAKE + 0x7000000, 200, 128)) == _lib.SQA_ERR_INVALID_ARG
+    assert b"N exceeds N_max" in lib.sqa_last_error_message()
+    assert lib.sqa_prefill(*args(FAKE + 0x6000000, FAKE + 0x7000000, 64, 0)) == _lib.SQA_ERR_UNSUPPORTED
+    assert lib.sqa_prefill(*args(FAKE + 0x6000000, FAKE + 0x6000040, 64, 128)) == _lib.SQA_ERR_INVALID_ARG
+    assert b"overlaps" in lib.sqa_last_error_message()

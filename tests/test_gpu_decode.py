@@ -1,0 +1,122 @@
+"""Prefill and key/value-cache decode (sqa_prefill, sqa_decode_step) on the GPU.
+
+A decode step for token t of a sequence must give row t of the causal SQA
+forward over the sequence's first t+1 tokens; the oracle computes exactly that
+row (oracle.sqa_forward_rows, causal). The caches must hold the step-1 keys and
+values of the cached tokens.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_query_attention_amd as sqa
+import workloads as wl
+from parity import compare, device_inputs, log, oracle_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    sqa._lib.load()   # the HIP library, never a stand-in
+    return torch.device("cuda:0")
+
+
+def _caches(w, N_max, dev, fill=float("nan")):
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    shp = (w.B, w.H_kv, N_max, w.d_head)
+    return (torch.full(shp, fill, dtype=tdt, device=dev), torch.full(shp, fill, dtype=tdt, device=dev))
+
+
+def _oracle_rows(host, w, rows):
+    o = oracle_inputs(host)
+    return oracle.sqa_forward_rows(o["X"], o["Wq"], o["Wk"], o["Wv"], o["Wo"], w.H_q, w.H_kv,
+                                   w.d_head, True, bf16=(w.dtype == "bf16"), rows=rows)["Y_rows"]
+
+
+def test_prefill_is_the_causal_forward_and_fills_the_caches(dev):
+    w = wl.Workload("prefill", B=2, N=300, d_model=1024, H=16, H_q=8, H_kv=4, causal=True,
+                    dtype="bf16", seed=81)
+    _, d = device_inputs(w, dev)
+    kc, vc = _caches(w, 512, dev)
+    y = sqa.prefill(d["X"], d["Wq"], d["Wk"], d["Wv"], d["Wo"], kc, vc, H=w.H, H_q=w.H_q, H_kv=w.H_kv)
+    y_ref = sqa.forward(d["X"], d["Wq"], d["Wk"], d["Wv"], d["Wo"], H=w.H, H_q=w.H_q, H_kv=w.H_kv,
+                        causal=True)
+    q, k, vt = sqa.qkv_projection(d["X"], d["Wq"], d["Wk"], d["Wv"], H=w.H, H_q=w.H_q, H_kv=w.H_kv)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_ref)
+    assert torch.equal(kc[:, :, :w.N], k[:, :, :w.N])
+    assert torch.equal(vc[:, :, :w.N], vt[..., :w.N].transpose(-1, -2))
+    assert bool(torch.isnan(kc[:, :, w.N:]).all()) and bool(torch.isnan(vc[:, :, w.N:]).all())
+
+
+DECODE_SHAPES = [
+    # (H, d_head, H_q, H_kv, dtype): g = 2, 1, 4, 16 (two head groups), fp32, d = 32
+    (16, 64, 8, 4, "bf16"), (16, 64, 4, 4, "bf16"), (16, 64, 4, 1, "bf16"),
+    (16, 64, 16, 1, "bf16"), (8, 32, 4, 2, "fp32"), (8, 32, 6, 2, "bf16"),
+]
+
+
+@pytest.mark.parametrize("H,dh,H_q,H_kv,dtype", DECODE_SHAPES, ids=lambda v: str(v))
+def test_generation_loop_matches_causal_forward(dev, H, dh, H_q, H_kv, dtype):
+    """Prefill 150 tokens, then decode tokens 150..157 one step at a time."""
+    T, t0, N_max = 158, 150, 256
+    w = wl.Workload("gen", B=3, N=T, d_model=H * dh, H=H, H_q=H_q, H_kv=H_kv, causal=True,
+                    dtype=dtype, seed=82 + H_q * 7 + H_kv)
+    log(f"case decode loop H={H} d={dh} H_q={H_q} H_kv={H_kv} {dtype}")
+    host, d = device_inputs(w, dev)
+    kc, vc = _caches(w, N_max, dev)
+    sqa.prefill(d["X"][:, :t0].contiguous(), d["Wq"], d["Wk"], d["Wv"], d["Wo"], kc, vc, H=w.H,
+                H_q=w.H_q, H_kv=w.H_kv)
+    ys = []
+    for t in range(t0, T):
+        pos = torch.full((w.B,), t, dtype=torch.int32, device=dev)
+        ys.append(sqa.decode_step(d["X"][:, t].contiguous(), d["Wq"], d["Wk"], d["Wv"], d["Wo"], kc, vc,
+                                  pos, H=w.H, H_q=w.H_q, H_kv=w.H_kv))
+    torch.cuda.synchronize()
+    got = np.stack([wl.widen(y.cpu()) for y in ys], axis=1)          # [B, steps, d_model]
+    rows = np.array([b * T + t for b in range(w.B) for t in range(t0, T)])
+    ref = _oracle_rows(host, w, rows).reshape(w.B, T - t0, w.d_model)
+    rep = compare(got, ref, dtype)
+    log(f"  {rep}")
+    assert rep.ok, rep
+
+
+def test_decode_at_mixed_positions_and_clamped_positions(dev):
+    """Each sequence at its own position; out-of-range positions are clamped."""
+    w = wl.Workload("mixed", B=5, N=400, d_model=1024, H=16, H_q=8, H_kv=2, causal=True,
+                    dtype="bf16", seed=90)
+    host, d = device_inputs(w, dev)
+    kc, vc = _caches(w, w.N, dev)
+    sqa.prefill(d["X"], d["Wq"], d["Wk"], d["Wv"], d["Wo"], kc, vc, H=w.H, H_q=w.H_q, H_kv=w.H_kv)
+    pos_in = np.array([0, 1, 399, 137, -4], dtype=np.int32)     # -4 behaves as 0
+    p = np.clip(pos_in, 0, w.N - 1)
+    x_new = torch.stack([d["X"][b, int(p[b])] for b in range(w.B)])
+    y = sqa.decode_step(x_new, d["Wq"], d["Wk"], d["Wv"], d["Wo"], kc, vc,
+                        torch.from_numpy(pos_in).to(dev), H=w.H, H_q=w.H_q, H_kv=w.H_kv)
+    torch.cuda.synchronize()
+    ref = _oracle_rows(host, w, [b * w.N + int(p[b]) for b in range(w.B)])
+    rep = compare(wl.widen(y.cpu()), ref, "bf16")
+    log(f"  mixed positions: {rep}")
+    assert rep.ok, rep
+
+
+def test_decode_over_a_long_cache(dev):
+    """32k-token caches: many key chunks per sequence, merged across workgroups."""
+    w = wl.Workload("long_decode", B=4, N=32768, d_model=1024, H=16, H_q=8, H_kv=4, causal=True,
+                    dtype="bf16", seed=91)
+    host, d = device_inputs(w, dev)
+    kc, vc = _caches(w, w.N, dev)
+    sqa.prefill(d["X"], d["Wq"], d["Wk"], d["Wv"], d["Wo"], kc, vc, H=w.H, H_q=w.H_q, H_kv=w.H_kv)
+    p = np.array([32767, 20000, 64, 4097], dtype=np.int32)
+    x_new = torch.stack([d["X"][b, int(p[b])] for b in range(w.B)])
+    y = sqa.decode_step(x_new, d["Wq"], d["Wk"], d["Wv"], d["Wo"], kc, vc,
+                        torch.from_numpy(p).to(dev), H=w.H, H_q=w.H_q, H_kv=w.H_kv)
+    torch.cuda.synchronize()
+    ref = _oracle_rows(host, w, [b * w.N + int(p[b]) for b in range(w.B)])
+    rep = compare(wl.widen(y.cpu()), ref, "bf16")
+    log(f"  long cache: {rep}")
+    assert rep.ok, rep
