@@ -204,6 +204,53 @@ def run_varlen(w: wl.Workload, steps: int, warmup: int, torch, sqa, dev):
     return res
 
 
+def run_decode(w: wl.Workload, steps: int, warmup: int, torch, sqa, dev):
+    """sqa_decode_step for B sequences whose caches hold w.N - 1 tokens (filled
+    by sqa_prefill): each step attends over w.N keys. Decode reads every cached
+    key and value once per step, so its roofline is HBM bandwidth; the bytes
+    counted are the caches' rows 0..N-1, the four weight matrices and the
+    tokens in and out."""
+    host = wl.to_device_dtype(wl.draw(w), w.dtype)
+    d = {k: v.to(dev) for k, v in host.items()}
+    del host
+    es = 2 if w.dtype == "bf16" else 4
+    tdt = d["X"].dtype
+    kc = torch.empty((w.B, w.H_kv, w.N, w.d_head), dtype=tdt, device=dev)
+    vc = torch.empty_like(kc)
+    sqa.prefill(d["X"][:, :w.N - 1].contiguous(), d["Wq"], d["Wk"], d["Wv"], d["Wo"], kc, vc, H=w.H,
+                H_q=w.H_q, H_kv=w.H_kv)
+    x_new = d["X"][:, w.N - 1].contiguous()
+    pos = torch.full((w.B,), w.N - 1, dtype=torch.int32, device=dev)
+    out = torch.empty_like(x_new)
+    del d["X"]
+    stream = torch.cuda.current_stream(dev)
+    tm = Timer(torch, stream)
+
+    def step():
+        sqa.decode_step(x_new, d["Wq"], d["Wk"], d["Wv"], d["Wo"], kc, vc, pos, H=w.H, H_q=w.H_q,
+                        H_kv=w.H_kv, out=out)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = tm.event()
+    for _ in range(steps):
+        step()
+    e1 = tm.event()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    cache_bytes = 2 * w.B * w.H_kv * w.N * w.d_head * es
+    weight_bytes = (w.d_model * (w.H_q + 2 * w.H_kv) * w.d_head + w.H_q * w.d_head * w.d_model) * es
+    io_bytes = 2 * w.B * w.d_model * es
+    total = cache_bytes + weight_bytes + io_bytes
+    del d, kc, vc
+    torch.cuda.empty_cache()
+    return {"B": w.B, "cache_tokens": w.N, "H_q": w.H_q, "H_kv": w.H_kv,
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(w.B / (ms / 1e3), 1),
+            "bytes_per_step": total, "gbs": round(total / (ms / 1e3) / 1e9, 1),
+            "frac_hbm_peak": round(total / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def cpu_baseline(w: wl.Workload, rows_sample: int = 24576):
     """The float64 oracle on a bounded sample: every key/value projection of the
     workload, plus the whole forward of `rows_sample` evenly spaced query rows.
@@ -330,6 +377,13 @@ def main():
         times = list(sweep.values())
         variants["hkv_sweep_n32768_hq4_attention_ms"] = dict(
             sweep, max_over_min=round(max(times) / min(times), 3))
+        # One decode step over 32k-token caches, SQA and its GQA baseline: the
+        # step is bound by reading the key/value caches, which SQA leaves at
+        # H_kv heads, so cutting query heads should not speed it up (abstract).
+        dec = wl.Workload("sqa_bf16_decode_b8_cache32768", B=8, N=32768, d_model=1024, H=16,
+                          H_q=8, H_kv=4, causal=True, dtype="bf16", seed=1006)
+        for v in (dec, dec.with_(name=dec.name + "_baseline", H_q=16)):
+            variants[v.name] = run_decode(v, max(10, args.steps), vwarm, torch, sqa, dev)
         # A padded batch of sequences of mixed length (sqa_forward_varlen).
         variants[wl.SQA_VARLEN_32K.name] = run_varlen(wl.SQA_VARLEN_32K, vsteps, vwarm, torch, sqa,
                                                       dev)
