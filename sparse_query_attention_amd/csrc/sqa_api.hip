@@ -3,6 +3,7 @@
 // gfx950 kernels (projection, attention core, output projection).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <mutex>
 #include <stdint.h>
 #include <stdio.h>
@@ -383,7 +384,7 @@ sqa_status sqa_decode_step(const void* x_new, const void* Wq, const void* Wk, co
                            const int32_t* pos, int64_t B, int64_t N_max, int64_t d_model,
                            int64_t H, int64_t H_q, int64_t H_kv, int64_t d_head, sqa_dtype dtype,
                            hipStream_t stream) {
-  // The B new tokens go through step 1 as one sequence of B tokens.
+  // Shape checks as for one sequence of B tokens (head counts, d_head, sizes).
   const Shape s{1, B, d_model, H, H_q, H_kv, d_head};
   SQA_TRY(check_dtype(dtype));
   SQA_TRY(check_heads(s, true));
@@ -419,30 +420,29 @@ sqa_status sqa_decode_step(const void* x_new, const void* Wq, const void* Wk, co
   if (overlap(out, yb, k_cache, (size_t)cb) || overlap(out, yb, v_cache, (size_t)cb))
     return fail(SQA_ERR_INVALID_ARG, "out overlaps a cache");
 
-  const int64_t part_b = (int64_t)sqa::decode_partial_bytes(B, H_q, H_kv, N_max, d_head);
-  const int64_t off_k = round256(z.q), off_v = off_k + round256(z.kv);
-  const int64_t off_a = off_v + round256(z.kv), off_p = off_a + round256(z.a);
-  const int64_t off_w1 = off_p + round256(part_b);
-  const int64_t off_w3 = off_w1 + round256((int64_t)sqa::qkv_wt_bytes(dtype, d_model, H_q, H_kv, d_head));
-  const int64_t total = off_w3 + round256((int64_t)sqa::out_wt_bytes(dtype, H_q * d_head, d_model));
+  // Workspace: q and a [B, H_q*d_head], then one fp32 scratch region that the
+  // three stages use in turn (stream order keeps them apart).
+  const int64_t qa_b = B * H_q * d_head * (int64_t)es;
+  const int64_t scratch_b = std::max<int64_t>(
+      {(int64_t)sqa::decode_partial_bytes(B, H_q, H_kv, N_max, d_head),
+       (int64_t)sqa::skinny_partial_bytes(B, d_model, (H_q + 2 * H_kv) * d_head),
+       (int64_t)sqa::skinny_partial_bytes(B, H_q * d_head, d_model)});
+  const int64_t off_a = round256(qa_b), off_p = off_a + round256(qa_b);
+  const int64_t total = off_p + round256(scratch_b);
   hipMemPool_t pool;
   SQA_TRY(pool_for(stream, &pool));
   void* ws = nullptr;
   hipError_t e = hipMallocFromPoolAsync(&ws, (size_t)total, pool, stream);
   if (e != hipSuccess) return fail_hip(e, "workspace allocation");
   char* base = (char*)ws;
-  void *q = base, *k = base + off_k, *vt = base + off_v, *a = base + off_a, *part = base + off_p;
-  void *w1 = base + off_w1, *w3 = base + off_w3;
-  e = sqa::launch_qkv_projection(dtype, x_new, Wq, Wk, Wv, w1, q, k, vt, 1, B, z.Np, d_model, H_q,
-                                 H_kv, d_head, nullptr, stream);
+  void *q = base, *a = base + off_a, *part = base + off_p;
+  e = sqa::launch_decode_qkv(dtype, x_new, Wq, Wk, Wv, pos, q, k_cache, v_cache, part, B, d_model,
+                             H_q, H_kv, d_head, N_max, stream);
   if (e == hipSuccess)
-    e = sqa::launch_append_kv(dtype, k, vt, k_cache, v_cache, pos, B, H_kv, d_head, z.Np, N_max, stream);
+    e = sqa::launch_decode_attention(dtype, q, k_cache, v_cache, pos, a, part, B, N_max, H_q, H_kv,
+                                     d_head, stream);
   if (e == hipSuccess)
-    e = sqa::launch_decode_attention(dtype, q, k_cache, v_cache, pos, a, part, B, z.Np, N_max, H_q,
-                                     H_kv, d_head, stream);
-  if (e == hipSuccess)
-    e = sqa::launch_output_projection(dtype, a, Wo, w3, out, B, H_q * d_head, d_model, nullptr, 1,
-                                      stream);
+    e = sqa::launch_decode_out(dtype, a, Wo, out, part, B, H_q * d_head, d_model, stream);
   const hipError_t ef = hipFreeAsync(ws, stream);
   if (e != hipSuccess) return fail_hip(e, "kernel launch");
   if (ef != hipSuccess) return fail_hip(ef, "workspace release");

@@ -70,25 +70,181 @@ __global__ __launch_bounds__(256) void transpose_v(const T* vt, T* vc, int N, in
   }
 }
 
-// ---- decode: the new tokens' K and V into row pos[b] of the caches ----
+// ---- decode: projections of the B new tokens ----
+// A decode step projects only B tokens, so these products are skinny: each
+// weight element is used B times, and the step is bound by reading the weights
+// once. They are read in their [in, out] layout, by many workgroups: a
+// workgroup owns 256 output columns (one 16-byte weight chunk per thread and
+// row), a slice of the K rows, which its thread phases split again, and up to
+// 8 of the tokens. fp32 partial sums per K slice go to scratch; a finalize
+// kernel adds the slices in a fixed order, rounds once to T, and stores.
 
-// k [H_kv, Npb, D] and vt [H_kv, D, Npb] hold the step's tokens as rows b < B.
+constexpr int SK_COLS = 256, SK_BR = 8, SK_KB = 64;    // columns, tokens, K rows per block
+constexpr int SK_SPLIT_MAX = 16;                        // K slices at most
+
+// part[ks][b][n] = sum over k in slice ks of x[b][k] * W[k][n], W = [W0 | W1 | W2]
+// (each segment's width a multiple of 32, so a thread's chunk lies in one).
 template <typename T>
-__global__ void append_kv(const T* k, const T* vt, T* kc, T* vc, const int32_t* pos, int H_kv,
-                          int D, int64_t Npb, int64_t N_max) {
-  const int b = blockIdx.x / H_kv, h = blockIdx.x % H_kv, c = threadIdx.x;
+__global__ __launch_bounds__(256) void skinny_partial(const T* x, int B, int K, const T* w0, int n0w,
+                                                      const T* w1, int n1w, const T* w2, int n2w,
+                                                      float* part, int ncols, int k_slice) {
+  constexpr int EPC = 16 / (int)sizeof(T);   // columns per thread
+  constexpr int TPR = SK_COLS / EPC;         // threads per weight row
+  constexpr int PH = 256 / TPR;              // thread phases over K
+  constexpr int J = SK_KB / PH;              // rows per thread and block
+  constexpr int RR = 4;                      // token rows per phase-reduction round
+  __shared__ __align__(16) float xs[SK_KB][SK_BR];
+  __shared__ float red[PH][TPR][EPC * RR];
+  const int tid = threadIdx.x, cc = tid % TPR, kp = tid / TPR;
+  const int col0 = blockIdx.x * SK_COLS + cc * EPC;
+  const int ks = blockIdx.y, kbeg = ks * k_slice, kend = min(K, kbeg + k_slice);
+  const int b0 = blockIdx.z * SK_BR, nb = min(SK_BR, B - b0);
+  const bool active = col0 < ncols;
+  const T* W = w0;   // threads past the last column read column 0 and discard it
+  int ld = n0w, cl = 0;
+  if (col0 < n0w) { cl = col0; }
+  else if (col0 < n0w + n1w) { W = w1; ld = n1w; cl = col0 - n0w; }
+  else if (active) { W = w2; ld = n2w; cl = col0 - n0w - n1w; }
+  float acc[SK_BR][EPC];
+#pragma unroll
+  for (int b = 0; b < SK_BR; ++b)
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[b][e] = 0.f;
+  for (int k0 = kbeg; k0 < kend; k0 += SK_KB) {
+    // Every load of the block is issued before any is used: the addresses are
+    // clamped to valid rows and the values of rows past the slice replaced by 0
+    // afterwards, so no load sits behind a branch.
+    Chunk raw[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int k = k0 + kp + j * PH;
+      raw[j] = *reinterpret_cast<const Chunk*>(W + (int64_t)(k < kend ? k : kbeg) * ld + cl);
+    }
+    constexpr int XPT = SK_KB * SK_BR / 256;   // x values per thread
+    T xr[XPT];
+#pragma unroll
+    for (int u = 0; u < XPT; ++u) {
+      const int i = tid + u * 256, b = i / SK_KB, k = k0 + i % SK_KB;
+      xr[u] = x[(int64_t)(b0 + (b < nb ? b : 0)) * K + (k < kend ? k : kbeg)];
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j) {   // a mask, not a branch, so the loads stay in flight
+      const uint32_t keep = active && k0 + kp + j * PH < kend ? ~0u : 0u;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) raw[j].w[w] &= keep;
+    }
+    __syncthreads();   // the previous block's reads of xs are done
+#pragma unroll
+    for (int u = 0; u < XPT; ++u) {
+      const int i = tid + u * 256, b = i / SK_KB, kk = i % SK_KB;
+      xs[kk][b] = b < nb && k0 + kk < kend ? to_f32(xr[u]) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const T* wv = reinterpret_cast<const T*>(&raw[j]);
+      float wf[EPC];
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) wf[e] = to_f32(wv[e]);
+      const float4* xr = reinterpret_cast<const float4*>(&xs[kp + j * PH][0]);
+#pragma unroll
+      for (int b4 = 0; b4 < SK_BR / 4; ++b4) {
+        const float4 xv = xr[b4];
+        const float xb[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) acc[b4 * 4 + u][e] = fmaf(xb[u], wf[e], acc[b4 * 4 + u][e]);
+      }
+    }
+  }
+  // sum the thread phases, RR token rows a round, through LDS
+#pragma unroll
+  for (int r0 = 0; r0 < SK_BR; r0 += RR) {
+    if (r0 >= nb) break;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < RR; ++u)
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) red[kp][cc][u * EPC + e] = acc[r0 + u][e];
+    __syncthreads();
+    for (int i = tid; i < RR * SK_COLS; i += 256) {
+      const int u = i / SK_COLS, c = i % SK_COLS, b = r0 + u;
+      const int col = blockIdx.x * SK_COLS + c;
+      if (b < nb && col < ncols) {
+        float v = 0.f;
+#pragma unroll
+        for (int ph = 0; ph < PH; ++ph) v += red[ph][c / EPC][u * EPC + c % EPC];
+        part[((int64_t)ks * B + b0 + b) * ncols + col] = v;
+      }
+    }
+  }
+}
+
+// Grid of a skinny product: enough workgroups to spread the weight read over
+// the chip, K slices a multiple of SK_KB rows.
+struct SkinnyPlan { int col_blocks, split, k_slice, b_chunks; };
+
+SkinnyPlan skinny_plan(int64_t B, int64_t K, int64_t ncols) {
+  SkinnyPlan pl;
+  pl.col_blocks = (int)((ncols + SK_COLS - 1) / SK_COLS);
+  pl.b_chunks = (int)((B + SK_BR - 1) / SK_BR);
+  const int64_t k_blocks = (K + SK_KB - 1) / SK_KB;
+  const int64_t units = (int64_t)pl.col_blocks * pl.b_chunks;
+  const int64_t want =
+      std::min<int64_t>(std::min<int64_t>(k_blocks, SK_SPLIT_MAX), (512 + units - 1) / units);
+  const int64_t split = std::max<int64_t>(1, want);
+  pl.k_slice = (int)((k_blocks + split - 1) / split * SK_KB);
+  pl.split = (int)((K + pl.k_slice - 1) / pl.k_slice);
+  return pl;
+}
+
+// Sum of the K slices (n_split <= SK_SPLIT_MAX) of column n for token b, in
+// slice order, rounded once. All loads are issued first (indexes clamped).
+template <typename T>
+__device__ inline T skinny_sum(const float* part, int n_split, int B, int ncols, int b, int n) {
+  float pv[SK_SPLIT_MAX];
+#pragma unroll
+  for (int ks = 0; ks < SK_SPLIT_MAX; ++ks)
+    pv[ks] = part[((int64_t)(ks < n_split ? ks : 0) * B + b) * ncols + n];
+  float v = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < SK_SPLIT_MAX; ++ks)
+    if (ks < n_split) v += pv[ks];
+  return from_f32<T>(v);
+}
+
+// Q/K/V of the new tokens: q to [B, H_q*D]; k and v straight to cache row pos[b].
+template <typename T>
+__global__ __launch_bounds__(256) void finalize_qkv(const float* part, int n_split, int B,
+                                                    int wq_w, int wkv_w, int D, const int32_t* pos,
+                                                    T* q, T* kc, T* vc, int H_kv, int64_t N_max) {
+  const int ncols = wq_w + 2 * wkv_w;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)B * ncols) return;
+  const int b = (int)(i / ncols), n = (int)(i % ncols);
+  const T v = skinny_sum<T>(part, n_split, B, ncols, b, n);
+  if (n < wq_w) { q[(int64_t)b * wq_w + n] = v; return; }
+  const int nk = (n - wq_w) % wkv_w, h = nk / D, c = nk % D;
   const int64_t p = min(max((int64_t)pos[b], (int64_t)0), N_max - 1);
-  const int64_t dst = (((int64_t)b * H_kv + h) * N_max + p) * D + c;
-  kc[dst] = k[((int64_t)h * Npb + b) * D + c];
-  vc[dst] = vt[((int64_t)h * D + c) * Npb + b];
+  T* dst = n < wq_w + wkv_w ? kc : vc;
+  dst[(((int64_t)b * H_kv + h) * N_max + p) * D + c] = v;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void finalize_dense(const float* part, int n_split, int B,
+                                                      int ncols, T* out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)B * ncols) return;
+  out[i] = skinny_sum<T>(part, n_split, B, ncols, (int)(i / ncols), (int)(i % ncols));
 }
 
 struct DecParams {
-  const void* q;                 // [H_q, Npb, D]: query head i of token b at row b
+  const void* q;                 // [B, H_q * D]: query head i of token b at q[b][i*D ..]
   const void* kc; const void* vc;
   const int32_t* pos;
   float* part;                   // [B, H_q, n_chunks, D + 2]: o[D], m, l per chunk
-  int64_t Npb, N_max;
+  int64_t N_max;
   int H_q, H_kv, g, n_hg, n_chunks, chunk;   // chunk: keys per workgroup, a multiple of KB
   float c;                       // log2(e) / sqrt(D)
 };
@@ -127,7 +283,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_partial(DecParams p) {
   const T* Q = (const T*)p.q;
   for (int i = tid; i < G * D; i += DEC_THREADS) {
     const int hd = i / D, e = i % D;
-    qs[hd][e] = hd < gq ? to_f32(Q[((int64_t)(i0 + hd) * p.Npb + b) * D + e]) : 0.f;
+    qs[hd][e] = hd < gq ? to_f32(Q[((int64_t)b * p.H_q + i0 + hd) * D + e]) : 0.f;
   }
   __syncthreads();
 
@@ -153,10 +309,19 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_partial(DecParams p) {
     float s[G];
 #pragma unroll
     for (int i = 0; i < G; ++i) s[i] = 0.f;
+    Chunk kraw[CPK];   // the whole key row in flight before any use
+#pragma unroll
+    for (int ck = 0; ck < CPK; ++ck) kraw[ck] = *reinterpret_cast<const Chunk*>(krow + ck * EPC);
+    // value chunks of this block for phase 2, also issued now
+    Chunk vraw[CPK];
+#pragma unroll
+    for (int r = 0; r < CPK; ++r) {
+      const int jv = kb + r * KGS + kg;
+      vraw[r] = *reinterpret_cast<const Chunk*>(Vc + (int64_t)(jv < k_end ? jv : k_begin) * D + dc * EPC);
+    }
 #pragma unroll
     for (int ck = 0; ck < CPK; ++ck) {
-      const Chunk raw = *reinterpret_cast<const Chunk*>(krow + ck * EPC);
-      const T* kv = reinterpret_cast<const T*>(&raw);
+      const T* kv = reinterpret_cast<const T*>(&kraw[ck]);
 #pragma unroll
       for (int e = 0; e < EPC; ++e) {
         const float kf = to_f32(kv[e]);
@@ -188,10 +353,8 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_partial(DecParams p) {
       for (int e = 0; e < EPC; ++e) o[i][e] *= alpha[i];
 #pragma unroll
     for (int r = 0; r < CPK; ++r) {
-      const int jl = r * KGS + kg;   // key within the block
-      const int jj = kb + jl < k_end ? kb + jl : k_begin;   // in range; p is 0 past k_end
-      const Chunk raw = *reinterpret_cast<const Chunk*>(Vc + (int64_t)jj * D + dc * EPC);
-      const T* vv = reinterpret_cast<const T*>(&raw);
+      const int jl = r * KGS + kg;   // key within the block; past k_end it loaded a valid row, p = 0
+      const T* vv = reinterpret_cast<const T*>(&vraw[r]);
       float vf[EPC];
 #pragma unroll
       for (int e = 0; e < EPC; ++e) vf[e] = to_f32(vv[e]);
@@ -239,24 +402,52 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_partial(DecParams p) {
   }
 }
 
-// One workgroup of D threads per (sequence, query head): merges the chunks
-// that hold keys of that sequence and writes a[b, i*D + e].
+// One 256-thread workgroup per (sequence, query head) merges the chunks that
+// hold keys of that sequence and writes a[b, i*D + e]. The chunks' (m, l) go to
+// LDS in parallel; then 256/D column groups take every (256/D)-th chunk, so
+// their loads of o are independent, and the groups are summed through LDS.
+constexpr int MAX_CHUNKS = 1024;
+
 template <typename T, int D>
-__global__ __launch_bounds__(D) void decode_combine(const float* part, const int32_t* pos, T* a,
-                                                    int H_q, int n_chunks, int chunk, int64_t N_max) {
-  const int b = blockIdx.x / H_q, i = blockIdx.x % H_q, e = threadIdx.x;
+__global__ __launch_bounds__(256) void decode_combine(const float* part, const int32_t* pos, T* a,
+                                                      int H_q, int n_chunks, int chunk,
+                                                      int64_t N_max) {
+  constexpr int GR = 256 / D;
+  __shared__ float sm[MAX_CHUNKS], sl[MAX_CHUNKS];
+  __shared__ float wmax[4], red_o[GR][D], red_l[GR];
+  const int b = blockIdx.x / H_q, i = blockIdx.x % H_q, tid = threadIdx.x;
   const int64_t pb = min(max((int64_t)pos[b], (int64_t)0), N_max - 1);
   const int n_valid = (int)min((int64_t)n_chunks, (pb + 1 + chunk - 1) / chunk);
   const float* src = part + ((int64_t)b * H_q + i) * n_chunks * (D + 2);
-  float M = DEC_M_INIT;
-  for (int c = 0; c < n_valid; ++c) M = fmaxf(M, src[c * (D + 2) + D]);
-  float L = 0.f, O = 0.f;
-  for (int c = 0; c < n_valid; ++c) {
-    const float f = __builtin_amdgcn_exp2f(src[c * (D + 2) + D] - M);
-    L += src[c * (D + 2) + D + 1] * f;
-    O += src[c * (D + 2) + e] * f;
+  float lm = DEC_M_INIT;
+  for (int c = tid; c < n_valid; c += 256) {
+    const float m = src[c * (D + 2) + D];
+    sm[c] = m;
+    sl[c] = src[c * (D + 2) + D + 1];
+    lm = fmaxf(lm, m);
   }
-  a[((int64_t)b * H_q + i) * D + e] = from_f32<T>(O / L);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) lm = fmaxf(lm, __shfl_xor(lm, off));
+  if ((tid & 63) == 0) wmax[tid >> 6] = lm;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const int gr = tid / D, e = tid % D;
+  float O = 0.f, L = 0.f;
+#pragma unroll 4
+  for (int c = gr; c < n_valid; c += GR) {
+    const float f = __builtin_amdgcn_exp2f(sm[c] - M);
+    O = fmaf(src[c * (D + 2) + e], f, O);
+    L = fmaf(sl[c], f, L);
+  }
+  red_o[gr][e] = O;
+  if (e == 0) red_l[gr] = L;
+  __syncthreads();
+  if (tid < D) {
+    float o = 0.f, l = 0.f;
+#pragma unroll
+    for (int g2 = 0; g2 < GR; ++g2) { o += red_o[g2][tid]; l += red_l[g2]; }
+    a[((int64_t)b * H_q + i) * D + tid] = from_f32<T>(o / l);
+  }
 }
 
 // Chunking of a decode step: enough workgroups for the chip, chunks a multiple of KB.
@@ -295,20 +486,21 @@ hipError_t partial_for(int G, const DecParams& p, dim3 grid, hipStream_t stream)
 
 template <typename T, int D>
 hipError_t decode_impl(const void* q, const void* kc, const void* vc, const int32_t* pos, void* a,
-                       float* part, int64_t B, int64_t Npb, int64_t N_max, int64_t H_q,
-                       int64_t H_kv, hipStream_t stream) {
+                       float* part, int64_t B, int64_t N_max, int64_t H_q, int64_t H_kv,
+                       hipStream_t stream) {
   const DecodePlan pl = decode_plan(B, H_q, H_kv, N_max);
   DecParams p;
   p.q = q; p.kc = kc; p.vc = vc; p.pos = pos; p.part = part;
-  p.Npb = Npb; p.N_max = N_max;
+  p.N_max = N_max;
   p.H_q = (int)H_q; p.H_kv = (int)H_kv; p.g = (int)(H_q / H_kv); p.n_hg = pl.n_hg;
   p.n_chunks = pl.n_chunks; p.chunk = pl.chunk;
   p.c = (float)(1.4426950408889634 / sqrt((double)D));
   const dim3 grid((unsigned)pl.n_chunks, (unsigned)(H_kv * pl.n_hg), (unsigned)B);
   hipError_t e = partial_for<T, D>(pl.G, p, grid, stream);
   if (e != hipSuccess) return e;
-  decode_combine<T, D><<<(unsigned)(B * H_q), D, 0, stream>>>(part, pos, (T*)a, (int)H_q,
-                                                            pl.n_chunks, pl.chunk, N_max);
+  if (pl.n_chunks > MAX_CHUNKS) return hipErrorInvalidConfiguration;
+  decode_combine<T, D><<<(unsigned)(B * H_q), 256, 0, stream>>>(part, pos, (T*)a, (int)H_q,
+                                                              pl.n_chunks, pl.chunk, N_max);
   return hipGetLastError();
 }
 
@@ -342,30 +534,82 @@ hipError_t launch_fill_cache(sqa_dtype dt, const void* k, const void* vt, void* 
   return hipGetLastError();
 }
 
-hipError_t launch_append_kv(sqa_dtype dt, const void* k, const void* vt, void* kc, void* vc,
-                            const int32_t* pos, int64_t B, int64_t H_kv, int64_t d_head,
-                            int64_t Npb, int64_t N_max, hipStream_t stream) {
-  const unsigned grid = (unsigned)(B * H_kv), threads = (unsigned)d_head;
-  if (dt == SQA_DTYPE_BF16)
-    append_kv<bf16><<<grid, threads, 0, stream>>>((const bf16*)k, (const bf16*)vt, (bf16*)kc,
-                                                 (bf16*)vc, pos, (int)H_kv, (int)d_head, Npb, N_max);
-  else
-    append_kv<float><<<grid, threads, 0, stream>>>((const float*)k, (const float*)vt, (float*)kc,
-                                                  (float*)vc, pos, (int)H_kv, (int)d_head, Npb, N_max);
+size_t skinny_partial_bytes(int64_t B, int64_t K, int64_t ncols) {
+  return (size_t)(skinny_plan(B, K, ncols).split * B * ncols) * sizeof(float);
+}
+
+namespace {
+template <typename T>
+hipError_t skinny(const void* x, int64_t B, int64_t K, const void* w0, int64_t n0w, const void* w1,
+                  int64_t n1w, const void* w2, int64_t n2w, float* part, int* n_split,
+                  hipStream_t stream) {
+  const int64_t ncols = n0w + n1w + n2w;
+  const SkinnyPlan pl = skinny_plan(B, K, ncols);
+  *n_split = pl.split;
+  const dim3 grid((unsigned)pl.col_blocks, (unsigned)pl.split, (unsigned)pl.b_chunks);
+  skinny_partial<T><<<grid, 256, 0, stream>>>((const T*)x, (int)B, (int)K, (const T*)w0, (int)n0w,
+                                             (const T*)w1, (int)n1w, (const T*)w2, (int)n2w, part,
+                                             (int)ncols, pl.k_slice);
   return hipGetLastError();
 }
 
+template <typename T>
+hipError_t decode_qkv(const void* x_new, const void* wq, const void* wk, const void* wv,
+                      const int32_t* pos, void* q, void* kc, void* vc, float* part, int64_t B,
+                      int64_t d_model, int64_t H_q, int64_t H_kv, int64_t d_head, int64_t N_max,
+                      hipStream_t stream) {
+  const int64_t wq_w = H_q * d_head, wkv_w = H_kv * d_head, ncols = wq_w + 2 * wkv_w;
+  int n_split = 0;
+  hipError_t e = skinny<T>(x_new, B, d_model, wq, wq_w, wk, wkv_w, wv, wkv_w, part, &n_split, stream);
+  if (e != hipSuccess) return e;
+  const unsigned grid = (unsigned)((B * ncols + 255) / 256);
+  finalize_qkv<T><<<grid, 256, 0, stream>>>(part, n_split, (int)B, (int)wq_w, (int)wkv_w,
+                                           (int)d_head, pos, (T*)q, (T*)kc, (T*)vc, (int)H_kv, N_max);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t decode_out(const void* a, const void* wo, void* out, float* part, int64_t B, int64_t K,
+                      int64_t d_model, hipStream_t stream) {
+  int n_split = 0;
+  hipError_t e = skinny<T>(a, B, K, wo, d_model, nullptr, 0, nullptr, 0, part, &n_split, stream);
+  if (e != hipSuccess) return e;
+  const unsigned grid = (unsigned)((B * d_model + 255) / 256);
+  finalize_dense<T><<<grid, 256, 0, stream>>>(part, n_split, (int)B, (int)d_model, (T*)out);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_decode_qkv(sqa_dtype dt, const void* x_new, const void* wq, const void* wk,
+                             const void* wv, const int32_t* pos, void* q, void* kc, void* vc,
+                             void* part, int64_t B, int64_t d_model, int64_t H_q, int64_t H_kv,
+                             int64_t d_head, int64_t N_max, hipStream_t stream) {
+  if ((B + SK_BR - 1) / SK_BR > 65535) return hipErrorInvalidConfiguration;
+  return dt == SQA_DTYPE_BF16
+      ? decode_qkv<bf16>(x_new, wq, wk, wv, pos, q, kc, vc, (float*)part, B, d_model, H_q, H_kv,
+                         d_head, N_max, stream)
+      : decode_qkv<float>(x_new, wq, wk, wv, pos, q, kc, vc, (float*)part, B, d_model, H_q, H_kv,
+                          d_head, N_max, stream);
+}
+
+hipError_t launch_decode_out(sqa_dtype dt, const void* a, const void* wo, void* out, void* part,
+                             int64_t B, int64_t K, int64_t d_model, hipStream_t stream) {
+  if ((B + SK_BR - 1) / SK_BR > 65535) return hipErrorInvalidConfiguration;
+  return dt == SQA_DTYPE_BF16 ? decode_out<bf16>(a, wo, out, (float*)part, B, K, d_model, stream)
+                              : decode_out<float>(a, wo, out, (float*)part, B, K, d_model, stream);
+}
+
 hipError_t launch_decode_attention(sqa_dtype dt, const void* q, const void* kc, const void* vc,
-                                   const int32_t* pos, void* a, void* part, int64_t B, int64_t Npb,
+                                   const int32_t* pos, void* a, void* part, int64_t B,
                                    int64_t N_max, int64_t H_q, int64_t H_kv, int64_t d_head,
                                    hipStream_t stream) {
   if (B > 65535 || H_kv * ((H_q / H_kv + 7) / 8) > 65535) return hipErrorInvalidConfiguration;
   float* pf = (float*)part;
   if (dt == SQA_DTYPE_BF16)
-    return d_head == 64 ? decode_impl<bf16, 64>(q, kc, vc, pos, a, pf, B, Npb, N_max, H_q, H_kv, stream)
-                        : decode_impl<bf16, 32>(q, kc, vc, pos, a, pf, B, Npb, N_max, H_q, H_kv, stream);
-  return d_head == 64 ? decode_impl<float, 64>(q, kc, vc, pos, a, pf, B, Npb, N_max, H_q, H_kv, stream)
-                      : decode_impl<float, 32>(q, kc, vc, pos, a, pf, B, Npb, N_max, H_q, H_kv, stream);
+    return d_head == 64 ? decode_impl<bf16, 64>(q, kc, vc, pos, a, pf, B, N_max, H_q, H_kv, stream)
+                        : decode_impl<bf16, 32>(q, kc, vc, pos, a, pf, B, N_max, H_q, H_kv, stream);
+  return d_head == 64 ? decode_impl<float, 64>(q, kc, vc, pos, a, pf, B, N_max, H_q, H_kv, stream)
+                      : decode_impl<float, 32>(q, kc, vc, pos, a, pf, B, N_max, H_q, H_kv, stream);
 }
 
 }  // namespace sqa

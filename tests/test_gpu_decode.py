@@ -54,9 +54,10 @@ def test_prefill_is_the_causal_forward_and_fills_the_caches(dev):
 
 
 DECODE_SHAPES = [
-    # (H, d_head, H_q, H_kv, dtype): g = 2, 1, 4, 16 (two head groups), fp32, d = 32
+    # (H, d_head, H_q, H_kv, dtype): g = 2, 1, 4, 16 (two head groups), fp32, d = 32, and
+    # d_model = 160 (projection widths that are not multiples of the 256-column blocks)
     (16, 64, 8, 4, "bf16"), (16, 64, 4, 4, "bf16"), (16, 64, 4, 1, "bf16"),
-    (16, 64, 16, 1, "bf16"), (8, 32, 4, 2, "fp32"), (8, 32, 6, 2, "bf16"),
+    (16, 64, 16, 1, "bf16"), (8, 32, 4, 2, "fp32"), (8, 32, 6, 2, "bf16"), (5, 32, 5, 1, "bf16"),
 ]
 
 
@@ -119,4 +120,22 @@ def test_decode_over_a_long_cache(dev):
     ref = _oracle_rows(host, w, [b * w.N + int(p[b]) for b in range(w.B)])
     rep = compare(wl.widen(y.cpu()), ref, "bf16")
     log(f"  long cache: {rep}")
+    assert rep.ok, rep
+
+
+def test_decode_batch_of_many_sequences(dev):
+    """B = 19 sequences: the projections take the tokens in several chunks."""
+    w = wl.Workload("many", B=19, N=130, d_model=512, H=8, H_q=4, H_kv=2, causal=True,
+                    dtype="bf16", seed=92)
+    host, d = device_inputs(w, dev)
+    kc, vc = _caches(w, w.N, dev)
+    sqa.prefill(d["X"], d["Wq"], d["Wk"], d["Wv"], d["Wo"], kc, vc, H=w.H, H_q=w.H_q, H_kv=w.H_kv)
+    p = (np.arange(w.B, dtype=np.int32) * 7) % w.N
+    x_new = torch.stack([d["X"][b, int(p[b])] for b in range(w.B)])
+    y = sqa.decode_step(x_new, d["Wq"], d["Wk"], d["Wv"], d["Wo"], kc, vc,
+                        torch.from_numpy(p).to(dev), H=w.H, H_q=w.H_q, H_kv=w.H_kv)
+    torch.cuda.synchronize()
+    ref = _oracle_rows(host, w, [b * w.N + int(p[b]) for b in range(w.B)])
+    rep = compare(wl.widen(y.cpu()), ref, "bf16")
+    log(f"  19 sequences: {rep}")
     assert rep.ok, rep
