@@ -10,8 +10,9 @@ tokens, causal (H=16, H_q=8, H_kv=4, d_head=64, bf16). This is the middle of the
 32k-200k range that the SQA paper's abstract benchmarks. The other long
 workloads and their equally shaped MHA/GQA/MQA baselines are timed as well and
 reported under "variants", with a sweep of H_kv at fixed H_q (attention time
-should not depend on H_kv) and a padded batch of sequences of mixed length
-(sqa_forward_varlen).
+should not depend on H_kv), a padded batch of sequences of mixed length
+(sqa_forward_varlen) and one decode step per sequence over 32k-token key/value
+caches (sqa_decode_step; `--decode-only` times just that step).
 
 Prints ONE JSON line. FLOPs use the closed form: attention core
 4*B*H_q*N^2*d_head (halved when causal) plus the projections
@@ -204,6 +205,14 @@ def run_varlen(w: wl.Workload, steps: int, warmup: int, torch, sqa, dev):
     return res
 
 
+# One decode step over 32k-token caches, SQA and its GQA baseline: the step is
+# bound by reading the key/value caches, which SQA leaves at H_kv heads, so
+# cutting query heads should not speed it up much (abstract).
+_DEC = wl.Workload("sqa_bf16_decode_b8_cache32768", B=8, N=32768, d_model=1024, H=16, H_q=8, H_kv=4,
+                   causal=True, dtype="bf16", seed=1006)
+DECODE_WORKLOADS = (_DEC, _DEC.with_(name=_DEC.name + "_baseline", H_q=16))
+
+
 def run_decode(w: wl.Workload, steps: int, warmup: int, torch, sqa, dev):
     """sqa_decode_step for B sequences whose caches hold w.N - 1 tokens (filled
     by sqa_prefill): each step attends over w.N keys. Decode reads every cached
@@ -303,6 +312,8 @@ def main():
     ap.add_argument("--no-variants", action="store_true", help="time only the headline workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=24576)
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only time the decode step (B=8, 32k-token caches), SQA and GQA baseline")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (rocprofv3 counter calibration)")
     args = ap.parse_args()
@@ -322,6 +333,11 @@ def main():
     dev = torch.device("cuda:0")
     if args.calibrate_copy:
         calibrate_copy(torch, dev)
+        return
+    if args.decode_only:
+        for v in DECODE_WORKLOADS:
+            print(json.dumps({v.name: run_decode(v, args.steps, args.warmup, torch, sqa, dev)}),
+                  flush=True)
         return
 
     w = wl.WORKLOADS[args.workload]
@@ -377,12 +393,7 @@ def main():
         times = list(sweep.values())
         variants["hkv_sweep_n32768_hq4_attention_ms"] = dict(
             sweep, max_over_min=round(max(times) / min(times), 3))
-        # One decode step over 32k-token caches, SQA and its GQA baseline: the
-        # step is bound by reading the key/value caches, which SQA leaves at
-        # H_kv heads, so cutting query heads should not speed it up (abstract).
-        dec = wl.Workload("sqa_bf16_decode_b8_cache32768", B=8, N=32768, d_model=1024, H=16,
-                          H_q=8, H_kv=4, causal=True, dtype="bf16", seed=1006)
-        for v in (dec, dec.with_(name=dec.name + "_baseline", H_q=16)):
+        for v in DECODE_WORKLOADS:
             variants[v.name] = run_decode(v, max(10, args.steps), vwarm, torch, sqa, dev)
         # A padded batch of sequences of mixed length (sqa_forward_varlen).
         variants[wl.SQA_VARLEN_32K.name] = run_varlen(wl.SQA_VARLEN_32K, vsteps, vwarm, torch, sqa,
