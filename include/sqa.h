@@ -146,6 +146,36 @@ sqa_status sqa_decode_step(const void* x_new, const void* Wq, const void* Wk, co
                            hipStream_t stream);
 
 /*
+ * sqa_backward - gradients of the SQA layer for training: with Y = sqa_forward(x)
+ * and an upstream gradient dy = dL/dY [B, N, d_model], writes
+ *   dx  [B, N, d_model]         dL/dx
+ *   dWq [d_model, H_q*d_head]   dL/dWq   (dWk, dWv [d_model, H_kv*d_head] likewise)
+ *   dWo [H_q*d_head, d_model]   dL/dWo
+ * The model cards train this layer (ReactiveAI/xSMQAT-m and
+ * ReactiveAI/GQA-Ref-Micro, training examples). By the chain rule through the
+ * definition above (P_i = the attention weights of head i, O_i = P_i V_j):
+ *   dA = dy Wo^T, dWo = A^T dy
+ *   dS_i = P_i * (dA_i V_j^T - rowsum(dA_i * O_i)),  dQ_i = dS_i K_j / sqrt(d_head)
+ *   dK_j = sum over the heads i of group j of dS_i^T Q_i / sqrt(d_head)
+ *   dV_j = sum over the same heads of P_i^T dA_i
+ *   dx = dQ Wq^T + dK Wk^T + dV Wv^T, dWq = x^T dQ, dWk = x^T dK, dWv = x^T dV
+ * (weight gradients summed over the batch). The forward activations (Q, K, V,
+ * A and each row's softmax normalizer) are recomputed, not passed in.
+ * Arithmetic: dA, dQ, dK, dV and the five outputs are each rounded once to
+ * `dtype`; P, dS and the row sums are fp32; D uses A as stored.
+ * Workspace: about elem_size * B*Np * (8*(H_q + H_kv)*d_head + 2*d_model)
+ * bytes (Np = sqa_padded_length(N)), plus 8*B*H_q*Np bytes of fp32 row
+ * statistics and the fp32 split-K partial sums of the weight gradients, from
+ * the stream-ordered pool (see sqa_forward). Outputs must not overlap each other or any input; other
+ * checks and errors as in sqa_forward.
+ */
+sqa_status sqa_backward(const void* x, const void* Wq, const void* Wk, const void* Wv,
+                        const void* Wo, const void* dy, void* dx, void* dWq, void* dWk, void* dWv,
+                        void* dWo, int64_t B, int64_t N, int64_t d_model, int64_t H, int64_t H_q,
+                        int64_t H_kv, int64_t d_head, int causal, sqa_dtype dtype,
+                        hipStream_t stream);
+
+/*
  * sqa_padded_length - Np, the sequence length of the Q/K/V^T layouts below:
  * N rounded up to a multiple of 256. Returns -1 for N < 0.
  */

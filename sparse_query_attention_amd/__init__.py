@@ -20,7 +20,7 @@ from typing import Optional, Tuple
 from . import _lib
 from ._lib import SQAError
 
-__all__ = ["forward_varlen", "prefill", "decode_step", "forward", "qkv_projection", "attention", "output_projection", "padded_length",
+__all__ = ["forward_varlen", "backward", "prefill", "decode_step", "forward", "qkv_projection", "attention", "output_projection", "padded_length",
            "SQAError", "library_path"]
 
 library_path = _lib.LIB_PATH
@@ -82,6 +82,36 @@ def forward(x, Wq, Wk, Wv, Wo, *, H: int, H_q: int, H_kv: int, causal: bool = Fa
                                Wo.data_ptr(), out.data_ptr(), B, N, D, H, H_q, H_kv, d,
                                int(bool(causal)), _dtype_code(x), _stream(x.device)))
     return out
+
+
+def backward(x, Wq, Wk, Wv, Wo, dy, *, H: int, H_q: int, H_kv: int, causal: bool = False,
+             out=None):
+    """Gradients of the SQA layer (sqa_backward): for Y = forward(x, ...) and
+    dy = dL/dY, returns (dx, dWq, dWk, dWv, dWo) with the shapes of x and the
+    weights. `out` may pass those five tensors to write into."""
+    lib = _lib.load()
+    if x.dim() != 3:
+        raise ValueError("x must be [B, N, d_model]")
+    B, N, D = x.shape
+    if H <= 0 or D % H:
+        raise ValueError("d_model must be a multiple of H")
+    d = D // H
+    torch = _torch()
+    if out is None:
+        out = (torch.empty_like(x), torch.empty_like(Wq), torch.empty_like(Wk),
+               torch.empty_like(Wv), torch.empty_like(Wo))
+    dx, dWq, dWk, dWv, dWo = out
+    for name, t, shp in (("x", x, (B, N, D)), ("Wq", Wq, (D, H_q * d)), ("Wk", Wk, (D, H_kv * d)),
+                         ("Wv", Wv, (D, H_kv * d)), ("Wo", Wo, (H_q * d, D)), ("dy", dy, (B, N, D)),
+                         ("dx", dx, (B, N, D)), ("dWq", dWq, (D, H_q * d)),
+                         ("dWk", dWk, (D, H_kv * d)), ("dWv", dWv, (D, H_kv * d)),
+                         ("dWo", dWo, (H_q * d, D))):
+        _check_tensor(name, t, shp, x.dtype, x.device)
+    _lib.check(lib.sqa_backward(x.data_ptr(), Wq.data_ptr(), Wk.data_ptr(), Wv.data_ptr(),
+                                Wo.data_ptr(), dy.data_ptr(), dx.data_ptr(), dWq.data_ptr(),
+                                dWk.data_ptr(), dWv.data_ptr(), dWo.data_ptr(), B, N, D, H, H_q,
+                                H_kv, d, int(bool(causal)), _dtype_code(x), _stream(x.device)))
+    return dx, dWq, dWk, dWv, dWo
 
 
 def forward_varlen(x, Wq, Wk, Wv, Wo, lens, *, H: int, H_q: int, H_kv: int, causal: bool = False,

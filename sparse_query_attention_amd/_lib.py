@@ -18,6 +18,7 @@ SIGNATURES = {
     "sqa_forward_varlen": (_int, [_vp] * 7 + [_i64] * 7 + [_int, _int, _vp]),
     "sqa_prefill": (_int, [_vp] * 8 + [_i64] * 8 + [_int, _vp]),
     "sqa_decode_step": (_int, [_vp] * 9 + [_i64] * 7 + [_int, _vp]),
+    "sqa_backward": (_int, [_vp] * 11 + [_i64] * 7 + [_int, _int, _vp]),
     "sqa_padded_length": (_i64, [_i64]),
     "sqa_qkv_projection": (_int, [_vp] * 7 + [_i64] * 7 + [_int, _vp]),
     "sqa_attention": (_int, [_vp] * 4 + [_i64] * 5 + [_int, _int, _vp]),

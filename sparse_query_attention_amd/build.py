@@ -11,7 +11,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["sqa_api.hip", "sqa_gemm.hip", "sqa_attention.hip", "sqa_decode.hip"]
+SOURCES = ["sqa_api.hip", "sqa_gemm.hip", "sqa_attention.hip", "sqa_decode.hip", "sqa_backward.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # packed fp32 VALU forms stay off: the kernels are written for scalar fp32 math

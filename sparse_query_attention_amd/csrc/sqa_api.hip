@@ -240,6 +240,62 @@ sqa_status forward_impl(const void* x, const void* Wq, const void* Wk, const voi
   return ok();
 }
 
+sqa_status backward_impl(const void* x, const void* Wq, const void* Wk, const void* Wv,
+                         const void* Wo, const void* dy, void* dx, void* dWq, void* dWk, void* dWv,
+                         void* dWo, int64_t B, int64_t N, int64_t d_model, int64_t H, int64_t H_q,
+                         int64_t H_kv, int64_t d_head, int causal, sqa_dtype dtype,
+                         hipStream_t stream) {
+  const Shape s{B, N, d_model, H, H_q, H_kv, d_head};
+  SQA_TRY(check_dtype(dtype));
+  SQA_TRY(check_heads(s, true));
+  if (causal != 0 && causal != 1) return fail(SQA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (B * N == 0) return ok();
+  const void* ins[6] = {x, Wq, Wk, Wv, Wo, dy};
+  const char* in_names[6] = {"x", "Wq", "Wk", "Wv", "Wo", "dy"};
+  void* outs[5] = {dx, dWq, dWk, dWv, dWo};
+  const char* out_names[5] = {"dx", "dWq", "dWk", "dWv", "dWo"};
+  char msg[64];
+  for (int j = 0; j < 6; ++j) {
+    snprintf(msg, sizeof(msg), "%s is null or not 16-byte aligned", in_names[j]);
+    if (!ins[j] || !aligned16(ins[j])) return fail(SQA_ERR_INVALID_ARG, msg);
+  }
+  for (int j = 0; j < 5; ++j) {
+    snprintf(msg, sizeof(msg), "%s is null or not 16-byte aligned", out_names[j]);
+    if (!outs[j] || !aligned16(outs[j])) return fail(SQA_ERR_INVALID_ARG, msg);
+  }
+  Sizes z;
+  SQA_TRY(sizes_for(s, dtype, &z));
+  const int64_t es = (int64_t)elem_size(dtype);
+  // the largest workspace regions are token-major copies of widths up to
+  // d_model + (H_q + 2 H_kv) d_head; keep every byte count far from overflow
+  int64_t t;
+  if (!mul_ok(B, z.Np, &t) || !mul_ok(t, d_model + (H_q + 2 * H_kv) * d_head, &t) ||
+      !mul_ok(t, 64 * es, &t))
+    return fail(SQA_ERR_UNSUPPORTED, "size overflow");
+  const size_t xb = (size_t)(B * N * d_model * es);
+  const size_t wqb = (size_t)(d_model * H_q * d_head * es), wkb = (size_t)(d_model * H_kv * d_head * es);
+  const size_t inb[6] = {xb, wqb, wkb, wkb, wqb, xb};
+  const size_t outb[5] = {xb, wqb, wkb, wkb, wqb};
+  for (int j = 0; j < 5; ++j) {
+    for (int i = 0; i < 6; ++i)
+      if (overlap(outs[j], outb[j], ins[i], inb[i]))
+        return fail(SQA_ERR_INVALID_ARG, "an output overlaps an input");
+    for (int i = 0; i < j; ++i)
+      if (overlap(outs[j], outb[j], outs[i], outb[i]))
+        return fail(SQA_ERR_INVALID_ARG, "two outputs overlap");
+  }
+  PoolScratch ws;
+  SQA_TRY(ws.acquire(sqa::backward_workspace_bytes(dtype, B, N, z.Np, d_model, H_q, H_kv, d_head),
+                     stream));
+  const hipError_t e = sqa::launch_backward(dtype, x, Wq, Wk, Wv, Wo, dy, dx, dWq, dWk, dWv, dWo,
+                                            B, N, z.Np, d_model, H_q, H_kv, d_head, causal != 0,
+                                            ws.ptr, stream);
+  const hipError_t ef = ws.release();
+  if (e != hipSuccess) return fail_hip(e, "kernel launch");
+  if (ef != hipSuccess) return fail_hip(ef, "workspace release");
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -377,6 +433,15 @@ sqa_status sqa_prefill(const void* x, const void* Wq, const void* Wk, const void
   }
   return forward_impl(x, Wq, Wk, Wv, Wo, out, false, nullptr, k_cache, v_cache, N_max, B, N,
                       d_model, H, H_q, H_kv, d_head, 1, dtype, stream);
+}
+
+sqa_status sqa_backward(const void* x, const void* Wq, const void* Wk, const void* Wv,
+                        const void* Wo, const void* dy, void* dx, void* dWq, void* dWk, void* dWv,
+                        void* dWo, int64_t B, int64_t N, int64_t d_model, int64_t H, int64_t H_q,
+                        int64_t H_kv, int64_t d_head, int causal, sqa_dtype dtype,
+                        hipStream_t stream) {
+  return backward_impl(x, Wq, Wk, Wv, Wo, dy, dx, dWq, dWk, dWv, dWo, B, N, d_model, H, H_q, H_kv,
+                       d_head, causal, dtype, stream);
 }
 
 sqa_status sqa_decode_step(const void* x_new, const void* Wq, const void* Wk, const void* Wv,

@@ -56,6 +56,7 @@ constexpr float M_INIT = -1e30f;   // finite, so masked scores give exp2(-inf) =
 struct AttnParams {
   const void* q; const void* k; const void* vt; void* a;
   const int32_t* lens;   // null, or each sequence's length (clamped into [0, N])
+  float* lse;            // null, or [B, H_q, Np]: base-2 log-sum-exp of each row's scaled scores
   int N, Np, H_q, H_kv, g, G, n_sub, q_per_wg, n_qt, causal;
   int chunk, remap_end;   // XCD-aware workgroup order (see the kernel's block decode)
   float c;  // log2(e) / sqrt(d_head)
@@ -144,6 +145,8 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const int t = qw + 32 * qb + col;
+      if (p.lse && grp == 0 && t < p.Np)
+        p.lse[((int64_t)b * p.H_q + head) * p.Np + t] = INFINITY;
       if (t < p.N) {
         T* arow = (T*)p.a + ((int64_t)b * p.N + t) * ((int64_t)p.H_q * D) + head * D;
 #pragma unroll
@@ -164,13 +167,15 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
   const T* Vh = (const T*)p.vt + ((int64_t)b * p.H_kv + h) * (int64_t)D * p.Np;
 
   // Q as the B operand of S^T = K Q^T: lane -> query qw + 32*qb + col, k-group grp.
+  // A query tile may reach past Np (tiles of 512 rows, Np a multiple of 256):
+  // such rows read row Np-1 and are never stored.
   Frag qf[QB][D / MF::KS];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int s = 0; s < D / MF::KS; ++s)
-      qf[qb][s] = *reinterpret_cast<const Frag*>(Qh + (int64_t)(qw + 32 * qb + col) * D +
-                                                 s * MF::KS + grp * MF::E);
+      qf[qb][s] = *reinterpret_cast<const Frag*>(
+          Qh + (int64_t)min(qw + 32 * qb + col, p.Np - 1) * D + s * MF::KS + grp * MF::E);
 
   // All waves of the workgroup walk the same key range; rows past a wave's own
   // causal horizon are masked to zero weight.
@@ -467,8 +472,13 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int t = qw + 32 * qb + col;
-    const float inv = 1.f / (l_run[qb] + __shfl_xor(l_run[qb], 32));
+    const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32);
+    const float inv = 1.f / l_tot;
     const bool pad = t >= L;   // padding row of its sequence: stored as zeros
+    // p = exp2(s*c - m_ref) / l_tot = exp2(s*c - (m_ref + log2 l_tot)); padding
+    // rows get +inf, so every weight recomputed from it is 0
+    if (p.lse && grp == 0 && t < p.Np)
+      p.lse[((int64_t)b * p.H_q + head) * p.Np + t] = pad ? INFINITY : m_ref[qb] + log2f(l_tot);
     if (t < p.N) {
       T* arow = (T*)p.a + ((int64_t)b * p.N + t) * ((int64_t)p.H_q * D) + head * D;
 #pragma unroll
@@ -562,9 +572,10 @@ int cu_count(hipStream_t stream) {
 // fill their tail with short workgroups.
 hipError_t launch_attention(sqa_dtype dt, const void* q, const void* k, const void* vt, void* a,
                             int64_t B, int64_t N, int64_t Np, int64_t H_q, int64_t H_kv,
-                            int64_t d_head, bool causal, const int32_t* lens, hipStream_t stream) {
+                            int64_t d_head, bool causal, const int32_t* lens, hipStream_t stream,
+                            float* lse) {
   AttnParams p;
-  p.q = q; p.k = k; p.vt = vt; p.a = a; p.lens = lens;
+  p.q = q; p.k = k; p.vt = vt; p.a = a; p.lens = lens; p.lse = lse;
   p.N = (int)N; p.Np = (int)Np; p.H_q = (int)H_q; p.H_kv = (int)H_kv;
   p.g = (int)(H_q / H_kv);
   p.causal = causal ? 1 : 0;

@@ -1,0 +1,636 @@
+// Backward pass of the SQA layer on gfx950: the gradients of L = sum(Y * dY)
+// with respect to x and the four weight matrices, for an upstream gradient dY.
+//
+// The model cards train the SQA layer (ReactiveAI/xSMQAT-m and
+// ReactiveAI/GQA-Ref-Micro, training examples), and the paper's abstract puts
+// SQA's gains in training. By the chain rule through the forward:
+//   dA = dY Wo^T,  dWo = A^T dY
+//   per query head i and its key/value head j = floor(i / g), with
+//   P = softmax(Q_i K_j^T / sqrt(d)) recomputed from the forward's per-row
+//   log-sum-exp, D = rowsum(dO * O):
+//     dS = P * (dO V_j^T - D),  dQ_i = dS K_j / sqrt(d)
+//     dK_j = sum over the g heads of dS^T Q_i / sqrt(d),  dV_j = sum of P^T dO
+//   dX = [dQ | dK | dV] [Wq | Wk | Wv]^T,  [dWq | dWk | dWv] = X^T [dQ | dK | dV]
+//
+// Attention backward runs as two kernels and needs no atomics:
+//  * dkdv: a workgroup owns 128 keys of one key/value head (32 per wave, held
+//    as MFMA operands in registers) and walks the query tiles of all g heads of
+//    the group, so the g-way sum of dK and dV stays in registers. Per 32x32
+//    block: S = Q K^T and dP = dO V^T (lane = key), then dV^T += dO^T P and
+//    dK^T += Q^T dS with P and dS consumed from registers as B operands.
+//  * dq: a workgroup owns 256 queries of one head (64 per wave) and walks the
+//    key tiles: S^T = K Q^T and dP^T = V dO^T (lane = query, so the row's
+//    log-sum-exp and D are per-lane scalars), then dQ^T += K^T dS^T.
+// The contraction over the score rows needs the other operand with those rows
+// contiguous, so Q^T, dO^T, K^T and V row-major are written once by a
+// transpose kernel. Token-contiguous copies of X, A, dY and [dQ|dK|dV] feed the
+// weight-gradient products (split-K over all tokens).
+#include <math.h>
+
+#include <algorithm>
+
+#include "sqa_device.h"
+#include "sqa_internal.h"
+
+namespace sqa {
+namespace {
+
+__device__ inline float f32_of(float x) { return x; }
+__device__ inline float f32_of(bf16 x) { return (float)x; }
+
+// ---- layout helpers ----
+
+// dst[b][c][r] = src[b][r][c] for r < r_valid, 0 for r_valid <= r < r_total;
+// c < C. 64x64 tiles through LDS, 16-byte global accesses on both sides
+// (C and r_total are multiples of 16 / sizeof(T)).
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_kernel(const T* src, int64_t src_bs, int64_t src_ld,
+                                                        int r_valid, int r_total, T* dst,
+                                                        int64_t dst_bs, int64_t dst_ld, int C) {
+  constexpr int EPC = 16 / (int)sizeof(T), TP = 64 + EPC;   // padded LDS row
+  __shared__ __align__(16) T tile[64][TP];
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+  src += blockIdx.z * src_bs;
+  dst += blockIdx.z * dst_bs;
+  constexpr int CPR = 64 / EPC;   // chunks per 64-element line
+  for (int i = threadIdx.x; i < 64 * CPR; i += 256) {
+    const int r = i / CPR, cc = (i % CPR) * EPC;
+    Chunk v = zero_chunk();
+    if (r0 + r < r_valid && c0 + cc < C)
+      v = *reinterpret_cast<const Chunk*>(src + (int64_t)(r0 + r) * src_ld + c0 + cc);
+    const T* e = reinterpret_cast<const T*>(&v);
+#pragma unroll
+    for (int k = 0; k < EPC; ++k) tile[cc + k][r] = e[k];   // tile[c][r]
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * CPR; i += 256) {
+    const int c = i / CPR, rr = (i % CPR) * EPC;
+    if (c0 + c < C && r0 + rr < r_total)
+      *reinterpret_cast<Chunk*>(dst + (int64_t)(c0 + c) * dst_ld + r0 + rr) =
+          *reinterpret_cast<const Chunk*>(&tile[c][rr]);
+  }
+}
+
+// W_all [d_model, wq + 2*wkv] rows = [Wq row | Wk row | Wv row].
+template <typename T>
+__global__ __launch_bounds__(256) void concat_weights(const T* wq, const T* wk, const T* wv, T* w,
+                                                      int64_t d_model, int wq_w, int wkv_w) {
+  const int W = wq_w + 2 * wkv_w;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= d_model * W) return;
+  const int64_t r = i / W;
+  int c = (int)(i % W);
+  T v;
+  if (c < wq_w) v = wq[r * wq_w + c];
+  else if ((c -= wq_w) < wkv_w) v = wk[r * wkv_w + c];
+  else v = wv[r * wkv_w + c - wkv_w];
+  w[i] = v;
+}
+
+// D[b, i, t] = sum_c dO[b, i, t, c] * A[b, t, i*d + c] for t < N, 0 on padding rows.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void dvec_kernel(const T* dO, const T* a, float* dvec, int N,
+                                                   int64_t Np, int H_q, int64_t rows) {
+  const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (x >= rows) return;
+  const int64_t t = x % Np, bi = x / Np, i = bi % H_q, b = bi / H_q;
+  float s = 0.f;
+  if (t < N) {
+    const T* o = dO + x * D;
+    const T* av = a + ((b * N + t) * H_q + i) * D;
+#pragma unroll 8
+    for (int c = 0; c < D; ++c) s = fmaf(f32_of(o[c]), f32_of(av[c]), s);
+  }
+  dvec[x] = s;
+}
+
+// out segments [M, w0 | w1 | w2] = sum over the n_split partials, rounded once.
+template <typename T>
+__global__ __launch_bounds__(256) void reduce_splits(const float* part, int n_split, int64_t M,
+                                                     int ncols, T* o0, int w0, T* o1, int w1, T* o2,
+                                                     int w2) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= M * ncols) return;
+  const int64_t m = i / ncols;
+  int n = (int)(i % ncols);
+  float v = 0.f;
+  for (int s = 0; s < n_split; ++s) v += part[(int64_t)s * M * ncols + i];
+  const T r = from_f32<T>(v);
+  if (n < w0) o0[m * w0 + n] = r;
+  else if ((n -= w0) < w1) o1[m * w1 + n] = r;
+  else o2[m * w2 + n - w1] = r;
+}
+
+// ---- attention backward ----
+
+struct BwdParams {
+  const void* q;     // [B, H_q, Np, d]
+  const void* qt;    // [B, H_q, d, Np]
+  const void* k;     // [B, H_kv, Np, d]
+  const void* kt;    // [B, H_kv, d, Np]
+  const void* v;     // [B, H_kv, Np, d]
+  const void* dO;    // [B, H_q, Np, d]
+  const void* dOt;   // [B, H_q, d, Np]
+  const float* lse;  // [B, H_q, Np], base 2, of the scaled scores
+  const float* dvec; // [B, H_q, Np]
+  void* dqkv;        // [B, Np, W]: dQ heads, then dK heads, then dV heads
+  int N, Np, H_q, H_kv, g, causal, W;
+  float c;           // log2(e) / sqrt(d)
+  float scale;       // 1 / sqrt(d)
+};
+
+constexpr int BT = 64;   // tokens per LDS tile
+
+// A operand from a transposed LDS tile (rows = head dims, pitch TP elements):
+// row r, the score rows that a B operand packed from accumulator registers
+// carries in its k-slots: for k-step `half` of a 32-row block at `base`,
+// k-group grp holds rows base + 16*half + 8*(e/4) + 4*grp + e%4, e = 0..7.
+template <typename T, int TP>
+__device__ inline typename Mfma<T>::Frag frag_runs(const T* tile, int r, int base, int half, int grp) {
+  if constexpr (sizeof(T) == 2) {
+    const T* p = tile + r * TP + base + 16 * half + 4 * grp;
+    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
+    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 8);
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  } else {
+    // fp32: k-step st = half (0..15) holds row base + 8*(st/4) + 4*grp + st%4
+    return tile[r * TP + base + 8 * (half / 4) + 4 * grp + half % 4];
+  }
+}
+
+// B operand from accumulator registers x (C layout): k-step `half`.
+template <typename T>
+__device__ inline typename Mfma<T>::Frag frag_regs(const f32x16& x, int half) {
+  if constexpr (sizeof(T) == 2) {
+    bf16x8 f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = (bf16)x[8 * half + e];
+    return f;
+  } else {
+    return x[half];
+  }
+}
+
+template <typename T> constexpr int kHalves = sizeof(T) == 2 ? 2 : 16;   // k-steps per 32 rows
+
+// A tile of LINES lines of RL elements (source lines `ld` apart): loaded into
+// registers, 16-byte pieces spread over 256 threads, then stored into LDS with
+// line pitch TP. Row-major token tiles are 64 lines of D; transposed ones D
+// lines of 64 tokens.
+template <typename T, int RL, int TP, int LINES>
+struct Stage {
+  static constexpr int EPC = 16 / (int)sizeof(T);
+  static constexpr int CPL = RL / EPC, N = LINES * CPL / 256;   // pieces per thread
+  static_assert(N * 256 == LINES * CPL, "tile split");
+  Chunk r[N];
+  __device__ void load(const T* src, int64_t ld) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int x = threadIdx.x + i * 256, line = x / CPL, cc = x % CPL;
+      r[i] = *reinterpret_cast<const Chunk*>(src + (int64_t)line * ld + cc * EPC);
+    }
+  }
+  __device__ void store(T* dst) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int x = threadIdx.x + i * 256, line = x / CPL, cc = x % CPL;
+      *reinterpret_cast<Chunk*>(dst + line * TP + cc * EPC) = r[i];
+    }
+  }
+};
+
+// dK, dV: workgroup = (128 keys, KV head j, batch b); 4 waves x 32 keys.
+template <typename T, int D>
+__global__ __launch_bounds__(256, 2) void bwd_dkdv(BwdParams p) {
+  using MF = Mfma<T>;
+  using Frag = typename MF::Frag;
+  constexpr int EPC = 16 / (int)sizeof(T);
+  constexpr int RP = D + EPC;      // pitch of row-major tiles [64 tokens][D]
+  constexpr int TPT = BT + EPC;    // pitch of transposed tiles [D][64 tokens]
+  constexpr int NS = D / MF::KS;   // k-steps over the head dims
+  constexpr int QS = BT * RP, QTS = D * TPT;
+  constexpr int BUF = 2 * QS + 2 * QTS;   // elements: Q, dO, Q^T, dO^T
+  __shared__ __align__(16) T smem[2 * BUF];
+  __shared__ __align__(16) float sv[2][2][BT];   // per buffer: lse, D
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, grp = lane >> 5;
+  const int n_kt = p.Np / 128;
+  int kt = blockIdx.x % n_kt;
+  const int bj = blockIdx.x / n_kt, j = bj % p.H_kv, b = bj / p.H_kv;
+  const int k0 = kt * 128, kw = k0 + 32 * wave;   // this wave's first key
+  const int key = kw + col;                       // this lane's key (column of S)
+
+  const T* Kh = (const T*)p.k + ((int64_t)b * p.H_kv + j) * (int64_t)p.Np * D;
+  const T* Vh = (const T*)p.v + ((int64_t)b * p.H_kv + j) * (int64_t)p.Np * D;
+  Frag kf[NS], vf[NS];   // B operands of S = Q K^T and dP = dO V^T
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    kf[s] = *reinterpret_cast<const Frag*>(Kh + (int64_t)key * D + s * MF::KS + grp * MF::E);
+    vf[s] = *reinterpret_cast<const Frag*>(Vh + (int64_t)key * D + s * MF::KS + grp * MF::E);
+  }
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb) { dk[nb] = f32x16{}; dv[nb] = f32x16{}; }
+
+  // Work list: (head, query tile) for the g heads of j; causal starts at the
+  // tile holding key k0 (earlier queries see none of these keys).
+  const int qt_first = p.causal ? k0 / BT : 0;
+  const int qt_end = (p.N + BT - 1) / BT;
+  const int per_head = max(0, qt_end - qt_first);
+  const int n_work = per_head * p.g;
+
+  Stage<T, D, RP, BT> sq, sdo;
+  Stage<T, BT, TPT, D> sqt, sdot;
+  float lse_r = 0.f, dv_r = 0.f;
+  auto load = [&](int w) {
+    const int i = j * p.g + w / per_head, q0 = (qt_first + w % per_head) * BT;
+    const int64_t hq = (int64_t)b * p.H_q + i;
+    sq.load((const T*)p.q + (hq * p.Np + q0) * D, D);
+    sdo.load((const T*)p.dO + (hq * p.Np + q0) * D, D);
+    sqt.load((const T*)p.qt + hq * D * p.Np + q0, p.Np);
+    sdot.load((const T*)p.dOt + hq * D * p.Np + q0, p.Np);
+    if (tid < BT) {
+      const int t = q0 + tid;
+      lse_r = t < p.N ? p.lse[hq * p.Np + t] : INFINITY;   // rows past N weigh 0
+      dv_r = t < p.N ? p.dvec[hq * p.Np + t] : 0.f;
+    }
+  };
+  auto store = [&](int buf) {
+    T* base = smem + buf * BUF;
+    sq.store(base);
+    sdo.store(base + QS);
+    sqt.store(base + 2 * QS);
+    sdot.store(base + 2 * QS + QTS);
+    if (tid < BT) { sv[buf][0][tid] = lse_r; sv[buf][1][tid] = dv_r; }
+  };
+
+  if (n_work > 0) {
+    load(0);
+    store(0);
+  }
+  __syncthreads();
+  for (int w = 0; w < n_work; ++w) {
+    const int buf = w & 1;
+    load(min(w + 1, n_work - 1));   // the last iteration reloads its own tile, unused
+    const T* Qs = smem + buf * BUF;
+    const T* Os = Qs + QS;
+    const T* QTs = Qs + 2 * QS;
+    const T* OTs = QTs + QTS;
+    const int q0 = (qt_first + w % per_head) * BT;
+#pragma unroll
+    for (int qs = 0; qs < BT / 32; ++qs) {
+      const int qb = q0 + 32 * qs;
+      // wave-uniform skips: every query before this wave's first key, or past N
+      if ((p.causal && qb + 31 < kw) || qb >= p.N) continue;
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        const int e = st * MF::KS + grp * MF::E;
+        const Frag qa = *reinterpret_cast<const Frag*>(Qs + (32 * qs + col) * RP + e);
+        const Frag oa = *reinterpret_cast<const Frag*>(Os + (32 * qs + col) * RP + e);
+        s = MF::run(qa, kf[st], s);
+        dp = MF::run(oa, vf[st], dp);
+      }
+      // rows of register r: query qb + 8*(r/4) + 4*grp + r%4; column: key
+      f32x16 pr, ds;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int rl = 32 * qs + 8 * r4 + 4 * grp;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sv[buf][0][rl]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sv[buf][1][rl]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * r4 + e, q = qb + 8 * r4 + 4 * grp + e;
+          const bool off = key >= p.N || (p.causal && key > q);
+          const float pv = off ? 0.f : __builtin_amdgcn_exp2f(fmaf(s[r], p.c, -l4[e]));
+          pr[r] = pv;
+          ds[r] = pv * (dp[r] - d4[e]);
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < kHalves<T>; ++h) {
+        const Frag pf = frag_regs<T>(pr, h), sf = frag_regs<T>(ds, h);
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb) {
+          dv[nb] = MF::run(frag_runs<T, TPT>(OTs, nb * 32 + col, 32 * qs, h, grp), pf, dv[nb]);
+          dk[nb] = MF::run(frag_runs<T, TPT>(QTs, nb * 32 + col, 32 * qs, h, grp), sf, dk[nb]);
+        }
+      }
+    }
+    store(buf ^ 1);   // every wave passed the barrier after its last read of buf ^ 1
+    __syncthreads();
+  }
+
+  // dK^T, dV^T: lane = key, register r = head dim 32*nb + 8*(r/4) + 4*grp + r%4.
+  T* row = (T*)p.dqkv + ((int64_t)b * p.Np + key) * p.W;
+  T* dkr = row + (int64_t)p.H_q * D + j * D;
+  T* dvr = row + (int64_t)(p.H_q + p.H_kv) * D + j * D;
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const int c = nb * 32 + 8 * rq + 4 * grp;
+      if constexpr (sizeof(T) == 2) {
+        *reinterpret_cast<bf16x4*>(dkr + c) =
+            bf16x4{(bf16)(dk[nb][4 * rq] * p.scale), (bf16)(dk[nb][4 * rq + 1] * p.scale),
+                   (bf16)(dk[nb][4 * rq + 2] * p.scale), (bf16)(dk[nb][4 * rq + 3] * p.scale)};
+        *reinterpret_cast<bf16x4*>(dvr + c) =
+            bf16x4{(bf16)dv[nb][4 * rq], (bf16)dv[nb][4 * rq + 1], (bf16)dv[nb][4 * rq + 2],
+                   (bf16)dv[nb][4 * rq + 3]};
+      } else {
+        *reinterpret_cast<f32x4*>(dkr + c) =
+            f32x4{dk[nb][4 * rq] * p.scale, dk[nb][4 * rq + 1] * p.scale,
+                  dk[nb][4 * rq + 2] * p.scale, dk[nb][4 * rq + 3] * p.scale};
+        *reinterpret_cast<f32x4*>(dvr + c) =
+            f32x4{dv[nb][4 * rq], dv[nb][4 * rq + 1], dv[nb][4 * rq + 2], dv[nb][4 * rq + 3]};
+      }
+    }
+}
+
+// dQ: workgroup = (256 queries, head i, batch b); 4 waves x 64 queries.
+template <typename T, int D>
+__global__ __launch_bounds__(256, 2) void bwd_dq(BwdParams p) {
+  using MF = Mfma<T>;
+  using Frag = typename MF::Frag;
+  constexpr int EPC = 16 / (int)sizeof(T);
+  constexpr int RP = D + EPC, TPT = BT + EPC;
+  constexpr int NS = D / MF::KS;
+  constexpr int QB = 2;                       // 32-query blocks per wave
+  constexpr int KS_ = BT * RP, KTS = D * TPT;
+  constexpr int BUF = 2 * KS_ + KTS;          // K, V, K^T
+  __shared__ __align__(16) T smem[2 * BUF];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, grp = lane >> 5;
+  const int n_qt = p.Np / 256;
+  int qt = blockIdx.x % n_qt;
+  if (p.causal) qt = n_qt - 1 - qt;   // heaviest first
+  const int bi = blockIdx.x / n_qt, i = bi % p.H_q, b = bi / p.H_q;
+  const int j = i / p.g;
+  const int q0 = qt * 256, qw = q0 + 64 * wave;
+  const int64_t hq = (int64_t)b * p.H_q + i, hk = (int64_t)b * p.H_kv + j;
+
+  Frag qf[QB][NS], of[QB][NS];
+  float lse[QB], dvq[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int t = qw + 32 * qb + col;
+    const T* qr = (const T*)p.q + (hq * p.Np + t) * D;
+    const T* orow = (const T*)p.dO + (hq * p.Np + t) * D;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      qf[qb][s] = *reinterpret_cast<const Frag*>(qr + s * MF::KS + grp * MF::E);
+      of[qb][s] = *reinterpret_cast<const Frag*>(orow + s * MF::KS + grp * MF::E);
+    }
+    lse[qb] = t < p.N ? p.lse[hq * p.Np + t] : INFINITY;
+    dvq[qb] = t < p.N ? p.dvec[hq * p.Np + t] : 0.f;
+  }
+  f32x16 dq[QB][D / 32];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb) dq[qb][nb] = f32x16{};
+
+  const int kv_len = p.causal ? min(p.N, q0 + 256) : p.N;
+  const int n_tiles = (kv_len + BT - 1) / BT;
+  const T* Kh = (const T*)p.k + hk * p.Np * D;
+  const T* Vh = (const T*)p.v + hk * p.Np * D;
+  const T* KTh = (const T*)p.kt + hk * D * p.Np;
+  Stage<T, D, RP, BT> sk, sv;
+  Stage<T, BT, TPT, D> skt;
+  auto load = [&](int t) {
+    const int k0 = t * BT;
+    sk.load(Kh + (int64_t)k0 * D, D);
+    sv.load(Vh + (int64_t)k0 * D, D);
+    skt.load(KTh + k0, p.Np);
+  };
+  auto store = [&](int buf) {
+    T* base = smem + buf * BUF;
+    sk.store(base);
+    sv.store(base + KS_);
+    skt.store(base + 2 * KS_);
+  };
+  if (n_tiles > 0) {
+    load(0);
+    store(0);
+  }
+  __syncthreads();
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    load(min(t + 1, n_tiles - 1));
+    const T* Ks = smem + buf * BUF;
+    const T* Vs = Ks + KS_;
+    const T* KTs = Ks + 2 * KS_;
+#pragma unroll
+    for (int jb = 0; jb < BT / 32; ++jb) {
+      const int kb = t * BT + 32 * jb;
+      if (kb >= p.N || (p.causal && kb > qw + 63)) continue;   // wave-uniform
+      f32x16 s[QB], dp[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) { s[qb] = f32x16{}; dp[qb] = f32x16{}; }
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        const int e = st * MF::KS + grp * MF::E;
+        const Frag ka = *reinterpret_cast<const Frag*>(Ks + (32 * jb + col) * RP + e);
+        const Frag va = *reinterpret_cast<const Frag*>(Vs + (32 * jb + col) * RP + e);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          s[qb] = MF::run(ka, qf[qb][st], s[qb]);
+          dp[qb] = MF::run(va, of[qb][st], dp[qb]);
+        }
+      }
+      // register r: key kb + 8*(r/4) + 4*grp + r%4; column: query qw + 32*qb + col
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int q = qw + 32 * qb + col;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb + 8 * (r / 4) + 4 * grp + r % 4;
+          const bool off = key >= p.N || (p.causal && key > q);
+          const float pv = off ? 0.f : __builtin_amdgcn_exp2f(fmaf(s[qb][r], p.c, -lse[qb]));
+          s[qb][r] = pv * (dp[qb][r] - dvq[qb]);   // dS^T
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < kHalves<T>; ++h)
+#pragma unroll
+        for (int nb = 0; nb < D / 32; ++nb) {
+          const Frag ka = frag_runs<T, TPT>(KTs, nb * 32 + col, 32 * jb, h, grp);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) dq[qb][nb] = MF::run(ka, frag_regs<T>(s[qb], h), dq[qb][nb]);
+        }
+    }
+    store(buf ^ 1);
+    __syncthreads();
+  }
+
+  // dQ^T: lane = query, register r = head dim 32*nb + 8*(r/4) + 4*grp + r%4.
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int t = qw + 32 * qb + col;
+    T* dqr = (T*)p.dqkv + ((int64_t)b * p.Np + t) * p.W + (int64_t)i * D;
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int c = nb * 32 + 8 * rq + 4 * grp;
+        const f32x16& a = dq[qb][nb];
+        if constexpr (sizeof(T) == 2) {
+          *reinterpret_cast<bf16x4*>(dqr + c) =
+              bf16x4{(bf16)(a[4 * rq] * p.scale), (bf16)(a[4 * rq + 1] * p.scale),
+                     (bf16)(a[4 * rq + 2] * p.scale), (bf16)(a[4 * rq + 3] * p.scale)};
+        } else {
+          *reinterpret_cast<f32x4*>(dqr + c) =
+              f32x4{a[4 * rq] * p.scale, a[4 * rq + 1] * p.scale, a[4 * rq + 2] * p.scale,
+                    a[4 * rq + 3] * p.scale};
+        }
+      }
+  }
+}
+
+template <typename T>
+hipError_t transpose(const void* src, int64_t src_bs, int64_t src_ld, int64_t r_valid,
+                     int64_t r_total, void* dst, int64_t dst_bs, int64_t dst_ld, int64_t C,
+                     int64_t nbatch, hipStream_t stream) {
+  const int64_t ry = (r_total + 63) / 64;
+  if (nbatch > 65535 || ry > 65535) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)((C + 63) / 64), (unsigned)ry, (unsigned)nbatch);
+  transpose_kernel<T><<<grid, 256, 0, stream>>>((const T*)src, src_bs, src_ld, (int)r_valid,
+                                                (int)r_total, (T*)dst, dst_bs, dst_ld, (int)C);
+  return hipGetLastError();
+}
+
+// Byte offsets of the backward workspace regions.
+struct BwdLayout {
+  int64_t q, k, vt, a, lse, wt, dO, dvec, qt, kt, v, dOt, dqkv, dqkvT, xT, wall, aT, dyT, part;
+  int64_t total;
+};
+
+inline int64_t r256(int64_t x) { return (x + 255) / 256 * 256; }
+
+BwdLayout bwd_layout(int64_t es, int64_t B, int64_t N, int64_t Np, int64_t d_model, int64_t H_q,
+                     int64_t H_kv, int64_t d) {
+  const int64_t W = (H_q + 2 * H_kv) * d, T = B * Np;
+  const SplitK s1 = splitk_plan(d_model, T, W), s2 = splitk_plan(H_q * d, T, d_model);
+  const int64_t part = std::max(s1.n_split * d_model * W, s2.n_split * H_q * d * d_model) * 4;
+  const int64_t sizes[] = {
+      es * B * H_q * Np * d, es * B * H_kv * Np * d, es * B * H_kv * Np * d, es * B * N * H_q * d,
+      4 * B * H_q * Np, (int64_t)qkv_wt_bytes(es == 2 ? SQA_DTYPE_BF16 : SQA_DTYPE_FP32, d_model, H_q, H_kv, d),
+      es * B * H_q * Np * d, 4 * B * H_q * Np, es * B * H_q * Np * d, es * B * H_kv * Np * d,
+      es * B * H_kv * Np * d, es * B * H_q * Np * d, es * T * W, es * T * W, es * d_model * T,
+      es * d_model * W, es * H_q * d * T, es * d_model * T, part};
+  BwdLayout L;
+  int64_t* out[] = {&L.q, &L.k, &L.vt, &L.a, &L.lse, &L.wt, &L.dO, &L.dvec, &L.qt, &L.kt, &L.v,
+                    &L.dOt, &L.dqkv, &L.dqkvT, &L.xT, &L.wall, &L.aT, &L.dyT, &L.part};
+  int64_t off = 0;
+  for (int x = 0; x < 19; ++x) {
+    *out[x] = off;
+    off += r256(sizes[x]);
+  }
+  L.total = off;
+  return L;
+}
+
+template <typename T, int D>
+hipError_t backward_impl(const void* x, const void* wq, const void* wk, const void* wv,
+                         const void* wo, const void* dy, void* dx, void* dwq, void* dwk, void* dwv,
+                         void* dwo, int64_t B, int64_t N, int64_t Np, int64_t d_model, int64_t H_q,
+                         int64_t H_kv, bool causal, char* ws, hipStream_t stream) {
+  const sqa_dtype dt = sizeof(T) == 2 ? SQA_DTYPE_BF16 : SQA_DTYPE_FP32;
+  const BwdLayout L = bwd_layout(sizeof(T), B, N, Np, d_model, H_q, H_kv, D);
+  const int64_t wq_w = H_q * D, wkv_w = H_kv * D, W = wq_w + 2 * wkv_w, TT = B * Np;
+  void *q = ws + L.q, *k = ws + L.k, *vt = ws + L.vt, *a = ws + L.a, *wt = ws + L.wt;
+  float* lse = (float*)(ws + L.lse);
+  float* dvec = (float*)(ws + L.dvec);
+  void *dO = ws + L.dO, *qt = ws + L.qt, *kt = ws + L.kt, *v = ws + L.v, *dOt = ws + L.dOt;
+  void *dqkv = ws + L.dqkv, *dqkvT = ws + L.dqkvT, *xT = ws + L.xT, *wall = ws + L.wall;
+  void *aT = ws + L.aT, *dyT = ws + L.dyT;
+  float* part = (float*)(ws + L.part);
+  hipError_t e;
+#define SQA_CK(call) do { e = (call); if (e != hipSuccess) return e; } while (0)
+  // forward activations and each row's log-sum-exp
+  SQA_CK(launch_qkv_projection(dt, x, wq, wk, wv, wt, q, k, vt, B, N, Np, d_model, H_q, H_kv, D,
+                               nullptr, stream));
+  SQA_CK(launch_attention(dt, q, k, vt, a, B, N, Np, H_q, H_kv, D, causal, nullptr, stream, lse));
+  // dO = dY Wo^T in the head layout of q (Wo [H_q*d, d_model] is W^T of that product)
+  SQA_CK(launch_gemm_heads(dt, dy, wo, dO, B, N, Np, d_model, wq_w, D, stream));
+  {
+    const int64_t rows = B * H_q * Np;
+    dvec_kernel<T, D><<<(unsigned)((rows + 255) / 256), 256, 0, stream>>>(
+        (const T*)dO, (const T*)a, dvec, (int)N, Np, (int)H_q, rows);
+    SQA_CK(hipGetLastError());
+  }
+  // head-dim-major copies for the contractions over tokens, V row-major
+  SQA_CK(transpose<T>(q, Np * D, D, Np, Np, qt, D * Np, Np, D, B * H_q, stream));
+  SQA_CK(transpose<T>(k, Np * D, D, Np, Np, kt, D * Np, Np, D, B * H_kv, stream));
+  SQA_CK(transpose<T>(vt, D * Np, Np, D, D, v, Np * D, D, Np, B * H_kv, stream));
+  SQA_CK(transpose<T>(dO, Np * D, D, Np, Np, dOt, D * Np, Np, D, B * H_q, stream));
+  BwdParams p;
+  p.q = q; p.qt = qt; p.k = k; p.kt = kt; p.v = v; p.dO = dO; p.dOt = dOt;
+  p.lse = lse; p.dvec = dvec; p.dqkv = dqkv;
+  p.N = (int)N; p.Np = (int)Np; p.H_q = (int)H_q; p.H_kv = (int)H_kv; p.g = (int)(H_q / H_kv);
+  p.causal = causal ? 1 : 0; p.W = (int)W;
+  p.c = (float)(1.4426950408889634 / sqrt((double)D));
+  p.scale = (float)(1.0 / sqrt((double)D));
+  if ((Np / 128) * B * H_kv > 0x7FFFFFFF || (Np / 256) * B * H_q > 0x7FFFFFFF)
+    return hipErrorInvalidConfiguration;
+  bwd_dkdv<T, D><<<(unsigned)((Np / 128) * B * H_kv), 256, 0, stream>>>(p);
+  SQA_CK(hipGetLastError());
+  bwd_dq<T, D><<<(unsigned)((Np / 256) * B * H_q), 256, 0, stream>>>(p);
+  SQA_CK(hipGetLastError());
+  // dX = [dQ | dK | dV] [Wq | Wk | Wv]^T
+  concat_weights<T><<<(unsigned)((d_model * W + 255) / 256), 256, 0, stream>>>(
+      (const T*)wq, (const T*)wk, (const T*)wv, (T*)wall, d_model, (int)wq_w, (int)wkv_w);
+  SQA_CK(hipGetLastError());
+  SQA_CK(launch_gemm_unpad(dt, dqkv, wall, dx, B, N, Np, W, d_model, stream));
+  // [dWq | dWk | dWv] = X^T [dQ | dK | dV] over all tokens (padding tokens are zero in X^T)
+  SQA_CK(transpose<T>(x, N * d_model, d_model, N, Np, xT, Np, TT, d_model, B, stream));
+  SQA_CK(transpose<T>(dqkv, 0, W, TT, TT, dqkvT, 0, TT, W, 1, stream));
+  {
+    const SplitK sk = splitk_plan(d_model, TT, W);
+    SQA_CK(launch_gemm_splitk(dt, xT, dqkvT, part, d_model, TT, W, sk, stream));
+    reduce_splits<T><<<(unsigned)((d_model * W + 255) / 256), 256, 0, stream>>>(
+        part, (int)sk.n_split, d_model, (int)W, (T*)dwq, (int)wq_w, (T*)dwk, (int)wkv_w, (T*)dwv,
+        (int)wkv_w);
+    SQA_CK(hipGetLastError());
+  }
+  // dWo = A^T dY
+  SQA_CK(transpose<T>(a, N * wq_w, wq_w, N, Np, aT, Np, TT, wq_w, B, stream));
+  SQA_CK(transpose<T>(dy, N * d_model, d_model, N, Np, dyT, Np, TT, d_model, B, stream));
+  {
+    const SplitK sk = splitk_plan(wq_w, TT, d_model);
+    SQA_CK(launch_gemm_splitk(dt, aT, dyT, part, wq_w, TT, d_model, sk, stream));
+    reduce_splits<T><<<(unsigned)((wq_w * d_model + 255) / 256), 256, 0, stream>>>(
+        part, (int)sk.n_split, wq_w, (int)d_model, (T*)dwo, (int)d_model, nullptr, 0, nullptr, 0);
+    SQA_CK(hipGetLastError());
+  }
+#undef SQA_CK
+  return hipSuccess;
+}
+
+}  // namespace
+
+size_t backward_workspace_bytes(sqa_dtype dt, int64_t B, int64_t N, int64_t Np, int64_t d_model,
+                                int64_t H_q, int64_t H_kv, int64_t d_head) {
+  return (size_t)bwd_layout(dt == SQA_DTYPE_BF16 ? 2 : 4, B, N, Np, d_model, H_q, H_kv, d_head).total;
+}
+
+hipError_t launch_backward(sqa_dtype dt, const void* x, const void* wq, const void* wk,
+                           const void* wv, const void* wo, const void* dy, void* dx, void* dwq,
+                           void* dwk, void* dwv, void* dwo, int64_t B, int64_t N, int64_t Np,
+                           int64_t d_model, int64_t H_q, int64_t H_kv, int64_t d_head, bool causal,
+                           void* ws, hipStream_t stream) {
+  char* w = (char*)ws;
+  if (dt == SQA_DTYPE_BF16)
+    return d_head == 64 ? backward_impl<bf16, 64>(x, wq, wk, wv, wo, dy, dx, dwq, dwk, dwv, dwo, B, N,
+                                                  Np, d_model, H_q, H_kv, causal, w, stream)
+                        : backward_impl<bf16, 32>(x, wq, wk, wv, wo, dy, dx, dwq, dwk, dwv, dwo, B, N,
+                                                  Np, d_model, H_q, H_kv, causal, w, stream);
+  return d_head == 64 ? backward_impl<float, 64>(x, wq, wk, wv, wo, dy, dx, dwq, dwk, dwv, dwo, B, N,
+                                                 Np, d_model, H_q, H_kv, causal, w, stream)
+                      : backward_impl<float, 32>(x, wq, wk, wv, wo, dy, dx, dwq, dwk, dwv, dwo, B, N,
+                                                 Np, d_model, H_q, H_kv, causal, w, stream);
+}
+
+}  // namespace sqa

@@ -26,6 +26,7 @@
 //    Q/K/V^T layouts), step 3 skips them.
 //  * The epilogue stages the C tile in LDS and writes it in 16-byte chunks that
 //    run along contiguous memory: rows of Q, K and Y, sequence runs of V^T.
+#include <algorithm>
 #include <type_traits>
 
 #include "sqa_device.h"
@@ -98,6 +99,7 @@ template <typename T> struct DenseRows {
 // one batch (Np is a multiple of 256). V^T blocks are column-major so that
 // their chunks are runs of t, contiguous in vt.
 template <typename T> struct QkvStore {
+  static constexpr bool kDirect = false;
   T* q; T* k; T* vt; int64_t N, Np; int H_q, H_kv, dsh, wq_w, wkv_w;   // d_head = 1 << dsh
   const int32_t* lens;   // null, or each sequence's length (clamped into [0, N])
   __device__ bool col_major(int n) const { return n >= wq_w + wkv_w; }
@@ -134,6 +136,7 @@ template <typename T> struct QkvStore {
 // lens, row m is token m % seq_n of sequence m / seq_n, and a tile that lies in
 // one sequence's padding is stored as zeros without computing it.
 template <typename T> struct DenseStore {
+  static constexpr bool kDirect = false;
   T* out; int64_t M; int ncols;
   const int32_t* lens; int64_t seq_n;
   __device__ bool col_major(int) const { return false; }
@@ -157,10 +160,51 @@ template <typename T> struct DenseStore {
   }
 };
 
+// Rows m = b*Np + t of a padded layout into out [B, N, ncols]: t >= N is not stored.
+template <typename T> struct UnpadStore {
+  static constexpr bool kDirect = false;
+  T* out; int64_t N, Np; int ncols;
+  __device__ bool col_major(int) const { return false; }
+  struct Tile {
+    T* out; int64_t rows_left; int ncols;   // rows from t0 on
+    __device__ bool all_zero() const { return false; }
+    __device__ bool zero_row(int) const { return false; }
+    __device__ void row_chunk(int r, int n, const Chunk& c) const {
+      if (r < rows_left) *reinterpret_cast<Chunk*>(out + (int64_t)r * ncols + n) = c;
+    }
+    __device__ void col_chunk(int, int, const Chunk&) const {}
+  };
+  __device__ Tile tile(int64_t m0) const {
+    const int64_t b = m0 / Np, t0 = m0 - b * Np;
+    return Tile{out + (b * N + t0) * ncols, N - t0, ncols};
+  }
+};
+
+// Split-K partial sums, fp32 and unrounded: part[blockIdx.y][m][n] for m < M.
+// The accumulators go straight from registers to memory (no LDS staging).
+struct F32PartStore {
+  static constexpr bool kDirect = true;
+  float* part; int64_t M; int ncols;
+  __device__ bool col_major(int) const { return false; }
+  struct Tile {   // the staged epilogue's interface, unused by a direct store
+    __device__ bool all_zero() const { return false; }
+    __device__ bool zero_row(int) const { return false; }
+    __device__ void row_chunk(int, int, const Chunk&) const {}
+    __device__ void col_chunk(int, int, const Chunk&) const {}
+  };
+  __device__ Tile tile(int64_t) const { return Tile{}; }
+  __device__ void put(int64_t m, int n, float v) const {
+    if (m < M) part[((int64_t)blockIdx.y * M + m) * ncols + n] = v;
+  }
+};
+
 // C = A * W with W given transposed (wt [ncols, K]); see the file header.
+// Workgroup row blockIdx.y sums k in [y*k_split, min(K, (y+1)*k_split)), a
+// multiple of BK (split-K; k_split = K otherwise).
 template <typename T, class Rows, class Store>
 __global__ __launch_bounds__(THREADS) void gemm_kernel(Rows rows, const T* wt, int ncols,
-                                                       Store store, int K, int n_rb, int n_ct) {
+                                                       Store store, int K, int n_rb, int n_ct,
+                                                       int k_split) {
   using C = GemmCfg<T>;
   using MF = Mfma<T>;
   using Frag = typename MF::Frag;
@@ -174,6 +218,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Rows rows, const T* wt, i
   if (rb >= n_rb) return;
   const int64_t m0 = (int64_t)rb * BM;
   const int n0 = ct * BN;
+  const int k_begin = blockIdx.y * k_split;
 
   // Per-thread sources of its direct loads (fixed rows, chunk swizzled per row).
   const T* a_src[C::A_INS];
@@ -182,16 +227,16 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Rows rows, const T* wt, i
   for (int i = 0; i < C::A_INS; ++i) {
     const int pos = (wave * C::A_INS + i) * 64 + lane;
     const int r = pos / C::CPR, slot = pos % C::CPR;
-    a_src[i] = rows.row(m0 + r) + (slot ^ swz<C::CPR>(r)) * C::EPC;
+    a_src[i] = rows.row(m0 + r) + k_begin + (slot ^ swz<C::CPR>(r)) * C::EPC;
   }
 #pragma unroll
   for (int i = 0; i < C::B_INS; ++i) {
     const int pos = (wave * C::B_INS + i) * 64 + lane;
     const int r = pos / C::CPR, slot = pos % C::CPR;
     const int n = min(n0 + r, ncols - 1);
-    b_src[i] = wt + (int64_t)n * K + (slot ^ swz<C::CPR>(r)) * C::EPC;
+    b_src[i] = wt + (int64_t)n * K + k_begin + (slot ^ swz<C::CPR>(r)) * C::EPC;
   }
-  const int nk = K / BK;
+  const int nk = (min(K, k_begin + k_split) - k_begin) / BK;
   auto issue = [&](int kt) {
     if (kt >= nk) return;
     T* st = smem + (kt % NST) * C::STAGE;
@@ -271,6 +316,21 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Rows rows, const T* wt, i
       }
     }
   };
+  if constexpr (Store::kDirect) {
+    // register r of this lane: row 8*(r/4) + 4*grp + r%4, column col
+    main_loop(std::false_type{});
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = n0 + wn * 64 + j * 32 + col;
+        if (n >= ncols) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          store.put(m0 + wm * 64 + i * 32 + 8 * (r / 4) + 4 * grp + r % 4, n, acc[i][j][r]);
+      }
+    return;
+  }
   // A tile wholly in the padding of its sequence keeps zero accumulators.
   const auto tile = store.tile(m0);
   if (tile.all_zero()) {
@@ -411,7 +471,7 @@ hipError_t qkv_impl(const void* x, const void* wq, const void* wk, const void* w
   const int dsh = d == 64 ? 6 : 5;   // d_head is 32 or 64 (checked by the caller)
   QkvStore<T> st{(T*)q, (T*)k, (T*)vt, N, Np, (int)H_q, (int)H_kv, dsh, wq_w, wkv_w, lens};
   gemm_kernel<T><<<(unsigned)grid_size(n_rb, n_ct), THREADS, 0, stream>>>(
-      rows, (const T*)wt, ncols, st, (int)d_model, (int)n_rb, (int)n_ct);
+      rows, (const T*)wt, ncols, st, (int)d_model, (int)n_rb, (int)n_ct, (int)d_model);
   return hipGetLastError();
 }
 
@@ -426,11 +486,61 @@ hipError_t out_impl(const void* a, const void* wo, void* wt, void* out, int64_t 
   DenseRows<T> rows{(const T*)a, M, (int)K};
   DenseStore<T> st{(T*)out, M, (int)d_model, lens, seq_n};
   gemm_kernel<T><<<(unsigned)grid_size(n_rb, n_ct), THREADS, 0, stream>>>(
-      rows, (const T*)wt, (int)d_model, st, (int)K, (int)n_rb, (int)n_ct);
+      rows, (const T*)wt, (int)d_model, st, (int)K, (int)n_rb, (int)n_ct, (int)K);
+  return hipGetLastError();
+}
+
+// out [B, ncols/d, Np, d] (head-major rows, zero past N) = x [B, N, K] * wt^T.
+template <typename T>
+hipError_t heads_impl(const void* x, const void* wt, void* out, int64_t B, int64_t N, int64_t Np,
+                      int64_t K, int64_t ncols, int64_t d, hipStream_t stream) {
+  const int64_t n_rb = B * Np / BM, n_ct = (ncols + BN - 1) / BN;
+  if (!grid_ok(n_rb, n_ct)) return hipErrorInvalidConfiguration;
+  PaddedRows<T> rows{(const T*)x, N, Np, (int)K};
+  const int dsh = d == 64 ? 6 : 5;
+  QkvStore<T> st{(T*)out, nullptr, nullptr, N, Np, (int)(ncols / d), 0, dsh, (int)ncols, 0, nullptr};
+  gemm_kernel<T><<<(unsigned)grid_size(n_rb, n_ct), THREADS, 0, stream>>>(
+      rows, (const T*)wt, (int)ncols, st, (int)K, (int)n_rb, (int)n_ct, (int)K);
+  return hipGetLastError();
+}
+
+// out [B, N, ncols] = a [B*Np, K] * wt^T, rows t >= N of each batch dropped.
+template <typename T>
+hipError_t unpad_impl(const void* a, const void* wt, void* out, int64_t B, int64_t N, int64_t Np,
+                      int64_t K, int64_t ncols, hipStream_t stream) {
+  const int64_t n_rb = B * Np / BM, n_ct = (ncols + BN - 1) / BN;
+  if (!grid_ok(n_rb, n_ct)) return hipErrorInvalidConfiguration;
+  DenseRows<T> rows{(const T*)a, B * Np, (int)K};
+  UnpadStore<T> st{(T*)out, N, Np, (int)ncols};
+  gemm_kernel<T><<<(unsigned)grid_size(n_rb, n_ct), THREADS, 0, stream>>>(
+      rows, (const T*)wt, (int)ncols, st, (int)K, (int)n_rb, (int)n_ct, (int)K);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t splitk_impl(const void* a, const void* wt, float* part, int64_t M, int64_t K,
+                       int64_t ncols, int64_t k_split, int64_t n_split, hipStream_t stream) {
+  const int64_t n_rb = (M + BM - 1) / BM, n_ct = (ncols + BN - 1) / BN;
+  if (!grid_ok(n_rb, n_ct) || n_split > 65535) return hipErrorInvalidConfiguration;
+  DenseRows<T> rows{(const T*)a, M, (int)K};
+  F32PartStore st{part, M, (int)ncols};
+  gemm_kernel<T><<<dim3((unsigned)grid_size(n_rb, n_ct), (unsigned)n_split), THREADS, 0, stream>>>(
+      rows, (const T*)wt, (int)ncols, st, (int)K, (int)n_rb, (int)n_ct, (int)k_split);
   return hipGetLastError();
 }
 
 }  // namespace
+
+SplitK splitk_plan(int64_t M, int64_t K, int64_t ncols) {
+  const int64_t tiles = grid_size((M + BM - 1) / BM, (ncols + BN - 1) / BN);
+  const int64_t steps = K / BK;
+  // about 1024 workgroups, each with at least 32 k-steps
+  int64_t n = std::max<int64_t>(1, std::min<int64_t>((1024 + tiles - 1) / tiles, steps / 32));
+  SplitK p;
+  p.k_split = (steps + n - 1) / n * BK;
+  p.n_split = (K + p.k_split - 1) / p.k_split;
+  return p;
+}
 
 size_t qkv_wt_bytes(sqa_dtype dt, int64_t d_model, int64_t H_q, int64_t H_kv, int64_t d_head) {
   return (size_t)(d_model * (H_q + 2 * H_kv) * d_head) * (dt == SQA_DTYPE_BF16 ? 2 : 4);
@@ -449,6 +559,26 @@ hipError_t launch_qkv_projection(sqa_dtype dt, const void* x, const void* wq, co
                           stream);
   return qkv_impl<float>(x, wq, wk, wv, wt, q, k, vt, B, N, Np, d_model, H_q, H_kv, d_head, lens,
                          stream);
+}
+
+hipError_t launch_gemm_heads(sqa_dtype dt, const void* x, const void* wt, void* out, int64_t B,
+                             int64_t N, int64_t Np, int64_t K, int64_t ncols, int64_t d_head,
+                             hipStream_t stream) {
+  return dt == SQA_DTYPE_BF16 ? heads_impl<bf16>(x, wt, out, B, N, Np, K, ncols, d_head, stream)
+                              : heads_impl<float>(x, wt, out, B, N, Np, K, ncols, d_head, stream);
+}
+
+hipError_t launch_gemm_unpad(sqa_dtype dt, const void* a, const void* wt, void* out, int64_t B,
+                             int64_t N, int64_t Np, int64_t K, int64_t ncols, hipStream_t stream) {
+  return dt == SQA_DTYPE_BF16 ? unpad_impl<bf16>(a, wt, out, B, N, Np, K, ncols, stream)
+                              : unpad_impl<float>(a, wt, out, B, N, Np, K, ncols, stream);
+}
+
+hipError_t launch_gemm_splitk(sqa_dtype dt, const void* a, const void* wt, float* part, int64_t M,
+                              int64_t K, int64_t ncols, const SplitK& sk, hipStream_t stream) {
+  return dt == SQA_DTYPE_BF16
+      ? splitk_impl<bf16>(a, wt, part, M, K, ncols, sk.k_split, sk.n_split, stream)
+      : splitk_impl<float>(a, wt, part, M, K, ncols, sk.k_split, sk.n_split, stream);
 }
 
 hipError_t launch_output_projection(sqa_dtype dt, const void* a, const void* wo, void* wt,

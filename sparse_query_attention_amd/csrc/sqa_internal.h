@@ -28,10 +28,12 @@ hipError_t launch_qkv_projection(sqa_dtype dt, const void* x, const void* wq, co
                                  int64_t d_head, const int32_t* lens, hipStream_t stream);
 
 // Step 2: attention core into a [B*N, H_q*d]; keys end at each sequence's
-// length, and rows at or past it are zero.
+// length, and rows at or past it are zero. With lse, also each row's base-2
+// log-sum-exp of the scaled scores, [B, H_q, Np] fp32 (+inf on padding rows).
 hipError_t launch_attention(sqa_dtype dt, const void* q, const void* k, const void* vt, void* a,
                             int64_t B, int64_t N, int64_t Np, int64_t H_q, int64_t H_kv,
-                            int64_t d_head, bool causal, const int32_t* lens, hipStream_t stream);
+                            int64_t d_head, bool causal, const int32_t* lens, hipStream_t stream,
+                            float* lse = nullptr);
 
 // Step 3: out [M, d_model] = a [M, K] * wo [K, d_model]. wt is device scratch of
 // out_wt_bytes() for the transposed weights. With lens, row m is token m % seq_n
@@ -41,6 +43,32 @@ size_t out_wt_bytes(sqa_dtype dt, int64_t K, int64_t d_model);
 hipError_t launch_output_projection(sqa_dtype dt, const void* a, const void* wo, void* wt,
                                     void* out, int64_t M, int64_t K, int64_t d_model,
                                     const int32_t* lens, int64_t seq_n, hipStream_t stream);
+
+// Other products on the projection GEMM, with W given transposed (wt [ncols, K],
+// k-contiguous rows). K and ncols are multiples of 32; Np of 256.
+//  heads:  out [B, ncols/d, Np, d] (head-major, rows t >= N zero) = x [B, N, K] wt^T
+//  unpad:  out [B, N, ncols] = a [B*Np, K] wt^T, rows t >= N of each batch not stored
+//  splitk: part [n_split, M, ncols] fp32 = a [M, K] wt^T, summed over the k of each split
+hipError_t launch_gemm_heads(sqa_dtype dt, const void* x, const void* wt, void* out, int64_t B,
+                             int64_t N, int64_t Np, int64_t K, int64_t ncols, int64_t d_head,
+                             hipStream_t stream);
+hipError_t launch_gemm_unpad(sqa_dtype dt, const void* a, const void* wt, void* out, int64_t B,
+                             int64_t N, int64_t Np, int64_t K, int64_t ncols, hipStream_t stream);
+struct SplitK { int64_t k_split, n_split; };
+SplitK splitk_plan(int64_t M, int64_t K, int64_t ncols);
+hipError_t launch_gemm_splitk(sqa_dtype dt, const void* a, const void* wt, float* part, int64_t M,
+                              int64_t K, int64_t ncols, const SplitK& sk, hipStream_t stream);
+
+// Backward pass: dx [B,N,d_model] and dWq, dWk, dWv, dWo (the weights' shapes)
+// for the upstream gradient dy [B,N,d_model], recomputing the forward
+// activations. ws is device scratch of backward_workspace_bytes().
+size_t backward_workspace_bytes(sqa_dtype dt, int64_t B, int64_t N, int64_t Np, int64_t d_model,
+                                int64_t H_q, int64_t H_kv, int64_t d_head);
+hipError_t launch_backward(sqa_dtype dt, const void* x, const void* wq, const void* wk,
+                           const void* wv, const void* wo, const void* dy, void* dx, void* dwq,
+                           void* dwk, void* dwv, void* dwo, int64_t B, int64_t N, int64_t Np,
+                           int64_t d_model, int64_t H_q, int64_t H_kv, int64_t d_head, bool causal,
+                           void* ws, hipStream_t stream);
 
 // Key/value caches [B, H_kv, N_max, d]: rows 0..N-1 from the step-1 layouts k and vt.
 hipError_t launch_fill_cache(sqa_dtype dt, const void* k, const void* vt, void* kc, void* vc,

@@ -189,3 +189,38 @@ def test_prefill_validates_the_caches():
     assert lib.sqa_prefill(*args(FAKE + 0x6000000, FAKE + 0x7000000, 64, 0)) == _lib.SQA_ERR_UNSUPPORTED
     assert lib.sqa_prefill(*args(FAKE + 0x6000000, FAKE + 0x6000040, 64, 128)) == _lib.SQA_ERR_INVALID_ARG
     assert b"overlaps" in lib.sqa_last_error_message()
+
+
+def _bwd(**kw):
+    a = dict(x=FAKE, Wq=FAKE + 0x1000000, Wk=FAKE + 0x2000000, Wv=FAKE + 0x3000000,
+             Wo=FAKE + 0x4000000, dy=FAKE + 0x5000000, dx=FAKE + 0x6000000, dWq=FAKE + 0x7000000,
+             dWk=FAKE + 0x8000000, dWv=FAKE + 0x9000000, dWo=FAKE + 0xA000000, B=2, N=100,
+             d_model=256, H=8, H_q=4, H_kv=2, d_head=32, causal=1, dtype=_lib.SQA_DTYPE_BF16)
+    a.update(kw)
+    lib = _lib.load()
+    st = lib.sqa_backward(*(a[k] for k in ("x", "Wq", "Wk", "Wv", "Wo", "dy", "dx", "dWq", "dWk",
+                                           "dWv", "dWo", "B", "N", "d_model", "H", "H_q", "H_kv",
+                                           "d_head", "causal", "dtype")), None)
+    return st, lib.sqa_last_error_message().decode()
+
+
+@pytest.mark.parametrize("kw,status,words", [
+    (dict(dy=0), _lib.SQA_ERR_INVALID_ARG, "dy is null"),
+    (dict(dWk=FAKE + 0x8000008), _lib.SQA_ERR_INVALID_ARG, "dWk is null or not 16-byte aligned"),
+    (dict(dx=FAKE + 0x5000000), _lib.SQA_ERR_INVALID_ARG, "output overlaps an input"),
+    (dict(dWo=FAKE + 0x7000040), _lib.SQA_ERR_INVALID_ARG, "two outputs overlap"),
+    (dict(dWq=FAKE + 0x40), _lib.SQA_ERR_INVALID_ARG, "output overlaps an input"),
+    (dict(causal=2), _lib.SQA_ERR_INVALID_ARG, "causal"),
+    (dict(H_kv=3), _lib.SQA_ERR_INVALID_ARG, "multiple of H_kv"),
+    (dict(d_model=128, H=8, d_head=16), _lib.SQA_ERR_UNSUPPORTED, "d_head"),
+    (dict(dtype=7), _lib.SQA_ERR_UNSUPPORTED, "dtype"),
+    (dict(N=(1 << 24) + 1), _lib.SQA_ERR_UNSUPPORTED, "SQA_MAX_N"),
+])
+def test_backward_rejects_invalid_arguments(kw, status, words):
+    st, msg = _bwd(**kw)
+    assert st == status, msg
+    assert words in msg
+
+
+def test_backward_of_an_empty_batch_is_a_no_op():
+    assert _bwd(B=0, x=0, dy=0)[0] == _lib.SQA_OK

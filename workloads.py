@@ -24,6 +24,9 @@ Draw recipe (the same everywhere):
   * A variable-length batch (sequences padded to N, as a training batch cut at
     a maximum sequence length holds them: model cards' training example) draws
     its lengths from stream 6, uniform integers in [varlen_min, N].
+  * The backward pass takes an upstream gradient dY [B, N, d_model] from
+    stream 7: N(0, 1/d_model) in float32, the scale of the gradient of a
+    per-token mean loss through an output layer of the same width.
 """
 from __future__ import annotations
 
@@ -32,7 +35,7 @@ from typing import Dict, Optional
 
 import numpy as np
 
-STREAM_X, STREAM_WQ, STREAM_WK, STREAM_WV, STREAM_WO, STREAM_OUTLIERS, STREAM_LENS = range(7)
+STREAM_X, STREAM_WQ, STREAM_WK, STREAM_WV, STREAM_WO, STREAM_OUTLIERS, STREAM_LENS, STREAM_DY = range(8)
 
 
 @dataclass(frozen=True)
@@ -133,6 +136,13 @@ def draw_weights(w: Workload) -> Dict[str, np.ndarray]:
               "Wo": (STREAM_WO, (w.H_q * d, w.d_model))}
     return {k: _rng(w.seed, s).standard_normal(shp, dtype=np.float32) * std
             for k, (s, shp) in shapes.items()}
+
+
+def draw_upstream_grad(w: Workload) -> np.ndarray:
+    """dY [B, N, d_model] (float32) for the backward pass, from stream 7."""
+    g = _rng(w.seed, STREAM_DY).standard_normal((w.B * w.N, w.d_model), dtype=np.float32)
+    g *= np.float32(1.0 / np.sqrt(w.d_model))
+    return g.reshape(w.B, w.N, w.d_model)
 
 
 def draw_lens(w: Workload) -> np.ndarray:
