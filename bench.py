@@ -12,7 +12,8 @@ workloads and their equally shaped MHA/GQA/MQA baselines are timed as well and
 reported under "variants", with a sweep of H_kv at fixed H_q (attention time
 should not depend on H_kv), a padded batch of sequences of mixed length
 (sqa_forward_varlen) and one decode step per sequence over 32k-token key/value
-caches (sqa_decode_step; `--decode-only` times just that step).
+caches (sqa_decode_step; `--decode-only` times just that step), and the
+backward pass of the headline workload (sqa_backward; `--backward-only`).
 
 Prints ONE JSON line. FLOPs use the closed form: attention core
 4*B*H_q*N^2*d_head (halved when causal) plus the projections
@@ -260,6 +261,60 @@ def run_decode(w: wl.Workload, steps: int, warmup: int, torch, sqa, dev):
             "frac_hbm_peak": round(total / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def run_backward(w: wl.Workload, steps: int, warmup: int, torch, sqa, dev):
+    """A training step of the layer on w with a seeded upstream gradient:
+    sqa_forward_train, then sqa_backward from its saved activations (also
+    timed recomputing them), with events on the launch stream. Algorithmic
+    work of the backward: the attention backward's five score-sized products
+    (2.5x the forward core) and the projection gradients (dA, dWo, dX and the
+    three input-weight gradients: 2x the forward projections)."""
+    arrays = wl.draw(w)
+    arrays["dY"] = wl.draw_upstream_grad(w)
+    host = wl.to_device_dtype(arrays, w.dtype)
+    d = {k: v.to(dev) for k, v in host.items()}
+    del host, arrays
+    outs = (torch.empty_like(d["X"]), torch.empty_like(d["Wq"]), torch.empty_like(d["Wk"]),
+            torch.empty_like(d["Wv"]), torch.empty_like(d["Wo"]))
+    stream = torch.cuda.current_stream(dev)
+    tm = Timer(torch, stream)
+
+    y = torch.empty_like(d["X"])
+    _, saved = sqa.forward_train(d["X"], d["Wq"], d["Wk"], d["Wv"], d["Wo"], H=w.H, H_q=w.H_q,
+                                 H_kv=w.H_kv, causal=w.causal, out=y)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = tm.event()
+        for _ in range(steps):
+            fn()
+        e1 = tm.event()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    def fwd_train():
+        sqa.forward_train(d["X"], d["Wq"], d["Wk"], d["Wv"], d["Wo"], H=w.H, H_q=w.H_q,
+                          H_kv=w.H_kv, causal=w.causal, out=y)
+
+    def bwd(sv):
+        return lambda: sqa.backward(d["X"], d["Wq"], d["Wk"], d["Wv"], d["Wo"], d["dY"], H=w.H,
+                                    H_q=w.H_q, H_kv=w.H_kv, causal=w.causal, saved=sv, out=outs)
+
+    ms = timed(bwd(saved))            # from the training forward's activations
+    ms_re = timed(bwd(None))          # recomputing them
+    ms_fwd = timed(fwd_train)
+    flop = 2.5 * core_flops(w) + 2.0 * proj_flops(w)
+    res = {"ms": round(ms, 4), "tflops_algorithmic": round(flop / (ms / 1e3) / 1e12, 2),
+           "algorithmic_flop": flop, "ms_recomputing_activations": round(ms_re, 4),
+           "forward_train_ms": round(ms_fwd, 4),
+           "training_step_ms": round(ms_fwd + ms, 4),
+           "training_tokens_per_s": round(w.tokens / ((ms_fwd + ms) / 1e3), 1)}
+    del d, outs, saved, y
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(w: wl.Workload, rows_sample: int = 24576):
     """The float64 oracle on a bounded sample: every key/value projection of the
     workload, plus the whole forward of `rows_sample` evenly spaced query rows.
@@ -312,6 +367,8 @@ def main():
     ap.add_argument("--no-variants", action="store_true", help="time only the headline workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=24576)
+    ap.add_argument("--backward-only", action="store_true",
+                    help="only time sqa_backward on the workload")
     ap.add_argument("--decode-only", action="store_true",
                     help="only time the decode step (B=8, 32k-token caches), SQA and GQA baseline")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -333,6 +390,11 @@ def main():
     dev = torch.device("cuda:0")
     if args.calibrate_copy:
         calibrate_copy(torch, dev)
+        return
+    if args.backward_only:
+        w = wl.WORKLOADS[args.workload]
+        print(json.dumps({w.name + "_backward": run_backward(w, args.steps, args.warmup, torch, sqa,
+                                                              dev)}), flush=True)
         return
     if args.decode_only:
         for v in DECODE_WORKLOADS:
@@ -395,6 +457,9 @@ def main():
             sweep, max_over_min=round(max(times) / min(times), 3))
         for v in DECODE_WORKLOADS:
             variants[v.name] = run_decode(v, max(10, args.steps), vwarm, torch, sqa, dev)
+        # Training: the gradients of the headline workload (sqa_backward), and
+        # forward + backward as one training step of the layer.
+        variants[w.name + "_backward"] = run_backward(w, vsteps, vwarm, torch, sqa, dev)
         # A padded batch of sequences of mixed length (sqa_forward_varlen).
         variants[wl.SQA_VARLEN_32K.name] = run_varlen(wl.SQA_VARLEN_32K, vsteps, vwarm, torch, sqa,
                                                       dev)

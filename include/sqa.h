@@ -146,34 +146,60 @@ sqa_status sqa_decode_step(const void* x_new, const void* Wq, const void* Wk, co
                            hipStream_t stream);
 
 /*
- * sqa_backward - gradients of the SQA layer for training: with Y = sqa_forward(x)
- * and an upstream gradient dy = dL/dY [B, N, d_model], writes
+ * Training. The model cards train this layer (ReactiveAI/xSMQAT-m and
+ * ReactiveAI/GQA-Ref-Micro, training examples).
+ *
+ * sqa_training_saved_bytes - size of the activation buffer that
+ * sqa_forward_train fills and sqa_backward reads: Q, K, V^T (the layouts of
+ * sqa_qkv_projection), A [B*N, H_q*d_head] and each row's softmax
+ * log-sum-exp (fp32), about elem_size*(B*Np*(H_q + 2*H_kv)*d_head +
+ * B*N*H_q*d_head) + 4*B*H_q*Np bytes. Returns 0 for an invalid shape or dtype.
+ */
+size_t sqa_training_saved_bytes(int64_t B, int64_t N, int64_t H_q, int64_t H_kv, int64_t d_head,
+                                sqa_dtype dtype);
+
+/*
+ * sqa_forward_train - sqa_forward that also keeps its activations in `saved`
+ * (a caller-owned device buffer of at least sqa_training_saved_bytes() bytes,
+ * 16-byte aligned, overlapping no input and not out), for sqa_backward. `out`
+ * is bitwise what sqa_forward writes. Its workspace is only the transposed
+ * weights.
+ */
+sqa_status sqa_forward_train(const void* x, const void* Wq, const void* Wk, const void* Wv,
+                             const void* Wo, void* out, void* saved, size_t saved_bytes, int64_t B,
+                             int64_t N, int64_t d_model, int64_t H, int64_t H_q, int64_t H_kv,
+                             int64_t d_head, int causal, sqa_dtype dtype, hipStream_t stream);
+
+/*
+ * sqa_backward - gradients of the SQA layer: with Y = sqa_forward(x) and an
+ * upstream gradient dy = dL/dY [B, N, d_model], writes
  *   dx  [B, N, d_model]         dL/dx
  *   dWq [d_model, H_q*d_head]   dL/dWq   (dWk, dWv [d_model, H_kv*d_head] likewise)
  *   dWo [H_q*d_head, d_model]   dL/dWo
- * The model cards train this layer (ReactiveAI/xSMQAT-m and
- * ReactiveAI/GQA-Ref-Micro, training examples). By the chain rule through the
- * definition above (P_i = the attention weights of head i, O_i = P_i V_j):
+ * By the chain rule through the definition above (P_i = the attention
+ * weights of head i, O_i = P_i V_j):
  *   dA = dy Wo^T, dWo = A^T dy
  *   dS_i = P_i * (dA_i V_j^T - rowsum(dA_i * O_i)),  dQ_i = dS_i K_j / sqrt(d_head)
  *   dK_j = sum over the heads i of group j of dS_i^T Q_i / sqrt(d_head)
  *   dV_j = sum over the same heads of P_i^T dA_i
  *   dx = dQ Wq^T + dK Wk^T + dV Wv^T, dWq = x^T dQ, dWk = x^T dK, dWv = x^T dV
- * (weight gradients summed over the batch). The forward activations (Q, K, V,
- * A and each row's softmax normalizer) are recomputed, not passed in.
+ * (weight gradients summed over the batch). The forward activations come from
+ * `saved`, as sqa_forward_train wrote them for the same x, weights, shapes and
+ * causal flag; if saved is NULL they are recomputed (saved_bytes is ignored).
  * Arithmetic: dA, dQ, dK, dV and the five outputs are each rounded once to
- * `dtype`; P, dS and the row sums are fp32; D uses A as stored.
+ * `dtype`; P, dS and the row sums are fp32; rowsum(dA_i * O_i) uses A as
+ * stored. The result does not depend on the launch (no atomics).
  * Workspace: about elem_size * B*Np * (8*(H_q + H_kv)*d_head + 2*d_model)
- * bytes (Np = sqa_padded_length(N)), plus 8*B*H_q*Np bytes of fp32 row
- * statistics and the fp32 split-K partial sums of the weight gradients, from
- * the stream-ordered pool (see sqa_forward). Outputs must not overlap each other or any input; other
- * checks and errors as in sqa_forward.
+ * bytes (less the saved activations when `saved` is given), 4*B*H_q*Np bytes
+ * of fp32 row sums, and the fp32 split-K partial sums of the weight gradients,
+ * from the stream-ordered pool (see sqa_forward). Outputs must not overlap
+ * each other, any input or `saved`; other checks and errors as in sqa_forward.
  */
 sqa_status sqa_backward(const void* x, const void* Wq, const void* Wk, const void* Wv,
-                        const void* Wo, const void* dy, void* dx, void* dWq, void* dWk, void* dWv,
-                        void* dWo, int64_t B, int64_t N, int64_t d_model, int64_t H, int64_t H_q,
-                        int64_t H_kv, int64_t d_head, int causal, sqa_dtype dtype,
-                        hipStream_t stream);
+                        const void* Wo, const void* dy, const void* saved, size_t saved_bytes,
+                        void* dx, void* dWq, void* dWk, void* dWv, void* dWo, int64_t B, int64_t N,
+                        int64_t d_model, int64_t H, int64_t H_q, int64_t H_kv, int64_t d_head,
+                        int causal, sqa_dtype dtype, hipStream_t stream);
 
 /*
  * sqa_padded_length - Np, the sequence length of the Q/K/V^T layouts below:

@@ -20,7 +20,7 @@ from typing import Optional, Tuple
 from . import _lib
 from ._lib import SQAError
 
-__all__ = ["forward_varlen", "backward", "prefill", "decode_step", "forward", "qkv_projection", "attention", "output_projection", "padded_length",
+__all__ = ["forward_varlen", "forward_train", "backward", "prefill", "decode_step", "forward", "qkv_projection", "attention", "output_projection", "padded_length",
            "SQAError", "library_path"]
 
 library_path = _lib.LIB_PATH
@@ -84,11 +84,41 @@ def forward(x, Wq, Wk, Wv, Wo, *, H: int, H_q: int, H_kv: int, causal: bool = Fa
     return out
 
 
+def forward_train(x, Wq, Wk, Wv, Wo, *, H: int, H_q: int, H_kv: int, causal: bool = False,
+                  out=None):
+    """forward() that also keeps the activations backward() needs
+    (sqa_forward_train). Returns (out, saved); saved is an opaque uint8 device
+    tensor to pass to backward() with the same inputs."""
+    lib = _lib.load()
+    if x.dim() != 3:
+        raise ValueError("x must be [B, N, d_model]")
+    B, N, D = x.shape
+    if H <= 0 or D % H:
+        raise ValueError("d_model must be a multiple of H")
+    d = D // H
+    torch = _torch()
+    if out is None:
+        out = torch.empty_like(x)
+    for name, t, shp in (("x", x, (B, N, D)), ("Wq", Wq, (D, H_q * d)), ("Wk", Wk, (D, H_kv * d)),
+                         ("Wv", Wv, (D, H_kv * d)), ("Wo", Wo, (H_q * d, D)), ("out", out, (B, N, D))):
+        _check_tensor(name, t, shp, x.dtype, x.device)
+    nbytes = int(lib.sqa_training_saved_bytes(B, N, H_q, H_kv, d, _dtype_code(x)))
+    if nbytes == 0 and B * N > 0:
+        raise ValueError("invalid shape for sqa_forward_train")
+    saved = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=x.device)
+    _lib.check(lib.sqa_forward_train(x.data_ptr(), Wq.data_ptr(), Wk.data_ptr(), Wv.data_ptr(),
+                                     Wo.data_ptr(), out.data_ptr(), saved.data_ptr(), saved.numel(),
+                                     B, N, D, H, H_q, H_kv, d, int(bool(causal)), _dtype_code(x),
+                                     _stream(x.device)))
+    return out, saved
+
+
 def backward(x, Wq, Wk, Wv, Wo, dy, *, H: int, H_q: int, H_kv: int, causal: bool = False,
-             out=None):
+             saved=None, out=None):
     """Gradients of the SQA layer (sqa_backward): for Y = forward(x, ...) and
     dy = dL/dY, returns (dx, dWq, dWk, dWv, dWo) with the shapes of x and the
-    weights. `out` may pass those five tensors to write into."""
+    weights. `saved` is forward_train()'s buffer for the same inputs (None:
+    the activations are recomputed). `out` may pass the five tensors to write."""
     lib = _lib.load()
     if x.dim() != 3:
         raise ValueError("x must be [B, N, d_model]")
@@ -107,10 +137,14 @@ def backward(x, Wq, Wk, Wv, Wo, dy, *, H: int, H_q: int, H_kv: int, causal: bool
                          ("dWk", dWk, (D, H_kv * d)), ("dWv", dWv, (D, H_kv * d)),
                          ("dWo", dWo, (H_q * d, D))):
         _check_tensor(name, t, shp, x.dtype, x.device)
+    if saved is not None and (saved.device != x.device or not saved.is_contiguous()):
+        raise ValueError("saved must be a contiguous tensor on x's device")
+    sp, sn = (saved.data_ptr(), saved.numel() * saved.element_size()) if saved is not None else (0, 0)
     _lib.check(lib.sqa_backward(x.data_ptr(), Wq.data_ptr(), Wk.data_ptr(), Wv.data_ptr(),
-                                Wo.data_ptr(), dy.data_ptr(), dx.data_ptr(), dWq.data_ptr(),
-                                dWk.data_ptr(), dWv.data_ptr(), dWo.data_ptr(), B, N, D, H, H_q,
-                                H_kv, d, int(bool(causal)), _dtype_code(x), _stream(x.device)))
+                                Wo.data_ptr(), dy.data_ptr(), sp or None, sn, dx.data_ptr(),
+                                dWq.data_ptr(), dWk.data_ptr(), dWv.data_ptr(), dWo.data_ptr(), B, N,
+                                D, H, H_q, H_kv, d, int(bool(causal)), _dtype_code(x),
+                                _stream(x.device)))
     return dx, dWq, dWk, dWv, dWo
 
 

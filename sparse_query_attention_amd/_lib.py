@@ -18,7 +18,10 @@ SIGNATURES = {
     "sqa_forward_varlen": (_int, [_vp] * 7 + [_i64] * 7 + [_int, _int, _vp]),
     "sqa_prefill": (_int, [_vp] * 8 + [_i64] * 8 + [_int, _vp]),
     "sqa_decode_step": (_int, [_vp] * 9 + [_i64] * 7 + [_int, _vp]),
-    "sqa_backward": (_int, [_vp] * 11 + [_i64] * 7 + [_int, _int, _vp]),
+    "sqa_training_saved_bytes": (ctypes.c_size_t, [_i64] * 5 + [_int]),
+    "sqa_forward_train": (_int, [_vp] * 7 + [ctypes.c_size_t] + [_i64] * 7 + [_int, _int, _vp]),
+    "sqa_backward": (_int, [_vp] * 7 + [ctypes.c_size_t] + [_vp] * 5 + [_i64] * 7
+                     + [_int, _int, _vp]),
     "sqa_padded_length": (_i64, [_i64]),
     "sqa_qkv_projection": (_int, [_vp] * 7 + [_i64] * 7 + [_int, _vp]),
     "sqa_attention": (_int, [_vp] * 4 + [_i64] * 5 + [_int, _int, _vp]),

@@ -162,13 +162,30 @@ struct PoolScratch {
   }
 };
 
-// sqa_forward (varlen false, lens unused), sqa_forward_varlen, and sqa_prefill
-// (kc, vc non-null: the caches [B, H_kv, N_max, d_head] receive K and V).
+// Checks a caller's buffer of saved training activations: its size, its
+// alignment, and that it overlaps none of the given buffers.
+sqa_status check_saved(const void* saved, size_t saved_bytes, const Shape& s, sqa_dtype dt,
+                       const void* const* bufs, const size_t* sizes, int n) {
+  if (!saved) return fail(SQA_ERR_INVALID_ARG, "saved is null");
+  if (!aligned16(saved)) return fail(SQA_ERR_INVALID_ARG, "saved is not 16-byte aligned");
+  const int64_t need =
+      sqa::saved_layout((int64_t)elem_size(dt), s.B, s.N, sqa::padded_length(s.N), s.H_q, s.H_kv, s.d).total;
+  if (saved_bytes < (size_t)need) return fail(SQA_ERR_INVALID_ARG, "saved_bytes is too small");
+  for (int j = 0; j < n; ++j)
+    if (overlap(saved, (size_t)need, bufs[j], sizes[j]))
+      return fail(SQA_ERR_INVALID_ARG, "saved overlaps another buffer");
+  return SQA_OK;
+}
+
+// sqa_forward (varlen false, lens unused), sqa_forward_varlen, sqa_prefill
+// (kc, vc non-null: the caches [B, H_kv, N_max, d_head] receive K and V) and
+// sqa_forward_train (saved non-null: the activations stay there, with each
+// row's log-sum-exp, instead of in the workspace).
 sqa_status forward_impl(const void* x, const void* Wq, const void* Wk, const void* Wv,
                         const void* Wo, void* out, bool varlen, const int32_t* lens, void* kc,
                         void* vc, int64_t N_max, int64_t B, int64_t N, int64_t d_model, int64_t H,
                         int64_t H_q, int64_t H_kv, int64_t d_head, int causal, sqa_dtype dtype,
-                        hipStream_t stream) {
+                        hipStream_t stream, void* saved = nullptr, size_t saved_bytes = 0) {
   const Shape s{B, N, d_model, H, H_q, H_kv, d_head};
   SQA_TRY(check_dtype(dtype));
   SQA_TRY(check_heads(s, true));
@@ -211,8 +228,15 @@ sqa_status forward_impl(const void* x, const void* Wq, const void* Wk, const voi
     }
   }
 
-  const int64_t off_k = round256(z.q), off_v = off_k + round256(z.kv);
-  const int64_t off_a = off_v + round256(z.kv), off_w1 = off_a + round256(z.a);
+  if (saved) {
+    const void* bufs[6] = {x, Wq, Wk, Wv, Wo, out};
+    const size_t sizes[6] = {yb, wqb, wkb, wkb, wqb, yb};
+    SQA_TRY(check_saved(saved, saved_bytes, s, dtype, bufs, sizes, 6));
+  }
+  // q, k, vt, a in the workspace, or in `saved` (then only the weight transposes are)
+  const int64_t act = saved ? 0 : 1;
+  const int64_t off_k = act * round256(z.q), off_v = off_k + act * round256(z.kv);
+  const int64_t off_a = off_v + act * round256(z.kv), off_w1 = off_a + act * round256(z.a);
   const int64_t off_w3 = off_w1 + round256((int64_t)sqa::qkv_wt_bytes(dtype, d_model, H_q, H_kv, d_head));
   const int64_t total = off_w3 + round256((int64_t)sqa::out_wt_bytes(dtype, H_q * d_head, d_model));
   hipMemPool_t pool;
@@ -223,6 +247,13 @@ sqa_status forward_impl(const void* x, const void* Wq, const void* Wk, const voi
   char* base = (char*)ws;
   void *q = base, *k = base + off_k, *vt = base + off_v, *a = base + off_a;
   void *w1 = base + off_w1, *w3 = base + off_w3;
+  float* lse = nullptr;
+  if (saved) {
+    const sqa::SavedLayout S = sqa::saved_layout((int64_t)es, B, N, z.Np, H_q, H_kv, d_head);
+    char* sv = (char*)saved;
+    q = sv + S.q; k = sv + S.k; vt = sv + S.vt; a = sv + S.a;
+    lse = (float*)(sv + S.lse);
+  }
 
   e = sqa::launch_qkv_projection(dtype, x, Wq, Wk, Wv, w1, q, k, vt, B, N, z.Np, d_model, H_q,
                                  H_kv, d_head, lens, stream);
@@ -230,7 +261,7 @@ sqa_status forward_impl(const void* x, const void* Wq, const void* Wk, const voi
     e = sqa::launch_fill_cache(dtype, k, vt, kc, vc, B, H_kv, N, z.Np, N_max, d_head, stream);
   if (e == hipSuccess)
     e = sqa::launch_attention(dtype, q, k, vt, a, B, N, z.Np, H_q, H_kv, d_head, causal != 0, lens,
-                              stream);
+                              stream, lse);
   if (e == hipSuccess)
     e = sqa::launch_output_projection(dtype, a, Wo, w3, out, B * N, H_q * d_head, d_model, lens, N,
                                       stream);
@@ -241,7 +272,8 @@ sqa_status forward_impl(const void* x, const void* Wq, const void* Wk, const voi
 }
 
 sqa_status backward_impl(const void* x, const void* Wq, const void* Wk, const void* Wv,
-                         const void* Wo, const void* dy, void* dx, void* dWq, void* dWk, void* dWv,
+                         const void* Wo, const void* dy, const void* saved, size_t saved_bytes,
+                         void* dx, void* dWq, void* dWk, void* dWv,
                          void* dWo, int64_t B, int64_t N, int64_t d_model, int64_t H, int64_t H_q,
                          int64_t H_kv, int64_t d_head, int causal, sqa_dtype dtype,
                          hipStream_t stream) {
@@ -284,10 +316,12 @@ sqa_status backward_impl(const void* x, const void* Wq, const void* Wk, const vo
       if (overlap(outs[j], outb[j], outs[i], outb[i]))
         return fail(SQA_ERR_INVALID_ARG, "two outputs overlap");
   }
+  if (saved) SQA_TRY(check_saved(saved, saved_bytes, s, dtype, outs, outb, 5));
   PoolScratch ws;
-  SQA_TRY(ws.acquire(sqa::backward_workspace_bytes(dtype, B, N, z.Np, d_model, H_q, H_kv, d_head),
+  SQA_TRY(ws.acquire(sqa::backward_workspace_bytes(dtype, B, N, z.Np, d_model, H_q, H_kv, d_head,
+                                                   saved != nullptr),
                      stream));
-  const hipError_t e = sqa::launch_backward(dtype, x, Wq, Wk, Wv, Wo, dy, dx, dWq, dWk, dWv, dWo,
+  const hipError_t e = sqa::launch_backward(dtype, x, Wq, Wk, Wv, Wo, dy, saved, dx, dWq, dWk, dWv, dWo,
                                             B, N, z.Np, d_model, H_q, H_kv, d_head, causal != 0,
                                             ws.ptr, stream);
   const hipError_t ef = ws.release();
@@ -435,13 +469,31 @@ sqa_status sqa_prefill(const void* x, const void* Wq, const void* Wk, const void
                       d_model, H, H_q, H_kv, d_head, 1, dtype, stream);
 }
 
+size_t sqa_training_saved_bytes(int64_t B, int64_t N, int64_t H_q, int64_t H_kv, int64_t d_head,
+                                sqa_dtype dtype) {
+  const Shape s{B, N, H_q * d_head, H_q, H_q, H_kv, d_head};
+  if (check_dtype(dtype) != SQA_OK || check_heads(s, false) != SQA_OK) return 0;
+  Sizes z;
+  if (sizes_for(s, dtype, &z) != SQA_OK) return 0;
+  return (size_t)sqa::saved_layout((int64_t)elem_size(dtype), B, N, z.Np, H_q, H_kv, d_head).total;
+}
+
+sqa_status sqa_forward_train(const void* x, const void* Wq, const void* Wk, const void* Wv,
+                             const void* Wo, void* out, void* saved, size_t saved_bytes, int64_t B,
+                             int64_t N, int64_t d_model, int64_t H, int64_t H_q, int64_t H_kv,
+                             int64_t d_head, int causal, sqa_dtype dtype, hipStream_t stream) {
+  if (B * N != 0 && !saved) return fail(SQA_ERR_INVALID_ARG, "saved is null");
+  return forward_impl(x, Wq, Wk, Wv, Wo, out, false, nullptr, nullptr, nullptr, 0, B, N, d_model,
+                      H, H_q, H_kv, d_head, causal, dtype, stream, saved, saved_bytes);
+}
+
 sqa_status sqa_backward(const void* x, const void* Wq, const void* Wk, const void* Wv,
-                        const void* Wo, const void* dy, void* dx, void* dWq, void* dWk, void* dWv,
-                        void* dWo, int64_t B, int64_t N, int64_t d_model, int64_t H, int64_t H_q,
-                        int64_t H_kv, int64_t d_head, int causal, sqa_dtype dtype,
-                        hipStream_t stream) {
-  return backward_impl(x, Wq, Wk, Wv, Wo, dy, dx, dWq, dWk, dWv, dWo, B, N, d_model, H, H_q, H_kv,
-                       d_head, causal, dtype, stream);
+                        const void* Wo, const void* dy, const void* saved, size_t saved_bytes,
+                        void* dx, void* dWq, void* dWk, void* dWv, void* dWo, int64_t B, int64_t N,
+                        int64_t d_model, int64_t H, int64_t H_q, int64_t H_kv, int64_t d_head,
+                        int causal, sqa_dtype dtype, hipStream_t stream) {
+  return backward_impl(x, Wq, Wk, Wv, Wo, dy, saved, saved_bytes, dx, dWq, dWk, dWv, dWo, B, N,
+                       d_model, H, H_q, H_kv, d_head, causal, dtype, stream);
 }
 
 sqa_status sqa_decode_step(const void* x_new, const void* Wq, const void* Wk, const void* Wv,

@@ -501,6 +501,23 @@ hipError_t transpose(const void* src, int64_t src_bs, int64_t src_ld, int64_t r_
   return hipGetLastError();
 }
 
+}  // namespace
+
+SavedLayout saved_layout(int64_t es, int64_t B, int64_t N, int64_t Np, int64_t H_q, int64_t H_kv,
+                         int64_t d) {
+  auto r = [](int64_t x) { return (x + 255) / 256 * 256; };
+  SavedLayout S;
+  S.q = 0;
+  S.k = S.q + r(es * B * H_q * Np * d);
+  S.vt = S.k + r(es * B * H_kv * Np * d);
+  S.a = S.vt + r(es * B * H_kv * Np * d);
+  S.lse = S.a + r(es * B * N * H_q * d);
+  S.total = S.lse + r(4 * B * H_q * Np);
+  return S;
+}
+
+namespace {
+
 // Byte offsets of the backward workspace regions.
 struct BwdLayout {
   int64_t q, k, vt, a, lse, wt, dO, dvec, qt, kt, v, dOt, dqkv, dqkvT, xT, wall, aT, dyT, part;
@@ -509,14 +526,19 @@ struct BwdLayout {
 
 inline int64_t r256(int64_t x) { return (x + 255) / 256 * 256; }
 
+// With `saved`, the forward activations (q, k, vt, a, lse) come from a
+// training forward in the caller's buffer, and those regions (and the weight
+// transpose that recomputing them needs) take no workspace.
 BwdLayout bwd_layout(int64_t es, int64_t B, int64_t N, int64_t Np, int64_t d_model, int64_t H_q,
-                     int64_t H_kv, int64_t d) {
+                     int64_t H_kv, int64_t d, bool saved) {
   const int64_t W = (H_q + 2 * H_kv) * d, T = B * Np;
   const SplitK s1 = splitk_plan(d_model, T, W), s2 = splitk_plan(H_q * d, T, d_model);
   const int64_t part = std::max(s1.n_split * d_model * W, s2.n_split * H_q * d * d_model) * 4;
+  const int64_t f = saved ? 0 : 1;
   const int64_t sizes[] = {
-      es * B * H_q * Np * d, es * B * H_kv * Np * d, es * B * H_kv * Np * d, es * B * N * H_q * d,
-      4 * B * H_q * Np, (int64_t)qkv_wt_bytes(es == 2 ? SQA_DTYPE_BF16 : SQA_DTYPE_FP32, d_model, H_q, H_kv, d),
+      f * es * B * H_q * Np * d, f * es * B * H_kv * Np * d, f * es * B * H_kv * Np * d,
+      f * es * B * N * H_q * d, f * 4 * B * H_q * Np,
+      f * (int64_t)qkv_wt_bytes(es == 2 ? SQA_DTYPE_BF16 : SQA_DTYPE_FP32, d_model, H_q, H_kv, d),
       es * B * H_q * Np * d, 4 * B * H_q * Np, es * B * H_q * Np * d, es * B * H_kv * Np * d,
       es * B * H_kv * Np * d, es * B * H_q * Np * d, es * T * W, es * T * W, es * d_model * T,
       es * d_model * W, es * H_q * d * T, es * d_model * T, part};
@@ -534,14 +556,21 @@ BwdLayout bwd_layout(int64_t es, int64_t B, int64_t N, int64_t Np, int64_t d_mod
 
 template <typename T, int D>
 hipError_t backward_impl(const void* x, const void* wq, const void* wk, const void* wv,
-                         const void* wo, const void* dy, void* dx, void* dwq, void* dwk, void* dwv,
-                         void* dwo, int64_t B, int64_t N, int64_t Np, int64_t d_model, int64_t H_q,
-                         int64_t H_kv, bool causal, char* ws, hipStream_t stream) {
+                         const void* wo, const void* dy, const char* saved, void* dx, void* dwq,
+                         void* dwk, void* dwv, void* dwo, int64_t B, int64_t N, int64_t Np,
+                         int64_t d_model, int64_t H_q, int64_t H_kv, bool causal, char* ws,
+                         hipStream_t stream) {
   const sqa_dtype dt = sizeof(T) == 2 ? SQA_DTYPE_BF16 : SQA_DTYPE_FP32;
-  const BwdLayout L = bwd_layout(sizeof(T), B, N, Np, d_model, H_q, H_kv, D);
+  const BwdLayout L = bwd_layout(sizeof(T), B, N, Np, d_model, H_q, H_kv, D, saved != nullptr);
   const int64_t wq_w = H_q * D, wkv_w = H_kv * D, W = wq_w + 2 * wkv_w, TT = B * Np;
   void *q = ws + L.q, *k = ws + L.k, *vt = ws + L.vt, *a = ws + L.a, *wt = ws + L.wt;
   float* lse = (float*)(ws + L.lse);
+  if (saved) {
+    const SavedLayout S = saved_layout(sizeof(T), B, N, Np, H_q, H_kv, D);
+    char* sv = const_cast<char*>(saved);   // read only below
+    q = sv + S.q; k = sv + S.k; vt = sv + S.vt; a = sv + S.a;
+    lse = (float*)(sv + S.lse);
+  }
   float* dvec = (float*)(ws + L.dvec);
   void *dO = ws + L.dO, *qt = ws + L.qt, *kt = ws + L.kt, *v = ws + L.v, *dOt = ws + L.dOt;
   void *dqkv = ws + L.dqkv, *dqkvT = ws + L.dqkvT, *xT = ws + L.xT, *wall = ws + L.wall;
@@ -549,10 +578,12 @@ hipError_t backward_impl(const void* x, const void* wq, const void* wk, const vo
   float* part = (float*)(ws + L.part);
   hipError_t e;
 #define SQA_CK(call) do { e = (call); if (e != hipSuccess) return e; } while (0)
-  // forward activations and each row's log-sum-exp
-  SQA_CK(launch_qkv_projection(dt, x, wq, wk, wv, wt, q, k, vt, B, N, Np, d_model, H_q, H_kv, D,
-                               nullptr, stream));
-  SQA_CK(launch_attention(dt, q, k, vt, a, B, N, Np, H_q, H_kv, D, causal, nullptr, stream, lse));
+  // forward activations and each row's log-sum-exp, unless a training forward kept them
+  if (!saved) {
+    SQA_CK(launch_qkv_projection(dt, x, wq, wk, wv, wt, q, k, vt, B, N, Np, d_model, H_q, H_kv, D,
+                                 nullptr, stream));
+    SQA_CK(launch_attention(dt, q, k, vt, a, B, N, Np, H_q, H_kv, D, causal, nullptr, stream, lse));
+  }
   // dO = dY Wo^T in the head layout of q (Wo [H_q*d, d_model] is W^T of that product)
   SQA_CK(launch_gemm_heads(dt, dy, wo, dO, B, N, Np, d_model, wq_w, D, stream));
   {
@@ -612,24 +643,27 @@ hipError_t backward_impl(const void* x, const void* wq, const void* wk, const vo
 }  // namespace
 
 size_t backward_workspace_bytes(sqa_dtype dt, int64_t B, int64_t N, int64_t Np, int64_t d_model,
-                                int64_t H_q, int64_t H_kv, int64_t d_head) {
-  return (size_t)bwd_layout(dt == SQA_DTYPE_BF16 ? 2 : 4, B, N, Np, d_model, H_q, H_kv, d_head).total;
+                                int64_t H_q, int64_t H_kv, int64_t d_head, bool saved) {
+  return (size_t)bwd_layout(dt == SQA_DTYPE_BF16 ? 2 : 4, B, N, Np, d_model, H_q, H_kv, d_head,
+                            saved).total;
 }
 
 hipError_t launch_backward(sqa_dtype dt, const void* x, const void* wq, const void* wk,
-                           const void* wv, const void* wo, const void* dy, void* dx, void* dwq,
+                           const void* wv, const void* wo, const void* dy, const void* saved,
+                           void* dx, void* dwq,
                            void* dwk, void* dwv, void* dwo, int64_t B, int64_t N, int64_t Np,
                            int64_t d_model, int64_t H_q, int64_t H_kv, int64_t d_head, bool causal,
                            void* ws, hipStream_t stream) {
   char* w = (char*)ws;
+  const char* sv = (const char*)saved;
   if (dt == SQA_DTYPE_BF16)
-    return d_head == 64 ? backward_impl<bf16, 64>(x, wq, wk, wv, wo, dy, dx, dwq, dwk, dwv, dwo, B, N,
+    return d_head == 64 ? backward_impl<bf16, 64>(x, wq, wk, wv, wo, dy, sv, dx, dwq, dwk, dwv, dwo, B, N,
                                                   Np, d_model, H_q, H_kv, causal, w, stream)
-                        : backward_impl<bf16, 32>(x, wq, wk, wv, wo, dy, dx, dwq, dwk, dwv, dwo, B, N,
+                        : backward_impl<bf16, 32>(x, wq, wk, wv, wo, dy, sv, dx, dwq, dwk, dwv, dwo, B, N,
                                                   Np, d_model, H_q, H_kv, causal, w, stream);
-  return d_head == 64 ? backward_impl<float, 64>(x, wq, wk, wv, wo, dy, dx, dwq, dwk, dwv, dwo, B, N,
+  return d_head == 64 ? backward_impl<float, 64>(x, wq, wk, wv, wo, dy, sv, dx, dwq, dwk, dwv, dwo, B, N,
                                                  Np, d_model, H_q, H_kv, causal, w, stream)
-                      : backward_impl<float, 32>(x, wq, wk, wv, wo, dy, dx, dwq, dwk, dwv, dwo, B, N,
+                      : backward_impl<float, 32>(x, wq, wk, wv, wo, dy, sv, dx, dwq, dwk, dwv, dwo, B, N,
                                                  Np, d_model, H_q, H_kv, causal, w, stream);
 }
 

@@ -59,16 +59,24 @@ SplitK splitk_plan(int64_t M, int64_t K, int64_t ncols);
 hipError_t launch_gemm_splitk(sqa_dtype dt, const void* a, const void* wt, float* part, int64_t M,
                               int64_t K, int64_t ncols, const SplitK& sk, hipStream_t stream);
 
+// Activations a training forward keeps for the backward pass, at these byte
+// offsets of one buffer: q, k, vt (the step-1 layouts), a [B*N, H_q*d] and the
+// per-row base-2 log-sum-exp [B, H_q, Np] fp32.
+struct SavedLayout { int64_t q, k, vt, a, lse, total; };
+SavedLayout saved_layout(int64_t es, int64_t B, int64_t N, int64_t Np, int64_t H_q, int64_t H_kv,
+                         int64_t d);
+
 // Backward pass: dx [B,N,d_model] and dWq, dWk, dWv, dWo (the weights' shapes)
-// for the upstream gradient dy [B,N,d_model], recomputing the forward
-// activations. ws is device scratch of backward_workspace_bytes().
+// for the upstream gradient dy [B,N,d_model]. The forward activations come
+// from `saved` (saved_layout) or, if it is null, are recomputed. ws is device
+// scratch of backward_workspace_bytes(..., saved != null).
 size_t backward_workspace_bytes(sqa_dtype dt, int64_t B, int64_t N, int64_t Np, int64_t d_model,
-                                int64_t H_q, int64_t H_kv, int64_t d_head);
+                                int64_t H_q, int64_t H_kv, int64_t d_head, bool saved);
 hipError_t launch_backward(sqa_dtype dt, const void* x, const void* wq, const void* wk,
-                           const void* wv, const void* wo, const void* dy, void* dx, void* dwq,
-                           void* dwk, void* dwv, void* dwo, int64_t B, int64_t N, int64_t Np,
-                           int64_t d_model, int64_t H_q, int64_t H_kv, int64_t d_head, bool causal,
-                           void* ws, hipStream_t stream);
+                           const void* wv, const void* wo, const void* dy, const void* saved,
+                           void* dx, void* dwq, void* dwk, void* dwv, void* dwo, int64_t B,
+                           int64_t N, int64_t Np, int64_t d_model, int64_t H_q, int64_t H_kv,
+                           int64_t d_head, bool causal, void* ws, hipStream_t stream);
 
 // Key/value caches [B, H_kv, N_max, d]: rows 0..N-1 from the step-1 layouts k and vt.
 hipError_t launch_fill_cache(sqa_dtype dt, const void* k, const void* vt, void* kc, void* vc,

@@ -194,13 +194,14 @@ def test_prefill_validates_the_caches():
 def _bwd(**kw):
     a = dict(x=FAKE, Wq=FAKE + 0x1000000, Wk=FAKE + 0x2000000, Wv=FAKE + 0x3000000,
              Wo=FAKE + 0x4000000, dy=FAKE + 0x5000000, dx=FAKE + 0x6000000, dWq=FAKE + 0x7000000,
-             dWk=FAKE + 0x8000000, dWv=FAKE + 0x9000000, dWo=FAKE + 0xA000000, B=2, N=100,
+             dWk=FAKE + 0x8000000, dWv=FAKE + 0x9000000, dWo=FAKE + 0xA000000, saved=None,
+             saved_bytes=0, B=2, N=100,
              d_model=256, H=8, H_q=4, H_kv=2, d_head=32, causal=1, dtype=_lib.SQA_DTYPE_BF16)
     a.update(kw)
     lib = _lib.load()
-    st = lib.sqa_backward(*(a[k] for k in ("x", "Wq", "Wk", "Wv", "Wo", "dy", "dx", "dWq", "dWk",
-                                           "dWv", "dWo", "B", "N", "d_model", "H", "H_q", "H_kv",
-                                           "d_head", "causal", "dtype")), None)
+    st = lib.sqa_backward(*(a[k] for k in ("x", "Wq", "Wk", "Wv", "Wo", "dy", "saved", "saved_bytes",
+                                           "dx", "dWq", "dWk", "dWv", "dWo", "B", "N", "d_model",
+                                           "H", "H_q", "H_kv", "d_head", "causal", "dtype")), None)
     return st, lib.sqa_last_error_message().decode()
 
 
@@ -215,6 +216,9 @@ def _bwd(**kw):
     (dict(d_model=128, H=8, d_head=16), _lib.SQA_ERR_UNSUPPORTED, "d_head"),
     (dict(dtype=7), _lib.SQA_ERR_UNSUPPORTED, "dtype"),
     (dict(N=(1 << 24) + 1), _lib.SQA_ERR_UNSUPPORTED, "SQA_MAX_N"),
+    (dict(saved=FAKE + 0xB000008, saved_bytes=1 << 24), _lib.SQA_ERR_INVALID_ARG, "saved is not 16"),
+    (dict(saved=FAKE + 0xB000000, saved_bytes=1000), _lib.SQA_ERR_INVALID_ARG, "too small"),
+    (dict(saved=FAKE + 0x9000100, saved_bytes=1 << 24), _lib.SQA_ERR_INVALID_ARG, "saved overlaps"),
 ])
 def test_backward_rejects_invalid_arguments(kw, status, words):
     st, msg = _bwd(**kw)
@@ -224,3 +228,23 @@ def test_backward_rejects_invalid_arguments(kw, status, words):
 
 def test_backward_of_an_empty_batch_is_a_no_op():
     assert _bwd(B=0, x=0, dy=0)[0] == _lib.SQA_OK
+
+
+def test_training_saved_bytes_and_forward_train_validate():
+    lib = _lib.load()
+    n = lib.sqa_training_saved_bytes(2, 100, 4, 2, 32, _lib.SQA_DTYPE_BF16)
+    # q + k + vt (Np = 256) + a (N = 100) in bf16, and the fp32 row statistics
+    want = sum((x + 255) // 256 * 256 for x in (2 * 2 * 256 * 4 * 32, 2 * 2 * 256 * 2 * 32,
+                                               2 * 2 * 256 * 2 * 32, 2 * 2 * 100 * 4 * 32,
+                                               4 * 2 * 4 * 256))
+    assert n == want
+    assert lib.sqa_training_saved_bytes(2, 100, 4, 3, 32, _lib.SQA_DTYPE_BF16) == 0
+    args = lambda saved, nb: (FAKE, FAKE + 0x1000000, FAKE + 0x2000000, FAKE + 0x3000000,
+                              FAKE + 0x4000000, FAKE + 0x5000000, saved, nb, 2, 100, 256, 8, 4, 2,
+                              32, 1, _lib.SQA_DTYPE_BF16, None)
+    assert lib.sqa_forward_train(*args(None, n)) == _lib.SQA_ERR_INVALID_ARG
+    assert b"saved is null" in lib.sqa_last_error_message()
+    assert lib.sqa_forward_train(*args(FAKE + 0x6000000, n - 1)) == _lib.SQA_ERR_INVALID_ARG
+    assert b"too small" in lib.sqa_last_error_message()
+    assert lib.sqa_forward_train(*args(FAKE + 0x5000000, n)) == _lib.SQA_ERR_INVALID_ARG
+    assert b"overlaps" in lib.sqa_last_error_message()

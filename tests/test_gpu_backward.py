@@ -116,3 +116,23 @@ def test_backward_at_full_size_is_finite_deterministic_and_scales(dev):
         assert float(x.abs().max()) > 0, k
         assert torch.equal(x, y), k
         assert torch.equal(z, x * 2), k
+
+
+@pytest.mark.parametrize("causal,dtype,dh", [(True, "bf16", 64), (False, "bf16", 32), (True, "fp32", 32)])
+def test_saved_activations_give_the_same_results(dev, causal, dtype, dh):
+    """forward_train is bitwise forward, and backward from its saved activations
+    is bitwise backward with recomputed ones (the same kernels produce them)."""
+    w = wl.Workload("train", B=2, N=333, d_model=8 * dh, H=8, H_q=4, H_kv=2, causal=causal,
+                    dtype=dtype, seed=410)
+    _, d = _inputs(w, dev)
+    y = sqa.forward(d["X"], d["Wq"], d["Wk"], d["Wv"], d["Wo"], H=w.H, H_q=w.H_q, H_kv=w.H_kv,
+                    causal=causal)
+    y2, saved = sqa.forward_train(d["X"], d["Wq"], d["Wk"], d["Wv"], d["Wo"], H=w.H, H_q=w.H_q,
+                                  H_kv=w.H_kv, causal=causal)
+    g = _run(w, d)
+    g2 = sqa.backward(d["X"], d["Wq"], d["Wk"], d["Wv"], d["Wo"], d["dY"], H=w.H, H_q=w.H_q,
+                      H_kv=w.H_kv, causal=causal, saved=saved)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    for k, a, b in zip(GRADS, g, g2):
+        assert torch.equal(a, b), k
