@@ -14,10 +14,11 @@
 //
 // Attention backward runs as two kernels and needs no atomics:
 //  * dkdv: a workgroup owns 128 keys of one key/value head (32 per wave, held
-//    as MFMA operands in registers) and walks the query tiles of all g heads of
-//    the group, so the g-way sum of dK and dV stays in registers. Per 32x32
-//    block: S = Q K^T and dP = dO V^T (lane = key), then dV^T += dO^T P and
-//    dK^T += Q^T dS with P and dS consumed from registers as B operands.
+//    as MFMA operands in registers) and walks the query
+//    tiles of all g heads of the group, so the g-way sum of dK and dV stays in
+//    registers. Per 32-query block: S = Q K^T and dP = dO V^T (lane = key),
+//    then dV^T += dO^T P and dK^T += Q^T dS with P and dS consumed from
+//    registers as B operands.
 //  * dq: a workgroup owns 256 queries of one head (64 per wave) and walks the
 //    key tiles: S^T = K Q^T and dP^T = V dO^T (lane = query, so the row's
 //    log-sum-exp and D are per-lane scalars), then dQ^T += K^T dS^T.
@@ -28,6 +29,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "sqa_device.h"
 #include "sqa_internal.h"
@@ -199,9 +201,12 @@ struct Stage {
   }
 };
 
-// dK, dV: workgroup = (128 keys, KV head j, batch b); 4 waves x 32 keys.
-template <typename T, int D>
-__global__ __launch_bounds__(256, 2) void bwd_dkdv(BwdParams p) {
+// dK, dV: workgroup = (128*KW keys, KV head j, batch b); 4 waves x 32*KW keys.
+// With KW = 2 every Q, dO, Q^T and dO^T fragment read from LDS feeds two
+// MFMAs (one per 32-key block), which halves the LDS bytes per MFMA; the
+// accumulators of 64 keys then need one wave per SIMD.
+template <typename T, int D, int KW>
+__global__ __launch_bounds__(256, KW == 1 ? 2 : 1) void bwd_dkdv(BwdParams p) {
   using MF = Mfma<T>;
   using Frag = typename MF::Frag;
   constexpr int EPC = 16 / (int)sizeof(T);
@@ -210,28 +215,35 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv(BwdParams p) {
   constexpr int NS = D / MF::KS;   // k-steps over the head dims
   constexpr int QS = BT * RP, QTS = D * TPT;
   constexpr int BUF = 2 * QS + 2 * QTS;   // elements: Q, dO, Q^T, dO^T
+  constexpr int KPW = 32 * KW;            // keys per wave
   __shared__ __align__(16) T smem[2 * BUF];
   __shared__ __align__(16) float sv[2][2][BT];   // per buffer: lse, D
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, grp = lane >> 5;
-  const int n_kt = p.Np / 128;
-  int kt = blockIdx.x % n_kt;
-  const int bj = blockIdx.x / n_kt, j = bj % p.H_kv, b = bj / p.H_kv;
-  const int k0 = kt * 128, kw = k0 + 32 * wave;   // this wave's first key
-  const int key = kw + col;                       // this lane's key (column of S)
+  // key tile kt of every (batch, KV head) before tile kt+1: with a causal mask
+  // the first tiles see the most queries, so the heaviest work starts first
+  const int n_bj = gridDim.x / (p.Np / (4 * KPW));
+  const int kt = blockIdx.x / n_bj, bj = blockIdx.x % n_bj;
+  const int j = bj % p.H_kv, b = bj / p.H_kv;
+  const int k0 = kt * 4 * KPW, kw = k0 + KPW * wave;   // this wave's first key
 
   const T* Kh = (const T*)p.k + ((int64_t)b * p.H_kv + j) * (int64_t)p.Np * D;
   const T* Vh = (const T*)p.v + ((int64_t)b * p.H_kv + j) * (int64_t)p.Np * D;
-  Frag kf[NS], vf[NS];   // B operands of S = Q K^T and dP = dO V^T
+  Frag kf[KW][NS], vf[KW][NS];   // B operands of S = Q K^T and dP = dO V^T
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    kf[s] = *reinterpret_cast<const Frag*>(Kh + (int64_t)key * D + s * MF::KS + grp * MF::E);
-    vf[s] = *reinterpret_cast<const Frag*>(Vh + (int64_t)key * D + s * MF::KS + grp * MF::E);
-  }
-  f32x16 dk[D / 32], dv[D / 32];
+  for (int kb = 0; kb < KW; ++kb)
 #pragma unroll
-  for (int nb = 0; nb < D / 32; ++nb) { dk[nb] = f32x16{}; dv[nb] = f32x16{}; }
+    for (int s = 0; s < NS; ++s) {
+      const int64_t key = kw + 32 * kb + col;
+      kf[kb][s] = *reinterpret_cast<const Frag*>(Kh + key * D + s * MF::KS + grp * MF::E);
+      vf[kb][s] = *reinterpret_cast<const Frag*>(Vh + key * D + s * MF::KS + grp * MF::E);
+    }
+  f32x16 dk[KW][D / 32], dv[KW][D / 32];
+#pragma unroll
+  for (int kb = 0; kb < KW; ++kb)
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb) { dk[kb][nb] = f32x16{}; dv[kb][nb] = f32x16{}; }
 
   // Work list: (head, query tile) for the g heads of j; causal starts at the
   // tile holding key k0 (earlier queries see none of these keys).
@@ -283,69 +295,93 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv(BwdParams p) {
       const int qb = q0 + 32 * qs;
       // wave-uniform skips: every query before this wave's first key, or past N
       if ((p.causal && qb + 31 < kw) || qb >= p.N) continue;
-      f32x16 s = f32x16{}, dp = f32x16{};
+      f32x16 s[KW], dp[KW];
+#pragma unroll
+      for (int kb = 0; kb < KW; ++kb) { s[kb] = f32x16{}; dp[kb] = f32x16{}; }
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
         const int e = st * MF::KS + grp * MF::E;
         const Frag qa = *reinterpret_cast<const Frag*>(Qs + (32 * qs + col) * RP + e);
         const Frag oa = *reinterpret_cast<const Frag*>(Os + (32 * qs + col) * RP + e);
-        s = MF::run(qa, kf[st], s);
-        dp = MF::run(oa, vf[st], dp);
-      }
-      // rows of register r: query qb + 8*(r/4) + 4*grp + r%4; column: key
-      f32x16 pr, ds;
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int rl = 32 * qs + 8 * r4 + 4 * grp;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sv[buf][0][rl]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sv[buf][1][rl]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * r4 + e, q = qb + 8 * r4 + 4 * grp + e;
-          const bool off = key >= p.N || (p.causal && key > q);
-          const float pv = off ? 0.f : __builtin_amdgcn_exp2f(fmaf(s[r], p.c, -l4[e]));
-          pr[r] = pv;
-          ds[r] = pv * (dp[r] - d4[e]);
+        for (int kb = 0; kb < KW; ++kb) {
+          s[kb] = MF::run(qa, kf[kb][st], s[kb]);
+          dp[kb] = MF::run(oa, vf[kb][st], dp[kb]);
         }
       }
+      // register r: query qb + 8*(r/4) + 4*grp + r%4; column: key kw + 32*kb + col.
+      // Only blocks that cross the diagonal or the sequence end are masked
+      // (a wave-uniform choice); elsewhere every key is visible.
+      const bool masked = kw + KPW > p.N || (p.causal && kw + KPW - 1 > qb);
+      auto softmax_grad = [&](auto mask_on) {
 #pragma unroll
-      for (int h = 0; h < kHalves<T>; ++h) {
-        const Frag pf = frag_regs<T>(pr, h), sf = frag_regs<T>(ds, h);
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int rl = 32 * qs + 8 * r4 + 4 * grp;
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sv[buf][0][rl]);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sv[buf][1][rl]);
+#pragma unroll
+          for (int kb = 0; kb < KW; ++kb) {
+            const int key = kw + 32 * kb + col;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * r4 + e, q = qb + 8 * r4 + 4 * grp + e;
+              float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][r], p.c, -l4[e]));
+              if constexpr (decltype(mask_on)::value)
+                pv = key >= p.N || (p.causal && key > q) ? 0.f : pv;
+              s[kb][r] = pv;                          // P
+              dp[kb][r] = pv * (dp[kb][r] - d4[e]);   // dS
+            }
+          }
+        }
+      };
+      if (masked) softmax_grad(std::true_type{});
+      else softmax_grad(std::false_type{});
+#pragma unroll
+      for (int h = 0; h < kHalves<T>; ++h)
 #pragma unroll
         for (int nb = 0; nb < D / 32; ++nb) {
-          dv[nb] = MF::run(frag_runs<T, TPT>(OTs, nb * 32 + col, 32 * qs, h, grp), pf, dv[nb]);
-          dk[nb] = MF::run(frag_runs<T, TPT>(QTs, nb * 32 + col, 32 * qs, h, grp), sf, dk[nb]);
+          const Frag oa = frag_runs<T, TPT>(OTs, nb * 32 + col, 32 * qs, h, grp);
+          const Frag qa = frag_runs<T, TPT>(QTs, nb * 32 + col, 32 * qs, h, grp);
+#pragma unroll
+          for (int kb = 0; kb < KW; ++kb) {
+            dv[kb][nb] = MF::run(oa, frag_regs<T>(s[kb], h), dv[kb][nb]);
+            dk[kb][nb] = MF::run(qa, frag_regs<T>(dp[kb], h), dk[kb][nb]);
+          }
         }
-      }
     }
     store(buf ^ 1);   // every wave passed the barrier after its last read of buf ^ 1
     __syncthreads();
   }
 
   // dK^T, dV^T: lane = key, register r = head dim 32*nb + 8*(r/4) + 4*grp + r%4.
-  T* row = (T*)p.dqkv + ((int64_t)b * p.Np + key) * p.W;
-  T* dkr = row + (int64_t)p.H_q * D + j * D;
-  T* dvr = row + (int64_t)(p.H_q + p.H_kv) * D + j * D;
 #pragma unroll
-  for (int nb = 0; nb < D / 32; ++nb)
+  for (int kb = 0; kb < KW; ++kb) {
+    T* row = (T*)p.dqkv + ((int64_t)b * p.Np + kw + 32 * kb + col) * p.W;
+    T* dkr = row + (int64_t)p.H_q * D + j * D;
+    T* dvr = row + (int64_t)(p.H_q + p.H_kv) * D + j * D;
 #pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      const int c = nb * 32 + 8 * rq + 4 * grp;
-      if constexpr (sizeof(T) == 2) {
-        *reinterpret_cast<bf16x4*>(dkr + c) =
-            bf16x4{(bf16)(dk[nb][4 * rq] * p.scale), (bf16)(dk[nb][4 * rq + 1] * p.scale),
-                   (bf16)(dk[nb][4 * rq + 2] * p.scale), (bf16)(dk[nb][4 * rq + 3] * p.scale)};
-        *reinterpret_cast<bf16x4*>(dvr + c) =
-            bf16x4{(bf16)dv[nb][4 * rq], (bf16)dv[nb][4 * rq + 1], (bf16)dv[nb][4 * rq + 2],
-                   (bf16)dv[nb][4 * rq + 3]};
-      } else {
-        *reinterpret_cast<f32x4*>(dkr + c) =
-            f32x4{dk[nb][4 * rq] * p.scale, dk[nb][4 * rq + 1] * p.scale,
-                  dk[nb][4 * rq + 2] * p.scale, dk[nb][4 * rq + 3] * p.scale};
-        *reinterpret_cast<f32x4*>(dvr + c) =
-            f32x4{dv[nb][4 * rq], dv[nb][4 * rq + 1], dv[nb][4 * rq + 2], dv[nb][4 * rq + 3]};
+    for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int c = nb * 32 + 8 * rq + 4 * grp;
+        const f32x16& K_ = dk[kb][nb];
+        const f32x16& V_ = dv[kb][nb];
+        if constexpr (sizeof(T) == 2) {
+          *reinterpret_cast<bf16x4*>(dkr + c) =
+              bf16x4{(bf16)(K_[4 * rq] * p.scale), (bf16)(K_[4 * rq + 1] * p.scale),
+                     (bf16)(K_[4 * rq + 2] * p.scale), (bf16)(K_[4 * rq + 3] * p.scale)};
+          *reinterpret_cast<bf16x4*>(dvr + c) =
+              bf16x4{(bf16)V_[4 * rq], (bf16)V_[4 * rq + 1], (bf16)V_[4 * rq + 2],
+                     (bf16)V_[4 * rq + 3]};
+        } else {
+          *reinterpret_cast<f32x4*>(dkr + c) =
+              f32x4{K_[4 * rq] * p.scale, K_[4 * rq + 1] * p.scale, K_[4 * rq + 2] * p.scale,
+                    K_[4 * rq + 3] * p.scale};
+          *reinterpret_cast<f32x4*>(dvr + c) =
+              f32x4{V_[4 * rq], V_[4 * rq + 1], V_[4 * rq + 2], V_[4 * rq + 3]};
+        }
       }
-    }
+  }
 }
 
 // dQ: workgroup = (256 queries, head i, batch b); 4 waves x 64 queries.
@@ -441,15 +477,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dq(BwdParams p) {
         }
       }
       // register r: key kb + 8*(r/4) + 4*grp + r%4; column: query qw + 32*qb + col
+      // Register r holds key kb + 4*grp + o_r with o_r = 8*(r/4) + r%4. The key
+      // is visible iff o_r < lim: lim = N - kb - 4*grp, and for causal also
+      // <= q - kb - 4*grp. One compare per score; away from the diagonal and
+      // the sequence end lim exceeds every o_r.
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const int q = qw + 32 * qb + col;
+        const int base = kb + 4 * grp;
+        const int lim = p.causal ? min(p.N - base, qw + 32 * qb + col - base + 1) : p.N - base;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = kb + 8 * (r / 4) + 4 * grp + r % 4;
-          const bool off = key >= p.N || (p.causal && key > q);
-          const float pv = off ? 0.f : __builtin_amdgcn_exp2f(fmaf(s[qb][r], p.c, -lse[qb]));
-          s[qb][r] = pv * (dp[qb][r] - dvq[qb]);   // dS^T
+          const float pv = __builtin_amdgcn_exp2f(fmaf(s[qb][r], p.c, -lse[qb]));
+          s[qb][r] = 8 * (r / 4) + r % 4 < lim ? pv * (dp[qb][r] - dvq[qb]) : 0.f;   // dS^T
         }
       }
 #pragma unroll
@@ -606,7 +645,10 @@ hipError_t backward_impl(const void* x, const void* wq, const void* wk, const vo
   p.scale = (float)(1.0 / sqrt((double)D));
   if ((Np / 128) * B * H_kv > 0x7FFFFFFF || (Np / 256) * B * H_q > 0x7FFFFFFF)
     return hipErrorInvalidConfiguration;
-  bwd_dkdv<T, D><<<(unsigned)((Np / 128) * B * H_kv), 256, 0, stream>>>(p);
+  // 32 keys per wave: 64 (KW = 2) reuses each LDS fragment twice but needs
+  // one wave per SIMD, and measured slower (99.6 against 83.4 ms)
+  constexpr int KW = 1;
+  bwd_dkdv<T, D, KW><<<(unsigned)((Np / (128 * KW)) * B * H_kv), 256, 0, stream>>>(p);
   SQA_CK(hipGetLastError());
   bwd_dq<T, D><<<(unsigned)((Np / 256) * B * H_q), 256, 0, stream>>>(p);
   SQA_CK(hipGetLastError());
