@@ -143,6 +143,12 @@ struct BwdParams {
 
 constexpr int BT = 64;   // tokens per LDS tile
 
+// Line pitch (elements) of a transposed LDS tile [D][64 tokens]. The MFMA
+// operands read from it are 8-byte pieces of 32 consecutive lines (bf16), and
+// a pitch of 34 banks puts those 32 lines on 32 distinct bank pairs (34*r mod
+// 64 is a bijection onto the even banks for r < 32). fp32 lines are 68 words.
+template <typename T> constexpr int kTPitch = 68;
+
 // A operand from a transposed LDS tile (rows = head dims, pitch TP elements):
 // row r, the score rows that a B operand packed from accumulator registers
 // carries in its k-slots: for k-step `half` of a 32-row block at `base`,
@@ -196,7 +202,13 @@ struct Stage {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int x = threadIdx.x + i * 256, line = x / CPL, cc = x % CPL;
-      *reinterpret_cast<Chunk*>(dst + line * TP + cc * EPC) = r[i];
+      T* d = dst + line * TP + cc * EPC;
+      if constexpr (TP * sizeof(T) % 16 == 0) {
+        *reinterpret_cast<Chunk*>(d) = r[i];
+      } else {   // lines 8-byte aligned only: two 8-byte halves
+        reinterpret_cast<uint2*>(d)[0] = make_uint2(r[i].w[0], r[i].w[1]);
+        reinterpret_cast<uint2*>(d)[1] = make_uint2(r[i].w[2], r[i].w[3]);
+      }
     }
   }
 };
@@ -211,7 +223,7 @@ __global__ __launch_bounds__(256, KW == 1 ? 2 : 1) void bwd_dkdv(BwdParams p) {
   using Frag = typename MF::Frag;
   constexpr int EPC = 16 / (int)sizeof(T);
   constexpr int RP = D + EPC;      // pitch of row-major tiles [64 tokens][D]
-  constexpr int TPT = BT + EPC;    // pitch of transposed tiles [D][64 tokens]
+  constexpr int TPT = kTPitch<T>;  // pitch of transposed tiles [D][64 tokens]
   constexpr int NS = D / MF::KS;   // k-steps over the head dims
   constexpr int QS = BT * RP, QTS = D * TPT;
   constexpr int BUF = 2 * QS + 2 * QTS;   // elements: Q, dO, Q^T, dO^T
@@ -295,19 +307,32 @@ __global__ __launch_bounds__(256, KW == 1 ? 2 : 1) void bwd_dkdv(BwdParams p) {
       const int qb = q0 + 32 * qs;
       // wave-uniform skips: every query before this wave's first key, or past N
       if ((p.causal && qb + 31 < kw) || qb >= p.N) continue;
+      // LDS reads are issued ahead of their use: the Q and dO fragments
+      // before the S/dP MFMAs, and the Q^T/dO^T fragments and row statistics
+      // of the second half before the softmax work, which hides their latency.
+      Frag qa[NS], oa[NS];
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        const int e = st * MF::KS + grp * MF::E;
+        qa[st] = *reinterpret_cast<const Frag*>(Qs + (32 * qs + col) * RP + e);
+        oa[st] = *reinterpret_cast<const Frag*>(Os + (32 * qs + col) * RP + e);
+      }
       f32x16 s[KW], dp[KW];
 #pragma unroll
       for (int kb = 0; kb < KW; ++kb) { s[kb] = f32x16{}; dp[kb] = f32x16{}; }
 #pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        const int e = st * MF::KS + grp * MF::E;
-        const Frag qa = *reinterpret_cast<const Frag*>(Qs + (32 * qs + col) * RP + e);
-        const Frag oa = *reinterpret_cast<const Frag*>(Os + (32 * qs + col) * RP + e);
+      for (int st = 0; st < NS; ++st)
 #pragma unroll
         for (int kb = 0; kb < KW; ++kb) {
-          s[kb] = MF::run(qa, kf[kb][st], s[kb]);
-          dp[kb] = MF::run(oa, vf[kb][st], dp[kb]);
+          s[kb] = MF::run(qa[st], kf[kb][st], s[kb]);
+          dp[kb] = MF::run(oa[st], vf[kb][st], dp[kb]);
         }
+      f32x4 l4s[4], d4s[4];
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int rl = 32 * qs + 8 * r4 + 4 * grp;
+        l4s[r4] = *reinterpret_cast<const f32x4*>(&sv[buf][0][rl]);
+        d4s[r4] = *reinterpret_cast<const f32x4*>(&sv[buf][1][rl]);
       }
       // register r: query qb + 8*(r/4) + 4*grp + r%4; column: key kw + 32*kb + col.
       // Only blocks that cross the diagonal or the sequence end are masked
@@ -316,9 +341,7 @@ __global__ __launch_bounds__(256, KW == 1 ? 2 : 1) void bwd_dkdv(BwdParams p) {
       auto softmax_grad = [&](auto mask_on) {
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const int rl = 32 * qs + 8 * r4 + 4 * grp;
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sv[buf][0][rl]);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sv[buf][1][rl]);
+          const f32x4 l4 = l4s[r4], d4 = d4s[r4];
 #pragma unroll
           for (int kb = 0; kb < KW; ++kb) {
             const int key = kw + 32 * kb + col;
@@ -339,15 +362,12 @@ __global__ __launch_bounds__(256, KW == 1 ? 2 : 1) void bwd_dkdv(BwdParams p) {
 #pragma unroll
       for (int h = 0; h < kHalves<T>; ++h)
 #pragma unroll
-        for (int nb = 0; nb < D / 32; ++nb) {
-          const Frag oa = frag_runs<T, TPT>(OTs, nb * 32 + col, 32 * qs, h, grp);
-          const Frag qa = frag_runs<T, TPT>(QTs, nb * 32 + col, 32 * qs, h, grp);
+        for (int nb = 0; nb < D / 32; ++nb)
 #pragma unroll
           for (int kb = 0; kb < KW; ++kb) {
-            dv[kb][nb] = MF::run(oa, frag_regs<T>(s[kb], h), dv[kb][nb]);
-            dk[kb][nb] = MF::run(qa, frag_regs<T>(dp[kb], h), dk[kb][nb]);
+            dv[kb][nb] = MF::run(frag_runs<T, TPT>(OTs, nb * 32 + col, 32 * qs, h, grp), frag_regs<T>(s[kb], h), dv[kb][nb]);
+            dk[kb][nb] = MF::run(frag_runs<T, TPT>(QTs, nb * 32 + col, 32 * qs, h, grp), frag_regs<T>(dp[kb], h), dk[kb][nb]);
           }
-        }
     }
     store(buf ^ 1);   // every wave passed the barrier after its last read of buf ^ 1
     __syncthreads();
@@ -390,7 +410,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq(BwdParams p) {
   using MF = Mfma<T>;
   using Frag = typename MF::Frag;
   constexpr int EPC = 16 / (int)sizeof(T);
-  constexpr int RP = D + EPC, TPT = BT + EPC;
+  constexpr int RP = D + EPC, TPT = kTPitch<T>;
   constexpr int NS = D / MF::KS;
   constexpr int QB = 2;                       // 32-query blocks per wave
   constexpr int KS_ = BT * RP, KTS = D * TPT;
@@ -462,20 +482,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dq(BwdParams p) {
     for (int jb = 0; jb < BT / 32; ++jb) {
       const int kb = t * BT + 32 * jb;
       if (kb >= p.N || (p.causal && kb > qw + 63)) continue;   // wave-uniform
+      // LDS reads ahead of their use (as in bwd_dkdv): K and V fragments
+      // before the S^T/dP^T MFMAs, K^T fragments before the softmax work.
+      Frag ka[NS], va[NS];
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        const int e = st * MF::KS + grp * MF::E;
+        ka[st] = *reinterpret_cast<const Frag*>(Ks + (32 * jb + col) * RP + e);
+        va[st] = *reinterpret_cast<const Frag*>(Vs + (32 * jb + col) * RP + e);
+      }
       f32x16 s[QB], dp[QB];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) { s[qb] = f32x16{}; dp[qb] = f32x16{}; }
 #pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        const int e = st * MF::KS + grp * MF::E;
-        const Frag ka = *reinterpret_cast<const Frag*>(Ks + (32 * jb + col) * RP + e);
-        const Frag va = *reinterpret_cast<const Frag*>(Vs + (32 * jb + col) * RP + e);
+      for (int st = 0; st < NS; ++st)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-          s[qb] = MF::run(ka, qf[qb][st], s[qb]);
-          dp[qb] = MF::run(va, of[qb][st], dp[qb]);
+          s[qb] = MF::run(ka[st], qf[qb][st], s[qb]);
+          dp[qb] = MF::run(va[st], of[qb][st], dp[qb]);
         }
-      }
+
       // register r: key kb + 8*(r/4) + 4*grp + r%4; column: query qw + 32*qb + col
       // Register r holds key kb + 4*grp + o_r with o_r = 8*(r/4) + r%4. The key
       // is visible iff o_r < lim: lim = N - kb - 4*grp, and for causal also
@@ -494,11 +520,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq(BwdParams p) {
 #pragma unroll
       for (int h = 0; h < kHalves<T>; ++h)
 #pragma unroll
-        for (int nb = 0; nb < D / 32; ++nb) {
-          const Frag ka = frag_runs<T, TPT>(KTs, nb * 32 + col, 32 * jb, h, grp);
+        for (int nb = 0; nb < D / 32; ++nb)
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) dq[qb][nb] = MF::run(ka, frag_regs<T>(s[qb], h), dq[qb][nb]);
-        }
+          for (int qb = 0; qb < QB; ++qb)
+            dq[qb][nb] = MF::run(frag_runs<T, TPT>(KTs, nb * 32 + col, 32 * jb, h, grp), frag_regs<T>(s[qb], h), dq[qb][nb]);
     }
     store(buf ^ 1);
     __syncthreads();
