@@ -110,7 +110,10 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
   static_assert(INS * WAVES == 2 * K_INS && K_INS * 64 * EPC == K_ELEMS, "tile split");
   __shared__ __align__(16) T smem[NBUF * TILE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // The wave index is the same in every lane; readfirstlane lets the compiler
+  // see that, so branches on it (the masked-block test) stay real branches
+  // instead of predicated code that every step would execute.
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, grp = lane >> 5;
 
   // Renumber the workgroups so that each XCD runs logical chunks of `chunk`

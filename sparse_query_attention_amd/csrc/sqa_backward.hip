@@ -231,7 +231,8 @@ __global__ __launch_bounds__(256, KW == 1 ? 2 : 1) void bwd_dkdv(BwdParams p) {
   __shared__ __align__(16) T smem[2 * BUF];
   __shared__ __align__(16) float sv[2][2][BT];   // per buffer: lse, D
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63,
+            wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int col = lane & 31, grp = lane >> 5;
   // key tile kt of every (batch, KV head) before tile kt+1: with a causal mask
   // the first tiles see the most queries, so the heaviest work starts first
@@ -417,7 +418,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq(BwdParams p) {
   constexpr int BUF = 2 * KS_ + KTS;          // K, V, K^T
   __shared__ __align__(16) T smem[2 * BUF];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63,
+            wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int col = lane & 31, grp = lane >> 5;
   const int n_qt = p.Np / 256;
   int qt = blockIdx.x % n_qt;

@@ -263,7 +263,8 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_partial(DecParams p) {
 
   const int chunk_id = blockIdx.x, h = blockIdx.y / p.n_hg, hg = blockIdx.y % p.n_hg;
   const int b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63,
+            wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int i0 = h * p.g + hg * G;             // first query head of this group
   const int gq = min(G, p.g - hg * G);         // query heads in this group
   const int64_t pb = min(max((int64_t)p.pos[b], (int64_t)0), p.N_max - 1);

@@ -210,7 +210,8 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Rows rows, const T* wt, i
   using Frag = typename MF::Frag;
   __shared__ __align__(16) T smem[NST * C::STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63,
+            wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int col = lane & 31, grp = lane >> 5;
   // block L runs on XCD L % 8; XCD x owns row blocks x, x+8, ... in turn
   const int L = blockIdx.x, xcd = L % XCDS, k_in_xcd = L / XCDS;
