@@ -238,7 +238,8 @@ sqa_status forward_impl(const void* x, const void* Wq, const void* Wk, const voi
   const int64_t off_k = act * round256(z.q), off_v = off_k + act * round256(z.kv);
   const int64_t off_a = off_v + act * round256(z.kv), off_w1 = off_a + act * round256(z.a);
   const int64_t off_w3 = off_w1 + round256((int64_t)sqa::qkv_wt_bytes(dtype, d_model, H_q, H_kv, d_head));
-  const int64_t total = off_w3 + round256((int64_t)sqa::out_wt_bytes(dtype, H_q * d_head, d_model));
+  const int64_t off_ord = off_w3 + round256((int64_t)sqa::out_wt_bytes(dtype, H_q * d_head, d_model));
+  const int64_t total = off_ord + (lens ? round256((int64_t)sqa::attention_order_bytes(B, N, H_q)) : 0);
   hipMemPool_t pool;
   SQA_TRY(pool_for(stream, &pool));
   void* ws = nullptr;
@@ -247,6 +248,7 @@ sqa_status forward_impl(const void* x, const void* Wq, const void* Wk, const voi
   char* base = (char*)ws;
   void *q = base, *k = base + off_k, *vt = base + off_v, *a = base + off_a;
   void *w1 = base + off_w1, *w3 = base + off_w3;
+  int32_t* order = lens ? (int32_t*)(base + off_ord) : nullptr;
   float* lse = nullptr;
   if (saved) {
     const sqa::SavedLayout S = sqa::saved_layout((int64_t)es, B, N, z.Np, H_q, H_kv, d_head);
@@ -261,7 +263,7 @@ sqa_status forward_impl(const void* x, const void* Wq, const void* Wk, const voi
     e = sqa::launch_fill_cache(dtype, k, vt, kc, vc, B, H_kv, N, z.Np, N_max, d_head, stream);
   if (e == hipSuccess)
     e = sqa::launch_attention(dtype, q, k, vt, a, B, N, z.Np, H_q, H_kv, d_head, causal != 0, lens,
-                              stream, lse);
+                              stream, lse, order);
   if (e == hipSuccess)
     e = sqa::launch_output_projection(dtype, a, Wo, w3, out, B * N, H_q * d_head, d_model, lens, N,
                                       stream);

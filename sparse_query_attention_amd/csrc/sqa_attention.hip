@@ -57,6 +57,7 @@ struct AttnParams {
   const void* q; const void* k; const void* vt; void* a;
   const int32_t* lens;   // null, or each sequence's length (clamped into [0, N])
   float* lse;            // null, or [B, H_q, Np]: base-2 log-sum-exp of each row's scaled scores
+  const int32_t* order;  // null, or the logical work item of each workgroup (lpt_order)
   int N, Np, H_q, H_kv, g, G, n_sub, q_per_wg, n_qt, causal;
   int chunk, remap_end;   // XCD-aware workgroup order (see the kernel's block decode)
   float c;  // log2(e) / sqrt(d_head)
@@ -96,6 +97,66 @@ template <int PER, int MAXN> __device__ inline void wait_vmcnt_tiles(int n) {
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
+// A logical work item: query tile qt (heaviest first when causal), head group
+// sub, key/value head h, sequence b.
+struct WorkItem { int qt, sub, h, b; };
+
+__device__ inline WorkItem decode_item(const AttnParams& p, int blk) {
+  WorkItem w;
+  w.qt = blk % p.n_qt;
+  blk /= p.n_qt;
+  if (p.causal) w.qt = p.n_qt - 1 - w.qt;
+  w.sub = blk % p.n_sub;
+  blk /= p.n_sub;
+  w.h = blk % p.H_kv;
+  w.b = blk / p.H_kv;
+  return w;
+}
+
+// Keys a work item processes (each of its waves walks them all); 0 for a tile
+// wholly in its sequence's padding.
+__device__ inline int item_keys(const AttnParams& p, const WorkItem& w) {
+  const int L = p.lens ? min(max(p.lens[w.b], 0), p.N) : p.N;
+  const int q0 = w.qt * p.q_per_wg;
+  if (q0 >= L) return 0;
+  return p.causal ? min(L, q0 + p.q_per_wg) : L;
+}
+
+constexpr int LPT_MAX = 8192;   // work items the one-workgroup sort holds in LDS
+
+// Longest-processing-time order of a ragged launch: one workgroup bitonic-sorts
+// the grid's logical work items by their key counts, largest first (ties by
+// index), so that the dispatcher starts the long tiles first and the short ones
+// fill the tail. Sequences of different lengths otherwise leave CUs idle at the
+// end of the grid.
+__global__ __launch_bounds__(1024) void lpt_order(AttnParams p, int grid, int n_pow2,
+                                                  int32_t* order) {
+  __shared__ int key[LPT_MAX], val[LPT_MAX];
+  for (int i = threadIdx.x; i < n_pow2; i += 1024) {
+    key[i] = i < grid ? item_keys(p, decode_item(p, i)) : -1;
+    val[i] = i;
+  }
+  __syncthreads();
+  for (int k = 2; k <= n_pow2; k <<= 1)
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      for (int i = threadIdx.x; i < n_pow2; i += 1024) {
+        const int l = i ^ jj;
+        if (l > i) {
+          // descending by key, ascending by index among equal keys
+          const bool i_first = key[i] > key[l] || (key[i] == key[l] && val[i] < val[l]);
+          const bool want_i_first = (i & k) == 0;
+          if (i_first != want_i_first) {
+            const int tk = key[i], tv = val[i];
+            key[i] = key[l]; val[i] = val[l];
+            key[l] = tk; val[l] = tv;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  for (int i = threadIdx.x; i < grid; i += 1024) order[i] = val[i];
+}
+
 template <typename T, int D, int WAVES>
 __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
   using MF = Mfma<T>;
@@ -124,17 +185,16 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
   // in reverse order on odd rounds: the assignment to XCDs is static, and with
   // causal work falling linearly along the chunks this gives every XCD the same
   // total. Blocks from remap_end on keep their index.
+  // A ragged launch may instead take its work items in a precomputed order.
   int blk = blockIdx.x;
-  if (blk < p.remap_end) {
+  if (p.order) {
+    blk = p.order[blk];
+  } else if (blk < p.remap_end) {
     const int xcd = blk % XCDS, s = blk / XCDS, r = s / p.chunk;
     blk = (r * XCDS + ((r & 1) ? XCDS - 1 - xcd : xcd)) * p.chunk + s % p.chunk;
   }
-  int qt = blk % p.n_qt;
-  blk /= p.n_qt;
-  if (p.causal) qt = p.n_qt - 1 - qt;   // heaviest query tiles first
-  const int sub = blk % p.n_sub;
-  blk /= p.n_sub;
-  const int h = blk % p.H_kv, b = blk / p.H_kv;
+  const WorkItem item = decode_item(p, blk);   // causal: heaviest query tiles first
+  const int qt = item.qt, sub = item.sub, h = item.h, b = item.b;
   const int waves_per_head = WAVES / p.G;
   const int head = h * p.g + sub * p.G + wave / waves_per_head;
   const int q0 = qt * p.q_per_wg;
@@ -534,14 +594,25 @@ void plan_order(AttnParams& p, int64_t grid, int64_t cus) {
 
 template <int WAVES>
 hipError_t dispatch(sqa_dtype dt, int64_t d_head, AttnParams& p, int64_t grid, int64_t cus,
-                    hipStream_t stream) {
+                    int32_t* order_ws, hipStream_t stream) {
   if (grid <= 0 || grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   plan_order<WAVES>(p, grid, cus);
   // Sequences of different lengths break the chunk order's premise (equal
   // streams whose work falls linearly), and its static XCD assignment then
-  // unbalances the XCDs: plain round-robin spreads any work profile evenly
-  // (4.8 against 5.5 ms on a batch of 8 sequences of 9k-28k tokens).
-  if (p.lens) p.remap_end = 0;
+  // unbalances the XCDs (5.5 against 4.8 ms for plain round-robin on a batch of
+  // 8 sequences of 9k-28k tokens). They run longest first instead.
+  p.order = nullptr;
+  if (p.lens) {
+    p.remap_end = 0;
+    if (order_ws && grid <= LPT_MAX) {
+      int n = 1;
+      while (n < grid) n <<= 1;
+      lpt_order<<<1, 1024, 0, stream>>>(p, (int)grid, n, order_ws);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      p.order = order_ws;
+    }
+  }
   if (dt == SQA_DTYPE_BF16)
     return d_head == 64 ? run<bf16, 64, WAVES>(p, (unsigned)grid, stream)
                         : run<bf16, 32, WAVES>(p, (unsigned)grid, stream);
@@ -573,10 +644,15 @@ int cu_count(hipStream_t stream) {
 // workgroup of a non-causal grid costs the same, and the smaller ones pack
 // that tail round over more CUs. Causal grids, dispatched heaviest first,
 // fill their tail with short workgroups.
+size_t attention_order_bytes(int64_t B, int64_t N, int64_t H_q) {
+  // a bound on the grid: query tiles of at least 64 rows, at most H_q head groups
+  return (size_t)(B * ((N + 63) / 64) * H_q) * sizeof(int32_t);
+}
+
 hipError_t launch_attention(sqa_dtype dt, const void* q, const void* k, const void* vt, void* a,
                             int64_t B, int64_t N, int64_t Np, int64_t H_q, int64_t H_kv,
                             int64_t d_head, bool causal, const int32_t* lens, hipStream_t stream,
-                            float* lse) {
+                            float* lse, int32_t* order_ws) {
   AttnParams p;
   p.q = q; p.k = k; p.vt = vt; p.a = a; p.lens = lens; p.lse = lse;
   p.N = (int)N; p.Np = (int)Np; p.H_q = (int)H_q; p.H_kv = (int)H_kv;
@@ -589,9 +665,9 @@ hipError_t launch_attention(sqa_dtype dt, const void* q, const void* k, const vo
   const int64_t tail = grid8 % cus;
   if (!causal && tail != 0 && 2 * tail <= cus) {
     const int64_t grid4 = plan<4>(p, B, H_kv);
-    return dispatch<4>(dt, d_head, p, grid4, cus, stream);
+    return dispatch<4>(dt, d_head, p, grid4, cus, order_ws, stream);
   }
-  return dispatch<8>(dt, d_head, p8, grid8, cus, stream);
+  return dispatch<8>(dt, d_head, p8, grid8, cus, order_ws, stream);
 }
 
 }  // namespace sqa

@@ -30,10 +30,13 @@ hipError_t launch_qkv_projection(sqa_dtype dt, const void* x, const void* wq, co
 // Step 2: attention core into a [B*N, H_q*d]; keys end at each sequence's
 // length, and rows at or past it are zero. With lse, also each row's base-2
 // log-sum-exp of the scaled scores, [B, H_q, Np] fp32 (+inf on padding rows).
+// With lens and order_ws (device scratch of attention_order_bytes()), the
+// workgroups take the work items longest first.
+size_t attention_order_bytes(int64_t B, int64_t N, int64_t H_q);
 hipError_t launch_attention(sqa_dtype dt, const void* q, const void* k, const void* vt, void* a,
                             int64_t B, int64_t N, int64_t Np, int64_t H_q, int64_t H_kv,
                             int64_t d_head, bool causal, const int32_t* lens, hipStream_t stream,
-                            float* lse = nullptr);
+                            float* lse = nullptr, int32_t* order_ws = nullptr);
 
 // Step 3: out [M, d_model] = a [M, K] * wo [K, d_model]. wt is device scratch of
 // out_wt_bytes() for the transposed weights. With lens, row m is token m % seq_n
