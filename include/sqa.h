@@ -151,9 +151,10 @@ sqa_status sqa_decode_step(const void* x_new, const void* Wq, const void* Wk, co
  *
  * sqa_training_saved_bytes - size of the activation buffer that
  * sqa_forward_train fills and sqa_backward reads: Q, K, V^T (the layouts of
- * sqa_qkv_projection), A [B*N, H_q*d_head] and each row's softmax
- * log-sum-exp (fp32), about elem_size*(B*Np*(H_q + 2*H_kv)*d_head +
- * B*N*H_q*d_head) + 4*B*H_q*Np bytes. Returns 0 for an invalid shape or dtype.
+ * sqa_qkv_projection), A [B*N, H_q*d_head], each row's softmax log-sum-exp
+ * (fp32) and A before its rounding to dtype (fp32), about
+ * elem_size*(B*Np*(H_q + 2*H_kv)*d_head + B*N*H_q*d_head) + 4*B*H_q*Np
+ * + 4*B*N*H_q*d_head bytes. Returns 0 for an invalid shape or dtype.
  */
 size_t sqa_training_saved_bytes(int64_t B, int64_t N, int64_t H_q, int64_t H_kv, int64_t d_head,
                                 sqa_dtype dtype);
@@ -187,8 +188,9 @@ sqa_status sqa_forward_train(const void* x, const void* Wq, const void* Wk, cons
  * `saved`, as sqa_forward_train wrote them for the same x, weights, shapes and
  * causal flag; if saved is NULL they are recomputed (saved_bytes is ignored).
  * Arithmetic: dA, dQ, dK, dV and the five outputs are each rounded once to
- * `dtype`; P, dS and the row sums are fp32; rowsum(dA_i * O_i) uses A as
- * stored. The result does not depend on the launch (no atomics).
+ * `dtype`; P, dS and the row sums are fp32; rowsum(dA_i * O_i) uses the
+ * attention output before its rounding (fp32). The result does not depend on
+ * the launch (no atomics).
  * Workspace: about elem_size * B*Np * (8*(H_q + H_kv)*d_head + 2*d_model)
  * bytes (less the saved activations when `saved` is given), 4*B*H_q*Np bytes
  * of fp32 row sums, and the fp32 split-K partial sums of the weight gradients,

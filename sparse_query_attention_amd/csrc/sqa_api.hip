@@ -250,11 +250,13 @@ sqa_status forward_impl(const void* x, const void* Wq, const void* Wk, const voi
   void *w1 = base + off_w1, *w3 = base + off_w3;
   int32_t* order = lens ? (int32_t*)(base + off_ord) : nullptr;
   float* lse = nullptr;
+  float* o32 = nullptr;
   if (saved) {
     const sqa::SavedLayout S = sqa::saved_layout((int64_t)es, B, N, z.Np, H_q, H_kv, d_head);
     char* sv = (char*)saved;
     q = sv + S.q; k = sv + S.k; vt = sv + S.vt; a = sv + S.a;
     lse = (float*)(sv + S.lse);
+    o32 = (float*)(sv + S.o32);
   }
 
   e = sqa::launch_qkv_projection(dtype, x, Wq, Wk, Wv, w1, q, k, vt, B, N, z.Np, d_model, H_q,
@@ -263,7 +265,7 @@ sqa_status forward_impl(const void* x, const void* Wq, const void* Wk, const voi
     e = sqa::launch_fill_cache(dtype, k, vt, kc, vc, B, H_kv, N, z.Np, N_max, d_head, stream);
   if (e == hipSuccess)
     e = sqa::launch_attention(dtype, q, k, vt, a, B, N, z.Np, H_q, H_kv, d_head, causal != 0, lens,
-                              stream, lse, order);
+                              stream, lse, order, o32);
   if (e == hipSuccess)
     e = sqa::launch_output_projection(dtype, a, Wo, w3, out, B * N, H_q * d_head, d_model, lens, N,
                                       stream);

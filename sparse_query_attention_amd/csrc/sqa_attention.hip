@@ -58,6 +58,7 @@ struct AttnParams {
   const int32_t* lens;   // null, or each sequence's length (clamped into [0, N])
   float* lse;            // null, or [B, H_q, Np]: base-2 log-sum-exp of each row's scaled scores
   const int32_t* order;  // null, or the logical work item of each workgroup (lpt_order)
+  float* o32;            // null, or [B*N, H_q*d]: the output before its rounding to T (fp32)
   int N, Np, H_q, H_kv, g, G, n_sub, q_per_wg, n_qt, causal;
   int chunk, remap_end;   // XCD-aware workgroup order (see the kernel's block decode)
   float c;  // log2(e) / sqrt(d_head)
@@ -219,6 +220,8 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
             T* dst = arow + nb * 32 + 8 * rq + 4 * grp;
             if constexpr (sizeof(T) == 2) *reinterpret_cast<bf16x4*>(dst) = bf16x4{};
             else *reinterpret_cast<f32x4*>(dst) = f32x4{};
+            if (p.o32)
+              *reinterpret_cast<f32x4*>(p.o32 + (arow - (T*)p.a) + nb * 32 + 8 * rq + 4 * grp) = f32x4{};
           }
       }
     }
@@ -560,6 +563,8 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
           } else {
             *reinterpret_cast<f32x4*>(dst) = f32x4{v0, v1, v2, v3};
           }
+          if (p.o32)   // the unrounded output, for the backward pass's rowsum(dO * O)
+            *reinterpret_cast<f32x4*>(p.o32 + (dst - (T*)p.a)) = f32x4{v0, v1, v2, v3};
         }
     }
   }
@@ -652,9 +657,9 @@ size_t attention_order_bytes(int64_t B, int64_t N, int64_t H_q) {
 hipError_t launch_attention(sqa_dtype dt, const void* q, const void* k, const void* vt, void* a,
                             int64_t B, int64_t N, int64_t Np, int64_t H_q, int64_t H_kv,
                             int64_t d_head, bool causal, const int32_t* lens, hipStream_t stream,
-                            float* lse, int32_t* order_ws) {
+                            float* lse, int32_t* order_ws, float* o32) {
   AttnParams p;
-  p.q = q; p.k = k; p.vt = vt; p.a = a; p.lens = lens; p.lse = lse;
+  p.q = q; p.k = k; p.vt = vt; p.a = a; p.lens = lens; p.lse = lse; p.o32 = o32;
   p.N = (int)N; p.Np = (int)Np; p.H_q = (int)H_q; p.H_kv = (int)H_kv;
   p.g = (int)(H_q / H_kv);
   p.causal = causal ? 1 : 0;

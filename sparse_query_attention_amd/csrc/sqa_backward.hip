@@ -89,9 +89,12 @@ __global__ __launch_bounds__(256) void concat_weights(const T* wq, const T* wk, 
   w[i] = v;
 }
 
-// D[b, i, t] = sum_c dO[b, i, t, c] * A[b, t, i*d + c] for t < N, 0 on padding rows.
+// D[b, i, t] = sum_c dO[b, i, t, c] * O[b, t, i*d + c] for t < N, 0 on padding
+// rows, with O the attention output before its rounding (fp32). The rounded A
+// would put a relative 2^-9 error into D, and dS = P (dP - D) keeps it even
+// where dP - D cancels (short sequences).
 template <typename T, int D>
-__global__ __launch_bounds__(256) void dvec_kernel(const T* dO, const T* a, float* dvec, int N,
+__global__ __launch_bounds__(256) void dvec_kernel(const T* dO, const float* a, float* dvec, int N,
                                                    int64_t Np, int H_q, int64_t rows) {
   const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (x >= rows) return;
@@ -99,7 +102,7 @@ __global__ __launch_bounds__(256) void dvec_kernel(const T* dO, const T* a, floa
   float s = 0.f;
   if (t < N) {
     const T* o = dO + x * D;
-    const T* av = a + ((b * N + t) * H_q + i) * D;
+    const float* av = a + ((b * N + t) * H_q + i) * D;
 #pragma unroll 8
     for (int c = 0; c < D; ++c) s = fmaf(f32_of(o[c]), f32_of(av[c]), s);
   }
@@ -578,7 +581,8 @@ SavedLayout saved_layout(int64_t es, int64_t B, int64_t N, int64_t Np, int64_t H
   S.vt = S.k + r(es * B * H_kv * Np * d);
   S.a = S.vt + r(es * B * H_kv * Np * d);
   S.lse = S.a + r(es * B * N * H_q * d);
-  S.total = S.lse + r(4 * B * H_q * Np);
+  S.o32 = S.lse + r(4 * B * H_q * Np);
+  S.total = S.o32 + r(4 * B * N * H_q * d);
   return S;
 }
 
@@ -586,7 +590,7 @@ namespace {
 
 // Byte offsets of the backward workspace regions.
 struct BwdLayout {
-  int64_t q, k, vt, a, lse, wt, dO, dvec, qt, kt, v, dOt, dqkv, dqkvT, xT, wall, aT, dyT, part;
+  int64_t q, k, vt, a, lse, o32, wt, dO, dvec, qt, kt, v, dOt, dqkv, dqkvT, xT, wall, aT, dyT, part;
   int64_t total;
 };
 
@@ -603,16 +607,17 @@ BwdLayout bwd_layout(int64_t es, int64_t B, int64_t N, int64_t Np, int64_t d_mod
   const int64_t f = saved ? 0 : 1;
   const int64_t sizes[] = {
       f * es * B * H_q * Np * d, f * es * B * H_kv * Np * d, f * es * B * H_kv * Np * d,
-      f * es * B * N * H_q * d, f * 4 * B * H_q * Np,
+      f * es * B * N * H_q * d, f * 4 * B * H_q * Np, f * 4 * B * N * H_q * d,
       f * (int64_t)qkv_wt_bytes(es == 2 ? SQA_DTYPE_BF16 : SQA_DTYPE_FP32, d_model, H_q, H_kv, d),
       es * B * H_q * Np * d, 4 * B * H_q * Np, es * B * H_q * Np * d, es * B * H_kv * Np * d,
       es * B * H_kv * Np * d, es * B * H_q * Np * d, es * T * W, es * T * W, es * d_model * T,
       es * d_model * W, es * H_q * d * T, es * d_model * T, part};
   BwdLayout L;
-  int64_t* out[] = {&L.q, &L.k, &L.vt, &L.a, &L.lse, &L.wt, &L.dO, &L.dvec, &L.qt, &L.kt, &L.v,
-                    &L.dOt, &L.dqkv, &L.dqkvT, &L.xT, &L.wall, &L.aT, &L.dyT, &L.part};
+  int64_t* out[] = {&L.q, &L.k, &L.vt, &L.a, &L.lse, &L.o32, &L.wt, &L.dO, &L.dvec, &L.qt, &L.kt,
+                    &L.v, &L.dOt, &L.dqkv, &L.dqkvT, &L.xT, &L.wall, &L.aT, &L.dyT, &L.part};
+  static_assert(sizeof(out) / sizeof(out[0]) == sizeof(sizes) / sizeof(sizes[0]), "regions");
   int64_t off = 0;
-  for (int x = 0; x < 19; ++x) {
+  for (int x = 0; x < (int)(sizeof(sizes) / sizeof(sizes[0])); ++x) {
     *out[x] = off;
     off += r256(sizes[x]);
   }
@@ -631,11 +636,13 @@ hipError_t backward_impl(const void* x, const void* wq, const void* wk, const vo
   const int64_t wq_w = H_q * D, wkv_w = H_kv * D, W = wq_w + 2 * wkv_w, TT = B * Np;
   void *q = ws + L.q, *k = ws + L.k, *vt = ws + L.vt, *a = ws + L.a, *wt = ws + L.wt;
   float* lse = (float*)(ws + L.lse);
+  float* o32 = (float*)(ws + L.o32);
   if (saved) {
     const SavedLayout S = saved_layout(sizeof(T), B, N, Np, H_q, H_kv, D);
     char* sv = const_cast<char*>(saved);   // read only below
     q = sv + S.q; k = sv + S.k; vt = sv + S.vt; a = sv + S.a;
     lse = (float*)(sv + S.lse);
+    o32 = (float*)(sv + S.o32);
   }
   float* dvec = (float*)(ws + L.dvec);
   void *dO = ws + L.dO, *qt = ws + L.qt, *kt = ws + L.kt, *v = ws + L.v, *dOt = ws + L.dOt;
@@ -648,14 +655,15 @@ hipError_t backward_impl(const void* x, const void* wq, const void* wk, const vo
   if (!saved) {
     SQA_CK(launch_qkv_projection(dt, x, wq, wk, wv, wt, q, k, vt, B, N, Np, d_model, H_q, H_kv, D,
                                  nullptr, stream));
-    SQA_CK(launch_attention(dt, q, k, vt, a, B, N, Np, H_q, H_kv, D, causal, nullptr, stream, lse));
+    SQA_CK(launch_attention(dt, q, k, vt, a, B, N, Np, H_q, H_kv, D, causal, nullptr, stream, lse,
+                            nullptr, o32));
   }
   // dO = dY Wo^T in the head layout of q (Wo [H_q*d, d_model] is W^T of that product)
   SQA_CK(launch_gemm_heads(dt, dy, wo, dO, B, N, Np, d_model, wq_w, D, stream));
   {
     const int64_t rows = B * H_q * Np;
     dvec_kernel<T, D><<<(unsigned)((rows + 255) / 256), 256, 0, stream>>>(
-        (const T*)dO, (const T*)a, dvec, (int)N, Np, (int)H_q, rows);
+        (const T*)dO, o32, dvec, (int)N, Np, (int)H_q, rows);
     SQA_CK(hipGetLastError());
   }
   // head-dim-major copies for the contractions over tokens, V row-major

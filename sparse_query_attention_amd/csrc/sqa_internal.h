@@ -29,14 +29,16 @@ hipError_t launch_qkv_projection(sqa_dtype dt, const void* x, const void* wq, co
 
 // Step 2: attention core into a [B*N, H_q*d]; keys end at each sequence's
 // length, and rows at or past it are zero. With lse, also each row's base-2
-// log-sum-exp of the scaled scores, [B, H_q, Np] fp32 (+inf on padding rows).
+// log-sum-exp of the scaled scores, [B, H_q, Np] fp32 (+inf on padding rows);
+// with o32, also the output before its rounding, [B*N, H_q*d] fp32.
 // With lens and order_ws (device scratch of attention_order_bytes()), the
 // workgroups take the work items longest first.
 size_t attention_order_bytes(int64_t B, int64_t N, int64_t H_q);
 hipError_t launch_attention(sqa_dtype dt, const void* q, const void* k, const void* vt, void* a,
                             int64_t B, int64_t N, int64_t Np, int64_t H_q, int64_t H_kv,
                             int64_t d_head, bool causal, const int32_t* lens, hipStream_t stream,
-                            float* lse = nullptr, int32_t* order_ws = nullptr);
+                            float* lse = nullptr, int32_t* order_ws = nullptr,
+                            float* o32 = nullptr);
 
 // Step 3: out [M, d_model] = a [M, K] * wo [K, d_model]. wt is device scratch of
 // out_wt_bytes() for the transposed weights. With lens, row m is token m % seq_n
@@ -63,9 +65,10 @@ hipError_t launch_gemm_splitk(sqa_dtype dt, const void* a, const void* wt, float
                               int64_t K, int64_t ncols, const SplitK& sk, hipStream_t stream);
 
 // Activations a training forward keeps for the backward pass, at these byte
-// offsets of one buffer: q, k, vt (the step-1 layouts), a [B*N, H_q*d] and the
-// per-row base-2 log-sum-exp [B, H_q, Np] fp32.
-struct SavedLayout { int64_t q, k, vt, a, lse, total; };
+// offsets of one buffer: q, k, vt (the step-1 layouts), a [B*N, H_q*d], the
+// per-row base-2 log-sum-exp [B, H_q, Np] fp32, and the attention output
+// before rounding, o32 [B*N, H_q*d] fp32.
+struct SavedLayout { int64_t q, k, vt, a, lse, o32, total; };
 SavedLayout saved_layout(int64_t es, int64_t B, int64_t N, int64_t Np, int64_t H_q, int64_t H_kv,
                          int64_t d);
 

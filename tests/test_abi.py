@@ -233,10 +233,10 @@ def test_backward_of_an_empty_batch_is_a_no_op():
 def test_training_saved_bytes_and_forward_train_validate():
     lib = _lib.load()
     n = lib.sqa_training_saved_bytes(2, 100, 4, 2, 32, _lib.SQA_DTYPE_BF16)
-    # q + k + vt (Np = 256) + a (N = 100) in bf16, and the fp32 row statistics
+    # q + k + vt (Np = 256) + a (N = 100) in bf16, the fp32 row statistics and fp32 a
     want = sum((x + 255) // 256 * 256 for x in (2 * 2 * 256 * 4 * 32, 2 * 2 * 256 * 2 * 32,
                                                2 * 2 * 256 * 2 * 32, 2 * 2 * 100 * 4 * 32,
-                                               4 * 2 * 4 * 256))
+                                               4 * 2 * 4 * 256, 4 * 2 * 100 * 4 * 32))
     assert n == want
     assert lib.sqa_training_saved_bytes(2, 100, 4, 3, 32, _lib.SQA_DTYPE_BF16) == 0
     args = lambda saved, nb: (FAKE, FAKE + 0x1000000, FAKE + 0x2000000, FAKE + 0x3000000,
