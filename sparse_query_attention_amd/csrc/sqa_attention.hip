@@ -74,9 +74,6 @@ template <> __device__ inline int swz<16>(int r) { return r & 15; }
 template <> __device__ inline int swz<8>(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 template <> __device__ inline int swz<4>(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
 
-// In-tile key index <-> LDS row: swap bits 2 and 3 (an involution).
-__device__ inline int swap23(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
-
 __device__ inline float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
 // Wait until at most N of this wave's vector-memory operations are outstanding

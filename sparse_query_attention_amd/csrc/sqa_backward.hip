@@ -44,8 +44,9 @@ __device__ inline float f32_of(bf16 x) { return (float)x; }
 
 // dst[b][c][r] = src[b][r][c] for r < r_valid, 0 for r_valid <= r < r_total;
 // c < C. 64x64 tiles through LDS, 16-byte global accesses on both sides
-// (C and r_total are multiples of 16 / sizeof(T)).
-template <typename T>
+// (C and r_total are multiples of 16 / sizeof(T)). With PERM the rows land in
+// swap23 order within each group of 16: dst[b][c][swap23(r)] = src[b][r][c].
+template <typename T, bool PERM>
 __global__ __launch_bounds__(256) void transpose_kernel(const T* src, int64_t src_bs, int64_t src_ld,
                                                         int r_valid, int r_total, T* dst,
                                                         int64_t dst_bs, int64_t dst_ld, int C) {
@@ -62,7 +63,7 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* src, int64_t sr
       v = *reinterpret_cast<const Chunk*>(src + (int64_t)(r0 + r) * src_ld + c0 + cc);
     const T* e = reinterpret_cast<const T*>(&v);
 #pragma unroll
-    for (int k = 0; k < EPC; ++k) tile[cc + k][r] = e[k];   // tile[c][r]
+    for (int k = 0; k < EPC; ++k) tile[cc + k][PERM ? swap23(r) : r] = e[k];   // tile[c][r]
   }
   __syncthreads();
   for (int i = threadIdx.x; i < 64 * CPR; i += 256) {
@@ -130,12 +131,12 @@ __global__ __launch_bounds__(256) void reduce_splits(const float* part, int n_sp
 
 struct BwdParams {
   const void* q;     // [B, H_q, Np, d]
-  const void* qt;    // [B, H_q, d, Np]
+  const void* qt;    // [B, H_q, d, Np], tokens in swap23 order
   const void* k;     // [B, H_kv, Np, d]
-  const void* kt;    // [B, H_kv, d, Np]
+  const void* kt;    // [B, H_kv, d, Np], tokens in swap23 order
   const void* v;     // [B, H_kv, Np, d]
   const void* dO;    // [B, H_q, Np, d]
-  const void* dOt;   // [B, H_q, d, Np]
+  const void* dOt;   // [B, H_q, d, Np], tokens in swap23 order
   const float* lse;  // [B, H_q, Np], base 2, of the scaled scores
   const float* dvec; // [B, H_q, Np]
   void* dqkv;        // [B, Np, W]: dQ heads, then dK heads, then dV heads
@@ -146,26 +147,26 @@ struct BwdParams {
 
 constexpr int BT = 64;   // tokens per LDS tile
 
-// Line pitch (elements) of a transposed LDS tile [D][64 tokens]. The MFMA
-// operands read from it are 8-byte pieces of 32 consecutive lines (bf16), and
-// a pitch of 34 banks puts those 32 lines on 32 distinct bank pairs (34*r mod
-// 64 is a bijection onto the even banks for r < 32). fp32 lines are 68 words.
-template <typename T> constexpr int kTPitch = 68;
+// Line pitch (elements) of a transposed LDS tile [D][64 tokens]. The bf16
+// MFMA operands read from it are 16-byte pieces of 32 consecutive lines; a
+// pitch of 144 bytes puts any 16 consecutive lines at 16 distinct 16-byte bank
+// groups (9*r mod 16 is a bijection), so the reads are free of bank conflicts.
+// fp32 lines are 68 words.
+template <typename T> constexpr int kTPitch = sizeof(T) == 2 ? 72 : 68;
 
-// A operand from a transposed LDS tile (rows = head dims, pitch TP elements):
-// row r, the score rows that a B operand packed from accumulator registers
-// carries in its k-slots: for k-step `half` of a 32-row block at `base`,
-// k-group grp holds rows base + 16*half + 8*(e/4) + 4*grp + e%4, e = 0..7.
+// A operand from a transposed LDS tile (rows = head dims, pitch TP elements,
+// tokens in swap23 order): row r, the score rows that a B operand packed from
+// accumulator registers carries in its k-slots. For k-step `half` of a 32-row
+// block at `base`, k-group grp holds rows base + 16*half + 8*(e/4) + 4*grp +
+// e%4 (e = 0..7), which sit at positions base + 16*half + 8*grp + e.
 template <typename T, int TP>
 __device__ inline typename Mfma<T>::Frag frag_runs(const T* tile, int r, int base, int half, int grp) {
   if constexpr (sizeof(T) == 2) {
-    const T* p = tile + r * TP + base + 16 * half + 4 * grp;
-    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
-    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 8);
-    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return *reinterpret_cast<const bf16x8*>(tile + r * TP + base + 16 * half + 8 * grp);
   } else {
-    // fp32: k-step st = half (0..15) holds row base + 8*(st/4) + 4*grp + st%4
-    return tile[r * TP + base + 8 * (half / 4) + 4 * grp + half % 4];
+    // fp32: k-step st = half (0..15) holds row base + 8*(st/4) + 4*grp + st%4,
+    // at position base + 16*(st/8) + 8*grp + st%8
+    return tile[r * TP + base + 16 * (half / 8) + 8 * grp + half % 8];
   }
 }
 
@@ -558,15 +559,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dq(BwdParams p) {
   }
 }
 
-template <typename T>
+template <typename T, bool PERM = false>
 hipError_t transpose(const void* src, int64_t src_bs, int64_t src_ld, int64_t r_valid,
                      int64_t r_total, void* dst, int64_t dst_bs, int64_t dst_ld, int64_t C,
                      int64_t nbatch, hipStream_t stream) {
   const int64_t ry = (r_total + 63) / 64;
   if (nbatch > 65535 || ry > 65535) return hipErrorInvalidConfiguration;
+  if (PERM && r_total % 64) return hipErrorInvalidValue;   // the permutation stays within 64-row tiles
   const dim3 grid((unsigned)((C + 63) / 64), (unsigned)ry, (unsigned)nbatch);
-  transpose_kernel<T><<<grid, 256, 0, stream>>>((const T*)src, src_bs, src_ld, (int)r_valid,
-                                                (int)r_total, (T*)dst, dst_bs, dst_ld, (int)C);
+  transpose_kernel<T, PERM><<<grid, 256, 0, stream>>>((const T*)src, src_bs, src_ld, (int)r_valid,
+                                                      (int)r_total, (T*)dst, dst_bs, dst_ld, (int)C);
   return hipGetLastError();
 }
 
@@ -666,11 +668,12 @@ hipError_t backward_impl(const void* x, const void* wq, const void* wk, const vo
         (const T*)dO, o32, dvec, (int)N, Np, (int)H_q, rows);
     SQA_CK(hipGetLastError());
   }
-  // head-dim-major copies for the contractions over tokens, V row-major
-  SQA_CK(transpose<T>(q, Np * D, D, Np, Np, qt, D * Np, Np, D, B * H_q, stream));
-  SQA_CK(transpose<T>(k, Np * D, D, Np, Np, kt, D * Np, Np, D, B * H_kv, stream));
+  // head-dim-major copies for the contractions over tokens (tokens in swap23
+  // order, the k-order of operands packed from accumulators), V row-major
+  SQA_CK((transpose<T, true>(q, Np * D, D, Np, Np, qt, D * Np, Np, D, B * H_q, stream)));
+  SQA_CK((transpose<T, true>(k, Np * D, D, Np, Np, kt, D * Np, Np, D, B * H_kv, stream)));
   SQA_CK(transpose<T>(vt, D * Np, Np, D, D, v, Np * D, D, Np, B * H_kv, stream));
-  SQA_CK(transpose<T>(dO, Np * D, D, Np, Np, dOt, D * Np, Np, D, B * H_q, stream));
+  SQA_CK((transpose<T, true>(dO, Np * D, D, Np, Np, dOt, D * Np, Np, D, B * H_q, stream)));
   BwdParams p;
   p.q = q; p.qt = qt; p.k = k; p.kt = kt; p.v = v; p.dO = dO; p.dOt = dOt;
   p.lse = lse; p.dvec = dvec; p.dqkv = dqkv;

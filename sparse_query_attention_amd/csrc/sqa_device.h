@@ -55,4 +55,11 @@ struct alignas(16) Chunk { uint32_t w[4]; };
 
 __device__ inline Chunk zero_chunk() { Chunk c; c.w[0] = c.w[1] = c.w[2] = c.w[3] = 0u; return c; }
 
+// Swap bits 2 and 3 of an index (an involution within each aligned group of
+// 16). A B operand packed from accumulator registers carries, in k-step h of a
+// 32-row block, rows 16h + 8*(e/4) + 4*grp + e%4 for its 8 slots e; after this
+// permutation of the rows those are the 8 consecutive positions 16h + 8*grp + e,
+// so the matching A operand is one 16-byte read.
+__host__ __device__ inline int swap23(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
+
 }  // namespace sqa
