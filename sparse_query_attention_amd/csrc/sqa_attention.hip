@@ -67,33 +67,7 @@ struct AttnParams {
 // The dispatcher hands workgroup i to XCD i % XCDS, and each XCD has its own L2.
 constexpr int XCDS = 8;
 
-// XOR swizzle of 16-byte chunks within an LDS row of CPR chunks. It spreads
-// the rows that one ds_read_b128 touches over distinct banks.
-template <int CPR> __device__ inline int swz(int r);
-template <> __device__ inline int swz<16>(int r) { return r & 15; }
-template <> __device__ inline int swz<8>(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-template <> __device__ inline int swz<4>(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
-
 __device__ inline float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
-
-// Wait until at most N of this wave's vector-memory operations are outstanding
-// (N < 64: vmcnt bits [3:0] and [15:14]). The other counters are left unconstrained.
-template <int N> __device__ inline void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// wait_vmcnt<n * PER>() for a runtime n in [0, MAXN].
-template <int PER, int MAXN> __device__ inline void wait_vmcnt_tiles(int n) {
-  if constexpr (MAXN > 0) {
-    if (n >= MAXN) { wait_vmcnt<MAXN * PER>(); return; }
-    wait_vmcnt_tiles<PER, MAXN - 1>(n);
-  } else {
-    wait_vmcnt<0>();
-  }
-}
-
-typedef __attribute__((address_space(3))) void* lds_ptr;
 
 // A logical work item: query tile qt (heaviest first when causal), head group
 // sub, key/value head h, sequence b.

@@ -147,27 +147,31 @@ struct BwdParams {
 
 constexpr int BT = 64;   // tokens per LDS tile
 
-// Line pitch (elements) of a transposed LDS tile [D][64 tokens]. The bf16
-// MFMA operands read from it are 16-byte pieces of 32 consecutive lines; a
-// pitch of 144 bytes puts any 16 consecutive lines at 16 distinct 16-byte bank
-// groups (9*r mod 16 is a bijection), so the reads are free of bank conflicts.
-// fp32 lines are 68 words.
-template <typename T> constexpr int kTPitch = sizeof(T) == 2 ? 72 : 68;
+// Operand tiles in LDS, as the direct loads place them: 16-byte chunks
+// XOR-swizzled per row (swz) so that the rows one 16-byte read touches sit on
+// distinct banks.
+// Row-major tile [64 tokens][D]: the MFMA operand of row `row`, k-step st over
+// the head dims.
+template <typename T, int D>
+__device__ inline typename Mfma<T>::Frag row_frag(const T* tile, int row, int st, int grp) {
+  constexpr int EPC = 16 / (int)sizeof(T), RC = D / EPC;
+  const int e = st * Mfma<T>::KS + grp * Mfma<T>::E;
+  return *reinterpret_cast<const typename Mfma<T>::Frag*>(tile + row * D + ((e / EPC) ^ swz<RC>(row)) * EPC +
+                                                           e % EPC);
+}
 
-// A operand from a transposed LDS tile (rows = head dims, pitch TP elements,
-// tokens in swap23 order): row r, the score rows that a B operand packed from
-// accumulator registers carries in its k-slots. For k-step `half` of a 32-row
-// block at `base`, k-group grp holds rows base + 16*half + 8*(e/4) + 4*grp +
-// e%4 (e = 0..7), which sit at positions base + 16*half + 8*grp + e.
-template <typename T, int TP>
-__device__ inline typename Mfma<T>::Frag frag_runs(const T* tile, int r, int base, int half, int grp) {
-  if constexpr (sizeof(T) == 2) {
-    return *reinterpret_cast<const bf16x8*>(tile + r * TP + base + 16 * half + 8 * grp);
-  } else {
-    // fp32: k-step st = half (0..15) holds row base + 8*(st/4) + 4*grp + st%4,
-    // at position base + 16*(st/8) + 8*grp + st%8
-    return tile[r * TP + base + 16 * (half / 8) + 8 * grp + half % 8];
-  }
+// Transposed tile [D][64 tokens], tokens in swap23 order: the A operand of line
+// `line` that matches a B operand packed from accumulator registers. For
+// k-step `half` of the 32-row block at `base`, k-group grp holds rows
+// base + 16*half + 8*(e/4) + 4*grp + e%4 (e = 0..7), at positions
+// base + 16*half + 8*grp + e; for fp32, k-step st (0..15) holds row
+// base + 8*(st/4) + 4*grp + st%4, at position base + 16*(st/8) + 8*grp + st%8.
+template <typename T>
+__device__ inline typename Mfma<T>::Frag line_frag(const T* tile, int line, int base, int half, int grp) {
+  constexpr int EPC = 16 / (int)sizeof(T), LC = 64 / EPC;
+  const int pos = sizeof(T) == 2 ? base + 16 * half + 8 * grp : base + 16 * (half / 8) + 8 * grp + half % 8;
+  return *reinterpret_cast<const typename Mfma<T>::Frag*>(tile + line * 64 + ((pos / EPC) ^ swz<LC>(line)) * EPC +
+                                                           pos % EPC);
 }
 
 // B operand from accumulator registers x (C layout): k-step `half`.
@@ -185,127 +189,117 @@ __device__ inline typename Mfma<T>::Frag frag_regs(const f32x16& x, int half) {
 
 template <typename T> constexpr int kHalves = sizeof(T) == 2 ? 2 : 16;   // k-steps per 32 rows
 
-// A tile of LINES lines of RL elements (source lines `ld` apart): loaded into
-// registers, 16-byte pieces spread over 256 threads, then stored into LDS with
-// line pitch TP. Row-major token tiles are 64 lines of D; transposed ones D
-// lines of 64 tokens.
-template <typename T, int RL, int TP, int LINES>
-struct Stage {
-  static constexpr int EPC = 16 / (int)sizeof(T);
-  static constexpr int CPL = RL / EPC, N = LINES * CPL / 256;   // pieces per thread
-  static_assert(N * 256 == LINES * CPL, "tile split");
-  Chunk r[N];
-  __device__ void load(const T* src, int64_t ld) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int x = threadIdx.x + i * 256, line = x / CPL, cc = x % CPL;
-      r[i] = *reinterpret_cast<const Chunk*>(src + (int64_t)line * ld + cc * EPC);
-    }
-  }
-  __device__ void store(T* dst) const {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int x = threadIdx.x + i * 256, line = x / CPL, cc = x % CPL;
-      T* d = dst + line * TP + cc * EPC;
-      if constexpr (TP * sizeof(T) % 16 == 0) {
-        *reinterpret_cast<Chunk*>(d) = r[i];
-      } else {   // lines 8-byte aligned only: two 8-byte halves
-        reinterpret_cast<uint2*>(d)[0] = make_uint2(r[i].w[0], r[i].w[1]);
-        reinterpret_cast<uint2*>(d)[1] = make_uint2(r[i].w[2], r[i].w[3]);
-      }
-    }
-  }
-};
-
-// dK, dV: workgroup = (128*KW keys, KV head j, batch b); 4 waves x 32*KW keys.
-// With KW = 2 every Q, dO, Q^T and dO^T fragment read from LDS feeds two
-// MFMAs (one per 32-key block), which halves the LDS bytes per MFMA; the
-// accumulators of 64 keys then need one wave per SIMD.
-template <typename T, int D, int KW>
-__global__ __launch_bounds__(256, KW == 1 ? 2 : 1) void bwd_dkdv(BwdParams p) {
+// dK, dV: workgroup = (256 keys, KV head j, batch b); 8 waves x 32 keys.
+// The query-side operand tiles (Q, dO, Q^T, dO^T and the rows' lse and D) of
+// each 64-query tile go straight from global memory into a ring of LDS slots
+// (global_load_lds), NBUF-1 tiles ahead of the one in use; no registers hold
+// them in transit. Row-major tiles [64][D] and transposed tiles [D][64] keep
+// their 16-byte chunks XOR-swizzled per row, so the MFMA operand reads are
+// free of bank conflicts.
+template <typename T, int D>
+__global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
   using MF = Mfma<T>;
   using Frag = typename MF::Frag;
+  constexpr int WAVES = 8, KPW = 32, KPG = WAVES * KPW;   // keys per wave, per workgroup
   constexpr int EPC = 16 / (int)sizeof(T);
-  constexpr int RP = D + EPC;      // pitch of row-major tiles [64 tokens][D]
-  constexpr int TPT = kTPitch<T>;  // pitch of transposed tiles [D][64 tokens]
-  constexpr int NS = D / MF::KS;   // k-steps over the head dims
-  constexpr int QS = BT * RP, QTS = D * TPT;
-  constexpr int BUF = 2 * QS + 2 * QTS;   // elements: Q, dO, Q^T, dO^T
-  constexpr int KPW = 32 * KW;            // keys per wave
-  __shared__ __align__(16) T smem[2 * BUF];
-  __shared__ __align__(16) float sv[2][2][BT];   // per buffer: lse, D
+  constexpr int RC = D / EPC, LC = BT / EPC;   // chunks per row [64][D], per line [D][64]
+  constexpr int NS = D / MF::KS;               // k-steps over the head dims
+  constexpr int TE = BT * D;                   // elements of one operand tile
+  constexpr int SE = 2 * BT * 4 / (int)sizeof(T);   // elements holding the rows' lse and D (fp32)
+  constexpr int TILE = 4 * TE + SE;            // Q, dO, Q^T, dO^T, row statistics
+  constexpr int NBUF = 4 * TE * (int)sizeof(T) <= 32768 ? 4 : 2;   // ring slots (LDS <= 130 KB)
+  constexpr int INS = TE * (int)sizeof(T) / 1024;                 // 1 KB loads per operand tile
+  constexpr int IPW = 4 * INS / WAVES;                            // per wave and tile
+  constexpr int VM_PER_TILE = IPW + 1;                            // and one of row statistics
+  static_assert(IPW * WAVES == 4 * INS && INS * 64 * EPC == TE, "tile split");
+  // One array for every direct-load target: the compiler then sees the
+  // ring's reads and the loads in flight into other slots as one object and
+  // adds no waits of its own between them.
+  __shared__ __align__(16) T smem[NBUF * TILE];
 
   const int tid = threadIdx.x, lane = tid & 63,
             wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int col = lane & 31, grp = lane >> 5;
   // key tile kt of every (batch, KV head) before tile kt+1: with a causal mask
   // the first tiles see the most queries, so the heaviest work starts first
-  const int n_bj = gridDim.x / (p.Np / (4 * KPW));
+  const int n_bj = gridDim.x / (p.Np / KPG);
   const int kt = blockIdx.x / n_bj, bj = blockIdx.x % n_bj;
   const int j = bj % p.H_kv, b = bj / p.H_kv;
-  const int k0 = kt * 4 * KPW, kw = k0 + KPW * wave;   // this wave's first key
+  const int k0 = kt * KPG, kw = k0 + KPW * wave;   // this wave's first key
 
   const T* Kh = (const T*)p.k + ((int64_t)b * p.H_kv + j) * (int64_t)p.Np * D;
   const T* Vh = (const T*)p.v + ((int64_t)b * p.H_kv + j) * (int64_t)p.Np * D;
-  Frag kf[KW][NS], vf[KW][NS];   // B operands of S = Q K^T and dP = dO V^T
+  f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
-  for (int kb = 0; kb < KW; ++kb)
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const int64_t key = kw + 32 * kb + col;
-      kf[kb][s] = *reinterpret_cast<const Frag*>(Kh + key * D + s * MF::KS + grp * MF::E);
-      vf[kb][s] = *reinterpret_cast<const Frag*>(Vh + key * D + s * MF::KS + grp * MF::E);
-    }
-  f32x16 dk[KW][D / 32], dv[KW][D / 32];
-#pragma unroll
-  for (int kb = 0; kb < KW; ++kb)
-#pragma unroll
-    for (int nb = 0; nb < D / 32; ++nb) { dk[kb][nb] = f32x16{}; dv[kb][nb] = f32x16{}; }
+  for (int nb = 0; nb < D / 32; ++nb) { dk[nb] = f32x16{}; dv[nb] = f32x16{}; }
 
   // Work list: (head, query tile) for the g heads of j; causal starts at the
-  // tile holding key k0 (earlier queries see none of these keys).
+  // tile holding key k0 (earlier queries see none of these keys). Every row of
+  // the tiles walked here has its lse and D written: +inf and 0 past N.
   const int qt_first = p.causal ? k0 / BT : 0;
   const int qt_end = (p.N + BT - 1) / BT;
   const int per_head = max(0, qt_end - qt_first);
   const int n_work = per_head * p.g;
 
-  Stage<T, D, RP, BT> sq, sdo;
-  Stage<T, BT, TPT, D> sqt, sdot;
-  float lse_r = 0.f, dv_r = 0.f;
-  auto load = [&](int w) {
+  // Loads of work item w into ring slot w % NBUF. Load `ins` of the tile's
+  // 4*INS covers 64 16-byte chunks of one operand tile; lane L's chunk lands
+  // at position 64*ins + L, which holds chunk (c ^ swz(row)) of its row.
+  auto issue = [&](int w) {
+    if (w >= n_work) return;
     const int i = j * p.g + w / per_head, q0 = (qt_first + w % per_head) * BT;
     const int64_t hq = (int64_t)b * p.H_q + i;
-    sq.load((const T*)p.q + (hq * p.Np + q0) * D, D);
-    sdo.load((const T*)p.dO + (hq * p.Np + q0) * D, D);
-    sqt.load((const T*)p.qt + hq * D * p.Np + q0, p.Np);
-    sdot.load((const T*)p.dOt + hq * D * p.Np + q0, p.Np);
-    if (tid < BT) {
-      const int t = q0 + tid;
-      lse_r = t < p.N ? p.lse[hq * p.Np + t] : INFINITY;   // rows past N weigh 0
-      dv_r = t < p.N ? p.dvec[hq * p.Np + t] : 0.f;
+    T* tb = smem + (w % NBUF) * TILE;
+#pragma unroll
+    for (int x = 0; x < IPW; ++x) {
+      const int ins = wave * IPW + x, arr = ins / INS, li = ins % INS;
+      const int pos = li * 64 + lane;
+      const T* src;
+      if (arr < 2) {   // Q, dO rows
+        const int r = pos / RC, c = pos % RC;
+        src = (const T*)(arr == 0 ? p.q : p.dO) + (hq * p.Np + q0 + r) * D + (c ^ swz<RC>(r)) * EPC;
+      } else {         // Q^T, dO^T lines (tokens in swap23 order)
+        const int r = pos / LC, c = pos % LC;
+        src = (const T*)(arr == 2 ? p.qt : p.dOt) + (hq * D + r) * (int64_t)p.Np + q0 +
+              (c ^ swz<LC>(r)) * EPC;
+      }
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)(tb + arr * TE + li * 64 * EPC), 16, 0, 0);
     }
-  };
-  auto store = [&](int buf) {
-    T* base = smem + buf * BUF;
-    sq.store(base);
-    sdo.store(base + QS);
-    sqt.store(base + 2 * QS);
-    sdot.store(base + 2 * QS + QTS);
-    if (tid < BT) { sv[buf][0][tid] = lse_r; sv[buf][1][tid] = dv_r; }
+    // row statistics: waves 0-3 load 16 lse values each, waves 4-7 16 D values
+    const int which = wave >> 2, part = wave & 3;
+    const float* src = (which ? p.dvec : p.lse) + hq * p.Np + q0 + part * 16 + (lane & 15);
+    float* dst = reinterpret_cast<float*>(tb + 4 * TE) + which * BT + part * 16;
+    if (lane < 16) __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)dst, 4, 0, 0);
   };
 
-  if (n_work > 0) {
-    load(0);
-    store(0);
+  // Prologue: work items 0..NBUF-2 in flight, then this wave's K and V
+  // fragments (B operands of S = Q K^T and dP = dO V^T), all landed before
+  // the loop, which then waits only on its own loads.
+#pragma unroll
+  for (int t = 0; t < NBUF - 1; ++t) issue(t);
+  Frag kf[NS], vf[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int64_t key = kw + col;
+    kf[s] = *reinterpret_cast<const Frag*>(Kh + key * D + s * MF::KS + grp * MF::E);
+    vf[s] = *reinterpret_cast<const Frag*>(Vh + key * D + s * MF::KS + grp * MF::E);
   }
+  wait_vmcnt<0>();
   __syncthreads();
+
   for (int w = 0; w < n_work; ++w) {
-    const int buf = w & 1;
-    load(min(w + 1, n_work - 1));   // the last iteration reloads its own tile, unused
-    const T* Qs = smem + buf * BUF;
-    const T* Os = Qs + QS;
-    const T* QTs = Qs + 2 * QS;
-    const T* OTs = QTs + QTS;
+    if (w > 0) {
+      // item w visible (items w+1.. may still be in flight), and every wave
+      // is done with slot (w-1) % NBUF, which takes item w+NBUF-1
+      wait_vmcnt_tiles<VM_PER_TILE, NBUF - 2>(min(NBUF - 2, max(0, n_work - 1 - w)));
+      ring_barrier();
+    }
+    issue(w + NBUF - 1);
+    const T* Qs = smem + (w % NBUF) * TILE;
+    const T* Os = Qs + TE;
+    const T* QTs = Qs + 2 * TE;
+    const T* OTs = Qs + 3 * TE;
+    const float* lse_s = reinterpret_cast<const float*>(Qs + 4 * TE);
+    const float* dv_s = lse_s + BT;
     const int q0 = (qt_first + w % per_head) * BT;
 #pragma unroll
     for (int qs = 0; qs < BT / 32; ++qs) {
@@ -313,33 +307,27 @@ __global__ __launch_bounds__(256, KW == 1 ? 2 : 1) void bwd_dkdv(BwdParams p) {
       // wave-uniform skips: every query before this wave's first key, or past N
       if ((p.causal && qb + 31 < kw) || qb >= p.N) continue;
       // LDS reads are issued ahead of their use: the Q and dO fragments
-      // before the S/dP MFMAs, and the Q^T/dO^T fragments and row statistics
-      // of the second half before the softmax work, which hides their latency.
+      // before the S/dP MFMAs, the row statistics before the softmax work.
       Frag qa[NS], oa[NS];
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
-        const int e = st * MF::KS + grp * MF::E;
-        qa[st] = *reinterpret_cast<const Frag*>(Qs + (32 * qs + col) * RP + e);
-        oa[st] = *reinterpret_cast<const Frag*>(Os + (32 * qs + col) * RP + e);
+        qa[st] = row_frag<T, D>(Qs, 32 * qs + col, st, grp);
+        oa[st] = row_frag<T, D>(Os, 32 * qs + col, st, grp);
       }
-      f32x16 s[KW], dp[KW];
+      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int kb = 0; kb < KW; ++kb) { s[kb] = f32x16{}; dp[kb] = f32x16{}; }
-#pragma unroll
-      for (int st = 0; st < NS; ++st)
-#pragma unroll
-        for (int kb = 0; kb < KW; ++kb) {
-          s[kb] = MF::run(qa[st], kf[kb][st], s[kb]);
-          dp[kb] = MF::run(oa[st], vf[kb][st], dp[kb]);
-        }
+      for (int st = 0; st < NS; ++st) {
+        s = MF::run(qa[st], kf[st], s);
+        dp = MF::run(oa[st], vf[st], dp);
+      }
       f32x4 l4s[4], d4s[4];
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int rl = 32 * qs + 8 * r4 + 4 * grp;
-        l4s[r4] = *reinterpret_cast<const f32x4*>(&sv[buf][0][rl]);
-        d4s[r4] = *reinterpret_cast<const f32x4*>(&sv[buf][1][rl]);
+        l4s[r4] = *reinterpret_cast<const f32x4*>(&lse_s[rl]);
+        d4s[r4] = *reinterpret_cast<const f32x4*>(&dv_s[rl]);
       }
-      // register r: query qb + 8*(r/4) + 4*grp + r%4; column: key kw + 32*kb + col.
+      // register r: query qb + 8*(r/4) + 4*grp + r%4; column: key kw + col.
       // Only blocks that cross the diagonal or the sequence end are masked
       // (a wave-uniform choice); elsewhere every key is visible.
       const bool masked = kw + KPW > p.N || (p.causal && kw + KPW - 1 > qb);
@@ -347,18 +335,15 @@ __global__ __launch_bounds__(256, KW == 1 ? 2 : 1) void bwd_dkdv(BwdParams p) {
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const f32x4 l4 = l4s[r4], d4 = d4s[r4];
+          const int key = kw + col;
 #pragma unroll
-          for (int kb = 0; kb < KW; ++kb) {
-            const int key = kw + 32 * kb + col;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * r4 + e, q = qb + 8 * r4 + 4 * grp + e;
-              float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][r], p.c, -l4[e]));
-              if constexpr (decltype(mask_on)::value)
-                pv = key >= p.N || (p.causal && key > q) ? 0.f : pv;
-              s[kb][r] = pv;                          // P
-              dp[kb][r] = pv * (dp[kb][r] - d4[e]);   // dS
-            }
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * r4 + e, q = qb + 8 * r4 + 4 * grp + e;
+            float pv = __builtin_amdgcn_exp2f(fmaf(s[r], p.c, -l4[e]));
+            if constexpr (decltype(mask_on)::value)
+              pv = key >= p.N || (p.causal && key > q) ? 0.f : pv;
+            s[r] = pv;                       // P
+            dp[r] = pv * (dp[r] - d4[e]);    // dS
           }
         }
       };
@@ -367,60 +352,60 @@ __global__ __launch_bounds__(256, KW == 1 ? 2 : 1) void bwd_dkdv(BwdParams p) {
 #pragma unroll
       for (int h = 0; h < kHalves<T>; ++h)
 #pragma unroll
-        for (int nb = 0; nb < D / 32; ++nb)
-#pragma unroll
-          for (int kb = 0; kb < KW; ++kb) {
-            dv[kb][nb] = MF::run(frag_runs<T, TPT>(OTs, nb * 32 + col, 32 * qs, h, grp), frag_regs<T>(s[kb], h), dv[kb][nb]);
-            dk[kb][nb] = MF::run(frag_runs<T, TPT>(QTs, nb * 32 + col, 32 * qs, h, grp), frag_regs<T>(dp[kb], h), dk[kb][nb]);
-          }
+        for (int nb = 0; nb < D / 32; ++nb) {
+          dv[nb] = MF::run(line_frag<T>(OTs, nb * 32 + col, 32 * qs, h, grp), frag_regs<T>(s, h), dv[nb]);
+          dk[nb] = MF::run(line_frag<T>(QTs, nb * 32 + col, 32 * qs, h, grp), frag_regs<T>(dp, h), dk[nb]);
+        }
     }
-    store(buf ^ 1);   // every wave passed the barrier after its last read of buf ^ 1
-    __syncthreads();
   }
 
   // dK^T, dV^T: lane = key, register r = head dim 32*nb + 8*(r/4) + 4*grp + r%4.
+  T* row = (T*)p.dqkv + ((int64_t)b * p.Np + kw + col) * p.W;
+  T* dkr = row + (int64_t)p.H_q * D + j * D;
+  T* dvr = row + (int64_t)(p.H_q + p.H_kv) * D + j * D;
 #pragma unroll
-  for (int kb = 0; kb < KW; ++kb) {
-    T* row = (T*)p.dqkv + ((int64_t)b * p.Np + kw + 32 * kb + col) * p.W;
-    T* dkr = row + (int64_t)p.H_q * D + j * D;
-    T* dvr = row + (int64_t)(p.H_q + p.H_kv) * D + j * D;
+  for (int nb = 0; nb < D / 32; ++nb)
 #pragma unroll
-    for (int nb = 0; nb < D / 32; ++nb)
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int c = nb * 32 + 8 * rq + 4 * grp;
-        const f32x16& K_ = dk[kb][nb];
-        const f32x16& V_ = dv[kb][nb];
-        if constexpr (sizeof(T) == 2) {
-          *reinterpret_cast<bf16x4*>(dkr + c) =
-              bf16x4{(bf16)(K_[4 * rq] * p.scale), (bf16)(K_[4 * rq + 1] * p.scale),
-                     (bf16)(K_[4 * rq + 2] * p.scale), (bf16)(K_[4 * rq + 3] * p.scale)};
-          *reinterpret_cast<bf16x4*>(dvr + c) =
-              bf16x4{(bf16)V_[4 * rq], (bf16)V_[4 * rq + 1], (bf16)V_[4 * rq + 2],
-                     (bf16)V_[4 * rq + 3]};
-        } else {
-          *reinterpret_cast<f32x4*>(dkr + c) =
-              f32x4{K_[4 * rq] * p.scale, K_[4 * rq + 1] * p.scale, K_[4 * rq + 2] * p.scale,
-                    K_[4 * rq + 3] * p.scale};
-          *reinterpret_cast<f32x4*>(dvr + c) =
-              f32x4{V_[4 * rq], V_[4 * rq + 1], V_[4 * rq + 2], V_[4 * rq + 3]};
-        }
+    for (int rq = 0; rq < 4; ++rq) {
+      const int c = nb * 32 + 8 * rq + 4 * grp;
+      const f32x16& K_ = dk[nb];
+      const f32x16& V_ = dv[nb];
+      if constexpr (sizeof(T) == 2) {
+        *reinterpret_cast<bf16x4*>(dkr + c) =
+            bf16x4{(bf16)(K_[4 * rq] * p.scale), (bf16)(K_[4 * rq + 1] * p.scale),
+                   (bf16)(K_[4 * rq + 2] * p.scale), (bf16)(K_[4 * rq + 3] * p.scale)};
+        *reinterpret_cast<bf16x4*>(dvr + c) =
+            bf16x4{(bf16)V_[4 * rq], (bf16)V_[4 * rq + 1], (bf16)V_[4 * rq + 2], (bf16)V_[4 * rq + 3]};
+      } else {
+        *reinterpret_cast<f32x4*>(dkr + c) =
+            f32x4{K_[4 * rq] * p.scale, K_[4 * rq + 1] * p.scale, K_[4 * rq + 2] * p.scale,
+                  K_[4 * rq + 3] * p.scale};
+        *reinterpret_cast<f32x4*>(dvr + c) = f32x4{V_[4 * rq], V_[4 * rq + 1], V_[4 * rq + 2], V_[4 * rq + 3]};
       }
-  }
+    }
 }
 
-// dQ: workgroup = (256 queries, head i, batch b); 4 waves x 64 queries.
+// dQ: workgroup = (256 queries, head i, batch b); 4 waves x 64 queries. The
+// key-side tiles (K, V and K^T, 64 keys each) go straight from global memory
+// into a ring of LDS slots (global_load_lds), NBUF-1 tiles ahead of the one in
+// use, XOR-swizzled per row as in bwd_dkdv.
 template <typename T, int D>
 __global__ __launch_bounds__(256, 2) void bwd_dq(BwdParams p) {
   using MF = Mfma<T>;
   using Frag = typename MF::Frag;
+  constexpr int WAVES = 4;
   constexpr int EPC = 16 / (int)sizeof(T);
-  constexpr int RP = D + EPC, TPT = kTPitch<T>;
+  constexpr int RC = D / EPC, LC = BT / EPC;   // chunks per row [64][D], per line [D][64]
   constexpr int NS = D / MF::KS;
-  constexpr int QB = 2;                       // 32-query blocks per wave
-  constexpr int KS_ = BT * RP, KTS = D * TPT;
-  constexpr int BUF = 2 * KS_ + KTS;          // K, V, K^T
-  __shared__ __align__(16) T smem[2 * BUF];
+  constexpr int QB = 2;                        // 32-query MFMA column blocks per wave
+  constexpr int TE = BT * D;
+  constexpr int TILE = 3 * TE;                 // K, V, K^T
+  constexpr int NBUF = TILE * (int)sizeof(T) <= 24576 ? 3 : 2;   // two workgroups per CU
+  constexpr int INS = TE * (int)sizeof(T) / 1024;
+  constexpr int IPW = 3 * INS / WAVES;
+  constexpr int VM_PER_TILE = IPW;
+  static_assert(IPW * WAVES == 3 * INS && INS * 64 * EPC == TE, "tile split");
+  __shared__ __align__(16) T smem[NBUF * TILE];
 
   const int tid = threadIdx.x, lane = tid & 63,
             wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
@@ -433,6 +418,42 @@ __global__ __launch_bounds__(256, 2) void bwd_dq(BwdParams p) {
   const int q0 = qt * 256, qw = q0 + 64 * wave;
   const int64_t hq = (int64_t)b * p.H_q + i, hk = (int64_t)b * p.H_kv + j;
 
+  const int kv_len = p.causal ? min(p.N, q0 + 256) : p.N;
+  const int n_tiles = (kv_len + BT - 1) / BT;
+  const T* Kh = (const T*)p.k + hk * p.Np * D;
+  const T* Vh = (const T*)p.v + hk * p.Np * D;
+  const T* KTh = (const T*)p.kt + hk * D * p.Np;
+
+  // Loads of key tile t into ring slot t % NBUF (see bwd_dkdv's issue).
+  auto issue = [&](int t) {
+    if (t >= n_tiles) return;
+    const int k0 = t * BT;
+    T* tb = smem + (t % NBUF) * TILE;
+#pragma unroll
+    for (int x = 0; x < IPW; ++x) {
+      const int ins = wave * IPW + x, arr = ins / INS, li = ins % INS;
+      const int pos = li * 64 + lane;
+      // a uniform base and a 32-bit per-lane byte offset (one VGPR per load)
+      const T* base;
+      uint32_t off;
+      if (arr < 2) {   // K, V rows
+        const int r = pos / RC, c = pos % RC;
+        base = (arr == 0 ? Kh : Vh) + (int64_t)k0 * D;
+        off = (uint32_t)((r * D + (c ^ swz<RC>(r)) * EPC) * (int)sizeof(T));
+      } else {         // K^T lines (keys in swap23 order)
+        const int r = pos / LC, c = pos % LC;
+        base = KTh + k0;
+        off = (uint32_t)r * (uint32_t)p.Np * (uint32_t)sizeof(T) + (uint32_t)((c ^ swz<LC>(r)) * EPC * (int)sizeof(T));
+      }
+      __builtin_amdgcn_global_load_lds((const void*)((const char*)base + off),
+                                       (lds_ptr)(tb + arr * TE + li * 64 * EPC), 16, 0, 0);
+    }
+  };
+  // Prologue: key tiles 0..NBUF-2 in flight, then this wave's Q and dO
+  // fragments (B operands of S^T = K Q^T and dP^T = V dO^T) and its rows'
+  // statistics, all landed before the loop.
+#pragma unroll
+  for (int t = 0; t < NBUF - 1; ++t) issue(t);
   Frag qf[QB][NS], of[QB][NS];
   float lse[QB], dvq[QB];
 #pragma unroll
@@ -453,49 +474,31 @@ __global__ __launch_bounds__(256, 2) void bwd_dq(BwdParams p) {
   for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int nb = 0; nb < D / 32; ++nb) dq[qb][nb] = f32x16{};
-
-  const int kv_len = p.causal ? min(p.N, q0 + 256) : p.N;
-  const int n_tiles = (kv_len + BT - 1) / BT;
-  const T* Kh = (const T*)p.k + hk * p.Np * D;
-  const T* Vh = (const T*)p.v + hk * p.Np * D;
-  const T* KTh = (const T*)p.kt + hk * D * p.Np;
-  Stage<T, D, RP, BT> sk, sv;
-  Stage<T, BT, TPT, D> skt;
-  auto load = [&](int t) {
-    const int k0 = t * BT;
-    sk.load(Kh + (int64_t)k0 * D, D);
-    sv.load(Vh + (int64_t)k0 * D, D);
-    skt.load(KTh + k0, p.Np);
-  };
-  auto store = [&](int buf) {
-    T* base = smem + buf * BUF;
-    sk.store(base);
-    sv.store(base + KS_);
-    skt.store(base + 2 * KS_);
-  };
-  if (n_tiles > 0) {
-    load(0);
-    store(0);
-  }
+  wait_vmcnt<0>();
   __syncthreads();
+
   for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    load(min(t + 1, n_tiles - 1));
-    const T* Ks = smem + buf * BUF;
-    const T* Vs = Ks + KS_;
-    const T* KTs = Ks + 2 * KS_;
+    if (t > 0) {
+      // tile t visible (tiles t+1.. may still be in flight), and every wave
+      // is done with slot (t-1) % NBUF, which takes tile t+NBUF-1
+      wait_vmcnt_tiles<VM_PER_TILE, NBUF - 2>(min(NBUF - 2, max(0, n_tiles - 1 - t)));
+      ring_barrier();
+    }
+    issue(t + NBUF - 1);
+    const T* Ks = smem + (t % NBUF) * TILE;
+    const T* Vs = Ks + TE;
+    const T* KTs = Ks + 2 * TE;
 #pragma unroll
     for (int jb = 0; jb < BT / 32; ++jb) {
       const int kb = t * BT + 32 * jb;
       if (kb >= p.N || (p.causal && kb > qw + 63)) continue;   // wave-uniform
-      // LDS reads ahead of their use (as in bwd_dkdv): K and V fragments
-      // before the S^T/dP^T MFMAs, K^T fragments before the softmax work.
+      // LDS reads ahead of their use: K and V fragments before the S^T/dP^T
+      // MFMAs, K^T fragments before the softmax work.
       Frag ka[NS], va[NS];
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
-        const int e = st * MF::KS + grp * MF::E;
-        ka[st] = *reinterpret_cast<const Frag*>(Ks + (32 * jb + col) * RP + e);
-        va[st] = *reinterpret_cast<const Frag*>(Vs + (32 * jb + col) * RP + e);
+        ka[st] = row_frag<T, D>(Ks, 32 * jb + col, st, grp);
+        va[st] = row_frag<T, D>(Vs, 32 * jb + col, st, grp);
       }
       f32x16 s[QB], dp[QB];
 #pragma unroll
@@ -508,11 +511,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq(BwdParams p) {
           dp[qb] = MF::run(va[st], of[qb][st], dp[qb]);
         }
 
-      // register r: key kb + 8*(r/4) + 4*grp + r%4; column: query qw + 32*qb + col
+      // register r: key kb + 8*(r/4) + 4*grp + r%4; column: query qw + 32*qb + col.
       // Register r holds key kb + 4*grp + o_r with o_r = 8*(r/4) + r%4. The key
       // is visible iff o_r < lim: lim = N - kb - 4*grp, and for causal also
       // <= q - kb - 4*grp. One compare per score; away from the diagonal and
-      // the sequence end lim exceeds every o_r.
+      // the sequence end lim exceeds every o_r. (A wave-uniform branch around
+      // an unmasked copy, as in bwd_dkdv, would push this kernel past 256
+      // VGPRs.)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const int base = kb + 4 * grp;
@@ -529,10 +534,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq(BwdParams p) {
         for (int nb = 0; nb < D / 32; ++nb)
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
-            dq[qb][nb] = MF::run(frag_runs<T, TPT>(KTs, nb * 32 + col, 32 * jb, h, grp), frag_regs<T>(s[qb], h), dq[qb][nb]);
+            dq[qb][nb] = MF::run(line_frag<T>(KTs, nb * 32 + col, 32 * jb, h, grp), frag_regs<T>(s[qb], h), dq[qb][nb]);
     }
-    store(buf ^ 1);
-    __syncthreads();
   }
 
   // dQ^T: lane = query, register r = head dim 32*nb + 8*(r/4) + 4*grp + r%4.
@@ -681,12 +684,11 @@ hipError_t backward_impl(const void* x, const void* wq, const void* wk, const vo
   p.causal = causal ? 1 : 0; p.W = (int)W;
   p.c = (float)(1.4426950408889634 / sqrt((double)D));
   p.scale = (float)(1.0 / sqrt((double)D));
-  if ((Np / 128) * B * H_kv > 0x7FFFFFFF || (Np / 256) * B * H_q > 0x7FFFFFFF)
+  // grids, and the 32-bit byte offsets of bwd_dq's loads within a K^T head
+  if ((Np / 256) * B * H_kv > 0x7FFFFFFF || (Np / 256) * B * H_q > 0x7FFFFFFF ||
+      (int64_t)D * Np * (int64_t)sizeof(T) > 0xFFFFFFFFll)
     return hipErrorInvalidConfiguration;
-  // 32 keys per wave: 64 (KW = 2) reuses each LDS fragment twice but needs
-  // one wave per SIMD, and measured slower (99.6 against 83.4 ms)
-  constexpr int KW = 1;
-  bwd_dkdv<T, D, KW><<<(unsigned)((Np / (128 * KW)) * B * H_kv), 256, 0, stream>>>(p);
+  bwd_dkdv<T, D><<<(unsigned)((Np / 256) * B * H_kv), 512, 0, stream>>>(p);
   SQA_CK(hipGetLastError());
   bwd_dq<T, D><<<(unsigned)((Np / 256) * B * H_q), 256, 0, stream>>>(p);
   SQA_CK(hipGetLastError());

@@ -62,4 +62,45 @@ __device__ inline Chunk zero_chunk() { Chunk c; c.w[0] = c.w[1] = c.w[2] = c.w[3
 // so the matching A operand is one 16-byte read.
 __host__ __device__ inline int swap23(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
 
+// XOR swizzle of 16-byte chunks within an LDS row of CPR chunks. It spreads
+// the rows that one ds_read_b128 touches over distinct banks.
+template <int CPR> __device__ inline int swz(int r);
+template <> __device__ inline int swz<16>(int r) { return r & 15; }
+template <> __device__ inline int swz<8>(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+template <> __device__ inline int swz<4>(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+
+// Direct global->LDS loads (global_load_lds): lane L of a 16-byte load lands
+// 16*L bytes past the load's LDS base, and the loads count in vmcnt.
+// Wait until at most N of this wave's vector-memory operations are outstanding
+// (N < 64: vmcnt bits [3:0] and [15:14]). The other counters are left unconstrained.
+template <int N> __device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// wait_vmcnt<n * PER>() for a runtime n in [0, MAXN].
+template <int PER, int MAXN> __device__ inline void wait_vmcnt_tiles(int n) {
+  if constexpr (MAXN > 0) {
+    if (n >= MAXN) { wait_vmcnt<MAXN * PER>(); return; }
+    wait_vmcnt_tiles<PER, MAXN - 1>(n);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// Workgroup barrier between the steps of a ring of LDS slots filled by direct
+// loads. The fences of __syncthreads() make the compiler drain every load in
+// flight (direct loads count in vmcnt), which would empty the ring at each
+// step. Callers first wait with wait_vmcnt for the loads the next step reads;
+// every LDS read of the slot about to be refilled has returned, since its data
+// was consumed before the barrier. The empty asm statements keep the compiler
+// from moving memory accesses across the barrier.
+__device__ inline void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 }  // namespace sqa
