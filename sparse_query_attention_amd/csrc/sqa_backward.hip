@@ -189,13 +189,23 @@ __device__ inline typename Mfma<T>::Frag frag_regs(const f32x16& x, int half) {
 
 template <typename T> constexpr int kHalves = sizeof(T) == 2 ? 2 : 16;   // k-steps per 32 rows
 
-// dK, dV: workgroup = (256 keys, KV head j, batch b); 8 waves x 32 keys.
-// The query-side operand tiles (Q, dO, Q^T, dO^T and the rows' lse and D) of
-// each 64-query tile go straight from global memory into a ring of LDS slots
-// (global_load_lds), NBUF-1 tiles ahead of the one in use; no registers hold
-// them in transit. Row-major tiles [64][D] and transposed tiles [D][64] keep
-// their 16-byte chunks XOR-swizzled per row, so the MFMA operand reads are
-// free of bank conflicts.
+// dK, dV: workgroup = (key tiles of 256 keys, KV head j, batch b); 8 waves x
+// 32 keys. The query-side operand tiles (Q, dO, Q^T, dO^T and the rows' lse
+// and D) of each 64-query tile go straight from global memory into a ring of
+// LDS slots (global_load_lds), NBUF-1 tiles ahead of the one in use; no
+// registers hold them in transit. Row-major tiles [64][D] and transposed tiles
+// [D][64] keep their 16-byte chunks XOR-swizzled per row, so the MFMA operand
+// reads are free of bank conflicts.
+//
+// Order of the work. Every query tile is read by every key tile at or before
+// it, and the workgroups that run at once on an XCD share its L2 only if they
+// read the same tiles at the same time. Causal: workgroup pr takes key tile
+// pr, walking its query tiles from the last one down, then key tile
+// n_kt-1-pr, walking up from its first. Each workgroup then has the same
+// number of items, and at step tau every workgroup in its first half reads
+// query tile qt_end-1-tau and every one in its second half the same tile
+// 4*(n_kt-1)-qt_end+tau, whatever pr is. Without a mask every workgroup walks
+// all query tiles upward. Within a query tile the g heads are adjacent.
 template <typename T, int D>
 __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
   using MF = Mfma<T>;
@@ -220,33 +230,37 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63,
             wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int col = lane & 31, grp = lane >> 5;
-  // key tile kt of every (batch, KV head) before tile kt+1: with a causal mask
-  // the first tiles see the most queries, so the heaviest work starts first
-  const int n_bj = gridDim.x / (p.Np / KPG);
-  const int kt = blockIdx.x / n_bj, bj = blockIdx.x % n_bj;
+  const int n_kt = p.Np / KPG;
+  const int n_bj = gridDim.x / (p.causal ? (n_kt + 1) / 2 : n_kt);
+  const int pr = blockIdx.x / n_bj, bj = blockIdx.x % n_bj;
   const int j = bj % p.H_kv, b = bj / p.H_kv;
-  const int k0 = kt * KPG, kw = k0 + KPW * wave;   // this wave's first key
+  const int kt0 = pr, kt1 = n_kt - 1 - pr;
+  const int qt_end = (p.N + BT - 1) / BT;
+  // Items: phase 0 is key tile kt0, phase 1 (causal, kt1 != kt0) key tile kt1.
+  // Causal key tile kt sees the query tiles from the one holding its first
+  // key. Every row of the tiles walked has its lse and D written: +inf and 0
+  // past N.
+  const int first0 = p.causal ? kt0 * (KPG / BT) : 0;
+  const int first1 = kt1 * (KPG / BT);
+  const int n0 = max(0, qt_end - first0) * p.g;
+  const int n_work = n0 + (p.causal && kt1 != kt0 ? max(0, qt_end - first1) * p.g : 0);
+
+  // item -> (query tile, head within the group)
+  auto item_tile = [&](int w) {
+    if (w < n0) return p.causal ? qt_end - 1 - w / p.g : w / p.g;
+    return first1 + (w - n0) / p.g;
+  };
+  auto item_head = [&](int w) { return (w < n0 ? w : w - n0) % p.g; };
 
   const T* Kh = (const T*)p.k + ((int64_t)b * p.H_kv + j) * (int64_t)p.Np * D;
   const T* Vh = (const T*)p.v + ((int64_t)b * p.H_kv + j) * (int64_t)p.Np * D;
-  f32x16 dk[D / 32], dv[D / 32];
-#pragma unroll
-  for (int nb = 0; nb < D / 32; ++nb) { dk[nb] = f32x16{}; dv[nb] = f32x16{}; }
-
-  // Work list: (head, query tile) for the g heads of j; causal starts at the
-  // tile holding key k0 (earlier queries see none of these keys). Every row of
-  // the tiles walked here has its lse and D written: +inf and 0 past N.
-  const int qt_first = p.causal ? k0 / BT : 0;
-  const int qt_end = (p.N + BT - 1) / BT;
-  const int per_head = max(0, qt_end - qt_first);
-  const int n_work = per_head * p.g;
 
   // Loads of work item w into ring slot w % NBUF. Load `ins` of the tile's
   // 4*INS covers 64 16-byte chunks of one operand tile; lane L's chunk lands
   // at position 64*ins + L, which holds chunk (c ^ swz(row)) of its row.
   auto issue = [&](int w) {
     if (w >= n_work) return;
-    const int i = j * p.g + w / per_head, q0 = (qt_first + w % per_head) * BT;
+    const int i = j * p.g + item_head(w), q0 = item_tile(w) * BT;
     const int64_t hq = (int64_t)b * p.H_q + i;
     T* tb = smem + (w % NBUF) * TILE;
 #pragma unroll
@@ -271,18 +285,54 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
     if (lane < 16) __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)dst, 4, 0, 0);
   };
 
-  // Prologue: work items 0..NBUF-2 in flight, then this wave's K and V
-  // fragments (B operands of S = Q K^T and dP = dO V^T), all landed before
-  // the loop, which then waits only on its own loads.
+  // This wave's K and V fragments (B operands of S = Q K^T and dP = dO V^T)
+  // for the key tile starting at key k0, and the store of its dK and dV.
+  Frag kf[NS], vf[NS];
+  auto load_kv = [&](int kw) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int64_t key = kw + col;
+      kf[s] = *reinterpret_cast<const Frag*>(Kh + key * D + s * MF::KS + grp * MF::E);
+      vf[s] = *reinterpret_cast<const Frag*>(Vh + key * D + s * MF::KS + grp * MF::E);
+    }
+  };
+  f32x16 dk[D / 32], dv[D / 32];
+  // dK^T, dV^T: lane = key, register r = head dim 32*nb + 8*(r/4) + 4*grp + r%4.
+  auto store_dkdv = [&](int kw) {
+    T* row = (T*)p.dqkv + ((int64_t)b * p.Np + kw + col) * p.W;
+    T* dkr = row + (int64_t)p.H_q * D + j * D;
+    T* dvr = row + (int64_t)(p.H_q + p.H_kv) * D + j * D;
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int c = nb * 32 + 8 * rq + 4 * grp;
+        const f32x16& K_ = dk[nb];
+        const f32x16& V_ = dv[nb];
+        if constexpr (sizeof(T) == 2) {
+          *reinterpret_cast<bf16x4*>(dkr + c) =
+              bf16x4{(bf16)(K_[4 * rq] * p.scale), (bf16)(K_[4 * rq + 1] * p.scale),
+                     (bf16)(K_[4 * rq + 2] * p.scale), (bf16)(K_[4 * rq + 3] * p.scale)};
+          *reinterpret_cast<bf16x4*>(dvr + c) =
+              bf16x4{(bf16)V_[4 * rq], (bf16)V_[4 * rq + 1], (bf16)V_[4 * rq + 2], (bf16)V_[4 * rq + 3]};
+        } else {
+          *reinterpret_cast<f32x4*>(dkr + c) =
+              f32x4{K_[4 * rq] * p.scale, K_[4 * rq + 1] * p.scale, K_[4 * rq + 2] * p.scale,
+                    K_[4 * rq + 3] * p.scale};
+          *reinterpret_cast<f32x4*>(dvr + c) = f32x4{V_[4 * rq], V_[4 * rq + 1], V_[4 * rq + 2], V_[4 * rq + 3]};
+        }
+      }
+  };
+
+  // Prologue: work items 0..NBUF-2 in flight, then the K and V fragments of
+  // the first key tile, all landed before the loop, which then waits only on
+  // its own loads.
+  int kw = kt0 * KPG + KPW * wave;   // this wave's first key
 #pragma unroll
   for (int t = 0; t < NBUF - 1; ++t) issue(t);
-  Frag kf[NS], vf[NS];
+  load_kv(kw);
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const int64_t key = kw + col;
-    kf[s] = *reinterpret_cast<const Frag*>(Kh + key * D + s * MF::KS + grp * MF::E);
-    vf[s] = *reinterpret_cast<const Frag*>(Vh + key * D + s * MF::KS + grp * MF::E);
-  }
+  for (int nb = 0; nb < D / 32; ++nb) { dk[nb] = f32x16{}; dv[nb] = f32x16{}; }
   wait_vmcnt<0>();
   __syncthreads();
 
@@ -294,13 +344,21 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
       ring_barrier();
     }
     issue(w + NBUF - 1);
+    if (w == n0) {   // second key tile: store the first one's gradients
+      store_dkdv(kw);
+      kw = kt1 * KPG + KPW * wave;
+      load_kv(kw);
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb) { dk[nb] = f32x16{}; dv[nb] = f32x16{}; }
+      wait_vmcnt<0>();
+    }
     const T* Qs = smem + (w % NBUF) * TILE;
     const T* Os = Qs + TE;
     const T* QTs = Qs + 2 * TE;
     const T* OTs = Qs + 3 * TE;
     const float* lse_s = reinterpret_cast<const float*>(Qs + 4 * TE);
     const float* dv_s = lse_s + BT;
-    const int q0 = (qt_first + w % per_head) * BT;
+    const int q0 = item_tile(w) * BT;
 #pragma unroll
     for (int qs = 0; qs < BT / 32; ++qs) {
       const int qb = q0 + 32 * qs;
@@ -358,37 +416,28 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
         }
     }
   }
-
-  // dK^T, dV^T: lane = key, register r = head dim 32*nb + 8*(r/4) + 4*grp + r%4.
-  T* row = (T*)p.dqkv + ((int64_t)b * p.Np + kw + col) * p.W;
-  T* dkr = row + (int64_t)p.H_q * D + j * D;
-  T* dvr = row + (int64_t)(p.H_q + p.H_kv) * D + j * D;
+  // The last key tile's gradients. A key tile that no query reaches (wholly
+  // past N) stores zeros: the weight gradients read those padding rows.
+  store_dkdv(kw);
+  if (p.causal && kt1 != kt0 && n_work == n0) {
+    kw = kt1 * KPG + KPW * wave;
 #pragma unroll
-  for (int nb = 0; nb < D / 32; ++nb)
-#pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      const int c = nb * 32 + 8 * rq + 4 * grp;
-      const f32x16& K_ = dk[nb];
-      const f32x16& V_ = dv[nb];
-      if constexpr (sizeof(T) == 2) {
-        *reinterpret_cast<bf16x4*>(dkr + c) =
-            bf16x4{(bf16)(K_[4 * rq] * p.scale), (bf16)(K_[4 * rq + 1] * p.scale),
-                   (bf16)(K_[4 * rq + 2] * p.scale), (bf16)(K_[4 * rq + 3] * p.scale)};
-        *reinterpret_cast<bf16x4*>(dvr + c) =
-            bf16x4{(bf16)V_[4 * rq], (bf16)V_[4 * rq + 1], (bf16)V_[4 * rq + 2], (bf16)V_[4 * rq + 3]};
-      } else {
-        *reinterpret_cast<f32x4*>(dkr + c) =
-            f32x4{K_[4 * rq] * p.scale, K_[4 * rq + 1] * p.scale, K_[4 * rq + 2] * p.scale,
-                  K_[4 * rq + 3] * p.scale};
-        *reinterpret_cast<f32x4*>(dvr + c) = f32x4{V_[4 * rq], V_[4 * rq + 1], V_[4 * rq + 2], V_[4 * rq + 3]};
-      }
-    }
+    for (int nb = 0; nb < D / 32; ++nb) { dk[nb] = f32x16{}; dv[nb] = f32x16{}; }
+    store_dkdv(kw);
+  }
 }
 
-// dQ: workgroup = (256 queries, head i, batch b); 4 waves x 64 queries. The
-// key-side tiles (K, V and K^T, 64 keys each) go straight from global memory
-// into a ring of LDS slots (global_load_lds), NBUF-1 tiles ahead of the one in
-// use, XOR-swizzled per row as in bwd_dkdv.
+// dQ: workgroup = (query tiles of 256 queries, head i, batch b); 4 waves x 64
+// queries. The key-side tiles (K, V and K^T, 64 keys each) go straight from
+// global memory into a ring of LDS slots (global_load_lds), NBUF-1 tiles ahead
+// of the one in use, XOR-swizzled per row as in bwd_dkdv.
+//
+// Order of the work, for L2 reuse as in bwd_dkdv: causal workgroup pr takes
+// query tile pr, walking its key tiles upward from the first, then query tile
+// n_qt-1-pr, walking its key tiles down from the last one it sees. Every
+// workgroup has the same number of items, and at each step all workgroups in
+// the same half read the same key tile. Without a mask every workgroup walks
+// all key tiles upward.
 template <typename T, int D>
 __global__ __launch_bounds__(256, 2) void bwd_dq(BwdParams p) {
   using MF = Mfma<T>;
@@ -411,23 +460,28 @@ __global__ __launch_bounds__(256, 2) void bwd_dq(BwdParams p) {
             wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int col = lane & 31, grp = lane >> 5;
   const int n_qt = p.Np / 256;
-  int qt = blockIdx.x % n_qt;
-  if (p.causal) qt = n_qt - 1 - qt;   // heaviest first
-  const int bi = blockIdx.x / n_qt, i = bi % p.H_q, b = bi / p.H_q;
+  const int n_units = p.causal ? (n_qt + 1) / 2 : n_qt;
+  const int pr = blockIdx.x % n_units, bi = blockIdx.x / n_units;
+  const int i = bi % p.H_q, b = bi / p.H_q;
   const int j = i / p.g;
-  const int q0 = qt * 256, qw = q0 + 64 * wave;
+  const int qt0 = pr, qt1 = n_qt - 1 - pr;
   const int64_t hq = (int64_t)b * p.H_q + i, hk = (int64_t)b * p.H_kv + j;
 
-  const int kv_len = p.causal ? min(p.N, q0 + 256) : p.N;
-  const int n_tiles = (kv_len + BT - 1) / BT;
+  // Items: the key tiles of query tile qt0 (phase 0), then, causal and
+  // qt1 != qt0, those of query tile qt1 (phase 1) in reverse.
+  auto kv_tiles = [&](int qt) { return ((p.causal ? min(p.N, qt * 256 + 256) : p.N) + BT - 1) / BT; };
+  const int n0 = kv_tiles(qt0);
+  const int nt1 = p.causal && qt1 != qt0 ? kv_tiles(qt1) : 0;
+  const int n_items = n0 + nt1;
+  auto item_tile = [&](int t) { return t < n0 ? t : nt1 - 1 - (t - n0); };
   const T* Kh = (const T*)p.k + hk * p.Np * D;
   const T* Vh = (const T*)p.v + hk * p.Np * D;
   const T* KTh = (const T*)p.kt + hk * D * p.Np;
 
-  // Loads of key tile t into ring slot t % NBUF (see bwd_dkdv's issue).
+  // Loads of item t (a key tile) into ring slot t % NBUF (see bwd_dkdv's issue).
   auto issue = [&](int t) {
-    if (t >= n_tiles) return;
-    const int k0 = t * BT;
+    if (t >= n_items) return;
+    const int k0 = item_tile(t) * BT;
     T* tb = smem + (t % NBUF) * TILE;
 #pragma unroll
     for (int x = 0; x < IPW; ++x) {
@@ -449,48 +503,86 @@ __global__ __launch_bounds__(256, 2) void bwd_dq(BwdParams p) {
                                        (lds_ptr)(tb + arr * TE + li * 64 * EPC), 16, 0, 0);
     }
   };
-  // Prologue: key tiles 0..NBUF-2 in flight, then this wave's Q and dO
-  // fragments (B operands of S^T = K Q^T and dP^T = V dO^T) and its rows'
-  // statistics, all landed before the loop.
-#pragma unroll
-  for (int t = 0; t < NBUF - 1; ++t) issue(t);
+
+  // This wave's Q and dO fragments (B operands of S^T = K Q^T and
+  // dP^T = V dO^T) and its rows' statistics for the query tile at q0, and the
+  // store of its dQ.
   Frag qf[QB][NS], of[QB][NS];
   float lse[QB], dvq[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int t = qw + 32 * qb + col;
-    const T* qr = (const T*)p.q + (hq * p.Np + t) * D;
-    const T* orow = (const T*)p.dO + (hq * p.Np + t) * D;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      qf[qb][s] = *reinterpret_cast<const Frag*>(qr + s * MF::KS + grp * MF::E);
-      of[qb][s] = *reinterpret_cast<const Frag*>(orow + s * MF::KS + grp * MF::E);
-    }
-    lse[qb] = t < p.N ? p.lse[hq * p.Np + t] : INFINITY;
-    dvq[qb] = t < p.N ? p.dvec[hq * p.Np + t] : 0.f;
-  }
   f32x16 dq[QB][D / 32];
+  auto load_q = [&](int qw) {
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
+    for (int qb = 0; qb < QB; ++qb) {
+      const int t = qw + 32 * qb + col;
+      const T* qr = (const T*)p.q + (hq * p.Np + t) * D;
+      const T* orow = (const T*)p.dO + (hq * p.Np + t) * D;
 #pragma unroll
-    for (int nb = 0; nb < D / 32; ++nb) dq[qb][nb] = f32x16{};
+      for (int s = 0; s < NS; ++s) {
+        qf[qb][s] = *reinterpret_cast<const Frag*>(qr + s * MF::KS + grp * MF::E);
+        of[qb][s] = *reinterpret_cast<const Frag*>(orow + s * MF::KS + grp * MF::E);
+      }
+      lse[qb] = t < p.N ? p.lse[hq * p.Np + t] : INFINITY;
+      dvq[qb] = t < p.N ? p.dvec[hq * p.Np + t] : 0.f;
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb) dq[qb][nb] = f32x16{};
+    }
+  };
+  // dQ^T: lane = query, register r = head dim 32*nb + 8*(r/4) + 4*grp + r%4.
+  auto store_dq = [&](int qw) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int t = qw + 32 * qb + col;
+      T* dqr = (T*)p.dqkv + ((int64_t)b * p.Np + t) * p.W + (int64_t)i * D;
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int c = nb * 32 + 8 * rq + 4 * grp;
+          const f32x16& a = dq[qb][nb];
+          if constexpr (sizeof(T) == 2) {
+            *reinterpret_cast<bf16x4*>(dqr + c) =
+                bf16x4{(bf16)(a[4 * rq] * p.scale), (bf16)(a[4 * rq + 1] * p.scale),
+                       (bf16)(a[4 * rq + 2] * p.scale), (bf16)(a[4 * rq + 3] * p.scale)};
+          } else {
+            *reinterpret_cast<f32x4*>(dqr + c) =
+                f32x4{a[4 * rq] * p.scale, a[4 * rq + 1] * p.scale, a[4 * rq + 2] * p.scale,
+                      a[4 * rq + 3] * p.scale};
+          }
+        }
+    }
+  };
+
+  // Prologue: items 0..NBUF-2 in flight, then the first query tile's
+  // fragments, all landed before the loop, which then waits only on its own
+  // loads.
+  int qw = qt0 * 256 + 64 * wave;   // this wave's first query
+#pragma unroll
+  for (int t = 0; t < NBUF - 1; ++t) issue(t);
+  load_q(qw);
   wait_vmcnt<0>();
   __syncthreads();
 
-  for (int t = 0; t < n_tiles; ++t) {
+  for (int t = 0; t < n_items; ++t) {
     if (t > 0) {
-      // tile t visible (tiles t+1.. may still be in flight), and every wave
-      // is done with slot (t-1) % NBUF, which takes tile t+NBUF-1
-      wait_vmcnt_tiles<VM_PER_TILE, NBUF - 2>(min(NBUF - 2, max(0, n_tiles - 1 - t)));
+      // item t visible (items t+1.. may still be in flight), and every wave
+      // is done with slot (t-1) % NBUF, which takes item t+NBUF-1
+      wait_vmcnt_tiles<VM_PER_TILE, NBUF - 2>(min(NBUF - 2, max(0, n_items - 1 - t)));
       ring_barrier();
     }
     issue(t + NBUF - 1);
+    if (t == n0) {   // second query tile: store the first one's dQ
+      store_dq(qw);
+      qw = qt1 * 256 + 64 * wave;
+      load_q(qw);
+      wait_vmcnt<0>();
+    }
     const T* Ks = smem + (t % NBUF) * TILE;
     const T* Vs = Ks + TE;
     const T* KTs = Ks + 2 * TE;
+    const int k0 = item_tile(t) * BT;
 #pragma unroll
     for (int jb = 0; jb < BT / 32; ++jb) {
-      const int kb = t * BT + 32 * jb;
+      const int kb = k0 + 32 * jb;
       if (kb >= p.N || (p.causal && kb > qw + 63)) continue;   // wave-uniform
       // LDS reads ahead of their use: K and V fragments before the S^T/dP^T
       // MFMAs, K^T fragments before the softmax work.
@@ -537,29 +629,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq(BwdParams p) {
             dq[qb][nb] = MF::run(line_frag<T>(KTs, nb * 32 + col, 32 * jb, h, grp), frag_regs<T>(s[qb], h), dq[qb][nb]);
     }
   }
-
-  // dQ^T: lane = query, register r = head dim 32*nb + 8*(r/4) + 4*grp + r%4.
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int t = qw + 32 * qb + col;
-    T* dqr = (T*)p.dqkv + ((int64_t)b * p.Np + t) * p.W + (int64_t)i * D;
-#pragma unroll
-    for (int nb = 0; nb < D / 32; ++nb)
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int c = nb * 32 + 8 * rq + 4 * grp;
-        const f32x16& a = dq[qb][nb];
-        if constexpr (sizeof(T) == 2) {
-          *reinterpret_cast<bf16x4*>(dqr + c) =
-              bf16x4{(bf16)(a[4 * rq] * p.scale), (bf16)(a[4 * rq + 1] * p.scale),
-                     (bf16)(a[4 * rq + 2] * p.scale), (bf16)(a[4 * rq + 3] * p.scale)};
-        } else {
-          *reinterpret_cast<f32x4*>(dqr + c) =
-              f32x4{a[4 * rq] * p.scale, a[4 * rq + 1] * p.scale, a[4 * rq + 2] * p.scale,
-                    a[4 * rq + 3] * p.scale};
-        }
-      }
-  }
+  store_dq(qw);
 }
 
 template <typename T, bool PERM = false>
@@ -688,9 +758,13 @@ hipError_t backward_impl(const void* x, const void* wq, const void* wk, const vo
   if ((Np / 256) * B * H_kv > 0x7FFFFFFF || (Np / 256) * B * H_q > 0x7FFFFFFF ||
       (int64_t)D * Np * (int64_t)sizeof(T) > 0xFFFFFFFFll)
     return hipErrorInvalidConfiguration;
-  bwd_dkdv<T, D><<<(unsigned)((Np / 256) * B * H_kv), 512, 0, stream>>>(p);
+  // causal: workgroups take pairs of 256-key tiles (kt, n_kt-1-kt)
+  const int64_t n_kt = Np / 256;
+  bwd_dkdv<T, D><<<(unsigned)((causal ? (n_kt + 1) / 2 : n_kt) * B * H_kv), 512, 0, stream>>>(p);
   SQA_CK(hipGetLastError());
-  bwd_dq<T, D><<<(unsigned)((Np / 256) * B * H_q), 256, 0, stream>>>(p);
+  // causal: workgroups take pairs of 256-query tiles (qt, n_qt-1-qt)
+  const int64_t n_qt = Np / 256;
+  bwd_dq<T, D><<<(unsigned)((causal ? (n_qt + 1) / 2 : n_qt) * B * H_q), 256, 0, stream>>>(p);
   SQA_CK(hipGetLastError());
   // dX = [dQ | dK | dV] [Wq | Wk | Wv]^T
   concat_weights<T><<<(unsigned)((d_model * W + 255) / 256), 256, 0, stream>>>(
