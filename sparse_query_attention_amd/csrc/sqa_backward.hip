@@ -257,31 +257,41 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
 
   // Loads of work item w into ring slot w % NBUF. Load `ins` of the tile's
   // 4*INS covers 64 16-byte chunks of one operand tile; lane L's chunk lands
-  // at position 64*ins + L, which holds chunk (c ^ swz(row)) of its row.
+  // at position 64*ins + L, which holds chunk (c ^ swz(row)) of its row. All
+  // of a wave's loads fall in one operand tile (arr), and their per-lane byte
+  // offsets are the same for every item, so they are computed once; an item
+  // only moves the wave-uniform base.
+  static_assert(INS % IPW == 0, "a wave's loads within one operand tile");
+  const int arr = wave * IPW / INS;
+  uint32_t loff[IPW];
+#pragma unroll
+  for (int x = 0; x < IPW; ++x) {
+    const int pos = (wave * IPW + x) % INS * 64 + lane;
+    if (arr < 2) {   // Q, dO rows
+      const int r = pos / RC, c = pos % RC;
+      loff[x] = (uint32_t)((r * D + (c ^ swz<RC>(r)) * EPC) * (int)sizeof(T));
+    } else {         // Q^T, dO^T lines (tokens in swap23 order)
+      const int r = pos / LC, c = pos % LC;
+      loff[x] = (uint32_t)r * (uint32_t)p.Np * (uint32_t)sizeof(T) + (uint32_t)((c ^ swz<LC>(r)) * EPC * (int)sizeof(T));
+    }
+  }
+  const T* arr_base = (const T*)(arr == 0 ? p.q : arr == 1 ? p.dO : arr == 2 ? p.qt : p.dOt);
+  const int which = wave >> 2, part = wave & 3;   // row statistics: lse (waves 0-3), D (4-7)
   auto issue = [&](int w) {
     if (w >= n_work) return;
     const int i = j * p.g + item_head(w), q0 = item_tile(w) * BT;
     const int64_t hq = (int64_t)b * p.H_q + i;
-    T* tb = smem + (w % NBUF) * TILE;
+    T* tb = smem + (w % NBUF) * TILE + arr * TE;
+    const T* base = arr_base + (arr < 2 ? (hq * p.Np + q0) * D : hq * D * p.Np + q0);
 #pragma unroll
     for (int x = 0; x < IPW; ++x) {
-      const int ins = wave * IPW + x, arr = ins / INS, li = ins % INS;
-      const int pos = li * 64 + lane;
-      const T* src;
-      if (arr < 2) {   // Q, dO rows
-        const int r = pos / RC, c = pos % RC;
-        src = (const T*)(arr == 0 ? p.q : p.dO) + (hq * p.Np + q0 + r) * D + (c ^ swz<RC>(r)) * EPC;
-      } else {         // Q^T, dO^T lines (tokens in swap23 order)
-        const int r = pos / LC, c = pos % LC;
-        src = (const T*)(arr == 2 ? p.qt : p.dOt) + (hq * D + r) * (int64_t)p.Np + q0 +
-              (c ^ swz<LC>(r)) * EPC;
-      }
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)(tb + arr * TE + li * 64 * EPC), 16, 0, 0);
+      const int li = (wave * IPW + x) % INS;
+      __builtin_amdgcn_global_load_lds((const void*)((const char*)base + loff[x]),
+                                       (lds_ptr)(tb + li * 64 * EPC), 16, 0, 0);
     }
-    // row statistics: waves 0-3 load 16 lse values each, waves 4-7 16 D values
-    const int which = wave >> 2, part = wave & 3;
+    // row statistics: 16 values per wave
     const float* src = (which ? p.dvec : p.lse) + hq * p.Np + q0 + part * 16 + (lane & 15);
-    float* dst = reinterpret_cast<float*>(tb + 4 * TE) + which * BT + part * 16;
+    float* dst = reinterpret_cast<float*>(smem + (w % NBUF) * TILE + 4 * TE) + which * BT + part * 16;
     if (lane < 16) __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)dst, 4, 0, 0);
   };
 
@@ -478,7 +488,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dq(BwdParams p) {
   const T* Vh = (const T*)p.v + hk * p.Np * D;
   const T* KTh = (const T*)p.kt + hk * D * p.Np;
 
-  // Loads of item t (a key tile) into ring slot t % NBUF (see bwd_dkdv's issue).
+  // Loads of item t (a key tile) into ring slot t % NBUF (see bwd_dkdv's
+  // issue): per-lane byte offsets computed once, wave-uniform bases per item.
+  uint32_t loff[IPW];
+#pragma unroll
+  for (int x = 0; x < IPW; ++x) {
+    const int ins = wave * IPW + x, arr = ins / INS, pos = ins % INS * 64 + lane;
+    if (arr < 2) {   // K, V rows
+      const int r = pos / RC, c = pos % RC;
+      loff[x] = (uint32_t)((r * D + (c ^ swz<RC>(r)) * EPC) * (int)sizeof(T));
+    } else {         // K^T lines (keys in swap23 order)
+      const int r = pos / LC, c = pos % LC;
+      loff[x] = (uint32_t)r * (uint32_t)p.Np * (uint32_t)sizeof(T) + (uint32_t)((c ^ swz<LC>(r)) * EPC * (int)sizeof(T));
+    }
+  }
   auto issue = [&](int t) {
     if (t >= n_items) return;
     const int k0 = item_tile(t) * BT;
@@ -486,20 +509,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq(BwdParams p) {
 #pragma unroll
     for (int x = 0; x < IPW; ++x) {
       const int ins = wave * IPW + x, arr = ins / INS, li = ins % INS;
-      const int pos = li * 64 + lane;
-      // a uniform base and a 32-bit per-lane byte offset (one VGPR per load)
-      const T* base;
-      uint32_t off;
-      if (arr < 2) {   // K, V rows
-        const int r = pos / RC, c = pos % RC;
-        base = (arr == 0 ? Kh : Vh) + (int64_t)k0 * D;
-        off = (uint32_t)((r * D + (c ^ swz<RC>(r)) * EPC) * (int)sizeof(T));
-      } else {         // K^T lines (keys in swap23 order)
-        const int r = pos / LC, c = pos % LC;
-        base = KTh + k0;
-        off = (uint32_t)r * (uint32_t)p.Np * (uint32_t)sizeof(T) + (uint32_t)((c ^ swz<LC>(r)) * EPC * (int)sizeof(T));
-      }
-      __builtin_amdgcn_global_load_lds((const void*)((const char*)base + off),
+      const T* base = arr == 0 ? Kh + (int64_t)k0 * D : arr == 1 ? Vh + (int64_t)k0 * D : KTh + k0;
+      __builtin_amdgcn_global_load_lds((const void*)((const char*)base + loff[x]),
                                        (lds_ptr)(tb + arr * TE + li * 64 * EPC), 16, 0, 0);
     }
   };
