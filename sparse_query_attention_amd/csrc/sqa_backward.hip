@@ -338,6 +338,11 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
   // the first key tile, all landed before the loop, which then waits only on
   // its own loads.
   int kw = kt0 * KPG + KPW * wave;   // this wave's first key
+  // Waves w and w+4 share a SIMD, and the barrier after each item starts them
+  // in the same phase (S/dP MFMAs, then softmax VALU, then dV/dK MFMAs).
+  // Issue priority for the lower half lets one run ahead into the phase the
+  // other is not in (1.2 % on the 131072-token causal shape).
+  if (wave < 4) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int t = 0; t < NBUF - 1; ++t) issue(t);
   load_kv(kw);
