@@ -578,72 +578,89 @@ __global__ __launch_bounds__(256, 2) void bwd_dq(BwdParams p) {
   wait_vmcnt<0>();
   __syncthreads();
 
-  for (int t = 0; t < n_items; ++t) {
-    if (t > 0) {
-      // item t visible (items t+1.. may still be in flight), and every wave
-      // is done with slot (t-1) % NBUF, which takes item t+NBUF-1
-      wait_vmcnt_tiles<VM_PER_TILE, NBUF - 2>(min(NBUF - 2, max(0, n_items - 1 - t)));
-      ring_barrier();
-    }
-    issue(t + NBUF - 1);
-    if (t == n0) {   // second query tile: store the first one's dQ
-      store_dq(qw);
-      qw = qt1 * 256 + 64 * wave;
-      load_q(qw);
-      wait_vmcnt<0>();
-    }
-    const T* Ks = smem + (t % NBUF) * TILE;
-    const T* Vs = Ks + TE;
-    const T* KTs = Ks + 2 * TE;
-    const int k0 = item_tile(t) * BT;
-#pragma unroll
-    for (int jb = 0; jb < BT / 32; ++jb) {
-      const int kb = k0 + 32 * jb;
-      if (kb >= p.N || (p.causal && kb > qw + 63)) continue;   // wave-uniform
-      // LDS reads ahead of their use: K and V fragments before the S^T/dP^T
-      // MFMAs, K^T fragments before the softmax work.
-      Frag ka[NS], va[NS];
-#pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        ka[st] = row_frag<T, D>(Ks, 32 * jb + col, st, grp);
-        va[st] = row_frag<T, D>(Vs, 32 * jb + col, st, grp);
+  // Items [t0, t1). Key tiles left of the diagonal and before the sequence
+  // end need no mask for any wave; the loop over them is compiled without the
+  // mask code (a fifth of the VALU work per block), and the few others run in
+  // a copy that keeps it. Separate loops, rather than a branch per block, keep
+  // each one's registers within 256.
+  auto run_items = [&](int t0, int t1, auto mask_on) {
+    constexpr bool MASK = decltype(mask_on)::value;
+    for (int t = t0; t < t1; ++t) {
+      if (t > 0) {
+        // item t visible (items t+1.. may still be in flight), and every wave
+        // is done with slot (t-1) % NBUF, which takes item t+NBUF-1
+        wait_vmcnt_tiles<VM_PER_TILE, NBUF - 2>(min(NBUF - 2, max(0, n_items - 1 - t)));
+        ring_barrier();
       }
-      f32x16 s[QB], dp[QB];
+      issue(t + NBUF - 1);
+      const T* Ks = smem + (t % NBUF) * TILE;
+      const T* Vs = Ks + TE;
+      const T* KTs = Ks + 2 * TE;
+      const int k0 = item_tile(t) * BT;
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) { s[qb] = f32x16{}; dp[qb] = f32x16{}; }
+      for (int jb = 0; jb < BT / 32; ++jb) {
+        const int kb = k0 + 32 * jb;
+        if (MASK && (kb >= p.N || (p.causal && kb > qw + 63))) continue;   // wave-uniform
+        // LDS reads ahead of their use: K and V fragments before the S^T/dP^T
+        // MFMAs, K^T fragments before the softmax work.
+        Frag ka[NS], va[NS];
 #pragma unroll
-      for (int st = 0; st < NS; ++st)
+        for (int st = 0; st < NS; ++st) {
+          ka[st] = row_frag<T, D>(Ks, 32 * jb + col, st, grp);
+          va[st] = row_frag<T, D>(Vs, 32 * jb + col, st, grp);
+        }
+        f32x16 s[QB], dp[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) { s[qb] = f32x16{}; dp[qb] = f32x16{}; }
+#pragma unroll
+        for (int st = 0; st < NS; ++st)
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            s[qb] = MF::run(ka[st], qf[qb][st], s[qb]);
+            dp[qb] = MF::run(va[st], of[qb][st], dp[qb]);
+          }
+        // register r: key kb + 8*(r/4) + 4*grp + r%4; column: query qw + 32*qb + col.
+        // Register r holds key kb + 4*grp + o_r with o_r = 8*(r/4) + r%4. The
+        // key is visible iff o_r < lim: lim = N - kb - 4*grp, and for causal
+        // also <= q - kb - 4*grp.
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-          s[qb] = MF::run(ka[st], qf[qb][st], s[qb]);
-          dp[qb] = MF::run(va[st], of[qb][st], dp[qb]);
-        }
-
-      // register r: key kb + 8*(r/4) + 4*grp + r%4; column: query qw + 32*qb + col.
-      // Register r holds key kb + 4*grp + o_r with o_r = 8*(r/4) + r%4. The key
-      // is visible iff o_r < lim: lim = N - kb - 4*grp, and for causal also
-      // <= q - kb - 4*grp. One compare per score; away from the diagonal and
-      // the sequence end lim exceeds every o_r. (A wave-uniform branch around
-      // an unmasked copy, as in bwd_dkdv, would push this kernel past 256
-      // VGPRs.)
+          const int base = kb + 4 * grp;
+          const int lim = p.causal ? min(p.N - base, qw + 32 * qb + col - base + 1) : p.N - base;
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const int base = kb + 4 * grp;
-        const int lim = p.causal ? min(p.N - base, qw + 32 * qb + col - base + 1) : p.N - base;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(s[qb][r], p.c, -lse[qb]));
-          s[qb][r] = 8 * (r / 4) + r % 4 < lim ? pv * (dp[qb][r] - dvq[qb]) : 0.f;   // dS^T
+          for (int r = 0; r < 16; ++r) {
+            const float pv = __builtin_amdgcn_exp2f(fmaf(s[qb][r], p.c, -lse[qb]));
+            const float ds = pv * (dp[qb][r] - dvq[qb]);   // dS^T
+            s[qb][r] = !MASK || 8 * (r / 4) + r % 4 < lim ? ds : 0.f;
+          }
         }
+#pragma unroll
+        for (int h = 0; h < kHalves<T>; ++h)
+#pragma unroll
+          for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+              dq[qb][nb] = MF::run(line_frag<T>(KTs, nb * 32 + col, 32 * jb, h, grp), frag_regs<T>(s[qb], h), dq[qb][nb]);
       }
-#pragma unroll
-      for (int h = 0; h < kHalves<T>; ++h)
-#pragma unroll
-        for (int nb = 0; nb < D / 32; ++nb)
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            dq[qb][nb] = MF::run(line_frag<T>(KTs, nb * 32 + col, 32 * jb, h, grp), frag_regs<T>(s[qb], h), dq[qb][nb]);
     }
+  };
+  // Key tiles [0, clear) are fully visible to every query of query tile qt:
+  // all of their keys precede the tile's first query (or any key is visible,
+  // without a mask) and lie before N.
+  auto clear_tiles = [&](int qt) { return min(p.causal ? qt * 256 / BT : p.N / BT, p.N / BT); };
+  // Phase 0 walks key tiles upward: the clear ones first.
+  const int d0 = min(clear_tiles(qt0), n0);
+  run_items(0, d0, std::false_type{});
+  run_items(d0, n0, std::true_type{});
+  if (n_items > n0) {   // second query tile: store the first one's dQ
+    store_dq(qw);
+    qw = qt1 * 256 + 64 * wave;
+    load_q(qw);
+    wait_vmcnt<0>();
+    // Phase 1 walks key tiles downward: the clear ones last.
+    const int m1 = n0 + max(0, nt1 - clear_tiles(qt1));
+    run_items(n0, m1, std::true_type{});
+    run_items(m1, n_items, std::false_type{});
   }
   store_dq(qw);
 }
