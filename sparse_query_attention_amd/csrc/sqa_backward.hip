@@ -351,60 +351,54 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
   wait_vmcnt<0>();
   __syncthreads();
 
-  for (int w = 0; w < n_work; ++w) {
-    if (w > 0) {
-      // item w visible (items w+1.. may still be in flight), and every wave
-      // is done with slot (w-1) % NBUF, which takes item w+NBUF-1
-      wait_vmcnt_tiles<VM_PER_TILE, NBUF - 2>(min(NBUF - 2, max(0, n_work - 1 - w)));
-      ring_barrier();
-    }
-    issue(w + NBUF - 1);
-    if (w == n0) {   // second key tile: store the first one's gradients
-      store_dkdv(kw);
-      kw = kt1 * KPG + KPW * wave;
-      load_kv(kw);
-#pragma unroll
-      for (int nb = 0; nb < D / 32; ++nb) { dk[nb] = f32x16{}; dv[nb] = f32x16{}; }
-      wait_vmcnt<0>();
-    }
-    const T* Qs = smem + (w % NBUF) * TILE;
-    const T* Os = Qs + TE;
-    const T* QTs = Qs + 2 * TE;
-    const T* OTs = Qs + 3 * TE;
-    const float* lse_s = reinterpret_cast<const float*>(Qs + 4 * TE);
-    const float* dv_s = lse_s + BT;
-    const int q0 = item_tile(w) * BT;
-#pragma unroll
-    for (int qs = 0; qs < BT / 32; ++qs) {
-      const int qb = q0 + 32 * qs;
-      // wave-uniform skips: every query before this wave's first key, or past N
-      if ((p.causal && qb + 31 < kw) || qb >= p.N) continue;
-      // LDS reads are issued ahead of their use: the Q and dO fragments
-      // before the S/dP MFMAs, the row statistics before the softmax work.
-      Frag qa[NS], oa[NS];
-#pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        qa[st] = row_frag<T, D>(Qs, 32 * qs + col, st, grp);
-        oa[st] = row_frag<T, D>(Os, 32 * qs + col, st, grp);
+  // Items [w0, w1). Query tiles that see every key of the key tile (all of
+  // them after its last key, and the keys before N) need no mask; the loop
+  // over them is compiled without the mask code and the few others run in a
+  // copy that keeps it (separate loops, as in bwd_dq).
+  auto run_items = [&](int w0, int w1, auto mask_on) {
+    constexpr bool MASK = decltype(mask_on)::value;
+    for (int w = w0; w < w1; ++w) {
+      if (w > 0) {
+        // item w visible (items w+1.. may still be in flight), and every wave
+        // is done with slot (w-1) % NBUF, which takes item w+NBUF-1
+        wait_vmcnt_tiles<VM_PER_TILE, NBUF - 2>(min(NBUF - 2, max(0, n_work - 1 - w)));
+        ring_barrier();
       }
-      f32x16 s = f32x16{}, dp = f32x16{};
+      issue(w + NBUF - 1);
+      const T* Qs = smem + (w % NBUF) * TILE;
+      const T* Os = Qs + TE;
+      const T* QTs = Qs + 2 * TE;
+      const T* OTs = Qs + 3 * TE;
+      const float* lse_s = reinterpret_cast<const float*>(Qs + 4 * TE);
+      const float* dv_s = lse_s + BT;
+      const int q0 = item_tile(w) * BT;
 #pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        s = MF::run(qa[st], kf[st], s);
-        dp = MF::run(oa[st], vf[st], dp);
-      }
-      f32x4 l4s[4], d4s[4];
+      for (int qs = 0; qs < BT / 32; ++qs) {
+        const int qb = q0 + 32 * qs;
+        // wave-uniform skips: every query before this wave's first key, or past N
+        if (MASK && ((p.causal && qb + 31 < kw) || qb >= p.N)) continue;
+        // LDS reads are issued ahead of their use: the Q and dO fragments
+        // before the S/dP MFMAs, the row statistics before the softmax work.
+        Frag qa[NS], oa[NS];
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int rl = 32 * qs + 8 * r4 + 4 * grp;
-        l4s[r4] = *reinterpret_cast<const f32x4*>(&lse_s[rl]);
-        d4s[r4] = *reinterpret_cast<const f32x4*>(&dv_s[rl]);
-      }
-      // register r: query qb + 8*(r/4) + 4*grp + r%4; column: key kw + col.
-      // Only blocks that cross the diagonal or the sequence end are masked
-      // (a wave-uniform choice); elsewhere every key is visible.
-      const bool masked = kw + KPW > p.N || (p.causal && kw + KPW - 1 > qb);
-      auto softmax_grad = [&](auto mask_on) {
+        for (int st = 0; st < NS; ++st) {
+          qa[st] = row_frag<T, D>(Qs, 32 * qs + col, st, grp);
+          oa[st] = row_frag<T, D>(Os, 32 * qs + col, st, grp);
+        }
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+          s = MF::run(qa[st], kf[st], s);
+          dp = MF::run(oa[st], vf[st], dp);
+        }
+        f32x4 l4s[4], d4s[4];
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int rl = 32 * qs + 8 * r4 + 4 * grp;
+          l4s[r4] = *reinterpret_cast<const f32x4*>(&lse_s[rl]);
+          d4s[r4] = *reinterpret_cast<const f32x4*>(&dv_s[rl]);
+        }
+        // register r: query qb + 8*(r/4) + 4*grp + r%4; column: key kw + col.
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const f32x4 l4 = l4s[r4], d4 = d4s[r4];
@@ -413,23 +407,44 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * r4 + e, q = qb + 8 * r4 + 4 * grp + e;
             float pv = __builtin_amdgcn_exp2f(fmaf(s[r], p.c, -l4[e]));
-            if constexpr (decltype(mask_on)::value)
-              pv = key >= p.N || (p.causal && key > q) ? 0.f : pv;
+            if (MASK) pv = key >= p.N || (p.causal && key > q) ? 0.f : pv;
             s[r] = pv;                       // P
             dp[r] = pv * (dp[r] - d4[e]);    // dS
           }
         }
-      };
-      if (masked) softmax_grad(std::true_type{});
-      else softmax_grad(std::false_type{});
 #pragma unroll
-      for (int h = 0; h < kHalves<T>; ++h)
+        for (int h = 0; h < kHalves<T>; ++h)
 #pragma unroll
-        for (int nb = 0; nb < D / 32; ++nb) {
-          dv[nb] = MF::run(line_frag<T>(OTs, nb * 32 + col, 32 * qs, h, grp), frag_regs<T>(s, h), dv[nb]);
-          dk[nb] = MF::run(line_frag<T>(QTs, nb * 32 + col, 32 * qs, h, grp), frag_regs<T>(dp, h), dk[nb]);
-        }
+          for (int nb = 0; nb < D / 32; ++nb) {
+            dv[nb] = MF::run(line_frag<T>(OTs, nb * 32 + col, 32 * qs, h, grp), frag_regs<T>(s, h), dv[nb]);
+            dk[nb] = MF::run(line_frag<T>(QTs, nb * 32 + col, 32 * qs, h, grp), frag_regs<T>(dp, h), dk[nb]);
+          }
+      }
     }
+  };
+  // Query tiles walked for key tile kt that see all of its keys: with a mask
+  // the ones after its last key, [4kt + 4, qt_end); without one, all. None if
+  // the key tile reaches past N.
+  auto clear_tiles = [&](int kt) {
+    if ((kt + 1) * KPG > p.N) return 0;
+    return p.causal ? max(0, qt_end - (kt + 1) * (KPG / BT)) : qt_end;
+  };
+  // Phase 0 walks its query tiles downward (upward without a mask, where they
+  // are all clear or all masked): the clear ones first.
+  const int c0 = min(n0, clear_tiles(kt0) * p.g);
+  run_items(0, c0, std::false_type{});
+  run_items(c0, n0, std::true_type{});
+  if (n_work > n0) {   // second key tile: store the first one's gradients
+    store_dkdv(kw);
+    kw = kt1 * KPG + KPW * wave;
+    load_kv(kw);
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb) { dk[nb] = f32x16{}; dv[nb] = f32x16{}; }
+    wait_vmcnt<0>();
+    // Phase 1 walks its query tiles upward: the clear ones last.
+    const int m1 = max(n0, n_work - clear_tiles(kt1) * p.g);
+    run_items(n0, m1, std::true_type{});
+    run_items(m1, n_work, std::false_type{});
   }
   // The last key tile's gradients. A key tile that no query reaches (wholly
   // past N) stores zeros: the weight gradients read those padding rows.
