@@ -13,19 +13,22 @@
 //   dX = [dQ | dK | dV] [Wq | Wk | Wv]^T,  [dWq | dWk | dWv] = X^T [dQ | dK | dV]
 //
 // Attention backward runs as two kernels and needs no atomics:
-//  * dkdv: a workgroup owns 128 keys of one key/value head (32 per wave, held
-//    as MFMA operands in registers) and walks the query
-//    tiles of all g heads of the group, so the g-way sum of dK and dV stays in
+//  * dkdv: a workgroup of 8 waves owns 256 keys of one key/value head (32 per
+//    wave, held as MFMA operands in registers) and walks the query tiles of
+//    all g heads of the group, so the g-way sum of dK and dV stays in
 //    registers. Per 32-query block: S = Q K^T and dP = dO V^T (lane = key),
 //    then dV^T += dO^T P and dK^T += Q^T dS with P and dS consumed from
 //    registers as B operands.
 //  * dq: a workgroup owns 256 queries of one head (64 per wave) and walks the
 //    key tiles: S^T = K Q^T and dP^T = V dO^T (lane = query, so the row's
 //    log-sum-exp and D are per-lane scalars), then dQ^T += K^T dS^T.
+// Both stream their tiles through rings of LDS slots filled by direct loads,
+// pair their tiles so that concurrent workgroups read the same tiles (L2
+// reuse), and run the tiles that need no mask in loops without mask code.
 // The contraction over the score rows needs the other operand with those rows
-// contiguous, so Q^T, dO^T, K^T and V row-major are written once by a
-// transpose kernel. Token-contiguous copies of X, A, dY and [dQ|dK|dV] feed the
-// weight-gradient products (split-K over all tokens).
+// contiguous, so Q^T, dO^T, K^T (tokens in swap23 order) and V row-major are
+// written once by a transpose kernel. Token-contiguous copies of X, A, dY and
+// [dQ|dK|dV] feed the weight-gradient products (split-K over all tokens).
 #include <math.h>
 
 #include <algorithm>
