@@ -375,53 +375,69 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
       const float* lse_s = reinterpret_cast<const float*>(Qs + 4 * TE);
       const float* dv_s = lse_s + BT;
       const int q0 = item_tile(w) * BT;
-#pragma unroll
-      for (int qs = 0; qs < BT / 32; ++qs) {
-        const int qb = q0 + 32 * qs;
-        // wave-uniform skips: every query before this wave's first key, or past N
-        if (MASK && ((p.causal && qb + 31 < kw) || qb >= p.N)) continue;
-        // LDS reads are issued ahead of their use: the Q and dO fragments
-        // before the S/dP MFMAs, the row statistics before the softmax work.
+      // S = Q K^T and dP = dO V^T of 32-query block qs (lane = key).
+      auto scores = [&](int qs, f32x16& sc, f32x16& dpc) {
         Frag qa[NS], oa[NS];
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
           qa[st] = row_frag<T, D>(Qs, 32 * qs + col, st, grp);
           oa[st] = row_frag<T, D>(Os, 32 * qs + col, st, grp);
         }
-        f32x16 s = f32x16{}, dp = f32x16{};
+        sc = f32x16{};
+        dpc = f32x16{};
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
-          s = MF::run(qa[st], kf[st], s);
-          dp = MF::run(oa[st], vf[st], dp);
+          sc = MF::run(qa[st], kf[st], sc);
+          dpc = MF::run(oa[st], vf[st], dpc);
         }
-        f32x4 l4s[4], d4s[4];
+      };
+      // P and dS in place (register r: query qb + 8*(r/4) + 4*grp + r%4; column:
+      // key kw + col), then dV^T += dO^T P and dK^T += Q^T dS. The row
+      // statistics are read four rows at a time, just before their use.
+      auto grads = [&](int qs, f32x16& sc, f32x16& dpc) {
+        const int qb = q0 + 32 * qs;
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const int rl = 32 * qs + 8 * r4 + 4 * grp;
-          l4s[r4] = *reinterpret_cast<const f32x4*>(&lse_s[rl]);
-          d4s[r4] = *reinterpret_cast<const f32x4*>(&dv_s[rl]);
-        }
-        // register r: query qb + 8*(r/4) + 4*grp + r%4; column: key kw + col.
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x4 l4 = l4s[r4], d4 = d4s[r4];
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse_s[rl]);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dv_s[rl]);
           const int key = kw + col;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * r4 + e, q = qb + 8 * r4 + 4 * grp + e;
-            float pv = __builtin_amdgcn_exp2f(fmaf(s[r], p.c, -l4[e]));
+            float pv = __builtin_amdgcn_exp2f(fmaf(sc[r], p.c, -l4[e]));
             if (MASK) pv = key >= p.N || (p.causal && key > q) ? 0.f : pv;
-            s[r] = pv;                       // P
-            dp[r] = pv * (dp[r] - d4[e]);    // dS
+            sc[r] = pv;                        // P
+            dpc[r] = pv * (dpc[r] - d4[e]);    // dS
           }
         }
 #pragma unroll
         for (int h = 0; h < kHalves<T>; ++h)
 #pragma unroll
           for (int nb = 0; nb < D / 32; ++nb) {
-            dv[nb] = MF::run(line_frag<T>(OTs, nb * 32 + col, 32 * qs, h, grp), frag_regs<T>(s, h), dv[nb]);
-            dk[nb] = MF::run(line_frag<T>(QTs, nb * 32 + col, 32 * qs, h, grp), frag_regs<T>(dp, h), dk[nb]);
+            dv[nb] = MF::run(line_frag<T>(OTs, nb * 32 + col, 32 * qs, h, grp), frag_regs<T>(sc, h), dv[nb]);
+            dk[nb] = MF::run(line_frag<T>(QTs, nb * 32 + col, 32 * qs, h, grp), frag_regs<T>(dpc, h), dk[nb]);
           }
+      };
+      if constexpr (!MASK) {
+        // Both blocks' scores first: the second block's MFMAs run while the
+        // first block's softmax takes the VALU, and its gradient MFMAs while
+        // the second block's softmax does.
+        f32x16 s0, dp0, s1, dp1;
+        scores(0, s0, dp0);
+        scores(1, s1, dp1);
+        grads(0, s0, dp0);
+        grads(1, s1, dp1);
+      } else {
+#pragma unroll
+        for (int qs = 0; qs < BT / 32; ++qs) {
+          const int qb = q0 + 32 * qs;
+          // wave-uniform skips: every query before this wave's first key, or past N
+          if ((p.causal && qb + 31 < kw) || qb >= p.N) continue;
+          f32x16 sc, dpc;
+          scores(qs, sc, dpc);
+          grads(qs, sc, dpc);
+        }
       }
     }
   };
