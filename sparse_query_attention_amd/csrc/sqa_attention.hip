@@ -462,8 +462,9 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
   // Masking touches only S(j), so it stays a small branch in front of the one
   // copy of the step body (two copies of the body would double its register
   // footprint at their merge).
-  auto run_step = [&](int j, f32x16 (&s_cur)[QB], f32x16 (&s_next)[QB]) {
-    const bool masked = j * 32 + 32 > L || (p.causal && j * 32 + 31 > qw);
+  auto run_step = [&](int j, f32x16 (&s_cur)[QB], f32x16 (&s_next)[QB], auto mask_on) {
+    const bool masked =
+        decltype(mask_on)::value && (j * 32 + 32 > L || (p.causal && j * 32 + 31 > qw));
     if (masked) mask(s_cur, j);
     float bsum[QB];
     if constexpr (sizeof(T) == 2) {
@@ -491,17 +492,31 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) sB[qb] = f32x16{};   // P(-1) = 0
   qk(0, sA);
-  for (int j = 0; j < nblk; j += 2) {
-    run_step(j, sA, sB);
+  // Before odd block 2t+1: tile t+1 must be visible (loads of tiles t+2.. may
+  // still be in flight), and tile t-1 is no longer read, so its slot takes
+  // tile t+NBUF-1.
+  auto advance = [&](int j) {
+    const int t = j >> 1;
+    wait_vmcnt_tiles<VM_PER_TILE, NBUF - 3>(min(NBUF - 3, max(0, n_tiles - (t + 2))));
+    __syncthreads();
+    issue(t + NBUF - 1);
+  };
+  // Blocks before jc (even) need no mask for this wave: their keys precede its
+  // first query (causal) and the sequence end. That loop is compiled without
+  // the mask code; the second keeps it. Every wave passes the barriers at the
+  // same blocks, whichever loop it is in.
+  const int jc = min(nblk, min(L / 32, p.causal ? qw / 32 : nblk)) & ~1;
+  int j = 0;
+  for (; j < jc; j += 2) {
+    run_step(j, sA, sB, std::false_type{});
+    advance(j);   // j + 1 < jc <= nblk
+    run_step(j + 1, sB, sA, std::false_type{});
+  }
+  for (; j < nblk; j += 2) {
+    run_step(j, sA, sB, std::true_type{});
     if (j + 1 < nblk) {
-      // Odd block 2t+1: tile t+1 must be visible (loads of tiles t+2.. may
-      // still be in flight), and tile t-1 is no longer read, so its slot
-      // takes tile t+NBUF-1.
-      const int t = j >> 1;
-      wait_vmcnt_tiles<VM_PER_TILE, NBUF - 3>(min(NBUF - 3, max(0, n_tiles - (t + 2))));
-      __syncthreads();
-      issue(t + NBUF - 1);
-      run_step(j + 1, sB, sA);
+      advance(j);
+      run_step(j + 1, sB, sA, std::true_type{});
     }
   }
   if (nblk & 1) pv(nblk - 1, sA); else pv(nblk - 1, sB);
