@@ -39,25 +39,6 @@ constexpr int BM = 128, BN = 128, BK = 32, THREADS = 256, WAVES = 4;
 constexpr int NST = 4;   // LDS ring stages
 constexpr int XCDS = 8;
 
-typedef __attribute__((address_space(3))) void* lds_ptr;
-
-template <int CPR> __device__ inline int swz(int r);
-template <> __device__ inline int swz<8>(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-template <> __device__ inline int swz<4>(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
-
-template <int N> __device__ inline void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-template <int PER, int MAXN> __device__ inline void wait_vmcnt_stages(int n) {
-  if constexpr (MAXN > 0) {
-    if (n >= MAXN) { wait_vmcnt<MAXN * PER>(); return; }
-    wait_vmcnt_stages<PER, MAXN - 1>(n);
-  } else {
-    wait_vmcnt<0>();
-  }
-}
-
 template <typename T> struct GemmCfg {
   static constexpr int EPC = 16 / sizeof(T);          // elements per 16-byte chunk
   static constexpr int CPR = BK / EPC;                 // chunks per tile row (4 bf16, 8 fp32)
@@ -288,7 +269,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Rows rows, const T* wt, i
     // All NST stages in flight; stage 0 visible; its first fragments read.
 #pragma unroll
     for (int s = 0; s < NST; ++s) issue(s);
-    wait_vmcnt_stages<C::VM, NST - 1>(min(NST - 1, nk - 1));
+    wait_vmcnt_tiles<C::VM, NST - 1>(min(NST - 1, nk - 1));
     __syncthreads();
     Frag ca[2], cb[2];
     read(0, 0, ca, cb);
@@ -302,7 +283,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Rows rows, const T* wt, i
           // Stage kt+1 complete for this wave (later stages may be in flight),
           // then visible to all; every wave's reads of stage kt are done, so
           // its slot takes stage kt+NST.
-          wait_vmcnt_stages<C::VM, NST - 2>(min(NST - 2, max(0, nk - 2 - kt)));
+          wait_vmcnt_tiles<C::VM, NST - 2>(min(NST - 2, max(0, nk - 2 - kt)));
           __syncthreads();
           issue(kt + NST);
           read(kt + 1, 0, na, nb);
