@@ -346,6 +346,103 @@ def cpu_baseline(w: wl.Workload, rows_sample: int = 24576):
             "seconds_measured": round(t_kv + t_rows, 2)}
 
 
+def _oracle_inputs(w: wl.Workload, n: int = None, grad: bool = False):
+    """w's seeded inputs rounded to its dtype and widened to float64, the first
+    n tokens of each sequence when n is given."""
+    arrays = wl.draw(w)
+    if grad:
+        arrays["dY"] = wl.draw_upstream_grad(w)
+    if n is not None:
+        for k in ("X", "dY"):
+            if k in arrays:
+                arrays[k] = arrays[k][:, :n]
+    host = wl.to_device_dtype(arrays, w.dtype)
+    return {k: wl.widen(v) for k, v in host.items()}
+
+
+def cpu_baseline_decode(w: wl.Workload):
+    """The float64 oracle on one decode step: the forward of the B new tokens'
+    rows (position N-1) against all N cached keys and values. The keys and
+    values are projected first, untimed, as the cache that prefill fills."""
+    import numpy as np
+    import oracle
+    o = _oracle_inputs(w)
+    cores = len(os.sched_getaffinity(0))
+    rows = np.arange(w.B, dtype=np.int64) * w.N + (w.N - 1)
+    cache = {}
+    args = (o["X"], o["Wq"], o["Wk"], o["Wv"], o["Wo"], w.H_q, w.H_kv, w.d_head, w.causal)
+    oracle.sqa_forward_rows(*args, bf16=(w.dtype == "bf16"), rows=rows, kv_cache=cache, workers=cores)
+    t0 = time.perf_counter()
+    oracle.sqa_forward_rows(*args, bf16=(w.dtype == "bf16"), rows=rows, kv_cache=cache, workers=cores)
+    t = time.perf_counter() - t0
+    return {"value": round(w.B / t, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": (f"float64 oracle: one decode step, {w.B} new rows against {w.N} cached keys "
+                       f"each ({t * 1e3:.0f} ms; the cache projection untimed)"),
+            "seconds_measured": round(t, 3)}
+
+
+def cpu_baseline_backward(w: wl.Workload, sizes=(2048, 4096)):
+    """The float64 oracle backward (gradients of x and the four weights) on
+    the first n tokens of the workload for two n, fitted as a*n + b*n^2
+    (projections, attention) and extrapolated to all N tokens."""
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    ts = []
+    for n in sizes:
+        o = _oracle_inputs(w, n, grad=True)
+        t0 = time.perf_counter()
+        oracle.sqa_backward(o["X"], o["Wq"], o["Wk"], o["Wv"], o["Wo"], o["dY"], w.H_q, w.H_kv,
+                            w.d_head, w.causal, bf16=(w.dtype == "bf16"), workers=cores)
+        ts.append(time.perf_counter() - t0)
+    (n1, n2), (t1, t2) = sizes, ts
+    b = max(0.0, (t2 / n2 - t1 / n1) / (n2 - n1))
+    a = max(0.0, t1 / n1 - b * n1)
+    full = a * w.N + b * w.N * w.N
+    return {"value": round(w.tokens / full, 2), "unit": "tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": (f"float64 oracle backward on the first {n1} and {n2} tokens ({t1:.1f} s, "
+                       f"{t2:.1f} s), fitted as a*n + b*n^2 and extrapolated to {w.N} tokens "
+                       f"= {full:.0f} s per step"),
+            "seconds_measured": round(t1 + t2, 2)}
+
+
+def cpu_baseline_varlen(w: wl.Workload, rows_per_seq: int = 1024):
+    """The float64 oracle on each sequence of w's length mix: its key/value
+    projection plus the forward of rows_per_seq evenly spaced rows, the row
+    time extrapolated linearly to the sequence's length."""
+    import numpy as np
+    import oracle
+    o = _oracle_inputs(w)
+    lens = wl.draw_lens(w)
+    cores = len(os.sched_getaffinity(0))
+    measured = full = 0.0
+    for b, L in enumerate(int(x) for x in lens):
+        if L == 0:
+            continue
+        k = min(rows_per_seq, L)
+        rows = ((np.arange(k) + 0.5) * L / k).astype(np.int64)
+        args = (o["X"][b:b + 1, :L], o["Wq"], o["Wk"], o["Wv"], o["Wo"], w.H_q, w.H_kv, w.d_head,
+                w.causal)
+        cache = {}
+        t0 = time.perf_counter()
+        oracle.sqa_forward_rows(*args, bf16=(w.dtype == "bf16"), rows=rows[:1], kv_cache=cache,
+                                workers=cores)
+        t_kv = time.perf_counter() - t0
+        t1 = time.perf_counter()
+        oracle.sqa_forward_rows(*args, bf16=(w.dtype == "bf16"), rows=rows, kv_cache=cache,
+                                workers=cores)
+        t_rows = time.perf_counter() - t1
+        measured += t_kv + t_rows
+        full += t_kv + t_rows * L / k
+    total = int(lens.sum())
+    return {"value": round(total / full, 1), "unit": "valid tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": (f"float64 oracle: per sequence, the key/value projection plus {rows_per_seq} "
+                       f"evenly spaced rows, extrapolated to its length; {total} valid tokens "
+                       f"= {full:.0f} s per step"),
+            "seconds_measured": round(measured, 2)}
+
+
 def calibrate_copy(torch, dev, nbytes: int = 1 << 30, reps: int = 3):
     """A plain device copy of known size, for scaling rocprofv3 FETCH_SIZE and
     WRITE_SIZE readings to bytes."""
@@ -492,6 +589,11 @@ def main():
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
+        # the same oracle beside the other rows of the path, on bounded samples
+        if not args.no_variants:
+            variants[DECODE_WORKLOADS[0].name]["cpu_baseline"] = cpu_baseline_decode(DECODE_WORKLOADS[0])
+            variants[w.name + "_backward"]["cpu_baseline"] = cpu_baseline_backward(w)
+            variants[wl.SQA_VARLEN_32K.name]["cpu_baseline"] = cpu_baseline_varlen(wl.SQA_VARLEN_32K)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)
