@@ -541,13 +541,10 @@ sqa_status sqa_decode_step(const void* x_new, const void* Wq, const void* Wk, co
   if (overlap(out, yb, k_cache, (size_t)cb) || overlap(out, yb, v_cache, (size_t)cb))
     return fail(SQA_ERR_INVALID_ARG, "out overlaps a cache");
 
-  // Workspace: q and a [B, H_q*d_head], then one fp32 scratch region that the
-  // three stages use in turn (stream order keeps them apart).
+  // Workspace: q and a [B, H_q*d_head], then the decode attention's fp32
+  // partial states of its key chunks.
   const int64_t qa_b = B * H_q * d_head * (int64_t)es;
-  const int64_t scratch_b = std::max<int64_t>(
-      {(int64_t)sqa::decode_partial_bytes(B, H_q, H_kv, N_max, d_head),
-       (int64_t)sqa::skinny_partial_bytes(B, d_model, (H_q + 2 * H_kv) * d_head),
-       (int64_t)sqa::skinny_partial_bytes(B, H_q * d_head, d_model)});
+  const int64_t scratch_b = (int64_t)sqa::decode_partial_bytes(B, H_q, H_kv, N_max, d_head);
   const int64_t off_a = round256(qa_b), off_p = off_a + round256(qa_b);
   const int64_t total = off_p + round256(scratch_b);
   hipMemPool_t pool;
@@ -557,13 +554,13 @@ sqa_status sqa_decode_step(const void* x_new, const void* Wq, const void* Wk, co
   if (e != hipSuccess) return fail_hip(e, "workspace allocation");
   char* base = (char*)ws;
   void *q = base, *a = base + off_a, *part = base + off_p;
-  e = sqa::launch_decode_qkv(dtype, x_new, Wq, Wk, Wv, pos, q, k_cache, v_cache, part, B, d_model,
-                             H_q, H_kv, d_head, N_max, stream);
+  e = sqa::launch_decode_qkv(dtype, x_new, Wq, Wk, Wv, pos, q, k_cache, v_cache, B, d_model, H_q,
+                             H_kv, d_head, N_max, stream);
   if (e == hipSuccess)
     e = sqa::launch_decode_attention(dtype, q, k_cache, v_cache, pos, a, part, B, N_max, H_q, H_kv,
                                      d_head, stream);
   if (e == hipSuccess)
-    e = sqa::launch_decode_out(dtype, a, Wo, out, part, B, H_q * d_head, d_model, stream);
+    e = sqa::launch_decode_out(dtype, a, Wo, out, B, H_q * d_head, d_model, stream);
   const hipError_t ef = hipFreeAsync(ws, stream);
   if (e != hipSuccess) return fail_hip(e, "kernel launch");
   if (ef != hipSuccess) return fail_hip(ef, "workspace release");

@@ -25,6 +25,7 @@
 //  * The four waves' partial states, then the chunks' partial states (a second
 //    kernel), are merged with the usual max/rescale rule.
 #include <algorithm>
+#include <cstdint>
 
 #include "sqa_device.h"
 #include "sqa_internal.h"
@@ -73,171 +74,160 @@ __global__ __launch_bounds__(256) void transpose_v(const T* vt, T* vc, int N, in
 // ---- decode: projections of the B new tokens ----
 // A decode step projects only B tokens, so these products are skinny: each
 // weight element is used B times, and the step is bound by reading the weights
-// once. They are read in their [in, out] layout, by many workgroups: a
-// workgroup owns 256 output columns (one 16-byte weight chunk per thread and
-// row), a slice of the K rows, which its thread phases split again, and up to
-// 8 of the tokens. fp32 partial sums per K slice go to scratch; a finalize
-// kernel adds the slices in a fixed order, rounds once to T, and stores.
+// once and, at a few MB, by latency. Each product is one launch. A workgroup
+// owns SK_COLS output columns over all K rows and up to SK_BR tokens, and reads
+// the weights in place from their [in, out] layout: one 16-byte chunk per
+// thread and row, the rows of a K block split over the thread phases. The
+// phases' fp32 sums meet in a reduce-scatter across the wave's lanes and then
+// across the four waves through LDS, in a fixed order; the workgroup rounds
+// once and stores its results itself (q and the new cache rows, or the output).
 
-constexpr int SK_COLS = 256, SK_BR = 8, SK_KB = 64;    // columns, tokens, K rows per block
-constexpr int SK_SPLIT_MAX = 16;                        // K slices at most
+constexpr int SK_COLS = 16, SK_BR = 8, SK_J = 8;    // columns and tokens per workgroup, rows per thread
 
-// part[ks][b][n] = sum over k in slice ks of x[b][k] * W[k][n], W = [W0 | W1 | W2]
-// (each segment's width a multiple of 32, so a thread's chunk lies in one).
-template <typename T>
-__global__ __launch_bounds__(256) void skinny_partial(const T* x, int B, int K, const T* w0, int n0w,
-                                                      const T* w1, int n1w, const T* w2, int n2w,
-                                                      float* part, int ncols, int k_slice) {
-  constexpr int EPC = 16 / (int)sizeof(T);   // columns per thread
-  constexpr int TPR = SK_COLS / EPC;         // threads per weight row
+// x staged as fp32 [k][token], 8 floats of padding after every 8 rows, so that
+// the transposing writes (lanes over tokens, then over 16-byte chunks of k) and
+// the row reads (two 16-byte reads per row) are free of bank conflicts.
+__device__ inline int xs_at(int k, int b) { return (k + (k >> 3)) * SK_BR + b; }
+
+// out[b][n] = sum over k of x[b][k] * W[k][n] for W = [W0 | W1 | W2], x [B, K].
+// Every segment width is a multiple of SK_COLS, so a workgroup's columns lie in
+// one segment. K is a multiple of the chunk width (16 bytes of T).
+template <typename T, typename Store>
+__global__ __launch_bounds__(256) void skinny(const T* x, int B, int K, const T* w0, int n0w,
+                                              const T* w1, int n1w, const T* w2, int n2w,
+                                              Store store) {
+  constexpr int EPC = 16 / (int)sizeof(T);   // columns per chunk
+  constexpr int TPR = SK_COLS / EPC;         // threads per weight row (lanes tid % TPR)
   constexpr int PH = 256 / TPR;              // thread phases over K
-  constexpr int J = SK_KB / PH;              // rows per thread and block
-  constexpr int RR = 4;                      // token rows per phase-reduction round
-  __shared__ __align__(16) float xs[SK_KB][SK_BR];
-  __shared__ float red[PH][TPR][EPC * RR];
-  const int tid = threadIdx.x, cc = tid % TPR, kp = tid / TPR;
-  const int col0 = blockIdx.x * SK_COLS + cc * EPC;
-  const int ks = blockIdx.y, kbeg = ks * k_slice, kend = min(K, kbeg + k_slice);
-  const int b0 = blockIdx.z * SK_BR, nb = min(SK_BR, B - b0);
-  const bool active = col0 < ncols;
-  const T* W = w0;   // threads past the last column read column 0 and discard it
-  int ld = n0w, cl = 0;
-  if (col0 < n0w) { cl = col0; }
-  else if (col0 < n0w + n1w) { W = w1; ld = n1w; cl = col0 - n0w; }
-  else if (active) { W = w2; ld = n2w; cl = col0 - n0w - n1w; }
-  float acc[SK_BR][EPC];
+  constexpr int KB = PH * SK_J;              // K rows per block
+  constexpr int XC = KB / EPC;               // x chunks per token and block
+  constexpr int XPT = XC * SK_BR / 256;      // x chunks per thread
+  constexpr int NV = SK_BR * EPC;            // partial sums per thread
+  constexpr int OUT = SK_BR * SK_COLS / 64;  // results per lane after the wave's reduce-scatter
+  static_assert(XPT * 256 == XC * SK_BR && OUT * 64 == SK_BR * SK_COLS, "split");
+  __shared__ __align__(16) float xs[(KB + KB / 8) * SK_BR];
+  __shared__ __align__(16) float red[4][SK_BR * SK_COLS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cc = tid % TPR, kp = tid / TPR;
+  const int n0 = blockIdx.x * SK_COLS;
+  const T* W = w0;
+  int ld = n0w, c0 = n0;
+  if (n0 >= n0w + n1w) { W = w2; ld = n2w; c0 = n0 - n0w - n1w; }
+  else if (n0 >= n0w) { W = w1; ld = n1w; c0 = n0 - n0w; }
+  c0 += cc * EPC;
+  const int b0 = blockIdx.y * SK_BR, nb = min(SK_BR, B - b0);
+
+  float acc[NV];
 #pragma unroll
-  for (int b = 0; b < SK_BR; ++b)
+  for (int i = 0; i < NV; ++i) acc[i] = 0.f;
+  for (int k0 = 0; k0 < K; k0 += KB) {
+    // Every load of the block is issued before any is used: row indexes are
+    // clamped to valid rows and the values of rows past K cleared afterwards,
+    // so no load sits behind a branch.
+    Chunk raw[SK_J];
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) acc[b][e] = 0.f;
-  for (int k0 = kbeg; k0 < kend; k0 += SK_KB) {
-    // Every load of the block is issued before any is used: the addresses are
-    // clamped to valid rows and the values of rows past the slice replaced by 0
-    // afterwards, so no load sits behind a branch.
-    Chunk raw[J];
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
+    for (int j = 0; j < SK_J; ++j) {
       const int k = k0 + kp + j * PH;
-      raw[j] = *reinterpret_cast<const Chunk*>(W + (int64_t)(k < kend ? k : kbeg) * ld + cl);
+      raw[j] = *reinterpret_cast<const Chunk*>(W + (int64_t)(k < K ? k : 0) * ld + c0);
     }
-    constexpr int XPT = SK_KB * SK_BR / 256;   // x values per thread
-    T xr[XPT];
+    Chunk xr[XPT];
 #pragma unroll
     for (int u = 0; u < XPT; ++u) {
-      const int i = tid + u * 256, b = i / SK_KB, k = k0 + i % SK_KB;
-      xr[u] = x[(int64_t)(b0 + (b < nb ? b : 0)) * K + (k < kend ? k : kbeg)];
+      const int i = tid + u * 256, b = i % SK_BR, k = k0 + i / SK_BR * EPC;
+      xr[u] = *reinterpret_cast<const Chunk*>(x + (int64_t)(b0 + (b < nb ? b : 0)) * K +
+                                              (k < K ? k : 0));
     }
 #pragma unroll
-    for (int j = 0; j < J; ++j) {   // a mask, not a branch, so the loads stay in flight
-      const uint32_t keep = active && k0 + kp + j * PH < kend ? ~0u : 0u;
+    for (int j = 0; j < SK_J; ++j) {
+      const uint32_t keep = k0 + kp + j * PH < K ? ~0u : 0u;
 #pragma unroll
       for (int w = 0; w < 4; ++w) raw[j].w[w] &= keep;
     }
     __syncthreads();   // the previous block's reads of xs are done
 #pragma unroll
     for (int u = 0; u < XPT; ++u) {
-      const int i = tid + u * 256, b = i / SK_KB, kk = i % SK_KB;
-      xs[kk][b] = b < nb && k0 + kk < kend ? to_f32(xr[u]) : 0.f;
+      const int i = tid + u * 256, b = i % SK_BR, kk = i / SK_BR * EPC;
+      const bool ok = b < nb && k0 + kk < K;
+      const T* xv = reinterpret_cast<const T*>(&xr[u]);
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) xs[xs_at(kk + e, b)] = ok ? to_f32(xv[e]) : 0.f;
     }
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
+    for (int j = 0; j < SK_J; ++j) {
       const T* wv = reinterpret_cast<const T*>(&raw[j]);
       float wf[EPC];
 #pragma unroll
       for (int e = 0; e < EPC; ++e) wf[e] = to_f32(wv[e]);
-      const float4* xr = reinterpret_cast<const float4*>(&xs[kp + j * PH][0]);
+      const float4* xrow = reinterpret_cast<const float4*>(&xs[xs_at(kp + j * PH, 0)]);
 #pragma unroll
       for (int b4 = 0; b4 < SK_BR / 4; ++b4) {
-        const float4 xv = xr[b4];
+        const float4 xv = xrow[b4];
         const float xb[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
-          for (int e = 0; e < EPC; ++e) acc[b4 * 4 + u][e] = fmaf(xb[u], wf[e], acc[b4 * 4 + u][e]);
+          for (int e = 0; e < EPC; ++e)
+            acc[(b4 * 4 + u) * EPC + e] = fmaf(xb[u], wf[e], acc[(b4 * 4 + u) * EPC + e]);
       }
     }
   }
-  // sum the thread phases, RR token rows a round, through LDS
+
+  // Reduce-scatter over the wave's phases (lane bits above those of cc): at
+  // the step over lane bit m a lane keeps the half of its sums selected by that
+  // bit, adds its partner's copy of that half and hands over the other half.
+  // After the last step a lane holds OUT consecutive flat indexes
+  // (lane / TPR) * OUT + i of acc, flat index = token * EPC + column in chunk.
+  float* v = acc;
 #pragma unroll
-  for (int r0 = 0; r0 < SK_BR; r0 += RR) {
-    if (r0 >= nb) break;
-    __syncthreads();
+  for (int n = NV, m = 32; n > OUT; n >>= 1, m >>= 1) {
+    const bool hi = (lane & m) != 0;
 #pragma unroll
-    for (int u = 0; u < RR; ++u)
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) red[kp][cc][u * EPC + e] = acc[r0 + u][e];
-    __syncthreads();
-    for (int i = tid; i < RR * SK_COLS; i += 256) {
-      const int u = i / SK_COLS, c = i % SK_COLS, b = r0 + u;
-      const int col = blockIdx.x * SK_COLS + c;
-      if (b < nb && col < ncols) {
-        float v = 0.f;
-#pragma unroll
-        for (int ph = 0; ph < PH; ++ph) v += red[ph][c / EPC][u * EPC + c % EPC];
-        part[((int64_t)ks * B + b0 + b) * ncols + col] = v;
-      }
+    for (int i = 0; i < n / 2; ++i) {
+      const float keep = hi ? v[n / 2 + i] : v[i];
+      const float give = hi ? v[i] : v[n / 2 + i];
+      v[i] = keep + __shfl_xor(give, m);
     }
+  }
+  {
+    const int f = (lane / TPR) * OUT, b = f / EPC, col = cc * EPC + f % EPC;
+#pragma unroll
+    for (int i = 0; i < OUT; ++i) red[wave][b * SK_COLS + col + i] = v[i];
+  }
+  __syncthreads();
+  const int b = tid / SK_COLS, c = tid % SK_COLS;
+  if (b < nb) {
+    const float s = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+    store(b0 + b, n0 + c, s);
   }
 }
 
-// Grid of a skinny product: enough workgroups to spread the weight read over
-// the chip, K slices a multiple of SK_KB rows.
-struct SkinnyPlan { int col_blocks, split, k_slice, b_chunks; };
-
-SkinnyPlan skinny_plan(int64_t B, int64_t K, int64_t ncols) {
-  SkinnyPlan pl;
-  pl.col_blocks = (int)((ncols + SK_COLS - 1) / SK_COLS);
-  pl.b_chunks = (int)((B + SK_BR - 1) / SK_BR);
-  const int64_t k_blocks = (K + SK_KB - 1) / SK_KB;
-  const int64_t units = (int64_t)pl.col_blocks * pl.b_chunks;
-  const int64_t want =
-      std::min<int64_t>(std::min<int64_t>(k_blocks, SK_SPLIT_MAX), (512 + units - 1) / units);
-  const int64_t split = std::max<int64_t>(1, want);
-  pl.k_slice = (int)((k_blocks + split - 1) / split * SK_KB);
-  pl.split = (int)((K + pl.k_slice - 1) / pl.k_slice);
-  return pl;
-}
-
-// Sum of the K slices (n_split <= SK_SPLIT_MAX) of column n for token b, in
-// slice order, rounded once. All loads are issued first (indexes clamped).
+// Results of the Q/K/V product: q to [B, H_q*D]; the new key and value of
+// token b straight to cache row pos[b] (clamped into [0, N_max-1]).
 template <typename T>
-__device__ inline T skinny_sum(const float* part, int n_split, int B, int ncols, int b, int n) {
-  float pv[SK_SPLIT_MAX];
-#pragma unroll
-  for (int ks = 0; ks < SK_SPLIT_MAX; ++ks)
-    pv[ks] = part[((int64_t)(ks < n_split ? ks : 0) * B + b) * ncols + n];
-  float v = 0.f;
-#pragma unroll
-  for (int ks = 0; ks < SK_SPLIT_MAX; ++ks)
-    if (ks < n_split) v += pv[ks];
-  return from_f32<T>(v);
-}
-
-// Q/K/V of the new tokens: q to [B, H_q*D]; k and v straight to cache row pos[b].
-template <typename T>
-__global__ __launch_bounds__(256) void finalize_qkv(const float* part, int n_split, int B,
-                                                    int wq_w, int wkv_w, int D, const int32_t* pos,
-                                                    T* q, T* kc, T* vc, int H_kv, int64_t N_max) {
-  const int ncols = wq_w + 2 * wkv_w;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (int64_t)B * ncols) return;
-  const int b = (int)(i / ncols), n = (int)(i % ncols);
-  const T v = skinny_sum<T>(part, n_split, B, ncols, b, n);
-  if (n < wq_w) { q[(int64_t)b * wq_w + n] = v; return; }
-  const int nk = (n - wq_w) % wkv_w, h = nk / D, c = nk % D;
-  const int64_t p = min(max((int64_t)pos[b], (int64_t)0), N_max - 1);
-  T* dst = n < wq_w + wkv_w ? kc : vc;
-  dst[(((int64_t)b * H_kv + h) * N_max + p) * D + c] = v;
-}
+struct QkvRows {
+  T* q; T* kc; T* vc;
+  const int32_t* pos;
+  int wq_w, wkv_w, D, H_kv;
+  int64_t N_max;
+  __device__ void operator()(int b, int n, float v) const {
+    const T r = from_f32<T>(v);
+    if (n < wq_w) { q[(int64_t)b * wq_w + n] = r; return; }
+    const int nk = (n - wq_w) % wkv_w, h = nk / D, c = nk % D;
+    const int64_t p = min(max((int64_t)pos[b], (int64_t)0), N_max - 1);
+    T* dst = n < wq_w + wkv_w ? kc : vc;
+    dst[(((int64_t)b * H_kv + h) * N_max + p) * D + c] = r;
+  }
+};
 
 template <typename T>
-__global__ __launch_bounds__(256) void finalize_dense(const float* part, int n_split, int B,
-                                                      int ncols, T* out) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (int64_t)B * ncols) return;
-  out[i] = skinny_sum<T>(part, n_split, B, ncols, (int)(i / ncols), (int)(i % ncols));
-}
+struct DenseRows {   // out [B, ncols]
+  T* out;
+  int ncols;
+  __device__ void operator()(int b, int n, float v) const {
+    out[(int64_t)b * ncols + n] = from_f32<T>(v);
+  }
+};
 
 struct DecParams {
   const void* q;                 // [B, H_q * D]: query head i of token b at q[b][i*D ..]
@@ -256,7 +246,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_partial(DecParams p) {
   constexpr int CPK = D / EPC;               // chunks per key row
   constexpr int KGS = 64 / CPK;              // key groups in phase 2
   static_assert(CPK * KGS == 64, "lane split");
-  __shared__ float qs[G][D];
+  __shared__ __align__(16) float qs[G][D];
   __shared__ float ps[DEC_WAVES][KB][G];
   __shared__ float red_ml[DEC_WAVES][G][2];
   __shared__ float red_o[DEC_WAVES][G][D];
@@ -320,14 +310,25 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_partial(DecParams p) {
       const int jv = kb + r * KGS + kg;
       vraw[r] = *reinterpret_cast<const Chunk*>(Vc + (int64_t)(jv < k_end ? jv : k_begin) * D + dc * EPC);
     }
+    // The queries are read from LDS in the loop: an opaque zero offset keeps
+    // the compiler from hoisting G*D of them into registers, which at G >= 2
+    // cost more occupancy than the broadcast reads cost time.
+    int qo = 0;
+    asm volatile("" : "+s"(qo));
+    const float* qb = &qs[0][0] + qo;
 #pragma unroll
     for (int ck = 0; ck < CPK; ++ck) {
       const T* kv = reinterpret_cast<const T*>(&kraw[ck]);
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) {
-        const float kf = to_f32(kv[e]);
+      for (int e4 = 0; e4 < EPC / 4; ++e4) {
+        const float k0 = to_f32(kv[e4 * 4]), k1 = to_f32(kv[e4 * 4 + 1]),
+                    k2 = to_f32(kv[e4 * 4 + 2]), k3 = to_f32(kv[e4 * 4 + 3]);
 #pragma unroll
-        for (int i = 0; i < G; ++i) s[i] = fmaf(qs[i][ck * EPC + e], kf, s[i]);
+        for (int i = 0; i < G; ++i) {
+          const float4 q4 = *reinterpret_cast<const float4*>(qb + i * D + ck * EPC + e4 * 4);
+          s[i] = fmaf(q4.x, k0, s[i]); s[i] = fmaf(q4.y, k1, s[i]);
+          s[i] = fmaf(q4.z, k2, s[i]); s[i] = fmaf(q4.w, k3, s[i]);
+        }
       }
     }
     float alpha[G];
@@ -535,69 +536,58 @@ hipError_t launch_fill_cache(sqa_dtype dt, const void* k, const void* vt, void* 
   return hipGetLastError();
 }
 
-size_t skinny_partial_bytes(int64_t B, int64_t K, int64_t ncols) {
-  return (size_t)(skinny_plan(B, K, ncols).split * B * ncols) * sizeof(float);
-}
-
 namespace {
-template <typename T>
-hipError_t skinny(const void* x, int64_t B, int64_t K, const void* w0, int64_t n0w, const void* w1,
-                  int64_t n1w, const void* w2, int64_t n2w, float* part, int* n_split,
-                  hipStream_t stream) {
-  const int64_t ncols = n0w + n1w + n2w;
-  const SkinnyPlan pl = skinny_plan(B, K, ncols);
-  *n_split = pl.split;
-  const dim3 grid((unsigned)pl.col_blocks, (unsigned)pl.split, (unsigned)pl.b_chunks);
-  skinny_partial<T><<<grid, 256, 0, stream>>>((const T*)x, (int)B, (int)K, (const T*)w0, (int)n0w,
-                                             (const T*)w1, (int)n1w, (const T*)w2, (int)n2w, part,
-                                             (int)ncols, pl.k_slice);
+// Grid of a skinny product: SK_COLS columns by SK_BR tokens per workgroup.
+template <typename T, typename Store>
+hipError_t run_skinny(const void* x, int64_t B, int64_t K, const void* w0, int64_t n0w,
+                      const void* w1, int64_t n1w, const void* w2, int64_t n2w, const Store& st,
+                      hipStream_t stream) {
+  const int64_t ncols = n0w + n1w + n2w, epc = 16 / (int64_t)sizeof(T);
+  if (n0w % SK_COLS || n1w % SK_COLS || n2w % SK_COLS || K % epc || ncols / SK_COLS > 65535 ||
+      (B + SK_BR - 1) / SK_BR > 65535 || K > INT32_MAX || ncols > INT32_MAX)
+    return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)(ncols / SK_COLS), (unsigned)((B + SK_BR - 1) / SK_BR));
+  skinny<T, Store><<<grid, 256, 0, stream>>>((const T*)x, (int)B, (int)K, (const T*)w0, (int)n0w,
+                                             (const T*)w1, (int)n1w, (const T*)w2, (int)n2w, st);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t decode_qkv(const void* x_new, const void* wq, const void* wk, const void* wv,
-                      const int32_t* pos, void* q, void* kc, void* vc, float* part, int64_t B,
-                      int64_t d_model, int64_t H_q, int64_t H_kv, int64_t d_head, int64_t N_max,
-                      hipStream_t stream) {
-  const int64_t wq_w = H_q * d_head, wkv_w = H_kv * d_head, ncols = wq_w + 2 * wkv_w;
-  int n_split = 0;
-  hipError_t e = skinny<T>(x_new, B, d_model, wq, wq_w, wk, wkv_w, wv, wkv_w, part, &n_split, stream);
-  if (e != hipSuccess) return e;
-  const unsigned grid = (unsigned)((B * ncols + 255) / 256);
-  finalize_qkv<T><<<grid, 256, 0, stream>>>(part, n_split, (int)B, (int)wq_w, (int)wkv_w,
-                                           (int)d_head, pos, (T*)q, (T*)kc, (T*)vc, (int)H_kv, N_max);
-  return hipGetLastError();
+                      const int32_t* pos, void* q, void* kc, void* vc, int64_t B, int64_t d_model,
+                      int64_t H_q, int64_t H_kv, int64_t d_head, int64_t N_max, hipStream_t stream) {
+  const int64_t wq_w = H_q * d_head, wkv_w = H_kv * d_head;
+  QkvRows<T> st;
+  st.q = (T*)q; st.kc = (T*)kc; st.vc = (T*)vc; st.pos = pos;
+  st.wq_w = (int)wq_w; st.wkv_w = (int)wkv_w; st.D = (int)d_head; st.H_kv = (int)H_kv;
+  st.N_max = N_max;
+  return run_skinny<T>(x_new, B, d_model, wq, wq_w, wk, wkv_w, wv, wkv_w, st, stream);
 }
 
 template <typename T>
-hipError_t decode_out(const void* a, const void* wo, void* out, float* part, int64_t B, int64_t K,
+hipError_t decode_out(const void* a, const void* wo, void* out, int64_t B, int64_t K,
                       int64_t d_model, hipStream_t stream) {
-  int n_split = 0;
-  hipError_t e = skinny<T>(a, B, K, wo, d_model, nullptr, 0, nullptr, 0, part, &n_split, stream);
-  if (e != hipSuccess) return e;
-  const unsigned grid = (unsigned)((B * d_model + 255) / 256);
-  finalize_dense<T><<<grid, 256, 0, stream>>>(part, n_split, (int)B, (int)d_model, (T*)out);
-  return hipGetLastError();
+  DenseRows<T> st;
+  st.out = (T*)out; st.ncols = (int)d_model;
+  return run_skinny<T>(a, B, K, wo, d_model, nullptr, 0, nullptr, 0, st, stream);
 }
 }  // namespace
 
 hipError_t launch_decode_qkv(sqa_dtype dt, const void* x_new, const void* wq, const void* wk,
                              const void* wv, const int32_t* pos, void* q, void* kc, void* vc,
-                             void* part, int64_t B, int64_t d_model, int64_t H_q, int64_t H_kv,
-                             int64_t d_head, int64_t N_max, hipStream_t stream) {
-  if ((B + SK_BR - 1) / SK_BR > 65535) return hipErrorInvalidConfiguration;
+                             int64_t B, int64_t d_model, int64_t H_q, int64_t H_kv, int64_t d_head,
+                             int64_t N_max, hipStream_t stream) {
   return dt == SQA_DTYPE_BF16
-      ? decode_qkv<bf16>(x_new, wq, wk, wv, pos, q, kc, vc, (float*)part, B, d_model, H_q, H_kv,
-                         d_head, N_max, stream)
-      : decode_qkv<float>(x_new, wq, wk, wv, pos, q, kc, vc, (float*)part, B, d_model, H_q, H_kv,
-                          d_head, N_max, stream);
+      ? decode_qkv<bf16>(x_new, wq, wk, wv, pos, q, kc, vc, B, d_model, H_q, H_kv, d_head, N_max,
+                         stream)
+      : decode_qkv<float>(x_new, wq, wk, wv, pos, q, kc, vc, B, d_model, H_q, H_kv, d_head, N_max,
+                          stream);
 }
 
-hipError_t launch_decode_out(sqa_dtype dt, const void* a, const void* wo, void* out, void* part,
-                             int64_t B, int64_t K, int64_t d_model, hipStream_t stream) {
-  if ((B + SK_BR - 1) / SK_BR > 65535) return hipErrorInvalidConfiguration;
-  return dt == SQA_DTYPE_BF16 ? decode_out<bf16>(a, wo, out, (float*)part, B, K, d_model, stream)
-                              : decode_out<float>(a, wo, out, (float*)part, B, K, d_model, stream);
+hipError_t launch_decode_out(sqa_dtype dt, const void* a, const void* wo, void* out, int64_t B,
+                             int64_t K, int64_t d_model, hipStream_t stream) {
+  return dt == SQA_DTYPE_BF16 ? decode_out<bf16>(a, wo, out, B, K, d_model, stream)
+                              : decode_out<float>(a, wo, out, B, K, d_model, stream);
 }
 
 hipError_t launch_decode_attention(sqa_dtype dt, const void* q, const void* kc, const void* vc,

@@ -92,21 +92,18 @@ hipError_t launch_fill_cache(sqa_dtype dt, const void* k, const void* vt, void* 
 // Decode step over B new tokens. decode_qkv projects x_new [B, d_model] into
 // q [B, H_q*d] and writes token b's key and value straight to cache row pos[b]
 // (clamped into [0, N_max-1]); decode_attention writes a [B, H_q*d] over cache
-// rows 0..pos[b]; decode_out gives out [B, d_model] = a [B, K] * wo [K, d_model].
-// part is device scratch: skinny_partial_bytes(B, d_model, (H_q + 2*H_kv)*d) for
-// decode_qkv, skinny_partial_bytes(B, K, d_model) for decode_out, and
-// decode_partial_bytes() for decode_attention.
-size_t skinny_partial_bytes(int64_t B, int64_t K, int64_t ncols);
+// rows 0..pos[b], with device scratch part of decode_partial_bytes(); decode_out
+// gives out [B, d_model] = a [B, K] * wo [K, d_model].
 hipError_t launch_decode_qkv(sqa_dtype dt, const void* x_new, const void* wq, const void* wk,
                              const void* wv, const int32_t* pos, void* q, void* kc, void* vc,
-                             void* part, int64_t B, int64_t d_model, int64_t H_q, int64_t H_kv,
-                             int64_t d_head, int64_t N_max, hipStream_t stream);
+                             int64_t B, int64_t d_model, int64_t H_q, int64_t H_kv, int64_t d_head,
+                             int64_t N_max, hipStream_t stream);
 size_t decode_partial_bytes(int64_t B, int64_t H_q, int64_t H_kv, int64_t N_max, int64_t d_head);
 hipError_t launch_decode_attention(sqa_dtype dt, const void* q, const void* kc, const void* vc,
                                    const int32_t* pos, void* a, void* part, int64_t B,
                                    int64_t N_max, int64_t H_q, int64_t H_kv, int64_t d_head,
                                    hipStream_t stream);
-hipError_t launch_decode_out(sqa_dtype dt, const void* a, const void* wo, void* out, void* part,
-                             int64_t B, int64_t K, int64_t d_model, hipStream_t stream);
+hipError_t launch_decode_out(sqa_dtype dt, const void* a, const void* wo, void* out, int64_t B,
+                             int64_t K, int64_t d_model, hipStream_t stream);
 
 }  // namespace sqa
