@@ -126,3 +126,71 @@ def sqa_backward(X, Wq, Wk, Wv, Wo, dY, H_q: int, H_kv: int, d_head: int, causal
     dWo = _maybe_round(fwd["A"].reshape(B * N, -1).T @ dY.reshape(B * N, D), bf16)
     return {"dX": dX, "dWq": dWq, "dWk": dWk, "dWv": dWv, "dWo": dWo,
             "dA": dA, "dQ": dQ, "dK": dK, "dV": dV}
+
+
+def sqa_backward_rows(X, Wq, Wk, Wv, Wo, dY, H_q: int, H_kv: int, d_head: int, causal: bool,
+                      bf16: bool, rows, workers: Optional[int] = None, row_block: int = 128
+                      ) -> Dict[str, np.ndarray]:
+    """dX of ``sqa_backward`` evaluated only at the flat token rows ``rows``
+    (row = b*N + t), with the same definitions and rounding points.
+
+    Row t of dX takes row t of dQ, dK and dV. dQ[t] needs query row t's
+    softmax; dK[t] and dV[t] need every query row that attends key t: rows
+    t..N-1 when causal, all rows otherwise. Per sequence this evaluates the
+    query rows from the first sampled position on (all of them without the
+    mask) against all keys, so it is cheap for rows near the end of a causal
+    sequence. Returns dX_rows [R, d_model] and dQ_rows, dK_rows, dV_rows
+    [R, heads*d] in the order of ``rows``.
+    """
+    X, Wq, Wk, Wv, Wo, dY = (np.asarray(t, dtype=np.float64) for t in (X, Wq, Wk, Wv, Wo, dY))
+    B, N, D = check_shapes(X, Wq, Wk, Wv, Wo, H_q, H_kv, d_head)
+    if dY.shape != (B, N, D):
+        raise ValueError(f"dY has shape {dY.shape}, expected {(B, N, D)}")
+    rows = np.asarray(list(rows), dtype=np.int64)
+    if rows.size and (rows.min() < 0 or rows.max() >= B * N):
+        raise ValueError("row index out of range")
+    d = d_head
+    scale = 1.0 / math.sqrt(d)
+    dQr = np.zeros((rows.size, H_q * d))
+    dKr = np.zeros((rows.size, H_kv * d))
+    dVr = np.zeros((rows.size, H_kv * d))
+    for b in np.unique(rows // N):
+        b = int(b)
+        sel = np.nonzero(rows // N == b)[0]
+        pos = rows[sel] % N
+        lo = int(pos.min()) if causal else 0      # earlier query rows attend no sampled key
+        Kb = _maybe_round(X[b] @ Wk, bf16)
+        Vb = _maybe_round(X[b] @ Wv, bf16)
+        Qr = _maybe_round(X[b, lo:] @ Wq, bf16)
+        dAr = _maybe_round(dY[b, lo:] @ Wo.T, bf16)
+        qpos = np.arange(lo, N)
+
+        def one(j):   # every query head of key/value head j
+            kc = slice(j * d, (j + 1) * d)
+            k, v = Kb[:, kc], Vb[:, kc]
+            for i in range(H_q):
+                if kv_head_for(i, H_q, H_kv) != j:
+                    continue
+                hc = slice(i * d, (i + 1) * d)
+                for r0 in range(0, qpos.size, row_block):
+                    r1 = min(qpos.size, r0 + row_block)
+                    q, do = Qr[r0:r1, hc], dAr[r0:r1, hc]
+                    s = (q @ k.T) * scale
+                    if causal:
+                        s = np.where(np.arange(N)[None, :] <= qpos[r0:r1, None], s, -np.inf)
+                    s = s - s.max(axis=1, keepdims=True)
+                    e = np.exp(s)
+                    p = e / e.sum(axis=1, keepdims=True)
+                    o = p @ v
+                    Dr = np.sum(do * o, axis=1)
+                    ds = softmax_backward(p, do @ v.T, Dr)
+                    here = np.nonzero((pos >= qpos[r0]) & (pos < qpos[r1 - 1] + 1))[0]
+                    if here.size:
+                        dQr[sel[here], hc] = (ds[pos[here] - qpos[r0]] @ k) * scale
+                    dKr[sel, kc] += (ds[:, pos].T @ q) * scale
+                    dVr[sel, kc] += p[:, pos].T @ do
+
+        _run_tasks(one, list(range(H_kv)), _pool_workers(workers))
+    dQr, dKr, dVr = (_maybe_round(t, bf16) for t in (dQr, dKr, dVr))
+    dXr = _maybe_round(dQr @ Wq.T + dKr @ Wk.T + dVr @ Wv.T, bf16)
+    return {"dX_rows": dXr, "dQ_rows": dQr, "dK_rows": dKr, "dV_rows": dVr}

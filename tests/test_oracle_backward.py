@@ -140,6 +140,44 @@ def test_intermediates_have_the_forward_layouts():
 
 
 # ----------------------------------------------------------------------------------------------
+# sampled rows: sqa_backward_rows is sqa_backward (pinned above) restricted to some rows of dX
+
+@pytest.mark.parametrize("causal,bf16,H_q,H_kv", [(True, False, 4, 2), (True, True, 4, 2),
+                                                  (False, False, 2, 1), (False, True, 4, 4),
+                                                  (True, True, 4, 1)])
+def test_backward_rows_are_the_full_backward_at_those_rows(causal, bf16, H_q, H_kv):
+    d, N, B = 4, 41, 2
+    params, dY = _problem(91, B, N, 4, d, H_q, H_kv)
+    if bf16:
+        params = [oracle.round_bf16(p) for p in params]
+        dY = oracle.round_bf16(dY)
+    full = oracle.sqa_backward(*params, dY, H_q, H_kv, d, causal, bf16=bf16)
+    rows = [0, 1, 17, 40, N + 0, N + 23, N + 39, N + 40, 17]   # both sequences, ends, a repeat
+    got = oracle.sqa_backward_rows(*params, dY, H_q, H_kv, d, causal, bf16, rows, row_block=8)
+    flat = {k: full[k].reshape(B * N, -1) for k in ("dX", "dQ", "dK", "dV")}
+    for k in ("dX", "dQ", "dK", "dV"):
+        np.testing.assert_allclose(got[k + "_rows"], flat[k][rows], rtol=1e-12, atol=1e-14,
+                                   err_msg=k)
+
+
+def test_backward_rows_late_causal_rows_skip_the_early_queries():
+    """Causal rows near the end evaluate only the query rows from the first
+    sampled position on; the result is still the full backward's."""
+    d, N, H_q, H_kv = 4, 64, 2, 1
+    params, dY = _problem(92, 1, N, 2, d, H_q, H_kv)
+    full = oracle.sqa_backward(*params, dY, H_q, H_kv, d, True, bf16=False)
+    rows = [N - 1, N - 5, N - 9]
+    got = oracle.sqa_backward_rows(*params, dY, H_q, H_kv, d, True, False, rows)
+    np.testing.assert_allclose(got["dX_rows"], full["dX"][0, rows], rtol=1e-12, atol=1e-14)
+
+
+def test_backward_rows_reject_bad_rows():
+    params, dY = _problem(93, 1, 5, 2, 4, 2, 1)
+    with pytest.raises(ValueError):
+        oracle.sqa_backward_rows(*params, dY, 2, 1, 4, True, False, [5])
+
+
+# ----------------------------------------------------------------------------------------------
 # planted mistakes: each must make a pin fail
 
 def _fd_fails(monkeypatch_apply, case=(4, 2, 4, 2, True)):
