@@ -93,10 +93,11 @@ __global__ __launch_bounds__(256) void concat_weights(const T* wq, const T* wk, 
   w[i] = v;
 }
 
-// D[b, i, t] = sum_c dO[b, i, t, c] * O[b, t, i*d + c] for t < N, 0 on padding
-// rows, with O the attention output before its rounding (fp32). The rounded A
-// would put a relative 2^-9 error into D, and dS = P (dP - D) keeps it even
-// where dP - D cancels (short sequences).
+// dvec[b, i, t] = -D with D = sum_c dO[b, i, t, c] * O[b, t, i*d + c] for
+// t < N, 0 on padding rows, with O the attention output before its rounding
+// (fp32). The rounded A would put a relative 2^-9 error into D, and
+// dS = P (dP - D) keeps it even where dP - D cancels (short sequences). It is
+// stored negated because the dK/dV kernel starts its dP accumulation from it.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void dvec_kernel(const T* dO, const float* a, float* dvec, int N,
                                                    int64_t Np, int H_q, int64_t rows) {
@@ -110,7 +111,7 @@ __global__ __launch_bounds__(256) void dvec_kernel(const T* dO, const float* a, 
 #pragma unroll 8
     for (int c = 0; c < D; ++c) s = fmaf(f32_of(o[c]), f32_of(av[c]), s);
   }
-  dvec[x] = s;
+  dvec[x] = -s;
 }
 
 // out segments [M, w0 | w1 | w2] = sum over the n_split partials, rounded once.
@@ -141,7 +142,7 @@ struct BwdParams {
   const void* dO;    // [B, H_q, Np, d]
   const void* dOt;   // [B, H_q, d, Np], tokens in swap23 order
   const float* lse;  // [B, H_q, Np], base 2, of the scaled scores
-  const float* dvec; // [B, H_q, Np]
+  const float* dvec; // [B, H_q, Np]: -D per row
   void* dqkv;        // [B, Np, W]: dQ heads, then dK heads, then dV heads
   int N, Np, H_q, H_kv, g, causal, W;
   float c;           // log2(e) / sqrt(d)
@@ -375,7 +376,9 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
       const float* lse_s = reinterpret_cast<const float*>(Qs + 4 * TE);
       const float* dv_s = lse_s + BT;
       const int q0 = item_tile(w) * BT;
-      // S = Q K^T and dP = dO V^T of 32-query block qs (lane = key).
+      // S = Q K^T and dP - D = dO V^T - D of 32-query block qs (lane = key):
+      // the accumulator of dP starts from the rows' -D (register r: query
+      // 8*(r/4) + 4*grp + r%4 of the block), which saves a subtraction per score.
       auto scores = [&](int qs, f32x16& sc, f32x16& dpc) {
         Frag qa[NS], oa[NS];
 #pragma unroll
@@ -384,7 +387,12 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
           oa[st] = row_frag<T, D>(Os, 32 * qs + col, st, grp);
         }
         sc = f32x16{};
-        dpc = f32x16{};
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dv_s[32 * qs + 8 * r4 + 4 * grp]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dpc[4 * r4 + e] = d4[e];
+        }
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
           sc = MF::run(qa[st], kf[st], sc);
@@ -392,15 +400,14 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
         }
       };
       // P and dS in place (register r: query qb + 8*(r/4) + 4*grp + r%4; column:
-      // key kw + col), then dV^T += dO^T P and dK^T += Q^T dS. The row
-      // statistics are read four rows at a time, just before their use.
+      // key kw + col), then dV^T += dO^T P and dK^T += Q^T dS. The rows'
+      // log-sum-exp values are read four rows at a time, just before their use.
       auto grads = [&](int qs, f32x16& sc, f32x16& dpc) {
         const int qb = q0 + 32 * qs;
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const int rl = 32 * qs + 8 * r4 + 4 * grp;
           const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse_s[rl]);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dv_s[rl]);
           const int key = kw + col;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -408,7 +415,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
             float pv = __builtin_amdgcn_exp2f(fmaf(sc[r], p.c, -l4[e]));
             if (MASK) pv = key >= p.N || (p.causal && key > q) ? 0.f : pv;
             sc[r] = pv;                        // P
-            dpc[r] = pv * (dpc[r] - d4[e]);    // dS
+            dpc[r] = pv * dpc[r];              // dS = P (dP - D)
           }
         }
 #pragma unroll
@@ -572,7 +579,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq(BwdParams p) {
         of[qb][s] = *reinterpret_cast<const Frag*>(orow + s * MF::KS + grp * MF::E);
       }
       lse[qb] = t < p.N ? p.lse[hq * p.Np + t] : INFINITY;
-      dvq[qb] = t < p.N ? p.dvec[hq * p.Np + t] : 0.f;
+      dvq[qb] = t < p.N ? -p.dvec[hq * p.Np + t] : 0.f;   // D (stored negated)
 #pragma unroll
       for (int nb = 0; nb < D / 32; ++nb) dq[qb][nb] = f32x16{};
     }
