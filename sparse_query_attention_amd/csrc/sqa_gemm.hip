@@ -36,6 +36,8 @@ namespace sqa {
 namespace {
 
 constexpr int BM = 128, BN = 128, BK = 32, THREADS = 256, WAVES = 4;
+constexpr int WN = BN / 64, NBJ = BN / 32;   // waves along N; 32-column blocks per tile
+static_assert(BM / 64 * WN == WAVES, "each wave owns a 64x64 sub-tile");
 constexpr int NST = 4;   // LDS ring stages
 constexpr int XCDS = 8;
 
@@ -239,7 +241,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Rows rows, const T* wt, i
         &part[r * BK + (((e / C::EPC) ^ swz<C::CPR>(r)) * C::EPC) + e % C::EPC]);
   };
 
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   f32x16 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -262,7 +264,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Rows rows, const T* wt, i
   // stages four consecutive columns per write.
   bool rows_all = true;
 #pragma unroll
-  for (int bj = 0; bj < 4; ++bj) rows_all &= n0 + 32 * bj >= ncols || !store.col_major(n0 + 32 * bj);
+  for (int bj = 0; bj < NBJ; ++bj) rows_all &= n0 + 32 * bj >= ncols || !store.col_major(n0 + 32 * bj);
 
   auto main_loop = [&](auto transposed) {
     constexpr bool TR = decltype(transposed)::value;
@@ -338,7 +340,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Rows rows, const T* wt, i
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int bi = wm * 2 + i, bj = wn * 2 + j;
-      char* blk = ep + (bi * 4 + bj) * BLOCK;
+      char* blk = ep + (bi * NBJ + bj) * BLOCK;
       if (rows_all) {
         // transposed: register r holds row col, column 8*(r/4) + 4*grp + r%4
         const bool z = tile.zero_row(32 * bi + col);
@@ -387,7 +389,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Rows rows, const T* wt, i
 #pragma unroll
   for (int cidx = tid; cidx < CHUNKS; cidx += THREADS) {
     const int blkid = cidx / (32 * CPL), line = (cidx / CPL) % 32, qc = cidx % CPL;
-    const int bi = blkid / 4, bj = blkid % 4;
+    const int bi = blkid / NBJ, bj = blkid % NBJ;
     const int n_b = n0 + 32 * bj;
     if (n_b >= ncols) continue;
     const Chunk c = *reinterpret_cast<const Chunk*>(ep + blkid * BLOCK + line * LINE + qc * 16);
