@@ -607,8 +607,13 @@ hipError_t dispatch(sqa_dtype dt, int64_t d_head, AttnParams& p, int64_t grid, i
   if (dt == SQA_DTYPE_BF16)
     return d_head == 64 ? run<bf16, 64, WAVES>(p, (unsigned)grid, stream)
                         : run<bf16, 32, WAVES>(p, (unsigned)grid, stream);
-  return d_head == 64 ? run<float, 64, WAVES>(p, (unsigned)grid, stream)
-                      : run<float, 32, WAVES>(p, (unsigned)grid, stream);
+  if constexpr (WAVES == 8) {   // fp32 at d_head 64 always takes 4-wave workgroups
+    if (d_head == 64) return hipErrorInvalidValue;
+    return run<float, 32, WAVES>(p, (unsigned)grid, stream);
+  } else {
+    return d_head == 64 ? run<float, 64, WAVES>(p, (unsigned)grid, stream)
+                        : run<float, 32, WAVES>(p, (unsigned)grid, stream);
+  }
 }
 
 // Compute units of the stream's device (cached per device).
@@ -634,7 +639,9 @@ int cu_count(hipStream_t stream) {
 // under half full runs with 4-wave workgroups instead (two per CU): every
 // workgroup of a non-causal grid costs the same, and the smaller ones pack
 // that tail round over more CUs. Causal grids, dispatched heaviest first,
-// fill their tail with short workgroups.
+// fill their tail with short workgroups. fp32 at d_head 64 always runs with
+// 4-wave workgroups: its 8-wave form needs more than the 256 registers that
+// two waves per SIMD leave.
 size_t attention_order_bytes(int64_t B, int64_t N, int64_t H_q) {
   // a bound on the grid: query tiles of at least 64 rows, at most H_q head groups
   return (size_t)(B * ((N + 63) / 64) * H_q) * sizeof(int32_t);
@@ -654,7 +661,7 @@ hipError_t launch_attention(sqa_dtype dt, const void* q, const void* k, const vo
   const int64_t grid8 = plan<8>(p8, B, H_kv);
   const int64_t cus = cu_count(stream);
   const int64_t tail = grid8 % cus;
-  if (!causal && tail != 0 && 2 * tail <= cus) {
+  if ((!causal && tail != 0 && 2 * tail <= cus) || (dt == SQA_DTYPE_FP32 && d_head == 64)) {
     const int64_t grid4 = plan<4>(p, B, H_kv);
     return dispatch<4>(dt, d_head, p, grid4, cus, order_ws, stream);
   }
