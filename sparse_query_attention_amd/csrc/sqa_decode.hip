@@ -82,7 +82,7 @@ __global__ __launch_bounds__(256) void transpose_v(const T* vt, T* vc, int N, in
 // across the four waves through LDS, in a fixed order; the workgroup rounds
 // once and stores its results itself (q and the new cache rows, or the output).
 
-constexpr int SK_COLS = 16, SK_BR = 8, SK_J = 8;    // columns and tokens per workgroup, rows per thread
+constexpr int SK_COLS = 8, SK_BR = 8, SK_J = 4;     // columns and tokens per workgroup, rows per thread
 
 // x staged as fp32 [k][token], 8 floats of padding after every 8 rows, so that
 // the transposing writes (lanes over tokens, then over 16-byte chunks of k) and
