@@ -405,50 +405,48 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_partial(DecParams p) {
 }
 
 // One 256-thread workgroup per (sequence, query head) merges the chunks that
-// hold keys of that sequence and writes a[b, i*D + e]. The chunks' (m, l) go to
-// LDS in parallel; then 256/D column groups take every (256/D)-th chunk, so
-// their loads of o are independent, and the groups are summed through LDS.
-constexpr int MAX_CHUNKS = 1024;
+// hold keys of that sequence and writes a[b, i*D + e]. Thread (group gr,
+// column e) takes every (256/D)-th chunk from gr on and merges them as they
+// arrive with the max/rescale rule, so all its loads are independent of each
+// other; the groups' states then meet in LDS.
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_combine(const float* part, const int32_t* pos, T* a,
                                                       int H_q, int n_chunks, int chunk,
                                                       int64_t N_max) {
   constexpr int GR = 256 / D;
-  __shared__ float sm[MAX_CHUNKS], sl[MAX_CHUNKS];
-  __shared__ float wmax[4], red_o[GR][D], red_l[GR];
+  __shared__ float mo[GR][D], mm[GR], ml[GR];
   const int b = blockIdx.x / H_q, i = blockIdx.x % H_q, tid = threadIdx.x;
   const int64_t pb = min(max((int64_t)pos[b], (int64_t)0), N_max - 1);
   const int n_valid = (int)min((int64_t)n_chunks, (pb + 1 + chunk - 1) / chunk);
   const float* src = part + ((int64_t)b * H_q + i) * n_chunks * (D + 2);
-  float lm = DEC_M_INIT;
-  for (int c = tid; c < n_valid; c += 256) {
-    const float m = src[c * (D + 2) + D];
-    sm[c] = m;
-    sl[c] = src[c * (D + 2) + D + 1];
-    lm = fmaxf(lm, m);
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) lm = fmaxf(lm, __shfl_xor(lm, off));
-  if ((tid & 63) == 0) wmax[tid >> 6] = lm;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
   const int gr = tid / D, e = tid % D;
-  float O = 0.f, L = 0.f;
+  float M = DEC_M_INIT, L = 0.f, O = 0.f;
 #pragma unroll 4
   for (int c = gr; c < n_valid; c += GR) {
-    const float f = __builtin_amdgcn_exp2f(sm[c] - M);
-    O = fmaf(src[c * (D + 2) + e], f, O);
-    L = fmaf(sl[c], f, L);
+    const float* st = src + (int64_t)c * (D + 2);
+    const float m = st[D], l = st[D + 1], o = st[e];
+    const float Mn = fmaxf(M, m);
+    const float fa = __builtin_amdgcn_exp2f(M - Mn), fb = __builtin_amdgcn_exp2f(m - Mn);
+    L = L * fa + l * fb;
+    O = O * fa + o * fb;
+    M = Mn;
   }
-  red_o[gr][e] = O;
-  if (e == 0) red_l[gr] = L;
+  mo[gr][e] = O;
+  if (e == 0) { mm[gr] = M; ml[gr] = L; }
   __syncthreads();
   if (tid < D) {
-    float o = 0.f, l = 0.f;
+    float Mt = DEC_M_INIT;
 #pragma unroll
-    for (int g2 = 0; g2 < GR; ++g2) { o += red_o[g2][tid]; l += red_l[g2]; }
-    a[((int64_t)b * H_q + i) * D + tid] = from_f32<T>(o / l);
+    for (int g2 = 0; g2 < GR; ++g2) Mt = fmaxf(Mt, mm[g2]);
+    float Lt = 0.f, Ot = 0.f;
+#pragma unroll
+    for (int g2 = 0; g2 < GR; ++g2) {
+      const float f = __builtin_amdgcn_exp2f(mm[g2] - Mt);
+      Lt += ml[g2] * f;
+      Ot += mo[g2][tid] * f;
+    }
+    a[((int64_t)b * H_q + i) * D + tid] = from_f32<T>(Ot / Lt);   // Lt > 0: key 0 is in chunk 0
   }
 }
 
@@ -500,7 +498,6 @@ hipError_t decode_impl(const void* q, const void* kc, const void* vc, const int3
   const dim3 grid((unsigned)pl.n_chunks, (unsigned)(H_kv * pl.n_hg), (unsigned)B);
   hipError_t e = partial_for<T, D>(pl.G, p, grid, stream);
   if (e != hipSuccess) return e;
-  if (pl.n_chunks > MAX_CHUNKS) return hipErrorInvalidConfiguration;
   decode_combine<T, D><<<(unsigned)(B * H_q), 256, 0, stream>>>(part, pos, (T*)a, (int)H_q,
                                                               pl.n_chunks, pl.chunk, N_max);
   return hipGetLastError();
