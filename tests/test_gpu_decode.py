@@ -139,3 +139,25 @@ def test_decode_batch_of_many_sequences(dev):
     rep = compare(wl.widen(y.cpu()), ref, "bf16")
     log(f"  19 sequences: {rep}")
     assert rep.ok, rep
+
+
+@pytest.mark.parametrize("H_q", [8, 16], ids=["sqa", "gqa_baseline"])
+def test_decode_in_the_benchmark_launch(dev, H_q):
+    """The decode step the benchmark times: 8 sequences whose caches hold
+    32767 tokens from sqa_prefill, each stepping its token 32767 (same shapes
+    and seed), for SQA (H_q = 8) and its GQA baseline (H_q = 16)."""
+    w = wl.Workload("sqa_bf16_decode_b8_cache32768", B=8, N=32768, d_model=1024, H=16, H_q=H_q,
+                    H_kv=4, causal=True, dtype="bf16", seed=1006)
+    log(f"case decode benchmark launch H_q={H_q}")
+    host, d = device_inputs(w, dev)
+    kc, vc = _caches(w, w.N, dev)
+    sqa.prefill(d["X"][:, :w.N - 1].contiguous(), d["Wq"], d["Wk"], d["Wv"], d["Wo"], kc, vc,
+                H=w.H, H_q=w.H_q, H_kv=w.H_kv)
+    pos = torch.full((w.B,), w.N - 1, dtype=torch.int32, device=dev)
+    y = sqa.decode_step(d["X"][:, w.N - 1].contiguous(), d["Wq"], d["Wk"], d["Wv"], d["Wo"], kc,
+                        vc, pos, H=w.H, H_q=w.H_q, H_kv=w.H_kv)
+    torch.cuda.synchronize()
+    ref = _oracle_rows(host, w, [b * w.N + w.N - 1 for b in range(w.B)])
+    rep = compare(wl.widen(y.cpu()), ref, "bf16")
+    log(f"  benchmark decode launch H_q={H_q}: {rep}")
+    assert rep.ok, rep
