@@ -228,3 +228,27 @@ def test_empty_batch_is_a_no_op(dev):
          for k, s in (("q", (256, 128)), ("k", (256, 64)), ("v", (256, 64)), ("o", (128, 256)))}
     y = sqa.forward(x, W["q"], W["k"], W["v"], W["o"], H=8, H_q=4, H_kv=2)
     assert y.shape == (0, 5, 256)
+
+
+def test_maximum_sequence_length_on_sampled_rows(dev):
+    """N = SQA_MAX_N = 2^24 tokens (one head, d_head 32, causal): every token,
+    tile and workgroup index of the path at its largest, against the oracle on
+    rows spread over the whole sequence."""
+    N = 1 << 24
+    w = wl.Workload("max_n_causal", B=1, N=N, d_model=32, H=1, H_q=1, H_kv=1, causal=True,
+                    dtype="bf16", seed=1234)
+    log(f"case maximum length: N={N}")
+    host, d = device_inputs(w, dev)
+    y = run_forward(w, d)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y).all())
+    rows = np.array([0, 1, 31, 32, 511, 512, 65535, 65536, (1 << 23) - 1, 1 << 23, 12345678,
+                     N - 513, N - 512, N - 2, N - 1], dtype=np.int64)
+    yg = wl.widen(y.reshape(-1, w.d_model)[torch.from_numpy(rows).to(dev)].cpu())
+    del d, y
+    o = oracle_inputs(host)
+    ref = oracle.sqa_forward_rows(o["X"], o["Wq"], o["Wk"], o["Wv"], o["Wo"], w.H_q, w.H_kv,
+                                  w.d_head, w.causal, bf16=True, rows=rows, row_block=1)["Y_rows"]
+    rep = compare(yg, ref, w.dtype)
+    log(f"  {rows.size} rows: {rep}")
+    assert rep.ok, rep
