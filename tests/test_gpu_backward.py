@@ -150,3 +150,28 @@ def test_saved_activations_give_the_same_results(dev, causal, dtype, dh):
     assert torch.equal(y, y2)
     for k, a, b in zip(GRADS, g, g2):
         assert torch.equal(a, b), k
+
+
+def test_backward_past_65535_row_tiles(dev):
+    """N = 65536*64 + 64 tokens (one head, d_head 32, causal): the transposes
+    of the backward take more than 65535 tiles of 64 rows, which a 2-D grid
+    with rows along y could not launch. dX near the end against the oracle."""
+    N = 65536 * 64 + 64
+    w = wl.Workload("past_y_limit", B=1, N=N, d_model=32, H=1, H_q=1, H_kv=1, causal=True,
+                    dtype="bf16", seed=4322)
+    log(f"case backward N={N}")
+    host, d = _inputs(w, dev)
+    got = _run(w, d)
+    torch.cuda.synchronize()
+    for k, x in zip(GRADS, got):
+        assert bool(torch.isfinite(x).all()), k
+    rows = [N - 1, N - 2, N - 33, N - 64]
+    gx = wl.widen(got[0].reshape(N, -1)[rows].cpu())
+    del d, got
+    o = {k: wl.widen(v) for k, v in host.items()}
+    ref = oracle.sqa_backward_rows(o["X"], o["Wq"], o["Wk"], o["Wv"], o["Wo"], o["dY"], 1, 1, 32,
+                                   True, True, rows, row_block=8)
+    rep = compare(gx, ref["dX_rows"], w.dtype)
+    log(f"  dX at rows {rows}: {rep}; max |dX| {float(np.abs(ref['dX_rows']).max()):.3e}")
+    assert float(np.abs(ref["dX_rows"]).max()) > 0
+    assert rep.ok, rep
