@@ -49,8 +49,9 @@ __device__ inline float f32_of(bf16 x) { return (float)x; }
 // c < C. 64x64 tiles through LDS, 16-byte global accesses on both sides
 // (C and r_total are multiples of 16 / sizeof(T)). With PERM the rows land in
 // swap23 order within each group of 16: dst[b][c][swap23(r)] = src[b][r][c].
-// The tiles are numbered along x, column tiles fastest (rows and columns can
-// each run into the millions, past the 65535 limit of the y dimension).
+// The tiles of all batches are numbered along x, column tiles fastest (rows,
+// columns and batches can each run past the 65535 limit of the y and z
+// dimensions).
 template <typename T, bool PERM>
 __global__ __launch_bounds__(256) void transpose_kernel(const T* src, int64_t src_bs, int64_t src_ld,
                                                         int r_valid, int r_total, T* dst,
@@ -58,9 +59,11 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* src, int64_t sr
   constexpr int EPC = 16 / (int)sizeof(T), TP = 64 + EPC;   // padded LDS row
   __shared__ __align__(16) T tile[64][TP];
   const int n_ct = (C + 63) / 64;
-  const int c0 = (int)(blockIdx.x % n_ct) * 64, r0 = (int)(blockIdx.x / n_ct) * 64;
-  src += blockIdx.z * src_bs;
-  dst += blockIdx.z * dst_bs;
+  const int64_t per_batch = (int64_t)((r_total + 63) / 64) * n_ct;
+  const int64_t bz = blockIdx.x / per_batch, t = blockIdx.x % per_batch;
+  const int c0 = (int)(t % n_ct) * 64, r0 = (int)(t / n_ct) * 64;
+  src += bz * src_bs;
+  dst += bz * dst_bs;
   constexpr int CPR = 64 / EPC;   // chunks per 64-element line
   for (int i = threadIdx.x; i < 64 * CPR; i += 256) {
     const int r = i / CPR, cc = (i % CPR) * EPC;
@@ -713,11 +716,11 @@ template <typename T, bool PERM = false>
 hipError_t transpose(const void* src, int64_t src_bs, int64_t src_ld, int64_t r_valid,
                      int64_t r_total, void* dst, int64_t dst_bs, int64_t dst_ld, int64_t C,
                      int64_t nbatch, hipStream_t stream) {
-  const int64_t tiles = (r_total + 63) / 64 * ((C + 63) / 64);
-  if (nbatch > 65535 || tiles > 0x7FFFFFFF || r_total > 0x7FFFFFFF || C > 0x7FFFFFFF)
+  const int64_t tiles = (r_total + 63) / 64 * ((C + 63) / 64) * nbatch;
+  if (tiles > 0x7FFFFFFF || r_total > 0x7FFFFFFF || C > 0x7FFFFFFF)
     return hipErrorInvalidConfiguration;
   if (PERM && r_total % 64) return hipErrorInvalidValue;   // the permutation stays within 64-row tiles
-  const dim3 grid((unsigned)tiles, 1u, (unsigned)nbatch);
+  const dim3 grid((unsigned)tiles);
   transpose_kernel<T, PERM><<<grid, 256, 0, stream>>>((const T*)src, src_bs, src_ld, (int)r_valid,
                                                       (int)r_total, (T*)dst, dst_bs, dst_ld, (int)C);
   return hipGetLastError();

@@ -42,32 +42,38 @@ __device__ inline float to_f32(bf16 x) { return (float)x; }
 // ---- prefill: K and V of tokens 0..N-1 into rows 0..N-1 of the caches ----
 
 // k [BH, Np, d] -> kc [BH, N_max, d]: the first N rows are n16 contiguous chunks.
+// (sequence, head) pairs stride over the grid's y dimension (BH may pass 65535).
 __global__ __launch_bounds__(256) void copy_rows(const Chunk* k, Chunk* kc, int64_t n16,
-                                                 int64_t src_stride16, int64_t dst_stride16) {
-  const int64_t bh = blockIdx.y;
-  const Chunk* src = k + bh * src_stride16;
-  Chunk* dst = kc + bh * dst_stride16;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256)
-    dst[i] = src[i];
+                                                 int64_t src_stride16, int64_t dst_stride16,
+                                                 int64_t BH) {
+  for (int64_t bh = blockIdx.y; bh < BH; bh += gridDim.y) {
+    const Chunk* src = k + bh * src_stride16;
+    Chunk* dst = kc + bh * dst_stride16;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256)
+      dst[i] = src[i];
+  }
 }
 
-// vt [BH, D, Np] -> vc [BH, N_max, D] for t < N, 64 tokens per workgroup through LDS.
+// vt [BH, D, Np] -> vc [BH, N_max, D] for t < N, 64 tokens per workgroup through LDS;
+// (sequence, head) pairs stride over the grid's y dimension.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void transpose_v(const T* vt, T* vc, int N, int64_t Np,
-                                                   int64_t N_max) {
+                                                   int64_t N_max, int64_t BH) {
   __shared__ T tile[D][KB + 1];
-  const int64_t bh = blockIdx.y;
   const int t0 = blockIdx.x * KB;
-  const T* src = vt + bh * D * Np;
-  T* dst = vc + bh * N_max * D;
-  for (int i = threadIdx.x; i < D * KB; i += 256) {
-    const int c = i / KB, t = i % KB;
-    if (t0 + t < N) tile[c][t] = src[c * Np + t0 + t];
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < D * KB; i += 256) {
-    const int t = i / D, c = i % D;
-    if (t0 + t < N) dst[(int64_t)(t0 + t) * D + c] = tile[c][t];
+  for (int64_t bh = blockIdx.y; bh < BH; bh += gridDim.y) {
+    const T* src = vt + bh * D * Np;
+    T* dst = vc + bh * N_max * D;
+    __syncthreads();   // the previous pair's reads of the tile are done
+    for (int i = threadIdx.x; i < D * KB; i += 256) {
+      const int c = i / KB, t = i % KB;
+      if (t0 + t < N) tile[c][t] = src[(int64_t)c * Np + t0 + t];
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < D * KB; i += 256) {
+      const int t = i / D, c = i % D;
+      if (t0 + t < N) dst[(int64_t)(t0 + t) * D + c] = tile[c][t];
+    }
   }
 }
 
@@ -515,20 +521,20 @@ hipError_t launch_fill_cache(sqa_dtype dt, const void* k, const void* vt, void* 
                              int64_t d_head, hipStream_t stream) {
   const int64_t es = dt == SQA_DTYPE_BF16 ? 2 : 4;
   const int64_t BH = B * H_kv;
-  if (BH > 65535) return hipErrorInvalidConfiguration;
+  const unsigned gy = (unsigned)std::min<int64_t>(BH, 65535);
   const int64_t n16 = N * d_head * es / 16;
   const unsigned gx = (unsigned)std::min<int64_t>(1024, (n16 + 255) / 256);
-  copy_rows<<<dim3(gx, (unsigned)BH), 256, 0, stream>>>(
-      (const Chunk*)k, (Chunk*)kc, n16, Np * d_head * es / 16, N_max * d_head * es / 16);
+  copy_rows<<<dim3(gx, gy), 256, 0, stream>>>(
+      (const Chunk*)k, (Chunk*)kc, n16, Np * d_head * es / 16, N_max * d_head * es / 16, BH);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)((N + KB - 1) / KB), (unsigned)BH);
+  const dim3 grid((unsigned)((N + KB - 1) / KB), gy);
   if (dt == SQA_DTYPE_BF16) {
-    if (d_head == 64) transpose_v<bf16, 64><<<grid, 256, 0, stream>>>((const bf16*)vt, (bf16*)vc, (int)N, Np, N_max);
-    else transpose_v<bf16, 32><<<grid, 256, 0, stream>>>((const bf16*)vt, (bf16*)vc, (int)N, Np, N_max);
+    if (d_head == 64) transpose_v<bf16, 64><<<grid, 256, 0, stream>>>((const bf16*)vt, (bf16*)vc, (int)N, Np, N_max, BH);
+    else transpose_v<bf16, 32><<<grid, 256, 0, stream>>>((const bf16*)vt, (bf16*)vc, (int)N, Np, N_max, BH);
   } else {
-    if (d_head == 64) transpose_v<float, 64><<<grid, 256, 0, stream>>>((const float*)vt, (float*)vc, (int)N, Np, N_max);
-    else transpose_v<float, 32><<<grid, 256, 0, stream>>>((const float*)vt, (float*)vc, (int)N, Np, N_max);
+    if (d_head == 64) transpose_v<float, 64><<<grid, 256, 0, stream>>>((const float*)vt, (float*)vc, (int)N, Np, N_max, BH);
+    else transpose_v<float, 32><<<grid, 256, 0, stream>>>((const float*)vt, (float*)vc, (int)N, Np, N_max, BH);
   }
   return hipGetLastError();
 }

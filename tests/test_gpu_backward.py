@@ -175,3 +175,21 @@ def test_backward_past_65535_row_tiles(dev):
     log(f"  dX at rows {rows}: {rep}; max |dX| {float(np.abs(ref['dX_rows']).max()):.3e}")
     assert float(np.abs(ref["dX_rows"]).max()) > 0
     assert rep.ok, rep
+
+
+
+def test_backward_of_more_than_65535_sequence_heads(dev):
+    """B * H_q = 65600 (sequence, query head) pairs of 3 tokens each: the
+    per-head transposes take them along the grid's x dimension. Every gradient
+    against the oracle."""
+    w = wl.Workload("wide_batch", B=8200, N=3, d_model=256, H=8, H_q=8, H_kv=2, causal=True,
+                    dtype="bf16", seed=4323)
+    log(f"case backward B={w.B} N={w.N}")
+    host, d = _inputs(w, dev)
+    got = _run(w, d)
+    torch.cuda.synchronize()
+    ref = _oracle(w, host)
+    for k, g in zip(GRADS, got):
+        rep = compare(wl.widen(g.cpu()), ref[k], w.dtype)
+        log(f"  {k}: {rep}")
+        assert rep.ok, (k, rep)

@@ -53,6 +53,24 @@ def test_prefill_is_the_causal_forward_and_fills_the_caches(dev):
     assert bool(torch.isnan(kc[:, :, w.N:]).all()) and bool(torch.isnan(vc[:, :, w.N:]).all())
 
 
+
+def test_prefill_of_more_than_65535_sequence_heads(dev):
+    """B * H_kv = 65600 (sequence, key/value head) pairs: the cache fill strides
+    them over a grid of at most 65535 rows."""
+    w = wl.Workload("prefill_wide", B=16400, N=3, d_model=128, H=4, H_q=4, H_kv=4, causal=True,
+                    dtype="bf16", seed=83)
+    _, d = device_inputs(w, dev)
+    kc, vc = _caches(w, 4, dev)
+    y = sqa.prefill(d["X"], d["Wq"], d["Wk"], d["Wv"], d["Wo"], kc, vc, H=w.H, H_q=w.H_q, H_kv=w.H_kv)
+    y_ref = sqa.forward(d["X"], d["Wq"], d["Wk"], d["Wv"], d["Wo"], H=w.H, H_q=w.H_q, H_kv=w.H_kv,
+                        causal=True)
+    q, k, vt = sqa.qkv_projection(d["X"], d["Wq"], d["Wk"], d["Wv"], H=w.H, H_q=w.H_q, H_kv=w.H_kv)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_ref)
+    assert torch.equal(kc[:, :, :w.N], k[:, :, :w.N])
+    assert torch.equal(vc[:, :, :w.N], vt[..., :w.N].transpose(-1, -2))
+    assert bool(torch.isnan(kc[:, :, w.N:]).all()) and bool(torch.isnan(vc[:, :, w.N:]).all())
+
 DECODE_SHAPES = [
     # (H, d_head, H_q, H_kv, dtype): g = 2, 1, 4, 16 (two head groups), fp32, d = 32, and
     # d_model = 160 (projection widths that are not multiples of the 256-column blocks)
