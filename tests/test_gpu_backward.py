@@ -61,6 +61,7 @@ CASES = [
     ("g4_d1024", 1, 257, 16, 64, 8, 2, True, "bf16"),
     ("g4_d32", 2, 333, 8, 32, 4, 1, True, "bf16"),
     ("g16", 1, 129, 16, 64, 16, 1, False, "bf16"),
+    ("g64", 1, 150, 64, 32, 64, 1, True, "bf16"),
     ("mha_d32_full", 1, 100, 8, 32, 8, 8, False, "bf16"),
     ("fp32_full", 2, 150, 8, 32, 4, 2, False, "fp32"),
     ("fp32_causal_d64", 1, 90, 4, 64, 4, 2, True, "fp32"),

@@ -73,9 +73,11 @@ def test_prefill_of_more_than_65535_sequence_heads(dev):
 
 DECODE_SHAPES = [
     # (H, d_head, H_q, H_kv, dtype): g = 2, 1, 4, 16 (two head groups), fp32, d = 32, and
-    # d_model = 160 (projection widths that are not multiples of the 256-column blocks)
+    # d_model = 160 (projection widths that are not multiples of the 256-column blocks), and
+    # g = 64 (eight head groups of one key/value head)
     (16, 64, 8, 4, "bf16"), (16, 64, 4, 4, "bf16"), (16, 64, 4, 1, "bf16"),
     (16, 64, 16, 1, "bf16"), (8, 32, 4, 2, "fp32"), (8, 32, 6, 2, "bf16"), (5, 32, 5, 1, "bf16"),
+    (64, 32, 64, 1, "bf16"),
 ]
 
 

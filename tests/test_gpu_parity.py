@@ -252,3 +252,13 @@ def test_maximum_sequence_length_on_sampled_rows(dev):
     rep = compare(yg, ref, w.dtype)
     log(f"  {rows.size} rows: {rep}")
     assert rep.ok, rep
+
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_sixty_four_query_heads_per_key_value_head(dev, causal):
+    """g = 64 (H_q = 64, H_kv = 1): eight 8-head workgroups per key/value
+    stream in the attention, every stage against the oracle."""
+    w = wl.Workload(f"g64_{'c' if causal else 'nc'}", B=1, N=150, d_model=64 * 32, H=64, H_q=64,
+                    H_kv=1, causal=causal, dtype="bf16", seed=777)
+    full_check(w, dev, stages=True)
