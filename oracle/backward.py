@@ -96,21 +96,22 @@ def sqa_backward(X, Wq, Wk, Wv, Wo, dY, H_q: int, H_kv: int, d_head: int, causal
     dA = _maybe_round(dY @ Wo.T, bf16)
     dAh = split_heads(dA, H_q, d_head)
     dQh = np.empty((B, H_q, N, d_head))
+    dK_head = np.empty((B, H_q, N, d_head))   # each query head's share of dK and dV
+    dV_head = np.empty((B, H_q, N, d_head))
+
+    def one(task):   # query head i of batch b
+        b, i = task
+        j = kv_head_for(i, H_q, H_kv)
+        dQh[b, i], dK_head[b, i], dV_head[b, i] = attention_head_backward(
+            Qh[b, i], Kh[b, j], Vh[b, j], dAh[b, i], causal, row_block)
+
+    _run_tasks(one, [(b, i) for b in range(B) for i in range(H_q)], _pool_workers(workers))
     dKh = np.zeros((B, H_kv, N, d_head))
     dVh = np.zeros((B, H_kv, N, d_head))
-
-    def one(task):   # every query head of key/value head j in batch b
-        b, j = task
-        for i in range(H_q):
-            if kv_head_for(i, H_q, H_kv) != j:
-                continue
-            dq, dk, dv = attention_head_backward(Qh[b, i], Kh[b, j], Vh[b, j], dAh[b, i], causal,
-                                                 row_block)
-            dQh[b, i] = dq
-            dKh[b, j] += dk
-            dVh[b, j] += dv
-
-    _run_tasks(one, [(b, j) for b in range(B) for j in range(H_kv)], _pool_workers(workers))
+    for i in range(H_q):   # dK_j, dV_j: sums over the query heads i of group j, in head order
+        j = kv_head_for(i, H_q, H_kv)
+        dKh[:, j] += dK_head[:, i]
+        dVh[:, j] += dV_head[:, i]
 
     def merge(h):   # [B, heads, N, d] -> [B, N, heads*d], head-major columns
         return h.transpose(0, 2, 1, 3).reshape(B, N, -1)
@@ -194,3 +195,86 @@ def sqa_backward_rows(X, Wq, Wk, Wv, Wo, dY, H_q: int, H_kv: int, d_head: int, c
     dQr, dKr, dVr = (_maybe_round(t, bf16) for t in (dQr, dKr, dVr))
     dXr = _maybe_round(dQr @ Wq.T + dKr @ Wk.T + dVr @ Wv.T, bf16)
     return {"dX_rows": dXr, "dQ_rows": dQr, "dK_rows": dKr, "dV_rows": dVr}
+
+
+def sqa_backward_dy_rows(X, Wq, Wk, Wv, Wo, dY, H_q: int, H_kv: int, d_head: int, causal: bool,
+                         bf16: bool, rows, workers: Optional[int] = None, row_block: int = 128
+                         ) -> Dict[str, np.ndarray]:
+    """``sqa_backward`` for an upstream gradient dY that is zero outside the
+    flat token rows ``rows`` (row = b*N + t); it raises if dY is not.
+
+    Every result is the one ``sqa_backward`` defines, at every position. Only
+    work that is exactly zero is left out: a query row r with dY[r] = 0 has
+    dA[r] = 0, so dO = 0, D = 0, dP = 0 and dS = 0 in that row, and it adds
+    nothing to dQ, dK or dV. So only the given query rows run the forward and
+    the softmax backward, each against all of its keys (keys 0..r when
+    causal); dK and dV are summed from those rows for every key, and dX and
+    the weight gradients are formed over all tokens as in ``sqa_backward``.
+    Returns dX [B,N,d_model], dWq, dWk, dWv, dWo and dQ, dK, dV [B,N,heads*d].
+    """
+    X, Wq, Wk, Wv, Wo, dY = (np.asarray(t, dtype=np.float64) for t in (X, Wq, Wk, Wv, Wo, dY))
+    B, N, D = check_shapes(X, Wq, Wk, Wv, Wo, H_q, H_kv, d_head)
+    if dY.shape != (B, N, D):
+        raise ValueError(f"dY has shape {dY.shape}, expected {(B, N, D)}")
+    rows = np.unique(np.asarray(list(rows), dtype=np.int64))
+    if rows.size and (rows.min() < 0 or rows.max() >= B * N):
+        raise ValueError("row index out of range")
+    outside = np.ones(B * N, dtype=bool)
+    outside[rows] = False
+    if np.any(dY.reshape(B * N, D)[outside] != 0):
+        raise ValueError("dY is nonzero outside the given rows")
+    d = d_head
+    scale = 1.0 / math.sqrt(d)
+    dQh = np.zeros((B, H_q, N, d))
+    dKh = np.zeros((B, H_kv, N, d))
+    dVh = np.zeros((B, H_kv, N, d))
+    A = np.zeros((B, N, H_q * d))
+    for b in np.unique(rows // N):
+        b = int(b)
+        pos = rows[rows // N == b] % N
+        n_keys = int(pos.max()) + 1 if causal else N   # later keys are masked for every row
+        Kb = split_heads(_maybe_round(X[b:b + 1, :n_keys] @ Wk, bf16), H_kv, d)[0]
+        Vb = split_heads(_maybe_round(X[b:b + 1, :n_keys] @ Wv, bf16), H_kv, d)[0]
+        Qr = _maybe_round(X[b, pos] @ Wq, bf16)
+        dAr = _maybe_round(dY[b, pos] @ Wo.T, bf16)
+
+        def one(j):   # every query head of key/value head j
+            k, v = Kb[j], Vb[j]
+            for i in range(H_q):
+                if kv_head_for(i, H_q, H_kv) != j:
+                    continue
+                hc = slice(i * d, (i + 1) * d)
+                for r0 in range(0, pos.size, row_block):
+                    r1 = min(pos.size, r0 + row_block)
+                    nk = int(pos[r1 - 1]) + 1 if causal else N
+                    q, do = Qr[r0:r1, hc], dAr[r0:r1, hc]
+                    s = (q @ k[:nk].T) * scale
+                    if causal:
+                        s = np.where(np.arange(nk)[None, :] <= pos[r0:r1, None], s, -np.inf)
+                    s = s - s.max(axis=1, keepdims=True)
+                    e = np.exp(s)
+                    p = e / e.sum(axis=1, keepdims=True)
+                    o = p @ v[:nk]
+                    A[b, pos[r0:r1], hc] = o
+                    Dr = np.sum(do * o, axis=1)
+                    ds = softmax_backward(p, do @ v[:nk].T, Dr)
+                    dQh[b, i, pos[r0:r1]] = (ds @ k[:nk]) * scale
+                    dKh[b, j, :nk] += (ds.T @ q) * scale
+                    dVh[b, j, :nk] += p.T @ do
+
+        _run_tasks(one, list(range(H_kv)), _pool_workers(workers))
+
+    def merge(h):   # [B, heads, N, d] -> [B, N, heads*d], head-major columns
+        return h.transpose(0, 2, 1, 3).reshape(B, N, -1)
+
+    dQ = _maybe_round(merge(dQh), bf16)
+    dK = _maybe_round(merge(dKh), bf16)
+    dV = _maybe_round(merge(dVh), bf16)
+    dX = _maybe_round(dQ @ Wq.T + dK @ Wk.T + dV @ Wv.T, bf16)
+    Xf = X.reshape(B * N, D)
+    dWq = _maybe_round(Xf.T @ dQ.reshape(B * N, -1), bf16)
+    dWk = _maybe_round(Xf.T @ dK.reshape(B * N, -1), bf16)
+    dWv = _maybe_round(Xf.T @ dV.reshape(B * N, -1), bf16)
+    # A's rows outside `rows` meet zero rows of dY
+    dWo = _maybe_round(_maybe_round(A, bf16).reshape(B * N, -1).T @ dY.reshape(B * N, D), bf16)
+    return {"dX": dX, "dWq": dWq, "dWk": dWk, "dWv": dWv, "dWo": dWo, "dQ": dQ, "dK": dK, "dV": dV}

@@ -4,9 +4,23 @@ workload's dtype.
 
 Tolerances:
   fp32: max |Y - Y_ref| <= 1e-4.
-  bf16: ||Y - Y_ref|| / ||Y_ref|| <= 1e-2 over all compared elements, and
+  bf16: ||Y - Y_ref|| / ||Y_ref|| <= 1e-2 over all compared elements,
+        ||Y[r] - Y_ref[r]|| <= 1e-2 * max(||Y_ref[r]||, ROW_FLOOR * rms)
+        for every output row r, where rms is the root mean square of the
+        reference rows' norms (not applied when the whole reference is zero),
+        and
         |Y[r, c] - Y_ref[r, c]| <= 2e-2 * max(1, max_c' |Y_ref[r, c']|)
         for every output row r.
+The per-row bound catches an error confined to a few rows (one head's
+columns wrong in one row, say), which the global relative L2 norm averages
+away and which the elementwise bound misses wherever outputs are far below 1.
+Its floor at a quarter of the typical row norm is for rows that cancel: a
+weight-gradient row summed over a few tokens can be several times smaller
+than the terms it sums, and a one-ulp difference in a bf16-rounded
+intermediate (dV rounded from fp32 on the GPU, from fp64 in the oracle) then
+moves it by more than 1% of its own norm (3.3% on a 4-token dWv row whose
+norm is 0.15 of the typical row's). A row wrong at the typical magnitude is
+still caught.
 The elementwise bound scales with the row, not the element. Y[r, c] is a dot
 product of the attention row A[r, :] with a column of Wo. Rounding A to bf16
 (relative 2^-9 per element) therefore moves every element of the row by an
@@ -26,12 +40,15 @@ import numpy as np
 import workloads as wl
 
 
+ROW_FLOOR = 0.25
+
+
 @dataclass
 class Report:
     max_abs: float
     rel_l2: float
     worst_scaled: float      # max over rows of max_c |err[r, c]| / max(1, max_c |ref[r, c]|)
-    worst_row_rel: float     # max over rows of ||err[r]|| / ||ref[r]||
+    worst_row_rel: float     # max over rows of ||err[r]|| / max(||ref[r]||, ROW_FLOOR * rms)
     ok: bool
 
     def __str__(self):
@@ -40,8 +57,18 @@ class Report:
                 f"{'OK' if self.ok else 'FAIL'}")
 
 
-def compare(got: np.ndarray, ref: np.ndarray, dtype: str) -> Report:
-    """Compare outputs whose last axis is one output row (d_model wide)."""
+# Weight gradients sum over the batch's tokens; below this many tokens a row is
+# a combination of so few bf16-rounded vectors that a one-ulp difference in
+# one of them (dK rounded from fp32 on the GPU, from fp64 in the oracle) moves
+# the row by several percent (up to 5% on 4-token dWk rows), and the per-row
+# bound is not applied to them.
+MIN_TOKENS_FOR_ROW_GATE = 64
+
+
+def compare(got: np.ndarray, ref: np.ndarray, dtype: str, row_gate: bool = True) -> Report:
+    """Compare outputs whose last axis is one output row (d_model wide).
+    row_gate=False leaves out the per-row bound (bf16), for weight gradients
+    summed over fewer than MIN_TOKENS_FOR_ROW_GATE tokens."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (got.shape, ref.shape)
@@ -58,11 +85,15 @@ def compare(got: np.ndarray, ref: np.ndarray, dtype: str) -> Report:
     row_scale = np.maximum(1.0, np.abs(r2).max(axis=1))
     scaled = float((err.max(axis=1) / row_scale).max())
     rn = np.linalg.norm(r2, axis=1)
-    row_rel = float((np.linalg.norm(g2 - r2, axis=1) / np.where(rn > 0, rn, 1.0)).max())
+    en = np.linalg.norm(g2 - r2, axis=1)
+    den = np.maximum(rn, ROW_FLOOR * float(np.sqrt(np.mean(rn * rn))))
+    # an all-zero reference (one-token gradients, say) has no row scale: the
+    # absolute global and elementwise bounds decide alone
+    row_rel = float((en / den).max()) if (den > 0).all() else 0.0
     if dtype == "fp32":
         ok = max_abs <= 1e-4
     else:
-        ok = rel <= 1e-2 and scaled <= 2e-2
+        ok = rel <= 1e-2 and scaled <= 2e-2 and (row_rel <= 1e-2 or not row_gate)
     return Report(max_abs, rel, scaled, row_rel, ok)
 
 

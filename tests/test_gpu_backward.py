@@ -6,12 +6,20 @@ upstream gradient dY), with the tolerances of the workload's dtype
 (tests/parity.py). Weight gradients are compared row by row of the weight
 matrix. Shapes span several key and query tiles with ragged tails, every
 group size the kernels treat differently, both head widths and both dtypes.
-At the full 131072-token size the whole oracle cannot run in a test. There
-dX is compared with the oracle at sampled rows of the last 1024 positions:
-each such row takes dQ from one query row against every key, and dK and dV
-from every later query row, so the oracle computes them one by one
-(oracle.sqa_backward_rows). Determinism and exact scaling in dY are checked
-on every output.
+The headline head shape (H=16, H_q=8, H_kv=4, d_head=64, causal) is compared
+whole at 32768 tokens. At the full 131072-token size the whole oracle cannot
+run in a test, so two checks share it:
+  * dX at sampled rows of the last 1024 positions: each such row takes dQ
+    from one query row against every key, and dK and dV from every later
+    query row, so the oracle computes them one by one
+    (oracle.sqa_backward_rows);
+  * an upstream gradient that is zero outside two windows of query rows (the
+    middle and the end of the sequence): every key then still collects dK
+    and dV over the whole causal range of query tiles, the weight gradients
+    still sum over every token, and the oracle only runs the rows that carry
+    a gradient (oracle.sqa_backward_dy_rows). All five gradients are compared
+    at every position.
+Determinism and exact scaling in dY are checked on every output.
 """
 import numpy as np
 import pytest
@@ -20,7 +28,7 @@ import torch
 import oracle
 import sparse_query_attention_amd as sqa
 import workloads as wl
-from parity import compare, log
+from parity import MIN_TOKENS_FOR_ROW_GATE, compare, log
 
 pytestmark = pytest.mark.gpu
 
@@ -67,6 +75,7 @@ CASES = [
     ("fp32_causal_d64", 1, 90, 4, 64, 4, 2, True, "fp32"),
     ("one_token", 2, 1, 8, 64, 4, 2, True, "bf16"),
     ("sqa_n2048", 1, 2048, 16, 64, 8, 4, True, "bf16"),
+    ("sqa_n4097", 1, 4097, 16, 64, 8, 4, True, "bf16"),
 ]
 
 
@@ -83,7 +92,8 @@ def test_backward_matches_oracle(dev, case):
     ref = _oracle(w, host)
     bad = []
     for k, g in zip(GRADS, got):
-        rep = compare(wl.widen(g.cpu()), ref[k], dtype)
+        rep = compare(wl.widen(g.cpu()), ref[k], dtype,
+                      k == "dX" or w.tokens >= MIN_TOKENS_FOR_ROW_GATE)
         log(f"  {k}: {rep}")
         if not rep.ok:
             bad.append(k)
@@ -131,6 +141,65 @@ def test_backward_at_full_size_matches_sampled_rows_is_deterministic_and_scales(
     rep = compare(got, ref["dX_rows"], w.dtype)
     log(f"  dX at rows {rows}: {rep}")
     assert rep.ok, rep
+
+
+def test_backward_headline_heads_at_32768_tokens_all_gradients(dev):
+    """The benchmark's head shape (H=16, H_q=8, H_kv=4, d_head=64, causal) at
+    32768 tokens: every element of all five gradients against the oracle.
+    Early keys collect dK and dV over 32k query rows here, and the split-K
+    weight gradients sum over 32768 tokens."""
+    w = wl.SQA_131K_CAUSAL.with_(name="sqa_bf16_causal_n32768", N=32768)
+    log(f"case backward all gradients {w.name}")
+    host, d = _inputs(w, dev)
+    got = [g.cpu() for g in _run(w, d)]
+    torch.cuda.synchronize()
+    del d
+    ref = _oracle(w, host)
+    bad = []
+    for k, g in zip(GRADS, got):
+        rep = compare(wl.widen(g), ref[k], w.dtype)
+        log(f"  {k}: {rep}")
+        if not rep.ok:
+            bad.append(k)
+    assert not bad, bad
+
+
+def _dy_windows(N):
+    """Query rows that carry an upstream gradient: 1024 rows around the middle
+    of the sequence and its last 512 rows."""
+    return np.r_[np.arange(N // 2 - 512, N // 2 + 512), np.arange(N - 512, N)]
+
+
+def test_backward_at_full_size_with_dy_on_two_windows_all_gradients(dev):
+    """131072 tokens, causal, in the benchmark's launch, with dY zero outside
+    two windows of rows: all five gradients at every position against the
+    oracle. Every key's dK and dV sum over the whole causal range of query
+    tiles (most of them carry zeros), and dWk and dWv sum over all 131072
+    tokens."""
+    w = wl.SQA_131K_CAUSAL
+    rows = _dy_windows(w.N)
+    log(f"case backward full size, dY on {rows.size} rows, {w.name}")
+    arrays = wl.draw(w)
+    dy = np.zeros_like(wl.draw_upstream_grad(w))
+    dy[0, rows] = wl.draw_upstream_grad(w)[0, rows]
+    arrays["dY"] = dy
+    host = wl.to_device_dtype(arrays, w.dtype)
+    d = {k: v.to(dev) for k, v in host.items()}
+    got = [g.cpu() for g in _run(w, d)]
+    torch.cuda.synchronize()
+    del d
+    o = {k: wl.widen(v) for k, v in host.items()}
+    ref = oracle.sqa_backward_dy_rows(o["X"], o["Wq"], o["Wk"], o["Wv"], o["Wo"], o["dY"], w.H_q,
+                                      w.H_kv, w.d_head, True, True, rows)
+    bad = []
+    for k, g in zip(GRADS, got):
+        rep = compare(wl.widen(g), ref[k], w.dtype)
+        log(f"  {k}: {rep}")
+        if not rep.ok:
+            bad.append(k)
+    # rows before the first window still get gradients (through dK and dV)
+    assert (np.abs(ref["dX"][0, :1024]).max(axis=1) > 0).all()
+    assert not bad, bad
 
 
 @pytest.mark.parametrize("causal,dtype,dh", [(True, "bf16", 64), (False, "bf16", 32), (True, "fp32", 32)])

@@ -105,7 +105,7 @@ HEADS = [  # (H, d_head, H_q, H_kv): g = 1, 2, 16, 2, 8, 3
     (16, 64, 4, 4), (16, 64, 8, 4), (16, 64, 16, 1), (8, 32, 4, 2), (16, 32, 16, 2), (8, 32, 6, 2),
 ]
 LENGTHS = [(1, False), (2, True), (17, False), (63, True), (64, False), (65, True), (127, False),
-           (255, True), (257, False), (1000, True)]
+           (255, True), (257, False), (1000, True), (4097, True), (2500, False)]
 
 
 def _small_cases():

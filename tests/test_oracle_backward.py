@@ -178,6 +178,59 @@ def test_backward_rows_reject_bad_rows():
 
 
 # ----------------------------------------------------------------------------------------------
+# an upstream gradient on a few rows: sqa_backward_dy_rows against autograd and the full backward
+
+def _dy_on_rows(dY, rows):
+    B, N, D = dY.shape
+    out = np.zeros_like(dY).reshape(B * N, D)
+    out[rows] = dY.reshape(B * N, D)[rows]
+    return out.reshape(B, N, D)
+
+
+DY_ROWS_CASES = [(True, False, 4, 2), (True, True, 4, 2), (False, False, 4, 1),
+                 (False, True, 2, 2), (True, True, 8, 1)]
+
+
+@pytest.mark.parametrize("causal,bf16,H_q,H_kv", DY_ROWS_CASES)
+def test_dy_rows_backward_matches_torch_autograd(causal, bf16, H_q, H_kv):
+    """Every gradient, at every position, against autograd through a forward
+    written with torch ops, for dY zero outside a few rows of each sequence."""
+    d, N, B = 4, 37, 2
+    params, dY = _problem(95 + H_q, B, N, 8, d, H_q, H_kv)
+    rows = [3, 4, 20, 36, N + 0, N + 30]
+    dY = _dy_on_rows(dY, rows)
+    if bf16:
+        params = [oracle.round_bf16(p) for p in params]
+        dY = oracle.round_bf16(dY)
+    g = oracle.sqa_backward_dy_rows(*params, dY, H_q, H_kv, d, causal, bf16, rows, row_block=2)
+    ref = _torch_grads(params, dY, H_q, H_kv, d, causal, bf16)
+    for k in GRADS:
+        err = _rel_l2(g[k], ref[k])
+        assert err < (1e-5 if bf16 else 1e-12), (k, err)
+    if causal:   # keys past the last row carrying dY get nothing
+        assert not g["dX"][1, 31:].any() and g["dX"][1, 30].any()
+
+
+def test_dy_rows_backward_is_the_full_backward():
+    d, N, B, H_q, H_kv = 4, 50, 1, 4, 2
+    params, dY = _problem(96, B, N, 4, d, H_q, H_kv)
+    rows = list(range(10, 19)) + [44]
+    dY = _dy_on_rows(dY, rows)
+    full = oracle.sqa_backward(*params, dY, H_q, H_kv, d, True, bf16=False)
+    got = oracle.sqa_backward_dy_rows(*params, dY, H_q, H_kv, d, True, False, rows, row_block=4)
+    for k in GRADS + ["dQ", "dK", "dV"]:
+        np.testing.assert_allclose(got[k], full[k], rtol=1e-12, atol=1e-14, err_msg=k)
+
+
+def test_dy_rows_backward_rejects_dy_outside_the_rows():
+    params, dY = _problem(97, 1, 6, 2, 4, 2, 1)
+    with pytest.raises(ValueError):
+        oracle.sqa_backward_dy_rows(*params, dY, 2, 1, 4, True, False, [0, 1, 2])
+    with pytest.raises(ValueError):
+        oracle.sqa_backward_dy_rows(*params, _dy_on_rows(dY, [1]), 2, 1, 4, True, False, [6])
+
+
+# ----------------------------------------------------------------------------------------------
 # planted mistakes: each must make a pin fail
 
 def _fd_fails(monkeypatch_apply, case=(4, 2, 4, 2, True)):
