@@ -5,11 +5,11 @@
 // work scales with H_q ("Sparse Query Attention (SQA)...", arXiv 2510.01817,
 // abstract; ReactiveAI/GQA-Ref-Micro model card, description).
 //
-// Design (one workgroup = 4 waves of 64 lanes):
+// Design (one workgroup = 8 waves of 64 lanes, or 4 for some grids):
 //  * A workgroup owns one (batch, key/value head) pair, G query heads of that
-//    head's group and a tile of queries: 256x1, 128x2 or 64x4 queries x heads.
-//    Every key/value tile staged in LDS is read by all G heads, so repeated
-//    K/V is never materialised.
+//    head's group and a tile of queries: 512x1, 256x2, 128x4 or 64x8 queries x
+//    heads with 8 waves (half that with 4). Every key/value tile staged in LDS
+//    is read by all G heads, so repeated K/V is never materialised.
 //  * Each wave owns 64 query rows of one head (two 32-query MFMA blocks). It
 //    computes S^T = K Q^T, which puts one query per lane (lanes l and l+32
 //    share query l%32). Row max and row sum then need a single cross-lane
@@ -22,14 +22,18 @@
 //    are single 16-byte LDS reads.
 //  * Online softmax in the exp2 domain with fp32 running max and sum. The
 //    VALU, not the MFMA pipe, bounds this kernel at d_head = 64, so per score
-//    it spends: half a v_max3, one FMA, one v_exp, half a v_cvt_pk_bf16 and
-//    half a v_dot2 (the row sum is taken on the bf16 P that the PV product
-//    consumes). The O accumulators are rescaled lazily, only when a row's max
-//    outgrows the reference by 2^8.
+//    it spends one FMA, one v_exp, half a v_cvt_pk_bf16 and half a v_dot2
+//    (the row sum is taken on the bf16 P that the PV product consumes). No row
+//    max is taken on the common path: the exponentials use a reference that
+//    may lag the running max, and a block is redone against its exact max only
+//    when its sums show that the reference fell too far behind.
 //  * Causal: key tiles past a workgroup's last query are never loaded, and a
-//    wave skips the MFMAs of 32-key blocks past its own last query. Only
-//    blocks that cross the diagonal or the sequence end are masked. The
-//    heaviest query tiles are dispatched first.
+//    wave computes nothing for 32-key blocks past its own last query (it only
+//    keeps passing the workgroup's barriers and issuing its share of the tile
+//    loads). The two waves that share a SIMD take complementary query rows, so
+//    every SIMD carries the same causal work. Only blocks that cross the
+//    diagonal or the sequence end are masked. The heaviest query tiles are
+//    dispatched first.
 #include <math.h>
 
 #include <atomic>
@@ -46,12 +50,18 @@ constexpr int NBUF = 4;      // LDS tile ring: in use, visible next, NBUF-2 in f
 constexpr int QB = 2;             // 32-query MFMA column blocks per wave
 constexpr int FETCH_AHEAD = 2;    // LDS fragments read ahead of their first MFMA
 constexpr int QW = 32 * QB;       // query rows per wave
-// Exponentials are taken against a reference max m_ref that may lag the true
-// running max. A lane's block sum above SUM_LIMIT (or inf/NaN) means the
-// reference is too low for that block; only then is the block's exact max
-// computed, O and l rescaled and the block's exponentials redone.
-constexpr float SUM_LIMIT = 256.0f;
-constexpr float M_INIT = -1e30f;   // finite, so masked scores give exp2(-inf) = 0
+// Exponentials are taken against a reference m_ref (exp2 domain) set MARGIN
+// binades above a row's running max when it is (re)computed, and clamped to
+// [0, 1] (the clamp bit of v_exp_f32, free), so no weight can overflow however
+// far the reference lags. While the row's max stays within MARGIN - 5 binades
+// of where the reference was set, every weight is below 1/32 and a lane's sum
+// of 16 weights stays at or below SUM_LIMIT. A larger sum (or NaN) means the
+// reference fell too far behind for that block, possibly with clamped
+// weights: only then is the block's exact max computed, O and l rescaled and
+// the block redone. Weights more than 126 - MARGIN binades below a row's max
+// underflow to zero; they are below 2^-62 of the largest weight.
+constexpr float MARGIN = 64.0f;
+constexpr float SUM_LIMIT = 0.5f;
 
 struct AttnParams {
   const void* q; const void* k; const void* vt; void* a;
@@ -168,9 +178,13 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
   const WorkItem item = decode_item(p, blk);   // causal: heaviest query tiles first
   const int qt = item.qt, sub = item.sub, h = item.h, b = item.b;
   const int waves_per_head = WAVES / p.G;
-  const int head = h * p.g + sub * p.G + wave / waves_per_head;
+  // Waves w and w+4 of an 8-wave workgroup share a SIMD. The second four take
+  // the (head, row block) slots in reverse order, so each SIMD pairs a low
+  // row block with a high one and carries the same causal work.
+  const int slot = (WAVES == 8 && wave >= 4) ? 11 - wave : wave;
+  const int head = h * p.g + sub * p.G + slot / waves_per_head;
   const int q0 = qt * p.q_per_wg;
-  const int qw = q0 + (wave % waves_per_head) * QW;   // first query row of this wave
+  const int qw = q0 + (slot % waves_per_head) * QW;   // first query row of this wave
   // Tokens of this sequence: N, or its own length in a padded batch. Its keys
   // end there, and its rows from there on are zero.
   const int L = p.lens ? min(max(p.lens[b], 0), p.N) : p.N;
@@ -214,10 +228,12 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
       qf[qb][s] = *reinterpret_cast<const Frag*>(
           Qh + (int64_t)min(qw + 32 * qb + col, p.Np - 1) * D + s * MF::KS + grp * MF::E);
 
-  // All waves of the workgroup walk the same key range; rows past a wave's own
-  // causal horizon are masked to zero weight.
+  // The workgroup stages the keys of its last query; this wave computes the
+  // blocks up to its own last query (nblk_w) and only keeps pace with the
+  // tile ring for the rest.
   const int kv_len = p.causal ? min(L, q0 + p.q_per_wg) : L;
   const int nblk = (kv_len + 31) / 32;
+  const int nblk_w = p.causal ? (min(kv_len, qw + QW) + 31) / 32 : nblk;
   const int n_tiles = (kv_len + KT - 1) / KT;
 
   // Direct global->LDS loads of tile t into ring slot t % NBUF. Lane L of a
@@ -270,7 +286,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
     for (int nb = 0; nb < D / 32; ++nb) o[qb][nb] = f32x16{};
   float m_ref[QB], l_run[QB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) { m_ref[qb] = M_INIT; l_run[qb] = 0.f; }
+  for (int qb = 0; qb < QB; ++qb) l_run[qb] = 0.f;
   const float c = p.c;
 
   // S^T of block j for both query blocks. Register r of lane group grp holds
@@ -322,6 +338,12 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
     }
   };
 
+  // The weight of score s against reference m: exp2(s*c - m) clamped to [0, 1]
+  // (the median folds into the clamp bit of v_exp_f32).
+  auto expw = [&](float sv, float m) {
+    return __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(fmaf(sv, c, -m)), 0.0f, 1.0f);
+  };
+
   // p = exp2(s*c - m_ref) in place, packed as PV consumes it, and each lane's
   // block sums (taken on the rounded bf16 values that PV multiplies).
   auto exponentiate = [&](f32x16 (&s)[QB], float (&bsum)[QB]) {
@@ -329,7 +351,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
     for (int qb = 0; qb < QB; ++qb) {
       const float mb = m_ref[qb];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[qb][r] = __builtin_amdgcn_exp2f(fmaf(s[qb][r], c, -mb));
+      for (int r = 0; r < 16; ++r) s[qb][r] = expw(s[qb][r], mb);
       if constexpr (sizeof(T) == 2) {
         typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
         typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -368,39 +390,76 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
     }
   };
 
-  // The exact-rescale fallback of block j's softmax, used only when a block
-  // sum showed that m_ref was too low for it. Block j's keys are still in
-  // the LDS ring, so its scores are recomputed rather than kept.
-  auto rescale = [&](int j, f32x16 (&s)[QB], float (&bsum)[QB], bool masked) {
-    qk(j, s);
-    if (masked) mask(s, j);
+  // Each row's max over the scores s of one block (-inf if all are masked).
+  auto block_max = [&](const f32x16 (&s)[QB], float (&m)[QB]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float m = max3(s[qb][0], s[qb][1], s[qb][2]);
+      float v = max3(s[qb][0], s[qb][1], s[qb][2]);
 #pragma unroll
-      for (int r = 3; r < 15; r += 2) m = max3(m, s[qb][r], s[qb][r + 1]);
-      m = fmaxf(m, s[qb][15]);
-      m = fmaxf(m, __shfl_xor(m, 32));
-      const float m_new = fmaxf(m_ref[qb], m * c);
+      for (int r = 3; r < 15; r += 2) v = max3(v, s[qb][r], s[qb][r + 1]);
+      v = fmaxf(v, s[qb][15]);
+      m[qb] = fmaxf(v, __shfl_xor(v, 32));
+    }
+  };
+
+  // Raise each row's reference to MARGIN binades above the max of the scores
+  // s (never lower it), rescaling O and l by the change.
+  auto rebase = [&](const f32x16 (&s)[QB]) {
+    float m[QB];
+    block_max(s, m);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float m_new = fmaxf(m_ref[qb], fmaf(m[qb], c, MARGIN));
       const float alpha = __builtin_amdgcn_exp2f(m_ref[qb] - m_new);
       l_run[qb] *= alpha;
 #pragma unroll
       for (int nb = 0; nb < D / 32; ++nb) o[qb][nb] *= alpha;
       m_ref[qb] = m_new;
     }
+  };
+
+  // The exact fallback of block j's softmax, used only when its sums showed
+  // that m_ref fell too far behind for it (before its PV product). Block j's
+  // keys are still in the LDS ring, so its scores are recomputed, not kept.
+  auto rescale = [&](int j, f32x16 (&s)[QB], float (&bsum)[QB], bool masked) {
+    qk(j, s);
+    if (masked) mask(s, j);
+    rebase(s);
     exponentiate(s, bsum);
   };
 
-  // One pipeline step for block j. s_cur holds S(j); s_next holds P(j-1).
-  // The MFMAs of O += V^T P(j-1), then of S(j+1) = K Q^T (into s_next, once
-  // PV has read it), are independent of block j's softmax. The step is laid
-  // out as one group per MFMA, each carrying the VALU work of one pair of
-  // scores (the exponentials of the next pair and the bf16 packing and row
-  // sum of the current one) and, every other group, the LDS fragment read for
-  // the MFMA four groups ahead. sched_barrier keeps this order, so the MFMA
-  // pipe and the VALU stay busy together and the register set stays what the
-  // layout implies. S(j+1) of the last block and P(-1) = 0 are padding that
-  // keeps each step straight-line.
+  // The negated weights -P of scores s (bf16 path), packed as PV consumes
+  // them: the sign flip happens before the rounding to bf16, which rounds
+  // symmetrically, so they are exactly -P. (Flipping the sign bits of the
+  // packed pairs afterwards, an xor on the f32 vector slots, was miscompiled:
+  // the slots came out as copies of the first pair.)
+  auto neg_weights = [&](f32x16 (&s)[QB]) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float packed[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const bf16x2 pr = __builtin_convertvector(
+            f32x2{-expw(s[qb][2 * e], m_ref[qb]), -expw(s[qb][2 * e + 1], m_ref[qb])}, bf16x2);
+        packed[e] = __builtin_bit_cast(float, pr);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s[qb][e] = packed[e];
+    }
+  };
+
+  // One pipeline step for block j (bf16). s_cur holds S(j); s_next holds
+  // P(j-1). The MFMAs of O += V^T P(j-1), then of S(j+1) = K Q^T (into
+  // s_next, once PV has read it), are independent of block j's softmax. The
+  // step is laid out as one group per MFMA, each carrying the VALU work of one
+  // pair of scores (the exponentials of the next pair and the bf16 packing and
+  // row sum of the current one) and, every other group, the LDS fragment read
+  // for the MFMA four groups ahead. sched_barrier keeps this order, so the
+  // MFMA pipe and the VALU stay busy together and the register set stays what
+  // the layout implies. S(j+1) of the last block and P(-1) = 0 are padding
+  // that keeps each step straight-line.
   auto step_interleaved = [&](int j, f32x16 (&sc)[QB], f32x16 (&sn)[QB], float (&bsum)[QB]) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -427,8 +486,8 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
     float x[2 * PPG];   // exponentials of the pairs packed in the next group
     auto expo = [&](int pr, float* dst) {   // pair pr: scores 2e, 2e+1 of query block qb
       const int qb = pr / 8, e = pr % 8;
-      dst[0] = __builtin_amdgcn_exp2f(fmaf(sc[qb][2 * e], c, -m_ref[qb]));
-      dst[1] = __builtin_amdgcn_exp2f(fmaf(sc[qb][2 * e + 1], c, -m_ref[qb]));
+      dst[0] = expw(sc[qb][2 * e], m_ref[qb]);
+      dst[1] = expw(sc[qb][2 * e + 1], m_ref[qb]);
     };
 #pragma unroll
     for (int u = 0; u < FETCH_AHEAD * QB; u += QB) fetch(u);
@@ -457,32 +516,84 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
     }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) bsum[qb] = acc[qb][0] + acc[qb][1];
+    // Block j's weights and sums are dead on the rare path after this step
+    // (it recomputes them), so the compiler would sink their computation
+    // below that branch, out of the interleaved groups. This empty statement
+    // reads and redefines them here, which keeps the exponentials beside the
+    // MFMAs they were laid out with. (The row-sum dot2s still collect at the
+    // end of the step; keeping them in their groups as well measured 4%
+    // slower: each would wait on the bf16 pack just before it.)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) asm volatile("" : "+v"(sc[qb]), "+v"(bsum[qb]));
   };
 
   // Masking touches only S(j), so it stays a small branch in front of the one
   // copy of the step body (two copies of the body would double its register
-  // footprint at their merge).
-  auto run_step = [&](int j, f32x16 (&s_cur)[QB], f32x16 (&s_next)[QB], auto mask_on) {
+  // footprint at their merge). bsum carries the lane sums of the last block
+  // whose check is still to come: in bf16, block j-1 on entry and block j on
+  // exit (fp32 checks each block within its own step and leaves bsum at 0).
+  // bf16 checks block j-1's sums at the end of step j, one step after they
+  // were formed, so the branch never waits for them. If the check fails
+  // (rarely: a row's max grew by more than about MARGIN - 5 binades), block
+  // j-1's PV product is already in O: its clamped weights are recomputed
+  // (the same scores against the same reference give the same values) and
+  // that product is taken back out of O; then block j-1 is redone against its
+  // exact max, and block j, exponentiated against the old reference, is
+  // redone from its scores. s_cur serves as scratch; s_next keeps S(j+1).
+  auto run_step = [&](int j, f32x16 (&s_cur)[QB], f32x16 (&s_next)[QB], auto mask_on,
+                      float (&bsum)[QB]) {
     const bool masked =
         decltype(mask_on)::value && (j * 32 + 32 > L || (p.causal && j * 32 + 31 > qw));
     if (masked) mask(s_cur, j);
-    float bsum[QB];
+    float bcur[QB];
     if constexpr (sizeof(T) == 2) {
-      step_interleaved(j, s_cur, s_next, bsum);
+      step_interleaved(j, s_cur, s_next, bcur);
+      bool redo = false;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) redo |= !(bsum[qb] <= SUM_LIMIT);
+      if (__builtin_expect(__any(redo), 0)) {   // j >= 1: block -1's sums are 0
+        qk(j - 1, s_cur);
+        if (decltype(mask_on)::value) mask(s_cur, j - 1);
+        neg_weights(s_cur);
+        pv(j - 1, s_cur);   // O -= V^T P^T
+        rescale(j - 1, s_cur, bsum, decltype(mask_on)::value);
+        pv(j - 1, s_cur);
+        qk(j, s_cur);
+        if (masked) mask(s_cur, j);
+        exponentiate(s_cur, bcur);
+      }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) { l_run[qb] += bsum[qb]; bsum[qb] = bcur[qb]; }
     } else {
       pv(j > 0 ? j - 1 : 0, s_next);
       qk(j + 1, s_next);
-      exponentiate(s_cur, bsum);
+      exponentiate(s_cur, bcur);
+      bool redo = false;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) redo |= !(bcur[qb] <= SUM_LIMIT);
+      if (__builtin_expect(__any(redo), 0)) rescale(j, s_cur, bcur, masked);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) l_run[qb] += bcur[qb];
     }
-    bool redo = false;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) redo |= !(bsum[qb] <= SUM_LIMIT);
-    if (__any(redo)) rescale(j, s_cur, bsum, masked);
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) l_run[qb] += bsum[qb];
   };
 
-  // Prologue: tiles 0..NBUF-2 in flight, tile 0 visible, S of block 0.
+  // After a wave's last step, block j (in s_cur): its pending check (bf16),
+  // then its PV product.
+  auto finish = [&](int j, f32x16 (&s_cur)[QB], float (&bsum)[QB]) {
+    if constexpr (sizeof(T) == 2) {
+      bool redo = false;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) redo |= !(bsum[qb] <= SUM_LIMIT);
+      if (__builtin_expect(__any(redo), 0)) rescale(j, s_cur, bsum, true);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) l_run[qb] += bsum[qb];
+    }
+    pv(j, s_cur);
+  };
+
+  // Prologue: tiles 0..NBUF-2 in flight, tile 0 visible, S of block 0, and
+  // each row's reference MARGIN binades above its max over block 0 (key 0 is
+  // visible to every row, so that max is finite).
 #pragma unroll
   for (int t = 0; t < NBUF - 1; ++t) issue(t);
   wait_vmcnt<0>();
@@ -492,6 +603,16 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) sB[qb] = f32x16{};   // P(-1) = 0
   qk(0, sA);
+  if (32 > L || (p.causal && 31 > qw)) mask(sA, 0);
+  {
+    float m0[QB];
+    block_max(sA, m0);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) m_ref[qb] = fmaf(m0[qb], c, MARGIN);
+  }
+  float bsum[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) bsum[qb] = 0.f;
   // Before odd block 2t+1: tile t+1 must be visible (loads of tiles t+2.. may
   // still be in flight), and tile t-1 is no longer read, so its slot takes
   // tile t+NBUF-1.
@@ -504,22 +625,30 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
   // Blocks before jc (even) need no mask for this wave: their keys precede its
   // first query (causal) and the sequence end. That loop is compiled without
   // the mask code; the second keeps it. Every wave passes the barriers at the
-  // same blocks, whichever loop it is in.
+  // same blocks, whichever loop it is in, and steps only up to nblk_w
+  // (jc <= nblk_w). A wave's last block is finished right after its step: the
+  // next advance() but one recycles that block's tile.
   const int jc = min(nblk, min(L / 32, p.causal ? qw / 32 : nblk)) & ~1;
   int j = 0;
   for (; j < jc; j += 2) {
-    run_step(j, sA, sB, std::false_type{});
+    run_step(j, sA, sB, std::false_type{}, bsum);
     advance(j);   // j + 1 < jc <= nblk
-    run_step(j + 1, sB, sA, std::false_type{});
+    run_step(j + 1, sB, sA, std::false_type{}, bsum);
   }
   for (; j < nblk; j += 2) {
-    run_step(j, sA, sB, std::true_type{});
+    if (j < nblk_w) {
+      run_step(j, sA, sB, std::true_type{}, bsum);
+      if (j + 1 == nblk_w) finish(j, sA, bsum);
+    }
     if (j + 1 < nblk) {
       advance(j);
-      run_step(j + 1, sB, sA, std::true_type{});
+      if (j + 1 < nblk_w) {
+        run_step(j + 1, sB, sA, std::true_type{}, bsum);
+        if (j + 2 == nblk_w) finish(j + 1, sB, bsum);
+      }
     }
   }
-  if (nblk & 1) pv(nblk - 1, sA); else pv(nblk - 1, sB);
+  if (jc == nblk_w) finish(nblk_w - 1, sB, bsum);   // every block in the first loop (nblk_w even)
 
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
