@@ -87,6 +87,36 @@ sqa_status sqa_forward(const void* x, const void* Wq, const void* Wk, const void
                        int64_t H, int64_t H_q, int64_t H_kv, int64_t d_head, int causal,
                        sqa_dtype dtype, hipStream_t stream);
 
+/* Size of the fixed device array that sqa_forward_noalloc takes its workspace from. */
+#define SQA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+/*
+ * sqa_forward_noalloc - sqa_forward for callers that cannot allocate device
+ * memory: code under HIP graph capture, serving loops and harnesses that
+ * forbid allocation. Arguments, result and errors are those of sqa_forward,
+ * and the result is bitwise the same (the same kernels run).
+ *
+ * The call allocates and frees nothing. Its workspace (Q, K, V^T, A and the
+ * transposed weights, each rounded up to 256 bytes; see sqa_forward) comes
+ * from one fixed device array of SQA_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every device it runs on until the process ends. The first call on
+ * a device looks the array's device address up (hipGetSymbolAddress with that
+ * device current). A call whose workspace exceeds the array returns
+ * SQA_ERR_UNSUPPORTED and enqueues nothing; with the headline head shape
+ * (d_model 1024, H_q 8, H_kv 4, d_head 64, bf16) the limit is about 42k
+ * tokens (B*N).
+ *
+ * The array keeps what the last call left in it; nothing in it needs to start
+ * at zero (every region is written before it is read). Calls on one device
+ * share the array: calls that may overlap in time on that device (different
+ * streams without ordering between them) race and give wrong results. Calls
+ * ordered on one stream are safe.
+ */
+sqa_status sqa_forward_noalloc(const void* x, const void* Wq, const void* Wk, const void* Wv,
+                               const void* Wo, void* out, int64_t B, int64_t N, int64_t d_model,
+                               int64_t H, int64_t H_q, int64_t H_kv, int64_t d_head, int causal,
+                               sqa_dtype dtype, hipStream_t stream);
+
 /*
  * sqa_forward_varlen - sqa_forward over a batch of sequences of different
  * lengths, padded to a common N, as a training batch cut at a maximum sequence

@@ -20,7 +20,8 @@ from typing import Optional, Tuple
 from . import _lib
 from ._lib import SQAError
 
-__all__ = ["forward_varlen", "forward_train", "backward", "prefill", "decode_step", "forward", "qkv_projection", "attention", "output_projection", "padded_length",
+__all__ = ["forward_varlen", "forward_train", "backward", "prefill", "decode_step", "forward",
+           "forward_noalloc", "qkv_projection", "attention", "output_projection", "padded_length",
            "SQAError", "library_path"]
 
 library_path = _lib.LIB_PATH
@@ -81,6 +82,28 @@ def forward(x, Wq, Wk, Wv, Wo, *, H: int, H_q: int, H_kv: int, causal: bool = Fa
     _lib.check(lib.sqa_forward(x.data_ptr(), Wq.data_ptr(), Wk.data_ptr(), Wv.data_ptr(),
                                Wo.data_ptr(), out.data_ptr(), B, N, D, H, H_q, H_kv, d,
                                int(bool(causal)), _dtype_code(x), _stream(x.device)))
+    return out
+
+
+def forward_noalloc(x, Wq, Wk, Wv, Wo, *, H: int, H_q: int, H_kv: int, causal: bool = False,
+                    out):
+    """forward() through sqa_forward_noalloc: the library allocates nothing and
+    takes its workspace from its fixed device array (SQA_NOALLOC_SCRATCH_BYTES,
+    128 MiB); `out` must be given. Calls that may overlap in time on one device
+    share that array and race."""
+    lib = _lib.load()
+    if x.dim() != 3:
+        raise ValueError("x must be [B, N, d_model]")
+    B, N, D = x.shape
+    if H <= 0 or D % H:
+        raise ValueError("d_model must be a multiple of H")
+    d = D // H
+    for name, t, shp in (("x", x, (B, N, D)), ("Wq", Wq, (D, H_q * d)), ("Wk", Wk, (D, H_kv * d)),
+                         ("Wv", Wv, (D, H_kv * d)), ("Wo", Wo, (H_q * d, D)), ("out", out, (B, N, D))):
+        _check_tensor(name, t, shp, x.dtype, x.device)
+    _lib.check(lib.sqa_forward_noalloc(x.data_ptr(), Wq.data_ptr(), Wk.data_ptr(), Wv.data_ptr(),
+                                       Wo.data_ptr(), out.data_ptr(), B, N, D, H, H_q, H_kv, d,
+                                       int(bool(causal)), _dtype_code(x), _stream(x.device)))
     return out
 
 

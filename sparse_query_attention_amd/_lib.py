@@ -15,6 +15,7 @@ SQA_DTYPE_FP32, SQA_DTYPE_BF16 = 0, 1
 _i64, _vp, _int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
 SIGNATURES = {
     "sqa_forward": (_int, [_vp] * 6 + [_i64] * 7 + [_int, _int, _vp]),
+    "sqa_forward_noalloc": (_int, [_vp] * 6 + [_i64] * 7 + [_int, _int, _vp]),
     "sqa_forward_varlen": (_int, [_vp] * 7 + [_i64] * 7 + [_int, _int, _vp]),
     "sqa_prefill": (_int, [_vp] * 8 + [_i64] * 8 + [_int, _vp]),
     "sqa_decode_step": (_int, [_vp] * 9 + [_i64] * 7 + [_int, _vp]),

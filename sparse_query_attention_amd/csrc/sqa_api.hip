@@ -1,6 +1,7 @@
 // C ABI of libsqa (declared in include/sqa.h): argument validation on the
-// host, the stream-ordered workspace of sqa_forward, and dispatch to the three
-// gfx950 kernels (projection, attention core, output projection).
+// host, the stream-ordered workspace of sqa_forward (or the fixed device array
+// of sqa_forward_noalloc), and dispatch to the three gfx950 kernels
+// (projection, attention core, output projection).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -108,9 +109,45 @@ sqa_status sizes_for(const Shape& s, sqa_dtype dt, Sizes* out) {
 
 int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
 
+constexpr int kMaxDevices = 64;
+
+// The workspace of sqa_forward_noalloc: a fixed device array that every device
+// the library runs on holds from the module's load until the process ends.
+// Host code never passes its name to a kernel or a copy (in host code the name
+// stands for a host-side shadow, not the device array): the device address is
+// looked up once per device with hipGetSymbolAddress and kept in
+// g_scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[SQA_NOALLOC_SCRATCH_BYTES];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the device of `stream`, looked up on the
+// first call for that device with that device current.
+sqa_status noalloc_scratch(hipStream_t stream, void** out) {
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e, "device of stream");
+  if (dev < 0 || dev >= kMaxDevices) return fail(SQA_ERR_UNSUPPORTED, "device index too large");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return fail_hip(e, "hipSetDevice");
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    const hipError_t er = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return fail_hip(e, "hipGetSymbolAddress(scratch)");
+    if (er != hipSuccess) return fail_hip(er, "hipSetDevice");
+    if (!ptr) return fail(SQA_ERR_HIP, "hipGetSymbolAddress(scratch) returned null");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SQA_OK;
+}
+
 // One stream-ordered pool per device. Freed workspace stays in the pool for
 // reuse (release threshold = max) instead of going back to the driver.
-constexpr int kMaxDevices = 64;
 std::mutex g_pool_mu;
 hipMemPool_t g_pools[kMaxDevices] = {};
 
@@ -178,14 +215,16 @@ sqa_status check_saved(const void* saved, size_t saved_bytes, const Shape& s, sq
 }
 
 // sqa_forward (varlen false, lens unused), sqa_forward_varlen, sqa_prefill
-// (kc, vc non-null: the caches [B, H_kv, N_max, d_head] receive K and V) and
+// (kc, vc non-null: the caches [B, H_kv, N_max, d_head] receive K and V),
 // sqa_forward_train (saved non-null: the activations stay there, with each
-// row's log-sum-exp, instead of in the workspace).
+// row's log-sum-exp, instead of in the workspace) and sqa_forward_noalloc
+// (no_alloc: the workspace is the fixed device array `scratch`).
 sqa_status forward_impl(const void* x, const void* Wq, const void* Wk, const void* Wv,
                         const void* Wo, void* out, bool varlen, const int32_t* lens, void* kc,
                         void* vc, int64_t N_max, int64_t B, int64_t N, int64_t d_model, int64_t H,
                         int64_t H_q, int64_t H_kv, int64_t d_head, int causal, sqa_dtype dtype,
-                        hipStream_t stream, void* saved = nullptr, size_t saved_bytes = 0) {
+                        hipStream_t stream, void* saved = nullptr, size_t saved_bytes = 0,
+                        bool no_alloc = false) {
   const Shape s{B, N, d_model, H, H_q, H_kv, d_head};
   SQA_TRY(check_dtype(dtype));
   SQA_TRY(check_heads(s, true));
@@ -240,11 +279,22 @@ sqa_status forward_impl(const void* x, const void* Wq, const void* Wk, const voi
   const int64_t off_w3 = off_w1 + round256((int64_t)sqa::qkv_wt_bytes(dtype, d_model, H_q, H_kv, d_head));
   const int64_t off_ord = off_w3 + round256((int64_t)sqa::out_wt_bytes(dtype, H_q * d_head, d_model));
   const int64_t total = off_ord + (lens ? round256((int64_t)sqa::attention_order_bytes(B, N, H_q)) : 0);
-  hipMemPool_t pool;
-  SQA_TRY(pool_for(stream, &pool));
   void* ws = nullptr;
-  hipError_t e = hipMallocFromPoolAsync(&ws, (size_t)total, pool, stream);
-  if (e != hipSuccess) return fail_hip(e, "workspace allocation");
+  hipError_t e = hipSuccess;
+  if (no_alloc) {
+    if ((uint64_t)total > (uint64_t)SQA_NOALLOC_SCRATCH_BYTES) {
+      snprintf(g_err, sizeof(g_err),
+               "the workspace of %lld bytes exceeds SQA_NOALLOC_SCRATCH_BYTES (%llu)",
+               (long long)total, (unsigned long long)SQA_NOALLOC_SCRATCH_BYTES);
+      return SQA_ERR_UNSUPPORTED;
+    }
+    SQA_TRY(noalloc_scratch(stream, &ws));
+  } else {
+    hipMemPool_t pool;
+    SQA_TRY(pool_for(stream, &pool));
+    e = hipMallocFromPoolAsync(&ws, (size_t)total, pool, stream);
+    if (e != hipSuccess) return fail_hip(e, "workspace allocation");
+  }
   char* base = (char*)ws;
   void *q = base, *k = base + off_k, *vt = base + off_v, *a = base + off_a;
   void *w1 = base + off_w1, *w3 = base + off_w3;
@@ -269,7 +319,7 @@ sqa_status forward_impl(const void* x, const void* Wq, const void* Wk, const voi
   if (e == hipSuccess)
     e = sqa::launch_output_projection(dtype, a, Wo, w3, out, B * N, H_q * d_head, d_model, lens, N,
                                       stream);
-  const hipError_t ef = hipFreeAsync(ws, stream);
+  const hipError_t ef = no_alloc ? hipSuccess : hipFreeAsync(ws, stream);
   if (e != hipSuccess) return fail_hip(e, "kernel launch");
   if (ef != hipSuccess) return fail_hip(ef, "workspace release");
   return ok();
@@ -450,6 +500,14 @@ sqa_status sqa_forward(const void* x, const void* Wq, const void* Wk, const void
                        sqa_dtype dtype, hipStream_t stream) {
   return forward_impl(x, Wq, Wk, Wv, Wo, out, false, nullptr, nullptr, nullptr, 0, B, N, d_model, H, H_q, H_kv, d_head, causal,
                       dtype, stream);
+}
+
+sqa_status sqa_forward_noalloc(const void* x, const void* Wq, const void* Wk, const void* Wv,
+                               const void* Wo, void* out, int64_t B, int64_t N, int64_t d_model,
+                               int64_t H, int64_t H_q, int64_t H_kv, int64_t d_head, int causal,
+                               sqa_dtype dtype, hipStream_t stream) {
+  return forward_impl(x, Wq, Wk, Wv, Wo, out, false, nullptr, nullptr, nullptr, 0, B, N, d_model,
+                      H, H_q, H_kv, d_head, causal, dtype, stream, nullptr, 0, true);
 }
 
 sqa_status sqa_forward_varlen(const void* x, const void* Wq, const void* Wk, const void* Wv,

@@ -84,6 +84,37 @@ def test_empty_problem_is_a_no_op():
     assert _fwd(N=0)[0] == _lib.SQA_OK
 
 
+def _fwd_noalloc(**kw):
+    a = dict(x=FAKE, Wq=FAKE + (1 << 40), Wk=FAKE + (2 << 40), Wv=FAKE + (3 << 40),
+             Wo=FAKE + (4 << 40), out=FAKE + (5 << 40), B=1, N=256, d_model=1024, H=16, H_q=8,
+             H_kv=4, d_head=64, causal=1, dtype=_lib.SQA_DTYPE_BF16)
+    a.update(kw)
+    lib = _lib.load()
+    st = lib.sqa_forward_noalloc(a["x"], a["Wq"], a["Wk"], a["Wv"], a["Wo"], a["out"], a["B"],
+                                 a["N"], a["d_model"], a["H"], a["H_q"], a["H_kv"], a["d_head"],
+                                 a["causal"], a["dtype"], None)
+    return st, lib.sqa_last_error_message().decode()
+
+
+@pytest.mark.parametrize("kw,status,words", [
+    # the 16/8/4-head bf16 shape needs about 3 KB of workspace per token: 65536
+    # tokens exceed the 128 MiB array, rejected on the host before any HIP call
+    (dict(N=65536), _lib.SQA_ERR_UNSUPPORTED, "SQA_NOALLOC_SCRATCH_BYTES"),
+    (dict(B=4, N=16384), _lib.SQA_ERR_UNSUPPORTED, "SQA_NOALLOC_SCRATCH_BYTES"),
+    (dict(x=0), _lib.SQA_ERR_INVALID_ARG, "x is null"),
+    (dict(out=FAKE), _lib.SQA_ERR_INVALID_ARG, "overlaps"),
+    (dict(H_kv=3), _lib.SQA_ERR_INVALID_ARG, "multiple of H_kv"),
+])
+def test_forward_noalloc_rejects_on_the_host(kw, status, words):
+    st, msg = _fwd_noalloc(**kw)
+    assert st == status, msg
+    assert words in msg
+
+
+def test_forward_noalloc_empty_problem_is_a_no_op():
+    assert _fwd_noalloc(B=0, x=0, out=0)[0] == _lib.SQA_OK
+
+
 def test_stage_entry_points_validate():
     lib = _lib.load()
     st = lib.sqa_attention(FAKE, FAKE + 0x100000, FAKE + 0x200000, 0, 1, 10, 4, 2, 64, 0,
