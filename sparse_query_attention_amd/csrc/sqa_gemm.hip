@@ -10,8 +10,12 @@
 // Design:
 //  * W is first transposed to W^T [Ncols, K] (a few MB, once per call), so both
 //    MFMA operands are k-contiguous rows.
-//  * A 256-thread workgroup owns a 128x128 tile of C. Each of its four waves
-//    owns 64x64, i.e. 2x2 v_mfma_f32_32x32x16 tiles.
+//  * Two tilings. The bf16 forward projections run 512-thread workgroups that
+//    own a 256x256 tile of C, eight waves of 128x64 (4x2 v_mfma_f32_32x32x16
+//    tiles): six 16-byte LDS fragment reads feed eight MFMAs, and each
+//    workgroup runs long enough that its pipeline fill and epilogue are small.
+//    Every other product (fp32, the backward pass) runs 256-thread workgroups
+//    on 128x128 tiles, four waves of 64x64 (2x2 MFMA tiles).
 //  * K advances in steps of 32 through a 4-stage LDS ring filled by direct
 //    global->LDS loads (global_load_lds_dwordx4), three stages ahead, with one
 //    barrier per step. Each load lands lane-contiguously, so 16-byte chunks are
@@ -35,20 +39,30 @@
 namespace sqa {
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 32, THREADS = 256, WAVES = 4;
-constexpr int WN = BN / 64, NBJ = BN / 32;   // waves along N; 32-column blocks per tile
-static_assert(BM / 64 * WN == WAVES, "each wave owns a 64x64 sub-tile");
-constexpr int NST = 4;   // LDS ring stages
+constexpr int BK = 32;
 constexpr int XCDS = 8;
 
-template <typename T> struct GemmCfg {
+// A workgroup tiling: a BM x BN tile of C, WM x WN waves each owning
+// 32*MI x 32*NJ (MI x NJ MFMA tiles of 32x32), an NST-stage LDS ring.
+template <int BM_, int BN_, int WM_, int WN_, int NST_> struct Tiling {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NST = NST_;
+  static constexpr int WAVES = WM * WN, THREADS = 64 * WAVES;
+  static constexpr int MI = BM / WM / 32, NJ = BN / WN / 32;
+  static constexpr int NBI = BM / 32, NBJ = BN / 32;   // 32x32 blocks per tile
+  static_assert(MI * 32 * WM == BM && NJ * 32 * WN == BN, "wave tiles");
+};
+using SmallTiles = Tiling<128, 128, 2, 2, 4>;   // 4 waves of 64x64
+using LargeTiles = Tiling<256, 256, 2, 4, 4>;   // 8 waves of 128x64 (bf16 only: 128 KB of LDS)
+
+template <typename T, class TL> struct GemmCfg {
   static constexpr int EPC = 16 / sizeof(T);          // elements per 16-byte chunk
   static constexpr int CPR = BK / EPC;                 // chunks per tile row (4 bf16, 8 fp32)
-  static constexpr int A_ELEMS = BM * BK, B_ELEMS = BN * BK, STAGE = A_ELEMS + B_ELEMS;
-  static constexpr int A_INS = A_ELEMS / (64 * EPC) / WAVES;   // 1 KB loads per wave
-  static constexpr int B_INS = B_ELEMS / (64 * EPC) / WAVES;
-  static constexpr int VM = A_INS + B_INS;                     // loads per wave per stage
-  static_assert(A_INS * WAVES * 64 * EPC == A_ELEMS && B_INS * WAVES * 64 * EPC == B_ELEMS, "split");
+  static constexpr int A_ELEMS = TL::BM * BK, B_ELEMS = TL::BN * BK, STAGE = A_ELEMS + B_ELEMS;
+  static constexpr int A_INS = A_ELEMS / (64 * EPC) / TL::WAVES;   // 1 KB loads per wave
+  static constexpr int B_INS = B_ELEMS / (64 * EPC) / TL::WAVES;
+  static constexpr int VM = A_INS + B_INS;                          // loads per wave per stage
+  static_assert(A_INS * TL::WAVES * 64 * EPC == A_ELEMS && B_INS * TL::WAVES * 64 * EPC == B_ELEMS,
+                "split");
 };
 
 // Rows of X for step 1: output row gr = b*Np + t is X row b*N + t when t < N
@@ -78,8 +92,8 @@ template <typename T> struct DenseRows {
 //  * row_chunk(r, n, c): C[r][n .. n+E-1]; col_chunk(r, n, c): C[r .. r+E-1][n],
 //    with E = 16 / sizeof(T).
 
-// Step 1: column n goes to q, k or vt, row to (b, t). A 128-row tile lies in
-// one batch (Np is a multiple of 256). V^T blocks are column-major so that
+// Step 1: column n goes to q, k or vt, row to (b, t). A tile of 128 or 256
+// rows lies in one batch (Np is a multiple of 256). V^T blocks are column-major so that
 // their chunks are runs of t, contiguous in vt.
 template <typename T> struct QkvStore {
   static constexpr bool kDirect = false;
@@ -122,6 +136,7 @@ template <typename T> struct DenseStore {
   static constexpr bool kDirect = false;
   T* out; int64_t M; int ncols;
   const int32_t* lens; int64_t seq_n;
+  int bm;   // rows per tile
   __device__ bool col_major(int) const { return false; }
   struct Tile {
     T* out; int64_t rows_left; int ncols; bool pad;   // rows from m0 on
@@ -137,7 +152,7 @@ template <typename T> struct DenseStore {
     if (lens) {
       const int64_t b = m0 / seq_n, t0 = m0 - b * seq_n;
       const int64_t L = min(max((int64_t)lens[b], (int64_t)0), seq_n);
-      pad = t0 >= L && t0 + BM <= seq_n;   // the whole tile is padding of sequence b
+      pad = t0 >= L && t0 + bm <= seq_n;   // the whole tile is padding of sequence b
     }
     return Tile{out + m0 * ncols, M - m0, ncols, pad};
   }
@@ -184,13 +199,15 @@ struct F32PartStore {
 // C = A * W with W given transposed (wt [ncols, K]); see the file header.
 // Workgroup row blockIdx.y sums k in [y*k_split, min(K, (y+1)*k_split)), a
 // multiple of BK (split-K; k_split = K otherwise).
-template <typename T, class Rows, class Store>
-__global__ __launch_bounds__(THREADS) void gemm_kernel(Rows rows, const T* wt, int ncols,
-                                                       Store store, int K, int n_rb, int n_ct,
-                                                       int k_split) {
-  using C = GemmCfg<T>;
+template <typename T, class TL, class Rows, class Store>
+__global__ __launch_bounds__(TL::THREADS) void gemm_kernel(Rows rows, const T* wt, int ncols,
+                                                           Store store, int K, int n_rb, int n_ct,
+                                                           int k_split) {
+  using C = GemmCfg<T, TL>;
   using MF = Mfma<T>;
   using Frag = typename MF::Frag;
+  constexpr int BM = TL::BM, BN = TL::BN, NST = TL::NST, MI = TL::MI, NJ = TL::NJ;
+  constexpr int NBJ = TL::NBJ, THREADS = TL::THREADS;
   __shared__ __align__(16) T smem[NST * C::STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63,
@@ -241,21 +258,21 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Rows rows, const T* wt, i
         &part[r * BK + (((e / C::EPC) ^ swz<C::CPR>(r)) * C::EPC) + e % C::EPC]);
   };
 
-  const int wm = wave / WN, wn = wave % WN;
-  f32x16 acc[2][2];
+  const int wm = wave / TL::WN, wn = wave % TL::WN;
+  f32x16 acc[MI][NJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
 
-  // Fragments of stage kt, k-step s, for this wave's 2x2 MFMA tiles.
+  // Fragments of stage kt, k-step s, for this wave's MI x NJ MFMA tiles.
   constexpr int SUB = BK / MF::KS;
-  auto read = [&](int kt, int s, Frag (&a)[2], Frag (&b)[2]) {
+  auto read = [&](int kt, int s, Frag (&a)[MI], Frag (&b)[NJ]) {
     const T* st = smem + (kt % NST) * C::STAGE;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) a[i] = frag(st, wm * 64 + i * 32 + col, s);
+    for (int i = 0; i < MI; ++i) a[i] = frag(st, wm * MI * 32 + i * 32 + col, s);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) b[j] = frag(st + C::A_ELEMS, wn * 64 + j * 32 + col, s);
+    for (int j = 0; j < NJ; ++j) b[j] = frag(st + C::A_ELEMS, wn * NJ * 32 + j * 32 + col, s);
   };
 
   // The MFMA operand order fixes which way the accumulator's runs of four go:
@@ -273,12 +290,12 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Rows rows, const T* wt, i
     for (int s = 0; s < NST; ++s) issue(s);
     wait_vmcnt_tiles<C::VM, NST - 1>(min(NST - 1, nk - 1));
     __syncthreads();
-    Frag ca[2], cb[2];
+    Frag ca[MI], cb[NJ];
     read(0, 0, ca, cb);
     for (int kt = 0; kt < nk; ++kt) {
 #pragma unroll
       for (int s = 0; s < SUB; ++s) {
-        Frag na[2], nb[2];
+        Frag na[MI], nb[NJ];
         if (s + 1 < SUB) {
           read(kt, s + 1, na, nb);
         } else if (kt + 1 < nk) {
@@ -291,12 +308,14 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Rows rows, const T* wt, i
           read(kt + 1, 0, na, nb);
         }
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
+          for (int j = 0; j < NJ; ++j)
             acc[i][j] = TR ? MF::run(cb[j], ca[i], acc[i][j]) : MF::run(ca[i], cb[j], acc[i][j]);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) { ca[i] = na[i]; cb[i] = nb[i]; }
+        for (int i = 0; i < MI; ++i) ca[i] = na[i];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) cb[j] = nb[j];
       }
     }
   };
@@ -304,14 +323,14 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Rows rows, const T* wt, i
     // register r of this lane: row 8*(r/4) + 4*grp + r%4, column col
     main_loop(std::false_type{});
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int n = n0 + wn * 64 + j * 32 + col;
+      for (int j = 0; j < NJ; ++j) {
+        const int n = n0 + wn * NJ * 32 + j * 32 + col;
         if (n >= ncols) continue;
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          store.put(m0 + wm * 64 + i * 32 + 8 * (r / 4) + 4 * grp + r % 4, n, acc[i][j][r]);
+          store.put(m0 + wm * MI * 32 + i * 32 + 8 * (r / 4) + 4 * grp + r % 4, n, acc[i][j][r]);
       }
     return;
   }
@@ -324,77 +343,86 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Rows rows, const T* wt, i
     main_loop(std::false_type{});
   }
 
-  // Epilogue through LDS (the ring is free once every wave has passed this
-  // barrier). Block (bi, bj) is the 32x32 sub-tile at rows 32*bi, columns
-  // 32*bj; each is staged row- or column-major as the store asks, in lines of
-  // 32 elements with a 16-byte pad against bank conflicts. Then all threads
-  // write 16-byte chunks, four (bf16) or eight (fp32) per line.
+  // Epilogue through LDS (the ring is free once every wave has passed the
+  // first barrier). Block (bi, bj) is the 32x32 sub-tile at rows 32*bi,
+  // columns 32*bj; each is staged row- or column-major as the store asks, in
+  // lines of 32 elements with a 16-byte pad against bank conflicts. Then all
+  // threads write 16-byte chunks, four (bf16) or eight (fp32) per line. When
+  // the whole tile does not fit the ring, it goes out in WM passes of one wave
+  // row each.
   constexpr int LINE = 32 * (int)sizeof(T) + 16;   // bytes per staged line
   constexpr int BLOCK = 32 * LINE;
   constexpr int EPC = 16 / (int)sizeof(T);
-  static_assert(16 * BLOCK <= NST * C::STAGE * (int)sizeof(T), "epilogue fits the ring");
+  constexpr int PASSES = TL::NBI * NBJ * BLOCK <= NST * C::STAGE * (int)sizeof(T) ? 1 : TL::WM;
+  constexpr int BI_PASS = TL::NBI / PASSES;          // block rows staged per pass
+  static_assert(BI_PASS * NBJ * BLOCK <= NST * C::STAGE * (int)sizeof(T), "epilogue fits the ring");
   char* ep = reinterpret_cast<char*>(smem);
-  __syncthreads();
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int pass = 0; pass < PASSES; ++pass) {
+    __syncthreads();
+    if (PASSES == 1 || wm == pass) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int bi = wm * 2 + i, bj = wn * 2 + j;
-      char* blk = ep + (bi * NBJ + bj) * BLOCK;
-      if (rows_all) {
-        // transposed: register r holds row col, column 8*(r/4) + 4*grp + r%4
-        const bool z = tile.zero_row(32 * bi + col);
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          float v[4];
+        for (int j = 0; j < NJ; ++j) {
+          const int bi = wm * MI + i, bj = wn * NJ + j;
+          char* blk = ep + ((bi - pass * BI_PASS) * NBJ + bj) * BLOCK;
+          if (rows_all) {
+            // transposed: register r holds row col, column 8*(r/4) + 4*grp + r%4
+            const bool z = tile.zero_row(32 * bi + col);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = z ? 0.f : acc[i][j][4 * rq + e];
-          T* dst = reinterpret_cast<T*>(blk + col * LINE) + 8 * rq + 4 * grp;
-          if constexpr (sizeof(T) == 2) {
-            *reinterpret_cast<bf16x4*>(dst) =
-                bf16x4{from_f32<T>(v[0]), from_f32<T>(v[1]), from_f32<T>(v[2]), from_f32<T>(v[3])};
+            for (int rq = 0; rq < 4; ++rq) {
+              float v[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] = z ? 0.f : acc[i][j][4 * rq + e];
+              T* dst = reinterpret_cast<T*>(blk + col * LINE) + 8 * rq + 4 * grp;
+              if constexpr (sizeof(T) == 2) {
+                *reinterpret_cast<bf16x4*>(dst) =
+                    bf16x4{from_f32<T>(v[0]), from_f32<T>(v[1]), from_f32<T>(v[2]), from_f32<T>(v[3])};
+              } else {
+                *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+              }
+            }
+          } else if (store.col_major(n0 + 32 * bj)) {
+            // register r of this lane: row 8*(r/4) + 4*grp + r%4, column col
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+              const int r0 = 8 * rq + 4 * grp;
+              float v[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                v[e] = tile.zero_row(32 * bi + r0 + e) ? 0.f : acc[i][j][4 * rq + e];
+              T* dst = reinterpret_cast<T*>(blk + col * LINE) + r0;
+              if constexpr (sizeof(T) == 2) {
+                *reinterpret_cast<bf16x4*>(dst) =
+                    bf16x4{from_f32<T>(v[0]), from_f32<T>(v[1]), from_f32<T>(v[2]), from_f32<T>(v[3])};
+              } else {
+                *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+              }
+            }
           } else {
-            *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int row = 8 * (r / 4) + 4 * grp + r % 4;
+              const bool z = tile.zero_row(32 * bi + row);
+              reinterpret_cast<T*>(blk + row * LINE)[col] = from_f32<T>(z ? 0.f : acc[i][j][r]);
+            }
           }
         }
-      } else if (store.col_major(n0 + 32 * bj)) {
-        // register r of this lane: row 8*(r/4) + 4*grp + r%4, column col
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          const int r0 = 8 * rq + 4 * grp;
-          float v[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            v[e] = tile.zero_row(32 * bi + r0 + e) ? 0.f : acc[i][j][4 * rq + e];
-          T* dst = reinterpret_cast<T*>(blk + col * LINE) + r0;
-          if constexpr (sizeof(T) == 2) {
-            *reinterpret_cast<bf16x4*>(dst) =
-                bf16x4{from_f32<T>(v[0]), from_f32<T>(v[1]), from_f32<T>(v[2]), from_f32<T>(v[3])};
-          } else {
-            *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
-          }
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = 8 * (r / 4) + 4 * grp + r % 4;
-          const bool z = tile.zero_row(32 * bi + row);
-          reinterpret_cast<T*>(blk + row * LINE)[col] = from_f32<T>(z ? 0.f : acc[i][j][r]);
-        }
-      }
     }
-  __syncthreads();
-  constexpr int CPL = 32 / EPC;                  // chunks per line
-  constexpr int CHUNKS = 16 * 32 * CPL;
+    __syncthreads();
+    constexpr int CPL = 32 / EPC;                  // chunks per line
+    constexpr int CHUNKS = BI_PASS * NBJ * 32 * CPL;
 #pragma unroll
-  for (int cidx = tid; cidx < CHUNKS; cidx += THREADS) {
-    const int blkid = cidx / (32 * CPL), line = (cidx / CPL) % 32, qc = cidx % CPL;
-    const int bi = blkid / NBJ, bj = blkid % NBJ;
-    const int n_b = n0 + 32 * bj;
-    if (n_b >= ncols) continue;
-    const Chunk c = *reinterpret_cast<const Chunk*>(ep + blkid * BLOCK + line * LINE + qc * 16);
-    if (store.col_major(n_b)) tile.col_chunk(32 * bi + qc * EPC, n_b + line, c);
-    else tile.row_chunk(32 * bi + line, n_b + qc * EPC, c);
+    for (int cidx = tid; cidx < CHUNKS; cidx += THREADS) {
+      const int blkid = cidx / (32 * CPL), line = (cidx / CPL) % 32, qc = cidx % CPL;
+      const int bi = pass * BI_PASS + blkid / NBJ, bj = blkid % NBJ;
+      const int n_b = n0 + 32 * bj;
+      if (n_b >= ncols) continue;
+      const Chunk c = *reinterpret_cast<const Chunk*>(ep + blkid * BLOCK + line * LINE + qc * 16);
+      if (store.col_major(n_b)) tile.col_chunk(32 * bi + qc * EPC, n_b + line, c);
+      else tile.row_chunk(32 * bi + line, n_b + qc * EPC, c);
+    }
   }
 }
 
@@ -439,14 +467,20 @@ hipError_t transpose(const T* w0, int w0n, const T* w1, int w1n, const T* w2, in
   return hipGetLastError();
 }
 
+// The tiling of a forward projection: large tiles for bf16 (their 128 KB ring
+// would not fit the LDS with fp32 operands), the 128x128 tiling otherwise.
+template <typename T>
+using ProjTiles = typename std::conditional<sizeof(T) == 2, LargeTiles, SmallTiles>::type;
+
 template <typename T>
 hipError_t qkv_impl(const void* x, const void* wq, const void* wk, const void* wv, void* wt,
                     void* q, void* k, void* vt, int64_t B, int64_t N, int64_t Np, int64_t d_model,
                     int64_t H_q, int64_t H_kv, int64_t d, const int32_t* lens,
                     hipStream_t stream) {
+  using TL = ProjTiles<T>;
   const int wq_w = (int)(H_q * d), wkv_w = (int)(H_kv * d);
   const int ncols = wq_w + 2 * wkv_w;
-  const int64_t n_rb = B * Np / BM, n_ct = (ncols + BN - 1) / BN;
+  const int64_t n_rb = B * Np / TL::BM, n_ct = (ncols + TL::BN - 1) / TL::BN;
   if (!grid_ok(n_rb, n_ct)) return hipErrorInvalidConfiguration;
   hipError_t e = transpose<T>((const T*)wq, wq_w, (const T*)wk, wkv_w, (const T*)wv, wkv_w, (T*)wt,
                               (int)d_model, stream);
@@ -454,7 +488,7 @@ hipError_t qkv_impl(const void* x, const void* wq, const void* wk, const void* w
   PaddedRows<T> rows{(const T*)x, N, Np, (int)d_model};
   const int dsh = d == 64 ? 6 : 5;   // d_head is 32 or 64 (checked by the caller)
   QkvStore<T> st{(T*)q, (T*)k, (T*)vt, N, Np, (int)H_q, (int)H_kv, dsh, wq_w, wkv_w, lens};
-  gemm_kernel<T><<<(unsigned)grid_size(n_rb, n_ct), THREADS, 0, stream>>>(
+  gemm_kernel<T, TL><<<(unsigned)grid_size(n_rb, n_ct), TL::THREADS, 0, stream>>>(
       rows, (const T*)wt, ncols, st, (int)d_model, (int)n_rb, (int)n_ct, (int)d_model);
   return hipGetLastError();
 }
@@ -462,14 +496,15 @@ hipError_t qkv_impl(const void* x, const void* wq, const void* wk, const void* w
 template <typename T>
 hipError_t out_impl(const void* a, const void* wo, void* wt, void* out, int64_t M, int64_t K,
                     int64_t d_model, const int32_t* lens, int64_t seq_n, hipStream_t stream) {
-  const int64_t n_rb = (M + BM - 1) / BM, n_ct = (d_model + BN - 1) / BN;
+  using TL = ProjTiles<T>;
+  const int64_t n_rb = (M + TL::BM - 1) / TL::BM, n_ct = (d_model + TL::BN - 1) / TL::BN;
   if (!grid_ok(n_rb, n_ct)) return hipErrorInvalidConfiguration;
   hipError_t e = transpose<T>((const T*)wo, (int)d_model, nullptr, 0, nullptr, 0, (T*)wt, (int)K,
                               stream);
   if (e != hipSuccess) return e;
   DenseRows<T> rows{(const T*)a, M, (int)K};
-  DenseStore<T> st{(T*)out, M, (int)d_model, lens, seq_n};
-  gemm_kernel<T><<<(unsigned)grid_size(n_rb, n_ct), THREADS, 0, stream>>>(
+  DenseStore<T> st{(T*)out, M, (int)d_model, lens, seq_n, TL::BM};
+  gemm_kernel<T, TL><<<(unsigned)grid_size(n_rb, n_ct), TL::THREADS, 0, stream>>>(
       rows, (const T*)wt, (int)d_model, st, (int)K, (int)n_rb, (int)n_ct, (int)K);
   return hipGetLastError();
 }
@@ -478,12 +513,13 @@ hipError_t out_impl(const void* a, const void* wo, void* wt, void* out, int64_t 
 template <typename T>
 hipError_t heads_impl(const void* x, const void* wt, void* out, int64_t B, int64_t N, int64_t Np,
                       int64_t K, int64_t ncols, int64_t d, hipStream_t stream) {
-  const int64_t n_rb = B * Np / BM, n_ct = (ncols + BN - 1) / BN;
+  using TL = SmallTiles;
+  const int64_t n_rb = B * Np / TL::BM, n_ct = (ncols + TL::BN - 1) / TL::BN;
   if (!grid_ok(n_rb, n_ct)) return hipErrorInvalidConfiguration;
   PaddedRows<T> rows{(const T*)x, N, Np, (int)K};
   const int dsh = d == 64 ? 6 : 5;
   QkvStore<T> st{(T*)out, nullptr, nullptr, N, Np, (int)(ncols / d), 0, dsh, (int)ncols, 0, nullptr};
-  gemm_kernel<T><<<(unsigned)grid_size(n_rb, n_ct), THREADS, 0, stream>>>(
+  gemm_kernel<T, TL><<<(unsigned)grid_size(n_rb, n_ct), TL::THREADS, 0, stream>>>(
       rows, (const T*)wt, (int)ncols, st, (int)K, (int)n_rb, (int)n_ct, (int)K);
   return hipGetLastError();
 }
@@ -492,11 +528,12 @@ hipError_t heads_impl(const void* x, const void* wt, void* out, int64_t B, int64
 template <typename T>
 hipError_t unpad_impl(const void* a, const void* wt, void* out, int64_t B, int64_t N, int64_t Np,
                       int64_t K, int64_t ncols, hipStream_t stream) {
-  const int64_t n_rb = B * Np / BM, n_ct = (ncols + BN - 1) / BN;
+  using TL = SmallTiles;
+  const int64_t n_rb = B * Np / TL::BM, n_ct = (ncols + TL::BN - 1) / TL::BN;
   if (!grid_ok(n_rb, n_ct)) return hipErrorInvalidConfiguration;
   DenseRows<T> rows{(const T*)a, B * Np, (int)K};
   UnpadStore<T> st{(T*)out, N, Np, (int)ncols};
-  gemm_kernel<T><<<(unsigned)grid_size(n_rb, n_ct), THREADS, 0, stream>>>(
+  gemm_kernel<T, TL><<<(unsigned)grid_size(n_rb, n_ct), TL::THREADS, 0, stream>>>(
       rows, (const T*)wt, (int)ncols, st, (int)K, (int)n_rb, (int)n_ct, (int)K);
   return hipGetLastError();
 }
@@ -504,19 +541,22 @@ hipError_t unpad_impl(const void* a, const void* wt, void* out, int64_t B, int64
 template <typename T>
 hipError_t splitk_impl(const void* a, const void* wt, float* part, int64_t M, int64_t K,
                        int64_t ncols, int64_t k_split, int64_t n_split, hipStream_t stream) {
-  const int64_t n_rb = (M + BM - 1) / BM, n_ct = (ncols + BN - 1) / BN;
+  using TL = SmallTiles;
+  const int64_t n_rb = (M + TL::BM - 1) / TL::BM, n_ct = (ncols + TL::BN - 1) / TL::BN;
   if (!grid_ok(n_rb, n_ct) || n_split > 65535) return hipErrorInvalidConfiguration;
   DenseRows<T> rows{(const T*)a, M, (int)K};
   F32PartStore st{part, M, (int)ncols};
-  gemm_kernel<T><<<dim3((unsigned)grid_size(n_rb, n_ct), (unsigned)n_split), THREADS, 0, stream>>>(
-      rows, (const T*)wt, (int)ncols, st, (int)K, (int)n_rb, (int)n_ct, (int)k_split);
+  gemm_kernel<T, TL><<<dim3((unsigned)grid_size(n_rb, n_ct), (unsigned)n_split), TL::THREADS, 0,
+                       stream>>>(rows, (const T*)wt, (int)ncols, st, (int)K, (int)n_rb, (int)n_ct,
+                                 (int)k_split);
   return hipGetLastError();
 }
 
 }  // namespace
 
 SplitK splitk_plan(int64_t M, int64_t K, int64_t ncols) {
-  const int64_t tiles = grid_size((M + BM - 1) / BM, (ncols + BN - 1) / BN);
+  const int64_t tiles = grid_size((M + SmallTiles::BM - 1) / SmallTiles::BM,
+                                  (ncols + SmallTiles::BN - 1) / SmallTiles::BN);
   const int64_t steps = K / BK;
   // about 1024 workgroups, each with at least 32 k-steps
   int64_t n = std::max<int64_t>(1, std::min<int64_t>((1024 + tiles - 1) / tiles, steps / 32));
