@@ -413,8 +413,10 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_kernel(Rows rows, const T* w
     __syncthreads();
     constexpr int CPL = 32 / EPC;                  // chunks per line
     constexpr int CHUNKS = BI_PASS * NBJ * 32 * CPL;
+    static_assert(CHUNKS % THREADS == 0, "whole chunk rounds");
 #pragma unroll
-    for (int cidx = tid; cidx < CHUNKS; cidx += THREADS) {
+    for (int it = 0; it < CHUNKS / THREADS; ++it) {
+      const int cidx = it * THREADS + tid;
       const int blkid = cidx / (32 * CPL), line = (cidx / CPL) % 32, qc = cidx % CPL;
       const int bi = pass * BI_PASS + blkid / NBJ, bj = blkid % NBJ;
       const int n_b = n0 + 32 * bj;
