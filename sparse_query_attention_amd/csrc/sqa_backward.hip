@@ -40,6 +40,14 @@
 namespace sqa {
 namespace {
 
+// f(std::integral_constant<int, i>) for i = I .. N-1, in order.
+template <int I, int N, typename F> __device__ inline void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
 __device__ inline float f32_of(float x) { return x; }
 __device__ inline float f32_of(bf16 x) { return (float)x; }
 
@@ -104,8 +112,12 @@ __global__ __launch_bounds__(256) void concat_weights(const T* wq, const T* wk, 
 // (fp32). The rounded A would put a relative 2^-9 error into D, and
 // dS = P (dP - D) keeps it even where dP - D cancels (short sequences). It is
 // stored negated because the dK/dV kernel starts its dP accumulation from it.
+// nlse[b, i, t] = -lse / c (lse the base-2 log-sum-exp of the scaled scores,
+// c = log2(e) / sqrt(d)), -inf on padding rows: the dK/dV kernel starts its
+// S accumulation from it, so that a probability is exp2(c * acc).
 template <typename T, int D>
-__global__ __launch_bounds__(256) void dvec_kernel(const T* dO, const float* a, float* dvec, int N,
+__global__ __launch_bounds__(256) void dvec_kernel(const T* dO, const float* a, const float* lse,
+                                                   float c, float* dvec, float* nlse, int N,
                                                    int64_t Np, int H_q, int64_t rows) {
   const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (x >= rows) return;
@@ -115,9 +127,10 @@ __global__ __launch_bounds__(256) void dvec_kernel(const T* dO, const float* a, 
     const T* o = dO + x * D;
     const float* av = a + ((b * N + t) * H_q + i) * D;
 #pragma unroll 8
-    for (int c = 0; c < D; ++c) s = fmaf(f32_of(o[c]), f32_of(av[c]), s);
+    for (int k = 0; k < D; ++k) s = fmaf(f32_of(o[k]), f32_of(av[k]), s);
   }
   dvec[x] = -s;
+  nlse[x] = t < N ? -lse[x] / c : -INFINITY;
 }
 
 // out segments [M, w0 | w1 | w2] = sum over the n_split partials, rounded once.
@@ -148,6 +161,7 @@ struct BwdParams {
   const void* dO;    // [B, H_q, Np, d]
   const void* dOt;   // [B, H_q, d, Np], tokens in swap23 order
   const float* lse;  // [B, H_q, Np], base 2, of the scaled scores
+  const float* nlse; // [B, H_q, Np]: -lse / c
   const float* dvec; // [B, H_q, Np]: -D per row
   void* dqkv;        // [B, Np, W]: dQ heads, then dK heads, then dV heads
   int N, Np, H_q, H_kv, g, causal, W;
@@ -225,7 +239,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
   constexpr int RC = D / EPC, LC = BT / EPC;   // chunks per row [64][D], per line [D][64]
   constexpr int NS = D / MF::KS;               // k-steps over the head dims
   constexpr int TE = BT * D;                   // elements of one operand tile
-  constexpr int SE = 2 * BT * 4 / (int)sizeof(T);   // elements holding the rows' lse and D (fp32)
+  constexpr int SE = 2 * BT * 4 / (int)sizeof(T);   // elements holding the rows' -lse/c and -D (fp32)
   constexpr int TILE = 4 * TE + SE;            // Q, dO, Q^T, dO^T, row statistics
   constexpr int NBUF = 4 * TE * (int)sizeof(T) <= 32768 ? 4 : 2;   // ring slots (LDS <= 130 KB)
   constexpr int INS = TE * (int)sizeof(T) / 1024;                 // 1 KB loads per operand tile
@@ -248,8 +262,8 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
   const int qt_end = (p.N + BT - 1) / BT;
   // Items: phase 0 is key tile kt0, phase 1 (causal, kt1 != kt0) key tile kt1.
   // Causal key tile kt sees the query tiles from the one holding its first
-  // key. Every row of the tiles walked has its lse and D written: +inf and 0
-  // past N.
+  // key. Every row of the tiles walked has its -lse/c and -D written: -inf
+  // and 0 past N.
   const int first0 = p.causal ? kt0 * (KPG / BT) : 0;
   const int first1 = kt1 * (KPG / BT);
   const int n0 = max(0, qt_end - first0) * p.g;
@@ -286,23 +300,30 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
     }
   }
   const T* arr_base = (const T*)(arr == 0 ? p.q : arr == 1 ? p.dO : arr == 2 ? p.qt : p.dOt);
-  const int which = wave >> 2, part = wave & 3;   // row statistics: lse (waves 0-3), D (4-7)
+  const int which = wave >> 2, part = wave & 3;   // row statistics: -lse/c (waves 0-3), -D (4-7)
   auto issue = [&](int w) {
     if (w >= n_work) return;
     const int i = j * p.g + item_head(w), q0 = item_tile(w) * BT;
     const int64_t hq = (int64_t)b * p.H_q + i;
     T* tb = smem + (w % NBUF) * TILE + arr * TE;
     const T* base = arr_base + (arr < 2 ? (hq * p.Np + q0) * D : hq * D * p.Np + q0);
+    // Buffer loads: unlike global_load_lds, they count only in vmcnt, so the
+    // compiler's waits for the LDS fragment reads in flight stay exact
+    // (with a global_load_lds in flight it waits for every LDS read). The
+    // byte offsets stay below 2^32: the host checks D * Np * sizeof(T).
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)base, (short)0, (int)(arr < 2 ? TE * (uint32_t)sizeof(T) : (uint32_t)(D - 1) * (uint32_t)p.Np * (uint32_t)sizeof(T) + BT * (uint32_t)sizeof(T)),
+        0x00020000);
 #pragma unroll
     for (int x = 0; x < IPW; ++x) {
       const int li = (wave * IPW + x) % INS;
-      __builtin_amdgcn_global_load_lds((const void*)((const char*)base + loff[x]),
-                                       (lds_ptr)(tb + li * 64 * EPC), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(tb + li * 64 * EPC), 16, (int)loff[x], 0, 0, 0);
     }
     // row statistics: 16 values per wave
-    const float* src = (which ? p.dvec : p.lse) + hq * p.Np + q0 + part * 16 + (lane & 15);
+    const float* src = (which ? p.dvec : p.nlse) + hq * p.Np + q0 + part * 16;
+    const __amdgpu_buffer_rsrc_t rss = __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, 64, 0x00020000);
     float* dst = reinterpret_cast<float*>(smem + (w % NBUF) * TILE + 4 * TE) + which * BT + part * 16;
-    if (lane < 16) __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)dst, 4, 0, 0);
+    if (lane < 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(rss, (lds_ptr)dst, 4, lane * 4, 0, 0, 0);
   };
 
   // This wave's K and V fragments (B operands of S = Q K^T and dP = dO V^T)
@@ -344,47 +365,60 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
       }
   };
 
+  // Ring bookkeeping. Tiles [0, next_issue) have been issued; tile x lives in
+  // slot x % NBUF. sync(R, F) waits until this wave's loads of the tiles up to
+  // R have landed, then passes a barrier (every wave's loads of those tiles
+  // are visible, and every wave is done with the tiles before F), then issues
+  // the tiles whose slots that frees, up to F + NBUF - 1.
+  int next_issue = 0;
+  auto sync = [&](int R, int F) {
+    wait_vmcnt_tiles<VM_PER_TILE, NBUF - 2>(min(NBUF - 2, max(0, next_issue - 1 - R)));
+    ring_barrier();
+    const int last = min(F + NBUF - 1, n_work - 1);
+    for (; next_issue <= last; ++next_issue) issue(next_issue);
+  };
+  auto slot = [&](int x) { return (const T*)smem + (x % NBUF) * TILE; };
+
   // Prologue: work items 0..NBUF-2 in flight, then the K and V fragments of
   // the first key tile, all landed before the loop, which then waits only on
   // its own loads.
   int kw = kt0 * KPG + KPW * wave;   // this wave's first key
-  // Waves w and w+4 share a SIMD, and the barrier after each item starts them
-  // in the same phase (S/dP MFMAs, then softmax VALU, then dV/dK MFMAs).
-  // Issue priority for the lower half lets one run ahead into the phase the
-  // other is not in (1.2 % on the 131072-token causal shape).
-  if (wave < 4) __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-  for (int t = 0; t < NBUF - 1; ++t) issue(t);
+  for (; next_issue < min(NBUF - 1, n_work); ++next_issue) issue(next_issue);
   load_kv(kw);
 #pragma unroll
   for (int nb = 0; nb < D / 32; ++nb) { dk[nb] = f32x16{}; dv[nb] = f32x16{}; }
   wait_vmcnt<0>();
   __syncthreads();
 
-  // Items [w0, w1). Query tiles that see every key of the key tile (all of
-  // them after its last key, and the keys before N) need no mask; the loop
-  // over them is compiled without the mask code and the few others run in a
-  // copy that keeps it (separate loops, as in bwd_dq).
+  // The accumulators of S and dP - D for the 32 query rows at rb of a tile
+  // start from the rows' -lse/c and -D (register r: row rb + 8*(r/4) + 4*grp
+  // + r%4). The probability is then exp2(c * S) and dS = P (dP - D) one
+  // product, with no per-score subtraction.
+  auto init_scores = [&](const T* t, int rb, f32x16& sc, f32x16& dpc) {
+    const float* st = reinterpret_cast<const float*>(t + 4 * TE);
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const f32x4 n4 = *reinterpret_cast<const f32x4*>(&st[rb + 8 * r4 + 4 * grp]);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&st[BT + rb + 8 * r4 + 4 * grp]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { sc[4 * r4 + e] = n4[e]; dpc[4 * r4 + e] = d4[e]; }
+    }
+  };
+
+  // Items [w0, w1), one at a time, each of its 32-query blocks through
+  // scores, softmax gradient and the dV/dK products. Used for the items that
+  // need a mask, and in fp32 for all.
   auto run_items = [&](int w0, int w1, auto mask_on) {
     constexpr bool MASK = decltype(mask_on)::value;
     for (int w = w0; w < w1; ++w) {
-      if (w > 0) {
-        // item w visible (items w+1.. may still be in flight), and every wave
-        // is done with slot (w-1) % NBUF, which takes item w+NBUF-1
-        wait_vmcnt_tiles<VM_PER_TILE, NBUF - 2>(min(NBUF - 2, max(0, n_work - 1 - w)));
-        ring_barrier();
-      }
-      issue(w + NBUF - 1);
-      const T* Qs = smem + (w % NBUF) * TILE;
+      // item w visible; every wave done with the items before it
+      sync(w, w);
+      const T* Qs = slot(w);
       const T* Os = Qs + TE;
       const T* QTs = Qs + 2 * TE;
       const T* OTs = Qs + 3 * TE;
-      const float* lse_s = reinterpret_cast<const float*>(Qs + 4 * TE);
-      const float* dv_s = lse_s + BT;
       const int q0 = item_tile(w) * BT;
-      // S = Q K^T and dP - D = dO V^T - D of 32-query block qs (lane = key):
-      // the accumulator of dP starts from the rows' -D (register r: query
-      // 8*(r/4) + 4*grp + r%4 of the block), which saves a subtraction per score.
+      // S and dP - D of 32-query block qs (lane = key)
       auto scores = [&](int qs, f32x16& sc, f32x16& dpc) {
         Frag qa[NS], oa[NS];
 #pragma unroll
@@ -392,13 +426,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
           qa[st] = row_frag<T, D>(Qs, 32 * qs + col, st, grp);
           oa[st] = row_frag<T, D>(Os, 32 * qs + col, st, grp);
         }
-        sc = f32x16{};
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dv_s[32 * qs + 8 * r4 + 4 * grp]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) dpc[4 * r4 + e] = d4[e];
-        }
+        init_scores(Qs, 32 * qs, sc, dpc);
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
           sc = MF::run(qa[st], kf[st], sc);
@@ -406,23 +434,17 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
         }
       };
       // P and dS in place (register r: query qb + 8*(r/4) + 4*grp + r%4; column:
-      // key kw + col), then dV^T += dO^T P and dK^T += Q^T dS. The rows'
-      // log-sum-exp values are read four rows at a time, just before their use.
+      // key kw + col), then dV^T += dO^T P and dK^T += Q^T dS.
       auto grads = [&](int qs, f32x16& sc, f32x16& dpc) {
         const int qb = q0 + 32 * qs;
+        const int key = kw + col;
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int rl = 32 * qs + 8 * r4 + 4 * grp;
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse_s[rl]);
-          const int key = kw + col;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * r4 + e, q = qb + 8 * r4 + 4 * grp + e;
-            float pv = __builtin_amdgcn_exp2f(fmaf(sc[r], p.c, -l4[e]));
-            if (MASK) pv = key >= p.N || (p.causal && key > q) ? 0.f : pv;
-            sc[r] = pv;                        // P
-            dpc[r] = pv * dpc[r];              // dS = P (dP - D)
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int q = qb + 8 * (r / 4) + 4 * grp + r % 4;
+          float pv = __builtin_amdgcn_exp2f(sc[r] * p.c);
+          if (MASK) pv = key >= p.N || (p.causal && key > q) ? 0.f : pv;
+          sc[r] = pv;                        // P
+          dpc[r] = pv * dpc[r];              // dS = P (dP - D)
         }
 #pragma unroll
         for (int h = 0; h < kHalves<T>; ++h)
@@ -433,9 +455,6 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
           }
       };
       if constexpr (!MASK) {
-        // Both blocks' scores first: the second block's MFMAs run while the
-        // first block's softmax takes the VALU, and its gradient MFMAs while
-        // the second block's softmax does.
         f32x16 s0, dp0, s1, dp1;
         scores(0, s0, dp0);
         scores(1, s1, dp1);
@@ -454,6 +473,137 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
       }
     }
   };
+
+  // bf16 items [w0, w1) that need no mask, as a software pipeline over the
+  // 32-query blocks (two per item). A block passes three stages: its scores S
+  // and dP - D (MFMA), the softmax gradient P and dS (VALU, packed to bf16),
+  // and the products dV^T += dO^T P, dK^T += Q^T dS (MFMA). Iteration w runs
+  // two phases of 2*NS + 4*D/32 MFMAs each:
+  //   phase 0: dV/dK of block 1 of item w-1, scores of block 1 of item w;
+  //            softmax gradient of block 0 of item w
+  //   phase 1: dV/dK of block 0 of item w, scores of block 0 of item w+1;
+  //            softmax gradient of block 1 of item w
+  // so each phase's VALU work is independent of its MFMAs. Each MFMA forms a
+  // group with an equal share of the phase's VALU work and the LDS read of
+  // the fragment FA groups ahead; sched_barrier keeps the groups in order.
+  // An iteration reads the tiles of items w-1, w and w+1, so the ring keeps
+  // one item in flight beyond them.
+  auto run_clear = [&](int w0, int w1) {
+    if constexpr (sizeof(T) != 2) {
+      run_items(w0, w1, std::false_type{});
+      return;
+    } else {
+    if (w0 >= w1) return;
+    constexpr int NB = D / 32;
+    constexpr int NGG = 4 * NB;      // dV/dK MFMAs of a block
+    constexpr int NGS = 2 * NS;      // S/dP MFMAs of a block
+    constexpr int NGP = NGG + NGS;   // MFMAs (groups) of a phase
+    constexpr int SPG = 16 / NGP;    // scores per group
+    constexpr int FA = 3;            // fragment reads ahead
+    static_assert(SPG * NGP == 16 && FA <= NGG, "groups");
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    f32x16 sA, dA, sB, dB;           // S and dP - D of block 0 (A) and block 1 (B)
+    u32x4 pA[2][2], pB[2][2];        // [P, dS][half]: bf16 pairs, B operands
+    Frag fr[2 * NGP];                // the fragment of each MFMA of an iteration
+    // The fragment of MFMA u of the iteration over the tiles of items w-1
+    // (prev), w (cur) and w+1 (next).
+    auto fetch = [&](auto uc, const T* prev, const T* cur, const T* next) {
+      constexpr int u = decltype(uc)::value, ph = u / NGP, k = u % NGP;
+      if constexpr (k < NGG) {
+        constexpr int h = k / (2 * NB), nb = (k / 2) % NB, which = k % 2;   // 0: dV (dO^T), 1: dK (Q^T)
+        fr[u] = line_frag<T>((ph == 0 ? prev : cur) + (which ? 2 : 3) * TE, nb * 32 + col, ph == 0 ? 32 : 0, h, grp);
+      } else {
+        constexpr int st = (k - NGG) / 2, which = (k - NGG) % 2;             // 0: S (Q), 1: dP (dO)
+        fr[u] = row_frag<T, D>((ph == 0 ? cur : next) + which * TE, (ph == 0 ? 32 : 0) + col, st, grp);
+      }
+    };
+    // dV/dK MFMA k (< NGG) of a block with packed P and dS pk
+    auto grad_mfma = [&](auto kc, const Frag& a, const u32x4 (&pk)[2][2]) {
+      constexpr int k = decltype(kc)::value, h = k / (2 * NB), nb = (k / 2) % NB, which = k % 2;
+      const Frag b = __builtin_bit_cast(Frag, pk[which][h]);
+      if constexpr (which == 0) dv[nb] = MF::run(a, b, dv[nb]);
+      else dk[nb] = MF::run(a, b, dk[nb]);
+    };
+    float ex[16], ds[16];
+    auto group = [&](auto uc, const T* prev, const T* cur, const T* next) {
+      constexpr int u = decltype(uc)::value, ph = u / NGP, k = u % NGP;
+      f32x16& s_sc = ph == 0 ? sB : sA;   // scored in this phase
+      f32x16& d_sc = ph == 0 ? dB : dA;
+      const f32x16& s_sm = ph == 0 ? sA : sB;   // softmax gradient in this phase
+      const f32x16& d_sm = ph == 0 ? dA : dB;
+      u32x4 (&p_sm)[2][2] = ph == 0 ? pA : pB;
+      // the fragment FA groups ahead; past the iteration's end, the first
+      // groups of the next one (dV/dK of block 1 of item w: tile cur)
+      if constexpr (u + FA < 2 * NGP) fetch(std::integral_constant<int, u + FA>{}, prev, cur, next);
+      else fetch(std::integral_constant<int, u + FA - 2 * NGP>{}, cur, cur, cur);
+      if constexpr (k == NGG - FA) {   // accumulators of the block scored next, before its first MFMA
+        if constexpr (ph == 0) init_scores(cur, 32, sB, dB);
+        else init_scores(next, 0, sA, dA);
+      }
+      if constexpr (k < NGG) {
+        grad_mfma(std::integral_constant<int, k>{}, fr[u], ph == 0 ? pB : pA);
+      } else {
+        constexpr int st = (k - NGG) / 2, which = (k - NGG) % 2;
+        if constexpr (which == 0) s_sc = MF::run(fr[u], kf[st], s_sc);
+        else d_sc = MF::run(fr[u], vf[st], d_sc);
+      }
+      // softmax gradient of scores [k*SPG, (k+1)*SPG); exponentials one group ahead
+      if constexpr (k == 0) {
+#pragma unroll
+        for (int q = 0; q < SPG; ++q) ex[q] = __builtin_amdgcn_exp2f(s_sm[q] * p.c);
+      }
+#pragma unroll
+      for (int q = 0; q < SPG; ++q) {
+        const int r = k * SPG + q;
+        if (k + 1 < NGP) ex[r + SPG] = __builtin_amdgcn_exp2f(s_sm[r + SPG] * p.c);
+        ds[r] = ex[r] * d_sm[r];
+        if (r % 2 == 1) {
+          p_sm[0][r / 8][(r % 8) / 2] = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{ex[r - 1], ex[r]}, bf16x2));
+          p_sm[1][r / 8][(r % 8) / 2] = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{ds[r - 1], ds[r]}, bf16x2));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Prologue: tile w0 visible; scores of its block 0. Block "1 of item
+    // w0-1" is zeros, so the first phase's dV/dK MFMAs add exact zeros
+    // (reading tile w0's finite operands).
+    sync(w0, w0);
+    {
+      const T* t0 = slot(w0);
+      init_scores(t0, 0, sA, dA);
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        sA = MF::run(row_frag<T, D>(t0, col, st, grp), kf[st], sA);
+        dA = MF::run(row_frag<T, D>(t0 + TE, col, st, grp), vf[st], dA);
+      }
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) pB[a][h] = u32x4{0u, 0u, 0u, 0u};
+      static_for<0, FA>([&](auto uc) { fetch(uc, t0, t0, t0); });
+    }
+    for (int w = w0; w < w1; ++w) {
+      // items w and w+1 visible; every wave done with the items before w-1
+      sync(w + 1, w - 1);
+      const T* cur = slot(w);
+      const T* prev = w == w0 ? cur : slot(w - 1);
+      const T* next = slot(w + 1);   // past the loop's end: scores computed and dropped
+      static_for<0, 2 * NGP>([&](auto uc) { group(uc, prev, cur, next); });
+    }
+    // Epilogue: dV/dK of block 1 of the last item (its first FA fragments
+    // were read in the last iteration).
+    const T* lt = slot(w1 - 1);
+    static_for<0, NGG>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      if constexpr (k >= FA) fetch(kc, lt, lt, lt);
+      grad_mfma(kc, fr[k], pB);
+    });
+    }
+  };
+
   // Query tiles walked for key tile kt that see all of its keys: with a mask
   // the ones after its last key, [4kt + 4, qt_end); without one, all. None if
   // the key tile reaches past N.
@@ -464,7 +614,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
   // Phase 0 walks its query tiles downward (upward without a mask, where they
   // are all clear or all masked): the clear ones first.
   const int c0 = min(n0, clear_tiles(kt0) * p.g);
-  run_items(0, c0, std::false_type{});
+  run_clear(0, c0);
   run_items(c0, n0, std::true_type{});
   if (n_work > n0) {   // second key tile: store the first one's gradients
     store_dkdv(kw);
@@ -476,7 +626,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
     // Phase 1 walks its query tiles upward: the clear ones last.
     const int m1 = max(n0, n_work - clear_tiles(kt1) * p.g);
     run_items(n0, m1, std::true_type{});
-    run_items(m1, n_work, std::false_type{});
+    run_clear(m1, n_work);
   }
   // The last key tile's gradients. A key tile that no query reaches (wholly
   // past N) stores zeros: the weight gradients read those padding rows.
@@ -554,6 +704,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq(BwdParams p) {
       loff[x] = (uint32_t)r * (uint32_t)p.Np * (uint32_t)sizeof(T) + (uint32_t)((c ^ swz<LC>(r)) * EPC * (int)sizeof(T));
     }
   }
+  // Buffer loads (counted only in vmcnt, as in bwd_dkdv), byte offsets below 2^32.
   auto issue = [&](int t) {
     if (t >= n_items) return;
     const int k0 = item_tile(t) * BT;
@@ -562,8 +713,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq(BwdParams p) {
     for (int x = 0; x < IPW; ++x) {
       const int ins = wave * IPW + x, arr = ins / INS, li = ins % INS;
       const T* base = arr == 0 ? Kh + (int64_t)k0 * D : arr == 1 ? Vh + (int64_t)k0 * D : KTh + k0;
-      __builtin_amdgcn_global_load_lds((const void*)((const char*)base + loff[x]),
-                                       (lds_ptr)(tb + arr * TE + li * 64 * EPC), 16, 0, 0);
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)base, (short)0,
+          (int)(arr < 2 ? TE * (uint32_t)sizeof(T) : (uint32_t)(D - 1) * (uint32_t)p.Np * (uint32_t)sizeof(T) + BT * (uint32_t)sizeof(T)),
+          0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(tb + arr * TE + li * 64 * EPC), 16, (int)loff[x], 0, 0, 0);
     }
   };
 
@@ -765,7 +919,7 @@ BwdLayout bwd_layout(int64_t es, int64_t B, int64_t N, int64_t Np, int64_t d_mod
       f * es * B * H_q * Np * d, f * es * B * H_kv * Np * d, f * es * B * H_kv * Np * d,
       f * es * B * N * H_q * d, f * 4 * B * H_q * Np, f * 4 * B * N * H_q * d,
       f * (int64_t)qkv_wt_bytes(es == 2 ? SQA_DTYPE_BF16 : SQA_DTYPE_FP32, d_model, H_q, H_kv, d),
-      es * B * H_q * Np * d, 4 * B * H_q * Np, es * B * H_q * Np * d, es * B * H_kv * Np * d,
+      es * B * H_q * Np * d, 2 * 4 * B * H_q * Np, es * B * H_q * Np * d, es * B * H_kv * Np * d,
       es * B * H_kv * Np * d, es * B * H_q * Np * d, es * T * W, es * T * W, es * d_model * T,
       es * d_model * W, es * H_q * d * T, es * d_model * T, part};
   BwdLayout L;
@@ -800,7 +954,8 @@ hipError_t backward_impl(const void* x, const void* wq, const void* wk, const vo
     lse = (float*)(sv + S.lse);
     o32 = (float*)(sv + S.o32);
   }
-  float* dvec = (float*)(ws + L.dvec);
+  float* dvec = (float*)(ws + L.dvec);   // -D, then -lse/c
+  float* nlse = dvec + B * H_q * Np;
   void *dO = ws + L.dO, *qt = ws + L.qt, *kt = ws + L.kt, *v = ws + L.v, *dOt = ws + L.dOt;
   void *dqkv = ws + L.dqkv, *dqkvT = ws + L.dqkvT, *xT = ws + L.xT, *wall = ws + L.wall;
   void *aT = ws + L.aT, *dyT = ws + L.dyT;
@@ -819,7 +974,8 @@ hipError_t backward_impl(const void* x, const void* wq, const void* wk, const vo
   {
     const int64_t rows = B * H_q * Np;
     dvec_kernel<T, D><<<(unsigned)((rows + 255) / 256), 256, 0, stream>>>(
-        (const T*)dO, o32, dvec, (int)N, Np, (int)H_q, rows);
+        (const T*)dO, o32, lse, (float)(1.4426950408889634 / sqrt((double)D)), dvec, nlse, (int)N, Np,
+        (int)H_q, rows);
     SQA_CK(hipGetLastError());
   }
   // head-dim-major copies for the contractions over tokens (tokens in swap23
@@ -830,7 +986,7 @@ hipError_t backward_impl(const void* x, const void* wq, const void* wk, const vo
   SQA_CK((transpose<T, true>(dO, Np * D, D, Np, Np, dOt, D * Np, Np, D, B * H_q, stream)));
   BwdParams p;
   p.q = q; p.qt = qt; p.k = k; p.kt = kt; p.v = v; p.dO = dO; p.dOt = dOt;
-  p.lse = lse; p.dvec = dvec; p.dqkv = dqkv;
+  p.lse = lse; p.nlse = nlse; p.dvec = dvec; p.dqkv = dqkv;
   p.N = (int)N; p.Np = (int)Np; p.H_q = (int)H_q; p.H_kv = (int)H_kv; p.g = (int)(H_q / H_kv);
   p.causal = causal ? 1 : 0; p.W = (int)W;
   p.c = (float)(1.4426950408889634 / sqrt((double)D));
