@@ -614,11 +614,16 @@ sqa_status sqa_decode_step(const void* x_new, const void* Wq, const void* Wk, co
   void *q = base, *a = base + off_a, *part = base + off_p;
   e = sqa::launch_decode_qkv(dtype, x_new, Wq, Wk, Wv, pos, q, k_cache, v_cache, B, d_model, H_q,
                              H_kv, d_head, N_max, stream);
+  // The merge of the attention's key chunks runs inside the output
+  // projection where its LDS row fits, else as a launch of its own.
+  const bool fused = sqa::decode_merge_out_fits(B, N_max, H_q, H_kv, d_head, d_model);
   if (e == hipSuccess)
-    e = sqa::launch_decode_attention(dtype, q, k_cache, v_cache, pos, a, part, B, N_max, H_q, H_kv,
-                                     d_head, stream);
+    e = sqa::launch_decode_attention(dtype, q, k_cache, v_cache, pos, fused ? nullptr : a, part, B,
+                                     N_max, H_q, H_kv, d_head, stream);
   if (e == hipSuccess)
-    e = sqa::launch_decode_out(dtype, a, Wo, out, B, H_q * d_head, d_model, stream);
+    e = fused ? sqa::launch_decode_merge_out(dtype, part, pos, Wo, out, B, N_max, H_q, H_kv, d_head,
+                                             d_model, stream)
+              : sqa::launch_decode_out(dtype, a, Wo, out, B, H_q * d_head, d_model, stream);
   const hipError_t ef = hipFreeAsync(ws, stream);
   if (e != hipSuccess) return fail_hip(e, "kernel launch");
   if (ef != hipSuccess) return fail_hip(ef, "workspace release");

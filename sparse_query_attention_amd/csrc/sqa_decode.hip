@@ -95,6 +95,86 @@ constexpr int SK_COLS = 8, SK_BR = 8, SK_J = 4;     // columns and tokens per wo
 // the row reads (two 16-byte reads per row) are free of bank conflicts.
 __device__ inline int xs_at(int k, int b) { return (k + (k >> 3)) * SK_BR + b; }
 
+// Cross-lane steps on the VALU (no LDS round trip). Lane partners by stride:
+// 32 and 16 through v_permlane32_swap / v_permlane16_swap (they exchange the
+// upper lanes of one register with the lower lanes of another), 8 through DPP
+// row_ror:8 (lane ^ 8 within a row of 16), 2 and 1 through quad permutations;
+// for 4, row_ror:12 and row_ror:4 bring lane + 4 and lane - 4 within the row
+// (row_ror:n hands lane i the value of lane i - n), and the lane's bit 2 picks
+// one (lane ^ 4). dpp_partner<7> is lane ^ 7 within
+// 8 (row_half_mirror): enough for a full reduction, where every lane ends with
+// the same total.
+template <int M> __device__ inline float dpp_partner(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  unsigned r;
+  if constexpr (M == 8) r = __builtin_amdgcn_update_dpp(0u, u, 0x128, 0xF, 0xF, false);
+  else if constexpr (M == 7) r = __builtin_amdgcn_update_dpp(0u, u, 0x141, 0xF, 0xF, false);
+  else if constexpr (M == 2) r = __builtin_amdgcn_update_dpp(0u, u, 0x4E, 0xF, 0xF, false);
+  else r = __builtin_amdgcn_update_dpp(0u, u, 0xB1, 0xF, 0xF, false);
+  return __builtin_bit_cast(float, r);
+}
+__device__ inline float dpp_xor4(float x, bool hi) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const unsigned up = __builtin_amdgcn_update_dpp(0u, u, 0x12C, 0xF, 0xF, false);     // lane + 4
+  const unsigned down = __builtin_amdgcn_update_dpp(0u, u, 0x124, 0xF, 0xF, false);   // lane - 4
+  return __builtin_bit_cast(float, hi ? down : up);
+}
+// One reduce-scatter step over lane bit M on pairs (v[i], v[n/2 + i]): a lane
+// with the bit clear keeps v[i], one with it set keeps v[n/2 + i], and each
+// adds its partner's copy of the half it keeps.
+template <int M, int n, int NV> __device__ inline void rs_step(float (&v)[NV], int lane) {
+  if constexpr (M >= 16) {
+#pragma unroll
+    for (int i = 0; i < n / 2; ++i) {
+      const unsigned a = __builtin_bit_cast(unsigned, v[i]), b = __builtin_bit_cast(unsigned, v[n / 2 + i]);
+      unsigned r0, r1;
+      if constexpr (M == 32) {
+        const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+        r0 = r[0]; r1 = r[1];
+      } else {
+        const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+        r0 = r[0]; r1 = r[1];
+      }
+      v[i] = __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+    }
+  } else {
+    const bool hi = (lane & M) != 0;
+#pragma unroll
+    for (int i = 0; i < n / 2; ++i) {
+      const float keep = hi ? v[n / 2 + i] : v[i];
+      const float give = hi ? v[i] : v[n / 2 + i];
+      if constexpr (M == 4) v[i] = keep + dpp_xor4(give, hi);
+      else v[i] = keep + dpp_partner<M>(give);
+    }
+  }
+}
+// The reduce-scatter of N values per lane down to OUT, over lane bits M, M/2, ...
+template <int N, int M, int OUT, int NV> __device__ inline void rs_levels(float (&v)[NV], int lane) {
+  if constexpr (N > OUT) {
+    rs_step<M, N>(v, lane);
+    rs_levels<N / 2, M / 2, OUT>(v, lane);
+  }
+}
+// Reduction of x over the wave (every lane gets the result), in a fixed order.
+template <bool MAX> __device__ inline float wave_reduce(float x) {
+  auto op = [](float p, float q) { return MAX ? fmaxf(p, q) : p + q; };
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    x = op(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+  }
+  {
+    const unsigned w = __builtin_bit_cast(unsigned, x);
+    const auto r = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+    x = op(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+  }
+  x = op(x, dpp_partner<8>(x));
+  x = op(x, dpp_partner<7>(x));
+  x = op(x, dpp_partner<2>(x));
+  x = op(x, dpp_partner<1>(x));
+  return x;
+}
+
 // out[b][n] = sum over k of x[b][k] * W[k][n] for W = [W0 | W1 | W2], x [B, K].
 // Every segment width is a multiple of SK_COLS, so a workgroup's columns lie in
 // one segment. K is a multiple of the chunk width (16 bytes of T).
@@ -184,17 +264,8 @@ __global__ __launch_bounds__(256) void skinny(const T* x, int B, int K, const T*
   // bit, adds its partner's copy of that half and hands over the other half.
   // After the last step a lane holds OUT consecutive flat indexes
   // (lane / TPR) * OUT + i of acc, flat index = token * EPC + column in chunk.
-  float* v = acc;
-#pragma unroll
-  for (int n = NV, m = 32; n > OUT; n >>= 1, m >>= 1) {
-    const bool hi = (lane & m) != 0;
-#pragma unroll
-    for (int i = 0; i < n / 2; ++i) {
-      const float keep = hi ? v[n / 2 + i] : v[i];
-      const float give = hi ? v[i] : v[n / 2 + i];
-      v[i] = keep + __shfl_xor(give, m);
-    }
-  }
+  rs_levels<NV, 32, OUT>(acc, lane);
+  const float* v = acc;
   {
     const int f = (lane / TPR) * OUT, b = f / EPC, col = cc * EPC + f % EPC;
 #pragma unroll
@@ -341,15 +412,11 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_partial(DecParams p) {
 #pragma unroll
     for (int i = 0; i < G; ++i) {
       const float si = valid ? s[i] * p.c : -INFINITY;
-      float bm = si;
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) bm = fmaxf(bm, __shfl_xor(bm, off));
+      const float bm = wave_reduce<true>(si);
       const float m_new = fmaxf(m[i], bm);
       alpha[i] = __builtin_amdgcn_exp2f(m[i] - m_new);
       const float pi = __builtin_amdgcn_exp2f(si - m_new);
-      float bs = pi;
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) bs += __shfl_xor(bs, off);
+      const float bs = wave_reduce<false>(pi);
       l[i] = l[i] * alpha[i] + bs;
       m[i] = m_new;
       ps[wave][lane][i] = pi;
@@ -456,6 +523,182 @@ __global__ __launch_bounds__(256) void decode_combine(const float* part, const i
   }
 }
 
+// The merge of the key chunks fused with the output projection: workgroup
+// (block of MC output columns, token b) merges the chunk states of every query
+// head of token b into a[b] = o / l, rounded to T once (as decode_combine
+// stores it), keeps a[b] in LDS as fp32 and forms
+// out[b, n0 .. n0+MC) = a[b] * wo[:, n0 .. n0+MC). The merge takes two passes,
+// so that no load waits on another: a wave per head reduces the chunks' m
+// (max) and l (weighted sum) across its lanes and leaves each chunk's weight
+// exp2(m_c - M) in LDS, then every element sums its chunks' o with those
+// weights. Each of the d_model/MC workgroups of a token merges its states
+// again (from L2 after the first), which costs less than the launch it
+// saves. The first RJ rows per thread of wo are loaded before the merge, so
+// their latency overlaps it. LDS: a[b] [K], the weights [H_q][n_valid], 1/L
+// [H_q], then the phases' sums.
+constexpr int MC = 32;
+constexpr int MERGE_MAX_W = 4096;   // H_q * n_chunks weights in LDS
+template <typename T, int D>
+__global__ __launch_bounds__(256) void decode_merge_out(const float* part, const int32_t* pos,
+                                                        const T* wo, T* out, int H_q, int n_chunks,
+                                                        int chunk, int64_t N_max, int d_model) {
+  constexpr int EPC = 16 / (int)sizeof(T);   // columns per 16-byte chunk
+  constexpr int TPR = MC / EPC;              // threads per row of the column block
+  constexpr int PH = 256 / TPR;              // row phases
+  constexpr int RJ = 16;                     // rows per thread and k block
+  constexpr int KBLK = PH * RJ;
+  constexpr int SEG = 8;                     // first-level groups of the phase sums
+  static_assert(PH % SEG == 0 && 256 / MC == SEG, "split");
+  extern __shared__ float smem_f[];
+  const int K = H_q * D;
+  const int b = blockIdx.y, n0 = blockIdx.x * MC, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int64_t pb = min(max((int64_t)pos[b], (int64_t)0), N_max - 1);
+  const int nv = (int)min((int64_t)n_chunks, (pb + 1 + chunk - 1) / chunk);   // >= 1
+  float* a_s = smem_f;                       // [K]
+  float* w_s = a_s + K;                      // [H_q][nv]
+  float* il_s = w_s + H_q * nv;              // [H_q]
+  float* red = il_s + H_q;                   // [PH][MC]
+  float* red2 = red + PH * MC;               // [SEG][MC]
+  const int cc = tid % TPR, ph = tid / TPR;
+  const T* wcol = wo + n0 + cc * EPC;
+
+  auto load_rows = [&](int k0, Chunk (&raw)[RJ]) {
+#pragma unroll
+    for (int j = 0; j < RJ; ++j) {
+      const int k = k0 + ph + j * PH;
+      raw[j] = *reinterpret_cast<const Chunk*>(wcol + (int64_t)(k < K ? k : 0) * d_model);
+    }
+  };
+  Chunk raw[RJ];
+  load_rows(0, raw);   // in flight during the merge
+
+  const float* pbase = part + (int64_t)b * H_q * n_chunks * (D + 2);
+  // Common shape (at most FC chunks, at most FH heads, K <= FP * 512): every
+  // load the merge needs is issued at once, in the order of use (each wave's
+  // heads' m and l, then o as pairs of elements), with the wo rows already in
+  // flight behind them in the counter.
+  constexpr int FC = 32, FH = 16, FP = 2;
+  const bool fast = nv <= FC && H_q <= FH && K <= FP * 512;
+  if (fast) {
+    constexpr int HPW = FH / 4;   // heads per wave
+    float mh[HPW], lh[HPW];
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      const int i = wave + 4 * hh;
+      const float* st = pbase + ((int64_t)(i < H_q ? i : 0) * n_chunks + (lane < nv ? lane : 0)) * (D + 2);
+      mh[hh] = st[D];
+      lh[hh] = st[D + 1];
+    }
+    float2 o_r[FP][FC];
+#pragma unroll
+    for (int r = 0; r < FP; ++r) {
+      const int x = 2 * (tid + r * 256), xc = x < K ? x : 0;
+      const float* src = pbase + (int64_t)(xc / D) * n_chunks * (D + 2) + xc % D;
+#pragma unroll
+      for (int c = 0; c < FC; ++c)
+        o_r[r][c] = *reinterpret_cast<const float2*>(src + (int64_t)(c < nv ? c : 0) * (D + 2));
+    }
+    // pass 1: per head, M = max m_c, weights w_c = exp2(m_c - M), 1/L with L = sum w_c l_c
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      const int i = wave + 4 * hh;
+      if (i < H_q) {   // uniform per wave
+        const float mx = wave_reduce<true>(lane < nv ? mh[hh] : DEC_M_INIT);
+        const float w = __builtin_amdgcn_exp2f(mh[hh] - mx);
+        if (lane < nv) w_s[i * nv + lane] = w;
+        const float ls = wave_reduce<false>(lane < nv ? w * lh[hh] : 0.f);
+        if (lane == 0) il_s[i] = 1.f / ls;   // ls > 0: key 0 is in chunk 0
+      }
+    }
+    __syncthreads();
+    // pass 2: a[i*D + e] = (sum_c w_c o_c[e]) / L, chunks in order
+#pragma unroll
+    for (int r = 0; r < FP; ++r) {
+      const int x = 2 * (tid + r * 256);
+      if (x < K) {
+        const int i = x / D;
+        const float* wi = w_s + i * nv;
+        float O0 = 0.f, O1 = 0.f;
+#pragma unroll
+        for (int c = 0; c < FC; ++c)
+          if (c < nv) { O0 = fmaf(wi[c], o_r[r][c].x, O0); O1 = fmaf(wi[c], o_r[r][c].y, O1); }
+        a_s[x] = to_f32(from_f32<T>(O0 * il_s[i]));
+        a_s[x + 1] = to_f32(from_f32<T>(O1 * il_s[i]));
+      }
+    }
+  } else {
+    // pass 1 as above, a head per wave at a time
+    for (int i = wave; i < H_q; i += 4) {
+      const float* ph_ = pbase + (int64_t)i * n_chunks * (D + 2);
+      float mx = DEC_M_INIT, ls = 0.f;
+      for (int c = lane; c < nv; c += 64) mx = fmaxf(mx, ph_[(int64_t)c * (D + 2) + D]);
+      mx = wave_reduce<true>(mx);
+      for (int c = lane; c < nv; c += 64) {
+        const float* st = ph_ + (int64_t)c * (D + 2);
+        const float w = __builtin_amdgcn_exp2f(st[D] - mx);
+        w_s[i * nv + c] = w;
+        ls = fmaf(w, st[D + 1], ls);
+      }
+      ls = wave_reduce<false>(ls);
+      if (lane == 0) il_s[i] = 1.f / ls;
+    }
+    __syncthreads();
+    constexpr int OU = 8;   // chunk loads in flight per element
+    for (int x = tid; x < K; x += 256) {
+      const int i = x / D, e = x % D;
+      const float* src = pbase + (int64_t)i * n_chunks * (D + 2) + e;
+      const float* wi = w_s + i * nv;
+      float O = 0.f;
+      for (int c0 = 0; c0 < nv; c0 += OU) {
+        float o[OU];
+#pragma unroll
+        for (int u = 0; u < OU; ++u) o[u] = c0 + u < nv ? src[(int64_t)(c0 + u) * (D + 2)] : 0.f;
+#pragma unroll
+        for (int u = 0; u < OU; ++u)
+          if (c0 + u < nv) O = fmaf(wi[c0 + u], o[u], O);
+      }
+      a_s[x] = to_f32(from_f32<T>(O * il_s[i]));
+    }
+  }
+  __syncthreads();
+
+  float acc[EPC];
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
+  for (int k0 = 0; k0 < K; k0 += KBLK) {
+    if (k0 > 0) load_rows(k0, raw);
+#pragma unroll
+    for (int j = 0; j < RJ; ++j) {
+      const int k = k0 + ph + j * PH;
+      if (k < K) {
+        const T* wv = reinterpret_cast<const T*>(&raw[j]);
+        const float av = a_s[k];
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[e] = fmaf(av, to_f32(wv[e]), acc[e]);
+      }
+    }
+  }
+  // sums over the phases in a fixed order
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) red[ph * MC + cc * EPC + e] = acc[e];
+  __syncthreads();
+  {
+    const int col = tid % MC, sg = tid / MC;
+    float sum = 0.f;
+#pragma unroll
+    for (int q = 0; q < PH / SEG; ++q) sum += red[(sg * (PH / SEG) + q) * MC + col];
+    red2[sg * MC + col] = sum;
+  }
+  __syncthreads();
+  if (tid < MC) {
+    float sum = 0.f;
+#pragma unroll
+    for (int sg = 0; sg < SEG; ++sg) sum += red2[sg * MC + tid];
+    out[(int64_t)b * d_model + n0 + tid] = from_f32<T>(sum);
+  }
+}
+
 // Chunking of a decode step: enough workgroups for the chip, chunks a multiple of KB.
 struct DecodePlan { int G, n_hg, n_chunks, chunk; };
 
@@ -490,6 +733,8 @@ hipError_t partial_for(int G, const DecParams& p, dim3 grid, hipStream_t stream)
   }
 }
 
+// The chunk states into part, then, with a, their merge into a [B, H_q*D]
+// (without a, the caller merges them with decode_merge_out).
 template <typename T, int D>
 hipError_t decode_impl(const void* q, const void* kc, const void* vc, const int32_t* pos, void* a,
                        float* part, int64_t B, int64_t N_max, int64_t H_q, int64_t H_kv,
@@ -503,7 +748,7 @@ hipError_t decode_impl(const void* q, const void* kc, const void* vc, const int3
   p.c = (float)(1.4426950408889634 / sqrt((double)D));
   const dim3 grid((unsigned)pl.n_chunks, (unsigned)(H_kv * pl.n_hg), (unsigned)B);
   hipError_t e = partial_for<T, D>(pl.G, p, grid, stream);
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !a) return e;
   decode_combine<T, D><<<(unsigned)(B * H_q), 256, 0, stream>>>(part, pos, (T*)a, (int)H_q,
                                                               pl.n_chunks, pl.chunk, N_max);
   return hipGetLastError();
@@ -591,6 +836,38 @@ hipError_t launch_decode_out(sqa_dtype dt, const void* a, const void* wo, void* 
                              int64_t K, int64_t d_model, hipStream_t stream) {
   return dt == SQA_DTYPE_BF16 ? decode_out<bf16>(a, wo, out, B, K, d_model, stream)
                               : decode_out<float>(a, wo, out, B, K, d_model, stream);
+}
+
+bool decode_merge_out_fits(int64_t B, int64_t N_max, int64_t H_q, int64_t H_kv, int64_t d_head,
+                           int64_t d_model) {
+  return H_q * d_head <= 8192 && d_model % MC == 0 && d_model / MC <= 0x7FFFFFFF && B <= 65535 &&
+         H_q * decode_plan(B, H_q, H_kv, N_max).n_chunks <= MERGE_MAX_W;
+}
+
+hipError_t launch_decode_merge_out(sqa_dtype dt, const void* part, const int32_t* pos,
+                                   const void* wo, void* out, int64_t B, int64_t N_max,
+                                   int64_t H_q, int64_t H_kv, int64_t d_head, int64_t d_model,
+                                   hipStream_t stream) {
+  if (!decode_merge_out_fits(B, N_max, H_q, H_kv, d_head, d_model)) return hipErrorInvalidConfiguration;
+  const DecodePlan pl = decode_plan(B, H_q, H_kv, N_max);
+  const int tpr = MC / (dt == SQA_DTYPE_BF16 ? 8 : 4);
+  const size_t lds =
+      (size_t)(H_q * d_head + H_q * pl.n_chunks + H_q + (256 / tpr) * MC + 8 * MC) * sizeof(float);
+  const dim3 grid((unsigned)(d_model / MC), (unsigned)B);
+  const float* pf = (const float*)part;
+  const int hq = (int)H_q, dm = (int)d_model;
+  if (dt == SQA_DTYPE_BF16) {
+    if (d_head == 64)
+      decode_merge_out<bf16, 64><<<grid, 256, lds, stream>>>(pf, pos, (const bf16*)wo, (bf16*)out, hq, pl.n_chunks, pl.chunk, N_max, dm);
+    else
+      decode_merge_out<bf16, 32><<<grid, 256, lds, stream>>>(pf, pos, (const bf16*)wo, (bf16*)out, hq, pl.n_chunks, pl.chunk, N_max, dm);
+  } else {
+    if (d_head == 64)
+      decode_merge_out<float, 64><<<grid, 256, lds, stream>>>(pf, pos, (const float*)wo, (float*)out, hq, pl.n_chunks, pl.chunk, N_max, dm);
+    else
+      decode_merge_out<float, 32><<<grid, 256, lds, stream>>>(pf, pos, (const float*)wo, (float*)out, hq, pl.n_chunks, pl.chunk, N_max, dm);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_decode_attention(sqa_dtype dt, const void* q, const void* kc, const void* vc,

@@ -91,9 +91,12 @@ hipError_t launch_fill_cache(sqa_dtype dt, const void* k, const void* vt, void* 
 
 // Decode step over B new tokens. decode_qkv projects x_new [B, d_model] into
 // q [B, H_q*d] and writes token b's key and value straight to cache row pos[b]
-// (clamped into [0, N_max-1]); decode_attention writes a [B, H_q*d] over cache
-// rows 0..pos[b], with device scratch part of decode_partial_bytes(); decode_out
-// gives out [B, d_model] = a [B, K] * wo [K, d_model].
+// (clamped into [0, N_max-1]); decode_attention writes the states of its key
+// chunks over cache rows 0..pos[b] to device scratch part of
+// decode_partial_bytes() and, if a is not null, merges them into a [B, H_q*d];
+// decode_out gives out [B, d_model] = a [B, K] * wo [K, d_model];
+// decode_merge_out (where decode_merge_out_fits) merges the chunk states and
+// projects them in one launch.
 hipError_t launch_decode_qkv(sqa_dtype dt, const void* x_new, const void* wq, const void* wk,
                              const void* wv, const int32_t* pos, void* q, void* kc, void* vc,
                              int64_t B, int64_t d_model, int64_t H_q, int64_t H_kv, int64_t d_head,
@@ -105,5 +108,11 @@ hipError_t launch_decode_attention(sqa_dtype dt, const void* q, const void* kc, 
                                    hipStream_t stream);
 hipError_t launch_decode_out(sqa_dtype dt, const void* a, const void* wo, void* out, int64_t B,
                              int64_t K, int64_t d_model, hipStream_t stream);
+bool decode_merge_out_fits(int64_t B, int64_t N_max, int64_t H_q, int64_t H_kv, int64_t d_head,
+                           int64_t d_model);
+hipError_t launch_decode_merge_out(sqa_dtype dt, const void* part, const int32_t* pos,
+                                   const void* wo, void* out, int64_t B, int64_t N_max,
+                                   int64_t H_q, int64_t H_kv, int64_t d_head, int64_t d_model,
+                                   hipStream_t stream);
 
 }  // namespace sqa
