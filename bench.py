@@ -249,6 +249,7 @@ def run_decode(w: wl.Workload, steps: int, warmup: int, torch, sqa, dev):
     e1 = tm.event()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
+    kernel_us = decode_kernel_us(torch, step, steps)
     cache_bytes = 2 * w.B * w.H_kv * w.N * w.d_head * es
     weight_bytes = (w.d_model * (w.H_q + 2 * w.H_kv) * w.d_head + w.H_q * w.d_head * w.d_model) * es
     io_bytes = 2 * w.B * w.d_model * es
@@ -258,7 +259,28 @@ def run_decode(w: wl.Workload, steps: int, warmup: int, torch, sqa, dev):
     return {"B": w.B, "cache_tokens": w.N, "H_q": w.H_q, "H_kv": w.H_kv,
             "ms_per_step": round(ms, 4), "tokens_per_s": round(w.B / (ms / 1e3), 1),
             "bytes_per_step": total, "gbs": round(total / (ms / 1e3) / 1e9, 1),
-            "frac_hbm_peak": round(total / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+            "frac_hbm_peak": round(total / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "kernel_us_per_step": None if kernel_us is None else round(kernel_us, 2),
+            "kernel_frac_hbm_peak": None if kernel_us is None else
+            round(total / (kernel_us / 1e6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def decode_kernel_us(torch, step, steps: int):
+    """Device time of the decode step's own kernels per step (the sum of their
+    durations, without the gaps between launches or the workspace allocation),
+    from torch's profiler over `steps` more steps. The profiler records every
+    HIP kernel of the process, the library's included."""
+    try:
+        from torch.profiler import ProfilerActivity, profile
+        torch.cuda.synchronize()
+        with profile(activities=[ProfilerActivity.CUDA]) as prof:
+            for _ in range(steps):
+                step()
+            torch.cuda.synchronize()
+        total = sum(getattr(ev, "device_time_total", 0.0) for ev in prof.key_averages())
+    except Exception:   # profiler unavailable: report the step time only
+        return None
+    return total / steps if total > 0 else None
 
 
 def run_backward(w: wl.Workload, steps: int, warmup: int, torch, sqa, dev):

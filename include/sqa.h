@@ -166,7 +166,10 @@ sqa_status sqa_prefill(const void* x, const void* Wq, const void* Wk, const void
  * sqa_forward(causal = 1) over the sequence's first pos[b]+1 tokens, provided
  * that rows 0..pos[b]-1 of the caches hold those tokens' keys and values (from
  * sqa_prefill or earlier steps). Attention is split over key chunks, with
- * partial results in the workspace (stream-ordered pool, as in sqa_forward).
+ * partial results in a workspace that the library keeps per stream between
+ * calls (taken from the stream-ordered pool on a stream's first call or when a
+ * call needs more; held until the process ends). Calls on one stream are
+ * ordered and share it; calls on different streams use different ones.
  * 1 <= B <= 65535; pos must be 4-byte aligned.
  */
 sqa_status sqa_decode_step(const void* x_new, const void* Wq, const void* Wk, const void* Wv,

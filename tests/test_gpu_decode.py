@@ -181,3 +181,38 @@ def test_decode_in_the_benchmark_launch(dev, H_q):
     rep = compare(wl.widen(y.cpu()), ref, "bf16")
     log(f"  benchmark decode launch H_q={H_q}: {rep}")
     assert rep.ok, rep
+
+
+def test_decode_workspace_kept_per_stream(dev):
+    """The decode step keeps its workspace per stream between calls. A step on
+    a second stream, and a larger step after a smaller one on the same stream
+    (the workspace grows), each equal bitwise the same step on the default
+    stream."""
+    def setup(B, N, seed):
+        w = wl.Workload("dec_ws", B=B, N=N, d_model=512, H=8, H_q=4, H_kv=2, causal=True,
+                        dtype="bf16", seed=seed)
+        _, d = device_inputs(w, dev)
+        kc, vc = _caches(w, N, dev, fill=0.0)
+        sqa.prefill(d["X"][:, :N - 1].contiguous(), d["Wq"], d["Wk"], d["Wv"], d["Wo"], kc, vc,
+                    H=w.H, H_q=w.H_q, H_kv=w.H_kv)
+        pos = torch.full((B,), N - 1, dtype=torch.int32, device=dev)
+        return w, d, kc, vc, pos
+
+    def step(w, d, kc, vc, pos):
+        return sqa.decode_step(d["X"][:, w.N - 1].contiguous(), d["Wq"], d["Wk"], d["Wv"], d["Wo"],
+                               kc, vc, pos, H=w.H, H_q=w.H_q, H_kv=w.H_kv)
+
+    small = setup(2, 700, 91)
+    large = setup(6, 5000, 92)
+    ref_small, ref_large = step(*small), step(*large)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        got_small = step(*small)   # the side stream's first call
+        got_large = step(*large)   # needs more than that: the workspace grows
+        got_small2 = step(*small)  # fits what is there
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    for got, ref in ((got_small, ref_small), (got_large, ref_large), (got_small2, ref_small)):
+        assert torch.equal(got, ref)
