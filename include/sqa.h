@@ -35,8 +35,9 @@
  *   - Arithmetic: matrix products on the MFMA units with fp32 accumulation,
  *     softmax in fp32. Q, K, V, A and Y are each rounded once (to nearest,
  *     ties to even) to `dtype` when stored.
- *   - Calls on different streams may run concurrently. The library keeps only
- *     one stream-ordered memory pool per device (see sqa_forward).
+ *   - Calls on different streams may run concurrently. The library keeps one
+ *     stream-ordered memory pool per device, and small workspaces per stream
+ *     (see sqa_forward).
  */
 #ifndef SQA_H
 #define SQA_H
@@ -77,15 +78,23 @@ typedef enum { SQA_DTYPE_FP32 = 0, SQA_DTYPE_BF16 = 1 } sqa_dtype;
  * Workspace: Q, K, V^T and A intermediates plus the two weight matrices
  * transposed, about elem_size * (B*Np*d_head*(H_q + 2*H_kv) + B*N*H_q*d_head
  * + d_model*d_head*(2*H_q + 2*H_kv)) bytes with Np = sqa_padded_length(N).
- * It is taken from a per-device stream-ordered memory pool
- * (hipMallocFromPoolAsync) and returned to it (hipFreeAsync) on `stream`.
- * The pool keeps freed memory for reuse until the process ends.
+ * A workspace of up to SQA_STREAM_WORKSPACE_MAX bytes is kept per stream
+ * between calls: taken on a stream's first call (or when a call needs more)
+ * from a per-device stream-ordered memory pool and held until the process
+ * ends; calls on one stream run in order and share it. A larger workspace is
+ * taken from the pool (hipMallocFromPoolAsync) and returned to it
+ * (hipFreeAsync) on `stream` by each call; the pool keeps freed memory for
+ * reuse until the process ends. This holds for every entry point below that
+ * needs a workspace.
  * Returns SQA_ERR_OUT_OF_MEMORY if the pool cannot supply the workspace.
  */
 sqa_status sqa_forward(const void* x, const void* Wq, const void* Wk, const void* Wv,
                        const void* Wo, void* out, int64_t B, int64_t N, int64_t d_model,
                        int64_t H, int64_t H_q, int64_t H_kv, int64_t d_head, int causal,
                        sqa_dtype dtype, hipStream_t stream);
+
+/* Largest workspace that a call keeps with its stream (see sqa_forward). */
+#define SQA_STREAM_WORKSPACE_MAX ((size_t)64 << 20)
 
 /* Size of the fixed device array that sqa_forward_noalloc takes its workspace from. */
 #define SQA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
@@ -166,10 +175,8 @@ sqa_status sqa_prefill(const void* x, const void* Wq, const void* Wk, const void
  * sqa_forward(causal = 1) over the sequence's first pos[b]+1 tokens, provided
  * that rows 0..pos[b]-1 of the caches hold those tokens' keys and values (from
  * sqa_prefill or earlier steps). Attention is split over key chunks, with
- * partial results in a workspace that the library keeps per stream between
- * calls (taken from the stream-ordered pool on a stream's first call or when a
- * call needs more; held until the process ends). Calls on one stream are
- * ordered and share it; calls on different streams use different ones.
+ * partial results in the workspace (see sqa_forward: a few hundred KB to a few
+ * MB for decode shapes, so it stays with the stream between steps).
  * 1 <= B <= 65535; pos must be 4-byte aligned.
  */
 sqa_status sqa_decode_step(const void* x_new, const void* Wq, const void* Wk, const void* Wv,
@@ -227,7 +234,7 @@ sqa_status sqa_forward_train(const void* x, const void* Wq, const void* Wk, cons
  * Workspace: about elem_size * B*Np * (8*(H_q + H_kv)*d_head + 2*d_model)
  * bytes (less the saved activations when `saved` is given), 4*B*H_q*Np bytes
  * of fp32 row sums, and the fp32 split-K partial sums of the weight gradients,
- * from the stream-ordered pool (see sqa_forward). Outputs must not overlap
+ * (see sqa_forward). Outputs must not overlap
  * each other, any input or `saved`; other checks and errors as in sqa_forward.
  */
 sqa_status sqa_backward(const void* x, const void* Wq, const void* Wk, const void* Wv,
@@ -249,8 +256,8 @@ int64_t sqa_padded_length(int64_t N);
  *   k  [B, H_kv, Np, d_head]
  *   vt [B, H_kv, d_head, Np]   V transposed per head: vt[b, h, c, t] = V[b, t, h*d_head + c]
  * Rows t in [N, Np) are written as zeros. x and the weights are as in sqa_forward.
- * Scratch for the transposed weights (elem_size * d_model*d_head*(H_q + 2*H_kv)
- * bytes) comes from the same stream-ordered pool as sqa_forward's workspace.
+ * Workspace: the transposed weights (elem_size * d_model*d_head*(H_q + 2*H_kv)
+ * bytes), kept as sqa_forward's.
  */
 sqa_status sqa_qkv_projection(const void* x, const void* Wq, const void* Wk, const void* Wv,
                               void* q, void* k, void* vt, int64_t B, int64_t N,
@@ -271,8 +278,8 @@ sqa_status sqa_attention(const void* q, const void* k, const void* vt, void* a, 
 /*
  * sqa_output_projection - step 3, out[M, d_model] = a[M, K] Wo[K, d_model].
  * K and d_model must be multiples of 32; out must not overlap a or Wo.
- * Scratch for Wo transposed (elem_size * K * d_model bytes) comes from the
- * stream-ordered pool.
+ * Workspace: Wo transposed (elem_size * K * d_model bytes), kept as
+ * sqa_forward's.
  */
 sqa_status sqa_output_projection(const void* a, const void* Wo, void* out, int64_t M,
                                  int64_t K, int64_t d_model, sqa_dtype dtype,

@@ -180,17 +180,19 @@ sqa_status pool_for(hipStream_t stream, hipMemPool_t* out) {
   return SQA_OK;
 }
 
-// Per-stream workspace of the decode step, kept between calls. A decode step
-// runs every token, and a stream-ordered allocation and release per call cost
-// about 2.5 us of device time per step and made the host wait for the device
-// (about 270 us per call while earlier work was still running), so the
-// workspace stays with its stream instead: calls on one stream run in order,
-// so each finds the previous one's use finished. A larger request releases the
-// old buffer on the stream (work in flight still uses it) and takes a new one.
-// Buffers are held until the process ends: a few hundred KB to a few MB per
-// stream for decode shapes.
+// Per-stream workspace, kept between calls. A stream-ordered allocation and
+// release per call cost about 2.5 us of device time (a decode step takes about
+// 60 us), and while the pool grows they make the host wait for the device
+// (about 270 us per call with earlier work still running). So a workspace of
+// up to kStreamWsMax bytes stays with its stream instead: calls on one stream
+// run in order, so each finds the previous one's use finished. A larger
+// request takes a new buffer of at least twice the size; the old one is kept
+// too, never freed, since a call on the same stream from another host thread
+// may still be about to launch work on it (at most twice the largest
+// workspace per stream in all). Buffers are held until the process ends.
+constexpr size_t kStreamWsMax = SQA_STREAM_WORKSPACE_MAX;
 std::mutex g_stream_ws_mu;
-struct StreamWs { void* ptr; size_t bytes; };
+struct StreamWs { void* ptr; size_t bytes; };   // the current buffer; earlier ones stay allocated
 std::unordered_map<hipStream_t, StreamWs> g_stream_ws;
 
 sqa_status stream_workspace(hipStream_t stream, size_t bytes, void** out) {
@@ -202,35 +204,35 @@ sqa_status stream_workspace(hipStream_t stream, size_t bytes, void** out) {
   }
   hipMemPool_t pool;
   SQA_TRY(pool_for(stream, &pool));
-  if (w.ptr) {
-    const hipError_t e = hipFreeAsync(w.ptr, stream);
-    w.ptr = nullptr;
-    w.bytes = 0;
-    if (e != hipSuccess) return fail_hip(e, "workspace release");
-  }
+  const size_t want = std::min(kStreamWsMax, std::max(bytes, 2 * w.bytes));
   void* p = nullptr;
-  const hipError_t e = hipMallocFromPoolAsync(&p, bytes, pool, stream);
+  const hipError_t e = hipMallocFromPoolAsync(&p, want, pool, stream);
   if (e != hipSuccess) return fail_hip(e, "workspace allocation");
   w.ptr = p;
-  w.bytes = bytes;
+  w.bytes = want;
   *out = p;
   return SQA_OK;
 }
 
-// Stream-ordered scratch from the device's pool, released on the same stream.
-struct PoolScratch {
+// The workspace of one call: the stream's kept buffer up to kStreamWsMax
+// bytes, else stream-ordered memory from the device's pool, released on the
+// same stream after the call's launches.
+struct Workspace {
   void* ptr = nullptr;
   hipStream_t stream = nullptr;
+  bool pooled = false;
   sqa_status acquire(size_t bytes, hipStream_t s) {
+    stream = s;
+    if (bytes <= kStreamWsMax) return stream_workspace(s, bytes, &ptr);
     hipMemPool_t pool;
     SQA_TRY(pool_for(s, &pool));
     const hipError_t e = hipMallocFromPoolAsync(&ptr, bytes, pool, s);
-    if (e != hipSuccess) { ptr = nullptr; return fail_hip(e, "scratch allocation"); }
-    stream = s;
+    if (e != hipSuccess) { ptr = nullptr; return fail_hip(e, "workspace allocation"); }
+    pooled = true;
     return SQA_OK;
   }
   hipError_t release() {
-    if (!ptr) return hipSuccess;
+    if (!pooled || !ptr) return hipSuccess;
     const hipError_t e = hipFreeAsync(ptr, stream);
     ptr = nullptr;
     return e;
@@ -318,6 +320,7 @@ sqa_status forward_impl(const void* x, const void* Wq, const void* Wk, const voi
   const int64_t off_ord = off_w3 + round256((int64_t)sqa::out_wt_bytes(dtype, H_q * d_head, d_model));
   const int64_t total = off_ord + (lens ? round256((int64_t)sqa::attention_order_bytes(B, N, H_q)) : 0);
   void* ws = nullptr;
+  Workspace wsp;
   hipError_t e = hipSuccess;
   if (no_alloc) {
     if ((uint64_t)total > (uint64_t)SQA_NOALLOC_SCRATCH_BYTES) {
@@ -328,10 +331,8 @@ sqa_status forward_impl(const void* x, const void* Wq, const void* Wk, const voi
     }
     SQA_TRY(noalloc_scratch(stream, &ws));
   } else {
-    hipMemPool_t pool;
-    SQA_TRY(pool_for(stream, &pool));
-    e = hipMallocFromPoolAsync(&ws, (size_t)total, pool, stream);
-    if (e != hipSuccess) return fail_hip(e, "workspace allocation");
+    SQA_TRY(wsp.acquire((size_t)total, stream));
+    ws = wsp.ptr;
   }
   char* base = (char*)ws;
   void *q = base, *k = base + off_k, *vt = base + off_v, *a = base + off_a;
@@ -357,7 +358,7 @@ sqa_status forward_impl(const void* x, const void* Wq, const void* Wk, const voi
   if (e == hipSuccess)
     e = sqa::launch_output_projection(dtype, a, Wo, w3, out, B * N, H_q * d_head, d_model, lens, N,
                                       stream);
-  const hipError_t ef = no_alloc ? hipSuccess : hipFreeAsync(ws, stream);
+  const hipError_t ef = wsp.release();
   if (e != hipSuccess) return fail_hip(e, "kernel launch");
   if (ef != hipSuccess) return fail_hip(ef, "workspace release");
   return ok();
@@ -409,7 +410,7 @@ sqa_status backward_impl(const void* x, const void* Wq, const void* Wk, const vo
         return fail(SQA_ERR_INVALID_ARG, "two outputs overlap");
   }
   if (saved) SQA_TRY(check_saved(saved, saved_bytes, s, dtype, outs, outb, 5));
-  PoolScratch ws;
+  Workspace ws;
   SQA_TRY(ws.acquire(sqa::backward_workspace_bytes(dtype, B, N, z.Np, d_model, H_q, H_kv, d_head,
                                                    saved != nullptr),
                      stream));
@@ -473,7 +474,7 @@ sqa_status sqa_qkv_projection(const void* x, const void* Wq, const void* Wk, con
       if (overlap(outs[i], outb[i], outs[j], outb[j]))
         return fail(SQA_ERR_INVALID_ARG, "q, k and vt must not overlap");
   }
-  PoolScratch wt;
+  Workspace wt;
   SQA_TRY(wt.acquire(sqa::qkv_wt_bytes(dtype, d_model, H_q, H_kv, d_head), stream));
   hipError_t e = sqa::launch_qkv_projection(dtype, x, Wq, Wk, Wv, wt.ptr, q, k, vt, B, N, z.Np,
                                             d_model, H_q, H_kv, d_head, nullptr, stream);
@@ -522,7 +523,7 @@ sqa_status sqa_output_projection(const void* a, const void* Wo, void* out, int64
   if (overlap(out, (size_t)(M * d_model) * es, a, (size_t)(M * K) * es) ||
       overlap(out, (size_t)(M * d_model) * es, Wo, (size_t)(K * d_model) * es))
     return fail(SQA_ERR_INVALID_ARG, "out overlaps a or Wo");
-  PoolScratch wt;
+  Workspace wt;
   SQA_TRY(wt.acquire(sqa::out_wt_bytes(dtype, K, d_model), stream));
   hipError_t e = sqa::launch_output_projection(dtype, a, Wo, wt.ptr, out, M, K, d_model, nullptr, 1,
                                                stream);
@@ -643,9 +644,9 @@ sqa_status sqa_decode_step(const void* x_new, const void* Wq, const void* Wk, co
   const int64_t scratch_b = (int64_t)sqa::decode_partial_bytes(B, H_q, H_kv, N_max, d_head);
   const int64_t off_a = round256(qa_b), off_p = off_a + round256(qa_b);
   const int64_t total = off_p + round256(scratch_b);
-  void* ws = nullptr;
-  SQA_TRY(stream_workspace(stream, (size_t)total, &ws));
-  char* base = (char*)ws;
+  Workspace ws;
+  SQA_TRY(ws.acquire((size_t)total, stream));
+  char* base = (char*)ws.ptr;
   void *q = base, *a = base + off_a, *part = base + off_p;
   hipError_t e;
   e = sqa::launch_decode_qkv(dtype, x_new, Wq, Wk, Wv, pos, q, k_cache, v_cache, B, d_model, H_q,
@@ -660,7 +661,9 @@ sqa_status sqa_decode_step(const void* x_new, const void* Wq, const void* Wk, co
     e = fused ? sqa::launch_decode_merge_out(dtype, part, pos, Wo, out, B, N_max, H_q, H_kv, d_head,
                                              d_model, stream)
               : sqa::launch_decode_out(dtype, a, Wo, out, B, H_q * d_head, d_model, stream);
+  const hipError_t ef = ws.release();
   if (e != hipSuccess) return fail_hip(e, "kernel launch");
+  if (ef != hipSuccess) return fail_hip(ef, "workspace release");
   return ok();
 }
 
