@@ -250,6 +250,8 @@ def run_decode(w: wl.Workload, steps: int, warmup: int, torch, sqa, dev):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     kernel_us = decode_kernel_us(torch, step, steps)
+    if kernel_us is not None and kernel_us > ms * 1e3 * 1.02:
+        kernel_us = None   # not a sum of this step's kernels
     cache_bytes = 2 * w.B * w.H_kv * w.N * w.d_head * es
     weight_bytes = (w.d_model * (w.H_q + 2 * w.H_kv) * w.d_head + w.H_q * w.d_head * w.d_model) * es
     io_bytes = 2 * w.B * w.d_model * es
@@ -267,9 +269,11 @@ def run_decode(w: wl.Workload, steps: int, warmup: int, torch, sqa, dev):
 
 def decode_kernel_us(torch, step, steps: int):
     """Device time of the decode step's own kernels per step (the sum of their
-    durations, without the gaps between launches or the workspace allocation),
-    from torch's profiler over `steps` more steps. The profiler records every
-    HIP kernel of the process, the library's included."""
+    durations, without the gaps between launches), from torch's profiler over
+    `steps` more steps. The profiler records every HIP kernel of the process,
+    the library's included. None unless it saw the same number of kernels in
+    every step (3 or 4 launches); under another profiler (rocprofv3) it sees
+    only some."""
     try:
         from torch.profiler import ProfilerActivity, profile
         torch.cuda.synchronize()
@@ -277,10 +281,14 @@ def decode_kernel_us(torch, step, steps: int):
             for _ in range(steps):
                 step()
             torch.cuda.synchronize()
-        total = sum(getattr(ev, "device_time_total", 0.0) for ev in prof.key_averages())
+        kernels = [ev for ev in prof.key_averages() if getattr(ev, "device_time_total", 0.0) > 0]
+        total = sum(ev.device_time_total for ev in kernels)
+        launches = sum(ev.count for ev in kernels)
     except Exception:   # profiler unavailable: report the step time only
         return None
-    return total / steps if total > 0 else None
+    if total <= 0 or launches not in (3 * steps, 4 * steps):
+        return None
+    return total / steps
 
 
 def run_backward(w: wl.Workload, steps: int, warmup: int, torch, sqa, dev):

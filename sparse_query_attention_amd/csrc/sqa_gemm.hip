@@ -469,8 +469,11 @@ hipError_t transpose(const T* w0, int w0n, const T* w1, int w1n, const T* w2, in
   return hipGetLastError();
 }
 
-// The tiling of a forward projection: large tiles for bf16 (their 128 KB ring
-// would not fit the LDS with fp32 operands), the 128x128 tiling otherwise.
+// The tiling of the dense products over all tokens (the forward projections,
+// dO = dY Wo^T and dX): large tiles for bf16 (their 128 KB ring would not fit
+// the LDS with fp32 operands), the 128x128 tiling otherwise. The split-K
+// weight gradients keep 128x128 tiles: larger ones would need 2-4x the fp32
+// partial sums for the same number of workgroups.
 template <typename T>
 using ProjTiles = typename std::conditional<sizeof(T) == 2, LargeTiles, SmallTiles>::type;
 
@@ -515,7 +518,7 @@ hipError_t out_impl(const void* a, const void* wo, void* wt, void* out, int64_t 
 template <typename T>
 hipError_t heads_impl(const void* x, const void* wt, void* out, int64_t B, int64_t N, int64_t Np,
                       int64_t K, int64_t ncols, int64_t d, hipStream_t stream) {
-  using TL = SmallTiles;
+  using TL = ProjTiles<T>;
   const int64_t n_rb = B * Np / TL::BM, n_ct = (ncols + TL::BN - 1) / TL::BN;
   if (!grid_ok(n_rb, n_ct)) return hipErrorInvalidConfiguration;
   PaddedRows<T> rows{(const T*)x, N, Np, (int)K};
@@ -530,7 +533,7 @@ hipError_t heads_impl(const void* x, const void* wt, void* out, int64_t B, int64
 template <typename T>
 hipError_t unpad_impl(const void* a, const void* wt, void* out, int64_t B, int64_t N, int64_t Np,
                       int64_t K, int64_t ncols, hipStream_t stream) {
-  using TL = SmallTiles;
+  using TL = ProjTiles<T>;   // Np is a multiple of 256: no tile spans two sequences
   const int64_t n_rb = B * Np / TL::BM, n_ct = (ncols + TL::BN - 1) / TL::BN;
   if (!grid_ok(n_rb, n_ct)) return hipErrorInvalidConfiguration;
   DenseRows<T> rows{(const T*)a, B * Np, (int)K};
