@@ -240,6 +240,36 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
   // load lands at 16*L bytes past the load's LDS base, so the source address
   // chosen per lane realises the key permutation and the chunk swizzle. The
   // tile's 1 KB loads (K first, then V^T) are split evenly over the waves.
+  // bf16 loads through buffer resources over this head's K and V^T: a 32-bit
+  // per-lane offset fixed for the whole kernel and the tile's position as a
+  // scalar offset. That keeps one VGPR per load instead of a 64-bit address
+  // (the 4-wave form issues four loads per wave and spilled with addresses),
+  // and buffer loads count only in vmcnt, so the compiler's waits for the LDS
+  // fragment reads stay exact (with a global_load_lds in flight it waits for
+  // every LDS read). A head's K or V^T holds at most 2^31 bytes in bf16
+  // (N <= 2^24, d_head <= 64), so every offset, and the tile's scalar offset
+  // k0 * D * 2 < 2^31, fits; the resources take the whole 32-bit range as
+  // their size, which the in-range offsets never reach. fp32 heads can exceed
+  // 32-bit offsets and keep 64-bit addresses.
+  [[maybe_unused]] uint32_t loff[INS];
+  [[maybe_unused]] __amdgpu_buffer_rsrc_t rsK, rsV;
+  if constexpr (sizeof(T) == 2) {
+    rsK = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, -1, 0x00020000);
+    rsV = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, -1, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < INS; ++i) {
+      const int ins = wave * INS + i;
+      if (ins < K_INS) {
+        const int pos = ins * 64 + lane;
+        const int r = pos / KCPR, slot = pos % KCPR;
+        loff[i] = (uint32_t)((swap23(r) * D + (slot ^ swz<KCPR>(r)) * EPC) * (int)sizeof(T));
+      } else {
+        const int pos = (ins - K_INS) * 64 + lane;
+        const int r = pos / VCPR, slot = pos % VCPR;
+        loff[i] = (uint32_t)r * (uint32_t)p.Np * (uint32_t)sizeof(T) + (uint32_t)((slot ^ swz<VCPR>(r)) * EPC * (int)sizeof(T));
+      }
+    }
+  }
   auto issue = [&](int t) {
     if (t >= n_tiles) return;
     T* kb = smem + (t % NBUF) * TILE;
@@ -247,7 +277,14 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
 #pragma unroll
     for (int i = 0; i < INS; ++i) {
       const int ins = wave * INS + i;            // 0 .. 2*K_INS-1
-      if (ins < K_INS) {
+      if constexpr (sizeof(T) == 2) {
+        if (ins < K_INS)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsK, (lds_ptr)(kb + ins * 64 * EPC), 16, (int)loff[i],
+                                                   k0 * D * (int)sizeof(T), 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsV, (lds_ptr)(kb + K_ELEMS + (ins - K_INS) * 64 * EPC), 16,
+                                                   (int)loff[i], k0 * (int)sizeof(T), 0, 0);
+      } else if (ins < K_INS) {
         const int pos = ins * 64 + lane;
         const int r = pos / KCPR, slot = pos % KCPR;
         const T* src = Kh + (int64_t)(k0 + swap23(r)) * D + (slot ^ swz<KCPR>(r)) * EPC;
