@@ -38,6 +38,7 @@
 
 #include <atomic>
 #include <type_traits>
+#include <utility>
 
 #include "sqa_device.h"
 #include "sqa_internal.h"
@@ -47,6 +48,18 @@ namespace {
 
 constexpr int KT = 64;       // keys per LDS tile (two 32-key blocks)
 constexpr int NBUF = 4;      // LDS tile ring: in use, visible next, NBUF-2 in flight
+
+// A block index known only at run time (the other form is
+// std::integral_constant<int, j mod 2*NBUF>).
+struct DynBlock {};
+
+// f(std::integral_constant<int, i>) for i = I .. N-1, in order.
+template <int I, int N, typename F> __device__ inline void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
 constexpr int QB = 2;             // 32-query MFMA column blocks per wave
 constexpr int FETCH_AHEAD = 2;    // LDS fragments read ahead of their first MFMA
 constexpr int QW = 32 * QB;       // query rows per wave
@@ -299,20 +312,30 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
     }
   };
 
+  // The ring slot and the parity of block j, from j itself or, as
+  // std::integral_constant<int, M>, from M = j mod 2*NBUF known at compile
+  // time. Then a fragment's LDS address is a lane part the loop does not
+  // change plus a constant (the slot's byte offset fits a ds_read's 16-bit
+  // immediate), and the step spends no VALU on addresses.
+  auto slot_par = [&](int j, auto jm) {
+    if constexpr (std::is_same_v<decltype(jm), DynBlock>) return std::pair<int, int>{(j >> 1) % NBUF, j & 1};
+    else return std::pair<int, int>{(decltype(jm)::value >> 1) % NBUF, decltype(jm)::value & 1};
+  };
   // K fragment (A operand of S^T) of global 32-key block j, k-step st.
-  auto kfrag = [&](int j, int st) -> Frag {
-    const int r = (j & 1) * 32 + col;
+  auto kfrag = [&](int j, int st, auto jm) -> Frag {
+    const auto [sl, par] = slot_par(j, jm);
+    const int r = par * 32 + col;
     const int e = st * MF::KS + grp * MF::E;
-    const int off = ((j >> 1) % NBUF) * TILE + r * D + (((e / EPC) ^ swz<KCPR>(r)) * EPC) + e % EPC;
+    const int off = sl * TILE + r * D + (((e / EPC) ^ swz<KCPR>(r)) * EPC) + e % EPC;
     return *reinterpret_cast<const Frag*>(&smem[off]);
   };
   // V^T fragment (A operand of O^T) of block j: head dims 32*nb + col,
   // keys kk.. of the block (8 consecutive for bf16, one for fp32).
-  auto vfrag = [&](int j, int nb, int kk) -> Frag {
+  auto vfrag = [&](int j, int nb, int kk, auto jm) -> Frag {
+    const auto [sl, par] = slot_par(j, jm);
     const int r = nb * 32 + col;
-    const int key = (j & 1) * 32 + kk;
-    const int off = ((j >> 1) % NBUF) * TILE + K_ELEMS + r * KT +
-                    (((key / EPC) ^ swz<VCPR>(r)) * EPC) + key % EPC;
+    const int key = par * 32 + kk;
+    const int off = sl * TILE + K_ELEMS + r * KT + (((key / EPC) ^ swz<VCPR>(r)) * EPC) + key % EPC;
     return *reinterpret_cast<const Frag*>(&smem[off]);
   };
 
@@ -328,12 +351,12 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
 
   // S^T of block j for both query blocks. Register r of lane group grp holds
   // key 32*j + 16*(r/8) + 8*grp + r%8 (after the LDS row swap).
-  auto qk = [&](int j, f32x16 (&s)[QB]) {
+  auto qk = [&](int j, f32x16 (&s)[QB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) s[qb] = f32x16{};
 #pragma unroll
     for (int st = 0; st < D / MF::KS; ++st) {
-      const Frag a = kfrag(j, st);
+      const Frag a = kfrag(j, st, DynBlock{});
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) s[qb] = MF::run(a, qf[qb][st], s[qb]);
     }
@@ -353,13 +376,13 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
   };
 
   // O^T += V^T P^T for block j, with P in sp.
-  auto pv = [&](int j, const f32x16 (&sp)[QB]) {
+  auto pv = [&](int j, const f32x16 (&sp)[QB]) __attribute__((always_inline)) {
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
       for (int half = 0; half < 2; ++half)
 #pragma unroll
         for (int nb = 0; nb < D / 32; ++nb) {
-          const Frag a = vfrag(j, nb, half * 16 + grp * 8);
+          const Frag a = vfrag(j, nb, half * 16 + grp * 8, DynBlock{});
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) o[qb][nb] = MF::run(a, pfrag(sp[qb], half), o[qb][nb]);
         }
@@ -368,7 +391,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
       for (int st = 0; st < 16; ++st)
 #pragma unroll
         for (int nb = 0; nb < D / 32; ++nb) {
-          const Frag a = vfrag(j, nb, 16 * (st >> 3) + 8 * grp + (st & 7));
+          const Frag a = vfrag(j, nb, 16 * (st >> 3) + 8 * grp + (st & 7), DynBlock{});
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) o[qb][nb] = MF::run(a, pfrag(sp[qb], st), o[qb][nb]);
         }
@@ -383,7 +406,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
 
   // p = exp2(s*c - m_ref) in place, packed as PV consumes it, and each lane's
   // block sums (taken on the rounded bf16 values that PV multiplies).
-  auto exponentiate = [&](f32x16 (&s)[QB], float (&bsum)[QB]) {
+  auto exponentiate = [&](f32x16 (&s)[QB], float (&bsum)[QB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const float mb = m_ref[qb];
@@ -414,7 +437,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
     }
   };
 
-  auto mask = [&](f32x16 (&s)[QB], int j) {
+  auto mask = [&](f32x16 (&s)[QB], int j) __attribute__((always_inline)) {
     const int k0b = j * 32;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -428,7 +451,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
   };
 
   // Each row's max over the scores s of one block (-inf if all are masked).
-  auto block_max = [&](const f32x16 (&s)[QB], float (&m)[QB]) {
+  auto block_max = [&](const f32x16 (&s)[QB], float (&m)[QB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float v = max3(s[qb][0], s[qb][1], s[qb][2]);
@@ -441,7 +464,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
 
   // Raise each row's reference to MARGIN binades above the max of the scores
   // s (never lower it), rescaling O and l by the change.
-  auto rebase = [&](const f32x16 (&s)[QB]) {
+  auto rebase = [&](const f32x16 (&s)[QB]) __attribute__((always_inline)) {
     float m[QB];
     block_max(s, m);
 #pragma unroll
@@ -458,7 +481,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
   // The exact fallback of block j's softmax, used only when its sums showed
   // that m_ref fell too far behind for it (before its PV product). Block j's
   // keys are still in the LDS ring, so its scores are recomputed, not kept.
-  auto rescale = [&](int j, f32x16 (&s)[QB], float (&bsum)[QB], bool masked) {
+  auto rescale = [&](int j, f32x16 (&s)[QB], float (&bsum)[QB], bool masked) __attribute__((always_inline)) {
     qk(j, s);
     if (masked) mask(s, j);
     rebase(s);
@@ -470,7 +493,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
   // symmetrically, so they are exactly -P. (Flipping the sign bits of the
   // packed pairs afterwards, an xor on the f32 vector slots, was miscompiled:
   // the slots came out as copies of the first pair.)
-  auto neg_weights = [&](f32x16 (&s)[QB]) {
+  auto neg_weights = [&](f32x16 (&s)[QB]) __attribute__((always_inline)) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     typedef float f32x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
@@ -497,7 +520,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
   // MFMA pipe and the VALU stay busy together and the register set stays what
   // the layout implies. S(j+1) of the last block and P(-1) = 0 are padding
   // that keeps each step straight-line.
-  auto step_interleaved = [&](int j, f32x16 (&sc)[QB], f32x16 (&sn)[QB], float (&bsum)[QB]) {
+  auto step_interleaved = [&](int j, f32x16 (&sc)[QB], f32x16 (&sn)[QB], float (&bsum)[QB], auto jm) __attribute__((always_inline)) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     constexpr int NB = D / 32, NST = D / MF::KS;
@@ -511,10 +534,17 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
     auto fetch = [&](int u) {
       if (u < N_PV) {
         const int half = u / (NB * QB), nb = (u % (NB * QB)) / QB;
-        vf[half][nb] = vfrag(jp, nb, half * 16 + grp * 8);
+        if constexpr (std::is_same_v<decltype(jm), DynBlock>)
+          vf[half][nb] = vfrag(jp, nb, half * 16 + grp * 8, jm);
+        else   // a static step is never block 0, so jp = j - 1
+          vf[half][nb] = vfrag(jp, nb, half * 16 + grp * 8,
+                               std::integral_constant<int, (decltype(jm)::value + 2 * NBUF - 1) % (2 * NBUF)>{});
       } else if (u < NG) {
         const int st = (u - N_PV) / QB;
-        kf[st] = kfrag(j + 1, st);
+        if constexpr (std::is_same_v<decltype(jm), DynBlock>)
+          kf[st] = kfrag(j + 1, st, jm);
+        else
+          kf[st] = kfrag(j + 1, st, std::integral_constant<int, (decltype(jm)::value + 1) % (2 * NBUF)>{});
       }
     };
     float acc[QB][2];
@@ -578,13 +608,13 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
   // exact max, and block j, exponentiated against the old reference, is
   // redone from its scores. s_cur serves as scratch; s_next keeps S(j+1).
   auto run_step = [&](int j, f32x16 (&s_cur)[QB], f32x16 (&s_next)[QB], auto mask_on,
-                      float (&bsum)[QB]) {
+                      float (&bsum)[QB], auto jm) __attribute__((always_inline)) {
     const bool masked =
         decltype(mask_on)::value && (j * 32 + 32 > L || (p.causal && j * 32 + 31 > qw));
     if (masked) mask(s_cur, j);
     float bcur[QB];
     if constexpr (sizeof(T) == 2) {
-      step_interleaved(j, s_cur, s_next, bcur);
+      step_interleaved(j, s_cur, s_next, bcur, jm);
       bool redo = false;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) redo |= !(bsum[qb] <= SUM_LIMIT);
@@ -616,7 +646,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
 
   // After a wave's last step, block j (in s_cur): its pending check (bf16),
   // then its PV product.
-  auto finish = [&](int j, f32x16 (&s_cur)[QB], float (&bsum)[QB]) {
+  auto finish = [&](int j, f32x16 (&s_cur)[QB], float (&bsum)[QB]) __attribute__((always_inline)) {
     if constexpr (sizeof(T) == 2) {
       bool redo = false;
 #pragma unroll
@@ -653,7 +683,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
   // Before odd block 2t+1: tile t+1 must be visible (loads of tiles t+2.. may
   // still be in flight), and tile t-1 is no longer read, so its slot takes
   // tile t+NBUF-1.
-  auto advance = [&](int j) {
+  auto advance = [&](int j) __attribute__((always_inline)) {
     const int t = j >> 1;
     wait_vmcnt_tiles<VM_PER_TILE, NBUF - 3>(min(NBUF - 3, max(0, n_tiles - (t + 2))));
     __syncthreads();
@@ -666,21 +696,39 @@ __global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
   // (jc <= nblk_w). A wave's last block is finished right after its step: the
   // next advance() but one recycles that block's tile.
   const int jc = min(nblk, min(L / 32, p.causal ? qw / 32 : nblk)) & ~1;
+  // The mask-free loop runs its first 2*NBUF blocks with the slot from j (block
+  // 0's step reads block 0 for its padding PV), then NBUF tiles per iteration
+  // with every slot known at compile time, then the rest with the slot from j.
   int j = 0;
-  for (; j < jc; j += 2) {
-    run_step(j, sA, sB, std::false_type{}, bsum);
+  for (; j < jc && j < 2 * NBUF; j += 2) {
+    run_step(j, sA, sB, std::false_type{}, bsum, DynBlock{});
     advance(j);   // j + 1 < jc <= nblk
-    run_step(j + 1, sB, sA, std::false_type{}, bsum);
+    run_step(j + 1, sB, sA, std::false_type{}, bsum, DynBlock{});
+  }
+  if constexpr (sizeof(T) == 2) {
+    for (; j + 2 * NBUF <= jc; j += 2 * NBUF) {   // j % (2 * NBUF) == 0
+      static_for<0, NBUF>([&](auto tc) {
+        constexpr int m = 2 * decltype(tc)::value;
+        run_step(j + m, sA, sB, std::false_type{}, bsum, std::integral_constant<int, m>{});
+        advance(j + m);
+        run_step(j + m + 1, sB, sA, std::false_type{}, bsum, std::integral_constant<int, m + 1>{});
+      });
+    }
+  }
+  for (; j < jc; j += 2) {
+    run_step(j, sA, sB, std::false_type{}, bsum, DynBlock{});
+    advance(j);
+    run_step(j + 1, sB, sA, std::false_type{}, bsum, DynBlock{});
   }
   for (; j < nblk; j += 2) {
     if (j < nblk_w) {
-      run_step(j, sA, sB, std::true_type{}, bsum);
+      run_step(j, sA, sB, std::true_type{}, bsum, DynBlock{});
       if (j + 1 == nblk_w) finish(j, sA, bsum);
     }
     if (j + 1 < nblk) {
       advance(j);
       if (j + 1 < nblk_w) {
-        run_step(j + 1, sB, sA, std::true_type{}, bsum);
+        run_step(j + 1, sB, sA, std::true_type{}, bsum, DynBlock{});
         if (j + 2 == nblk_w) finish(j + 1, sB, bsum);
       }
     }
