@@ -301,12 +301,22 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
   }
   const T* arr_base = (const T*)(arr == 0 ? p.q : arr == 1 ? p.dO : arr == 2 ? p.qt : p.dOt);
   const int which = wave >> 2, part = wave & 3;   // row statistics: -lse/c (waves 0-3), -D (4-7)
-  auto issue = [&](int w) {
+  // Items are issued in order, so the next one's query tile and head are
+  // stepped along instead of divided out of its index (item_tile, item_head):
+  // the scalar work per item shrinks. it_soff = (b*H_q + head) * Np, the head's
+  // offset in the row statistics; times D it is the head's element offset in
+  // Q, dO ([.., Np, D]) and in Q^T, dO^T ([.., D, Np]) alike.
+  int next_issue = 0;
+  int it_tile = n0 > 0 ? (p.causal ? qt_end - 1 : 0) : first1, it_head = 0;
+  const int64_t it_soff0 = ((int64_t)b * p.H_q + (int64_t)j * p.g) * p.Np;
+  int64_t it_soff = it_soff0;
+  auto issue_next = [&]() {
+    const int w = next_issue++;
     if (w >= n_work) return;
-    const int i = j * p.g + item_head(w), q0 = item_tile(w) * BT;
-    const int64_t hq = (int64_t)b * p.H_q + i;
+    const int q0 = it_tile * BT;
+    const int64_t hoff = it_soff * D;
     T* tb = smem + (w % NBUF) * TILE + arr * TE;
-    const T* base = arr_base + (arr < 2 ? (hq * p.Np + q0) * D : hq * D * p.Np + q0);
+    const T* base = arr_base + hoff + (arr < 2 ? (int64_t)q0 * D : (int64_t)q0);
     // Buffer loads: unlike global_load_lds, they count only in vmcnt, so the
     // compiler's waits for the LDS fragment reads in flight stay exact
     // (with a global_load_lds in flight it waits for every LDS read). The
@@ -320,10 +330,19 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(tb + li * 64 * EPC), 16, (int)loff[x], 0, 0, 0);
     }
     // row statistics: 16 values per wave
-    const float* src = (which ? p.dvec : p.nlse) + hq * p.Np + q0 + part * 16;
+    const float* src = (which ? p.dvec : p.nlse) + it_soff + q0 + part * 16;
     const __amdgpu_buffer_rsrc_t rss = __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, 64, 0x00020000);
     float* dst = reinterpret_cast<float*>(smem + (w % NBUF) * TILE + 4 * TE) + which * BT + part * 16;
     if (lane < 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(rss, (lds_ptr)dst, 4, lane * 4, 0, 0, 0);
+    // step to item w + 1 (item_tile / item_head of it)
+    if (w + 1 == n0) {
+      it_tile = first1; it_head = 0; it_soff = it_soff0;
+    } else if (++it_head == p.g) {
+      it_head = 0; it_soff = it_soff0;
+      it_tile += (w + 1 < n0 && p.causal) ? -1 : 1;
+    } else {
+      it_soff += p.Np;
+    }
   };
 
   // This wave's K and V fragments (B operands of S = Q K^T and dP = dO V^T)
@@ -370,12 +389,11 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
   // R have landed, then passes a barrier (every wave's loads of those tiles
   // are visible, and every wave is done with the tiles before F), then issues
   // the tiles whose slots that frees, up to F + NBUF - 1.
-  int next_issue = 0;
   auto sync = [&](int R, int F) {
     wait_vmcnt_tiles<VM_PER_TILE, NBUF - 2>(min(NBUF - 2, max(0, next_issue - 1 - R)));
     ring_barrier();
     const int last = min(F + NBUF - 1, n_work - 1);
-    for (; next_issue <= last; ++next_issue) issue(next_issue);
+    while (next_issue <= last) issue_next();
   };
   auto slot = [&](int x) { return (const T*)smem + (x % NBUF) * TILE; };
 
@@ -383,7 +401,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
   // the first key tile, all landed before the loop, which then waits only on
   // its own loads.
   int kw = kt0 * KPG + KPW * wave;   // this wave's first key
-  for (; next_issue < min(NBUF - 1, n_work); ++next_issue) issue(next_issue);
+  while (next_issue < min(NBUF - 1, n_work)) issue_next();
   load_kv(kw);
 #pragma unroll
   for (int nb = 0; nb < D / 32; ++nb) { dk[nb] = f32x16{}; dv[nb] = f32x16{}; }
