@@ -40,6 +40,16 @@
 namespace sqa {
 namespace {
 
+// The LDS pointer p, with a value the compiler cannot see: the address of a
+// read at a constant offset from it is then one register (p plus the lane's
+// part, computed once) and an immediate, where from a known base beyond the
+// 64 KB reach of the immediate every offset would take a register of its own.
+template <typename T> __device__ __attribute__((always_inline)) inline const T* opaque_lds(const T* p) {
+  auto q = (__attribute__((address_space(3))) const T*)p;
+  asm("" : "+v"(q));
+  return (const T*)q;
+}
+
 // f(std::integral_constant<int, i>) for i = I .. N-1, in order.
 template <int I, int N, typename F> __device__ inline void static_for(F&& f) {
   if constexpr (I < N) {
@@ -240,7 +250,6 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
   constexpr int NS = D / MF::KS;               // k-steps over the head dims
   constexpr int TE = BT * D;                   // elements of one operand tile
   constexpr int SE = 2 * BT * 4 / (int)sizeof(T);   // elements holding the rows' -lse/c and -D (fp32)
-  constexpr int TILE = 4 * TE + SE;            // Q, dO, Q^T, dO^T, row statistics
   constexpr int NBUF = 4 * TE * (int)sizeof(T) <= 32768 ? 4 : 2;   // ring slots (LDS <= 130 KB)
   constexpr int INS = TE * (int)sizeof(T) / 1024;                 // 1 KB loads per operand tile
   constexpr int IPW = 4 * INS / WAVES;                            // per wave and tile
@@ -248,8 +257,20 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
   static_assert(IPW * WAVES == 4 * INS && INS * 64 * EPC == TE, "tile split");
   // One array for every direct-load target: the compiler then sees the
   // ring's reads and the loads in flight into other slots as one object and
-  // adds no waits of its own between them.
-  __shared__ __align__(16) T smem[NBUF * TILE];
+  // adds no waits of its own between them. It is laid out by operand: the
+  // NBUF slots of Q rows, then those of dO rows, Q^T, dO^T and the row
+  // statistics. The slots of the row tiles (Q, dO) then span 64 KB, as do
+  // those of the line tiles (Q^T, dO^T), so where a slot is known at compile
+  // time a fragment read's address is a per-lane register plus an immediate.
+  __shared__ __align__(16) T smem[NBUF * (4 * TE + SE)];
+  // operand tile a (0: Q, 1: dO, 2: Q^T, 3: dO^T) of ring slot s
+  const T* line_tiles = opaque_lds<T>(smem + 2 * NBUF * TE);
+  auto tile = [&](int a, int s) __attribute__((always_inline)) {
+    return a < 2 ? (const T*)smem + (a * NBUF + s) * TE : line_tiles + ((a - 2) * NBUF + s) * TE;
+  };
+  // the rows' -lse/c (BT values), then their -D (BT values), in ring slot s
+  const float* stat_tiles = opaque_lds<float>(reinterpret_cast<const float*>(smem + 4 * NBUF * TE));
+  auto stats = [&](int s) __attribute__((always_inline)) { return stat_tiles + s * (SE * (int)sizeof(T) / 4); };
 
   const int tid = threadIdx.x, lane = tid & 63,
             wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
@@ -315,7 +336,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
     if (w >= n_work) return;
     const int q0 = it_tile * BT;
     const int64_t hoff = it_soff * D;
-    T* tb = smem + (w % NBUF) * TILE + arr * TE;
+    T* tb = smem + (arr * NBUF + w % NBUF) * TE;
     const T* base = arr_base + hoff + (arr < 2 ? (int64_t)q0 * D : (int64_t)q0);
     // Buffer loads: unlike global_load_lds, they count only in vmcnt, so the
     // compiler's waits for the LDS fragment reads in flight stay exact
@@ -332,7 +353,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
     // row statistics: 16 values per wave
     const float* src = (which ? p.dvec : p.nlse) + it_soff + q0 + part * 16;
     const __amdgpu_buffer_rsrc_t rss = __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, 64, 0x00020000);
-    float* dst = reinterpret_cast<float*>(smem + (w % NBUF) * TILE + 4 * TE) + which * BT + part * 16;
+    float* dst = reinterpret_cast<float*>(smem + 4 * NBUF * TE + (w % NBUF) * SE) + which * BT + part * 16;
     if (lane < 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(rss, (lds_ptr)dst, 4, lane * 4, 0, 0, 0);
     // step to item w + 1 (item_tile / item_head of it)
     if (w + 1 == n0) {
@@ -395,7 +416,6 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
     const int last = min(F + NBUF - 1, n_work - 1);
     while (next_issue <= last) issue_next();
   };
-  auto slot = [&](int x) { return (const T*)smem + (x % NBUF) * TILE; };
 
   // Prologue: work items 0..NBUF-2 in flight, then the K and V fragments of
   // the first key tile, all landed before the loop, which then waits only on
@@ -405,6 +425,16 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
   load_kv(kw);
 #pragma unroll
   for (int nb = 0; nb < D / 32; ++nb) { dk[nb] = f32x16{}; dv[nb] = f32x16{}; }
+  if constexpr (sizeof(T) == 2) {
+    // The line tiles of the last slot start as zeros: a pipelined run that
+    // starts at item 0 reads them as the tiles of its (absent) previous item
+    // and multiplies them by zeros, which must not meet an Inf or NaN.
+    constexpr int ZC = TE * (int)sizeof(T) / 16;   // 16-byte chunks per tile
+#pragma unroll
+    for (int a = 2; a < 4; ++a)
+      for (int x = tid; x < ZC; x += WAVES * 64)
+        reinterpret_cast<f32x4*>(smem + (a * NBUF + NBUF - 1) * TE)[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   wait_vmcnt<0>();
   __syncthreads();
 
@@ -412,8 +442,8 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
   // start from the rows' -lse/c and -D (register r: row rb + 8*(r/4) + 4*grp
   // + r%4). The probability is then exp2(c * S) and dS = P (dP - D) one
   // product, with no per-score subtraction.
-  auto init_scores = [&](const T* t, int rb, f32x16& sc, f32x16& dpc) {
-    const float* st = reinterpret_cast<const float*>(t + 4 * TE);
+  auto init_scores = [&](int s, int rb, f32x16& sc, f32x16& dpc) __attribute__((always_inline)) {
+    const float* st = stats(s);
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const f32x4 n4 = *reinterpret_cast<const f32x4*>(&st[rb + 8 * r4 + 4 * grp]);
@@ -431,10 +461,11 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
     for (int w = w0; w < w1; ++w) {
       // item w visible; every wave done with the items before it
       sync(w, w);
-      const T* Qs = slot(w);
-      const T* Os = Qs + TE;
-      const T* QTs = Qs + 2 * TE;
-      const T* OTs = Qs + 3 * TE;
+      const int sw = w % NBUF;
+      const T* Qs = tile(0, sw);
+      const T* Os = tile(1, sw);
+      const T* QTs = tile(2, sw);
+      const T* OTs = tile(3, sw);
       const int q0 = item_tile(w) * BT;
       // S and dP - D of 32-query block qs (lane = key)
       auto scores = [&](int qs, f32x16& sc, f32x16& dpc) {
@@ -444,7 +475,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
           qa[st] = row_frag<T, D>(Qs, 32 * qs + col, st, grp);
           oa[st] = row_frag<T, D>(Os, 32 * qs + col, st, grp);
         }
-        init_scores(Qs, 32 * qs, sc, dpc);
+        init_scores(sw, 32 * qs, sc, dpc);
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
           sc = MF::run(qa[st], kf[st], sc);
@@ -525,27 +556,27 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
     f32x16 sA, dA, sB, dB;           // S and dP - D of block 0 (A) and block 1 (B)
     u32x4 pA[2][2], pB[2][2];        // [P, dS][half]: bf16 pairs, B operands
     Frag fr[2 * NGP];                // the fragment of each MFMA of an iteration
-    // The fragment of MFMA u of the iteration over the tiles of items w-1
-    // (prev), w (cur) and w+1 (next).
-    auto fetch = [&](auto uc, const T* prev, const T* cur, const T* next) {
+    // The fragment of MFMA u of the iteration over the ring slots of items
+    // w-1 (prev), w (cur) and w+1 (next).
+    auto fetch = [&](auto uc, int prev, int cur, int next) __attribute__((always_inline)) {
       constexpr int u = decltype(uc)::value, ph = u / NGP, k = u % NGP;
       if constexpr (k < NGG) {
         constexpr int h = k / (2 * NB), nb = (k / 2) % NB, which = k % 2;   // 0: dV (dO^T), 1: dK (Q^T)
-        fr[u] = line_frag<T>((ph == 0 ? prev : cur) + (which ? 2 : 3) * TE, nb * 32 + col, ph == 0 ? 32 : 0, h, grp);
+        fr[u] = line_frag<T>(tile(which ? 2 : 3, ph == 0 ? prev : cur), nb * 32 + col, ph == 0 ? 32 : 0, h, grp);
       } else {
         constexpr int st = (k - NGG) / 2, which = (k - NGG) % 2;             // 0: S (Q), 1: dP (dO)
-        fr[u] = row_frag<T, D>((ph == 0 ? cur : next) + which * TE, (ph == 0 ? 32 : 0) + col, st, grp);
+        fr[u] = row_frag<T, D>(tile(which, ph == 0 ? cur : next), (ph == 0 ? 32 : 0) + col, st, grp);
       }
     };
     // dV/dK MFMA k (< NGG) of a block with packed P and dS pk
-    auto grad_mfma = [&](auto kc, const Frag& a, const u32x4 (&pk)[2][2]) {
+    auto grad_mfma = [&](auto kc, const Frag& a, const u32x4 (&pk)[2][2]) __attribute__((always_inline)) {
       constexpr int k = decltype(kc)::value, h = k / (2 * NB), nb = (k / 2) % NB, which = k % 2;
       const Frag b = __builtin_bit_cast(Frag, pk[which][h]);
       if constexpr (which == 0) dv[nb] = MF::run(a, b, dv[nb]);
       else dk[nb] = MF::run(a, b, dk[nb]);
     };
     float ex[16], ds[16];
-    auto group = [&](auto uc, const T* prev, const T* cur, const T* next) {
+    auto group = [&](auto uc, int prev, int cur, int next) __attribute__((always_inline)) {
       constexpr int u = decltype(uc)::value, ph = u / NGP, k = u % NGP;
       f32x16& s_sc = ph == 0 ? sB : sA;   // scored in this phase
       f32x16& d_sc = ph == 0 ? dB : dA;
@@ -585,35 +616,41 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
       __builtin_amdgcn_sched_barrier(0);
     };
 
-    // Prologue: tile w0 visible; scores of its block 0. Block "1 of item
-    // w0-1" is zeros, so the first phase's dV/dK MFMAs add exact zeros
-    // (reading tile w0's finite operands).
+    // Prologue: tile w0 visible; scores of its block 0. The P and dS of
+    // block "1 of item w0-1" are zeros, so the first phase's dV/dK MFMAs add
+    // exact zeros: their other operands, the tiles in the slot before w0's,
+    // hold item w0-1 (finite) or, before item 0, zeros.
     sync(w0, w0);
     {
-      const T* t0 = slot(w0);
-      init_scores(t0, 0, sA, dA);
+      const int s0 = w0 % NBUF;
+      init_scores(s0, 0, sA, dA);
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
-        sA = MF::run(row_frag<T, D>(t0, col, st, grp), kf[st], sA);
-        dA = MF::run(row_frag<T, D>(t0 + TE, col, st, grp), vf[st], dA);
+        sA = MF::run(row_frag<T, D>(tile(0, s0), col, st, grp), kf[st], sA);
+        dA = MF::run(row_frag<T, D>(tile(1, s0), col, st, grp), vf[st], dA);
       }
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int h = 0; h < 2; ++h) pB[a][h] = u32x4{0u, 0u, 0u, 0u};
-      static_for<0, FA>([&](auto uc) { fetch(uc, t0, t0, t0); });
+      static_for<0, FA>([&](auto uc) { fetch(uc, (s0 + NBUF - 1) % NBUF, s0, s0); });
     }
+    // Iteration w reads the slots of items w-1 (prev), w (cur) and w+1
+    // (next; past the loop's end, item w+1's scores are computed and
+    // dropped). There is one copy of it per slot of w, so that every slot is
+    // a compile-time constant.
     for (int w = w0; w < w1; ++w) {
       // items w and w+1 visible; every wave done with the items before w-1
       sync(w + 1, w - 1);
-      const T* cur = slot(w);
-      const T* prev = w == w0 ? cur : slot(w - 1);
-      const T* next = slot(w + 1);   // past the loop's end: scores computed and dropped
-      static_for<0, 2 * NGP>([&](auto uc) { group(uc, prev, cur, next); });
+      const int m = w % NBUF;
+      static_for<0, NBUF>([&](auto mc) {
+        constexpr int c = decltype(mc)::value;
+        if (m == c) static_for<0, 2 * NGP>([&](auto uc) { group(uc, (c + NBUF - 1) % NBUF, c, (c + 1) % NBUF); });
+      });
     }
     // Epilogue: dV/dK of block 1 of the last item (its first FA fragments
     // were read in the last iteration).
-    const T* lt = slot(w1 - 1);
+    const int lt = (w1 - 1) % NBUF;
     static_for<0, NGG>([&](auto kc) {
       constexpr int k = decltype(kc)::value;
       if constexpr (k >= FA) fetch(kc, lt, lt, lt);
