@@ -613,6 +613,11 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
           p_sm[1][r / 8][(r % 8) / 2] = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{ds[r - 1], ds[r]}, bf16x2));
         }
       }
+      // within the group: the MFMA, the LDS reads, then the VALU work, so
+      // that the MFMAs of consecutive groups never issue back to back
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);
       __builtin_amdgcn_sched_barrier(0);
     };
 
@@ -921,6 +926,327 @@ __global__ __launch_bounds__(256, 2) void bwd_dq(BwdParams p) {
   store_dq(qw);
 }
 
+// dQ for bf16 at d_head = 64, as a software pipeline: workgroup = (query
+// tiles of 256 queries, head i, batch b) as in bwd_dq, but 8 waves of 32
+// queries (two waves per SIMD at up to 256 VGPRs). The key-side tiles (K, V
+// and K^T) of each 64-key tile come through a ring of NBUF LDS slots, laid
+// out by operand as in bwd_dkdv so that a fragment read whose slot is known at
+// compile time is a lane register plus an immediate. The rows' statistics sit
+// in two accumulator tiles (every register of a lane holds its query's -lse/c,
+// or its -D), the start of every S^T and dP^T chain, so that P = exp2(c S) and
+// dS = P (dP - D) are one product each. The work items are the key tiles, in
+// bwd_dq's order; those that need a mask run one 32-key block at a time, the
+// others through a pipeline like bwd_dkdv's run_clear: iteration t (a key
+// tile, two 32-key blocks) runs two phases of 2*NS + 2*D/32 MFMAs each,
+//   phase 0: S^T and dP^T of block 1 of tile t, then dQ of block 1 of tile
+//            t-1; softmax gradient of block 0 of tile t
+//   phase 1: S^T and dP^T of block 0 of tile t+1, then dQ of block 0 of tile
+//            t; softmax gradient of block 1 of tile t
+// and each MFMA forms a group with a share of the phase's VALU work and the
+// LDS read of the fragment FA groups ahead.
+template <int D>
+__global__ __launch_bounds__(512, 2) void bwd_dq_pipe(BwdParams p) {
+  using T = bf16;
+  using MF = Mfma<T>;
+  using Frag = typename MF::Frag;
+  constexpr int WAVES = 8;
+  constexpr int EPC = 8;
+  constexpr int RC = D / EPC, LC = BT / EPC;   // chunks per row [64][D], per line [D][64]
+  constexpr int NS = D / MF::KS;               // k-steps over the head dims
+  constexpr int NB = D / 32;                   // 32-dim blocks of dQ
+  constexpr int TE = BT * D;                   // elements of one operand tile
+  constexpr int NBUF = 6;                      // ring slots: tiles t-1, t, t+1 and three in flight
+  constexpr int INS = TE * 2 / 1024;           // 1 KB loads per operand tile
+  constexpr int IPW = 3 * INS / WAVES;         // per wave and tile
+  static_assert(IPW * WAVES == 3 * INS && INS * 64 * EPC == TE, "tile split");
+  __shared__ __align__(16) T smem[3 * NBUF * TE];   // K rows, V rows, K^T lines; NBUF slots each
+
+  const int tid = threadIdx.x, lane = tid & 63,
+            wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+  const int col = lane & 31, grp = lane >> 5;
+  const int n_qt = p.Np / 256;
+  const int n_units = p.causal ? (n_qt + 1) / 2 : n_qt;
+  const int pr = blockIdx.x % n_units, bi = blockIdx.x / n_units;
+  const int i = bi % p.H_q, b = bi / p.H_q;
+  const int j = i / p.g;
+  const int qt0 = pr, qt1 = n_qt - 1 - pr;
+  const int64_t hq = (int64_t)b * p.H_q + i, hk = (int64_t)b * p.H_kv + j;
+
+  // Items: the key tiles of query tile qt0 (phase 0), then, causal and
+  // qt1 != qt0, those of query tile qt1 (phase 1) in reverse.
+  auto kv_tiles = [&](int qt) { return ((p.causal ? min(p.N, qt * 256 + 256) : p.N) + BT - 1) / BT; };
+  const int n0 = kv_tiles(qt0);
+  const int nt1 = p.causal && qt1 != qt0 ? kv_tiles(qt1) : 0;
+  const int n_items = n0 + nt1;
+  auto item_tile = [&](int t) { return t < n0 ? t : nt1 - 1 - (t - n0); };
+  const T* Kh = (const T*)p.k + hk * p.Np * D;
+  const T* Vh = (const T*)p.v + hk * p.Np * D;
+  const T* KTh = (const T*)p.kt + hk * D * p.Np;
+
+  // operand tile a (0: K, 1: V, 2: K^T) of ring slot s
+  const T* v_tiles = opaque_lds<T>(smem + NBUF * TE);
+  const T* line_tiles = opaque_lds<T>(smem + 2 * NBUF * TE);
+  auto tile = [&](int a, int s) __attribute__((always_inline)) {
+    return (a == 0 ? (const T*)smem : a == 1 ? v_tiles : line_tiles) + s * TE;
+  };
+
+  // Loads of item t into ring slot t % NBUF: load `ins` (of 3*INS) covers 64
+  // 16-byte chunks of operand tile ins / INS; lane L's chunk lands at position
+  // 64*(ins % INS) + L, which holds chunk (c ^ swz(row)) of its row. The
+  // per-lane byte offsets are the same for every item and computed once.
+  uint32_t loff[IPW];
+#pragma unroll
+  for (int x = 0; x < IPW; ++x) {
+    const int ins = wave * IPW + x, arr = ins / INS, pos = ins % INS * 64 + lane;
+    if (arr < 2) {   // K, V rows
+      const int r = pos / RC, c = pos % RC;
+      loff[x] = (uint32_t)((r * D + (c ^ swz<RC>(r)) * EPC) * 2);
+    } else {         // K^T lines (keys in swap23 order)
+      const int r = pos / LC, c = pos % LC;
+      loff[x] = (uint32_t)r * (uint32_t)p.Np * 2u + (uint32_t)((c ^ swz<LC>(r)) * EPC * 2);
+    }
+  }
+  int next_issue = 0;
+  auto issue_next = [&]() {
+    const int t = next_issue++;
+    if (t >= n_items) return;
+    const int k0 = item_tile(t) * BT;
+#pragma unroll
+    for (int x = 0; x < IPW; ++x) {
+      const int ins = wave * IPW + x, arr = ins / INS, li = ins % INS;
+      const T* base = arr == 0 ? Kh + (int64_t)k0 * D : arr == 1 ? Vh + (int64_t)k0 * D : KTh + k0;
+      // byte offsets below 2^32: the host checks D * Np * sizeof(T)
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)base, (short)0,
+          (int)(arr < 2 ? TE * 2u : (uint32_t)(D - 1) * (uint32_t)p.Np * 2u + BT * 2u), 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(smem + (arr * NBUF + t % NBUF) * TE + li * 64 * EPC),
+                                               16, (int)loff[x], 0, 0, 0);
+    }
+  };
+  // Ring bookkeeping as in bwd_dkdv: sync(R, F) waits for this wave's loads
+  // of the tiles up to R, passes a barrier (every wave's loads of those tiles
+  // are visible, every wave is done with the tiles before F) and issues the
+  // tiles whose slots that frees, up to F + NBUF - 1.
+  auto sync = [&](int R, int F) {
+    wait_vmcnt_tiles<IPW, NBUF - 2>(min(NBUF - 2, max(0, next_issue - 1 - R)));
+    ring_barrier();
+    const int last = min(F + NBUF - 1, n_items - 1);
+    while (next_issue <= last) issue_next();
+  };
+
+  // This wave's Q and dO fragments (B operands of S^T = K Q^T and
+  // dP^T = V dO^T), the accumulator tiles of its rows' statistics, and its dQ.
+  Frag qf[NS], of[NS];
+  f32x16 s_init, d_init, dq[NB];
+  auto load_q = [&](int qw) {
+    const int t = qw + col;
+    const T* qr = (const T*)p.q + (hq * p.Np + t) * D;
+    const T* orow = (const T*)p.dO + (hq * p.Np + t) * D;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      qf[s] = *reinterpret_cast<const Frag*>(qr + s * MF::KS + grp * MF::E);
+      of[s] = *reinterpret_cast<const Frag*>(orow + s * MF::KS + grp * MF::E);
+    }
+    // -lse/c and -D of every row of the tiles walked: -inf and 0 past N
+    const float nl = p.nlse[hq * p.Np + t], nd = p.dvec[hq * p.Np + t];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { s_init[r] = nl; d_init[r] = nd; }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) dq[nb] = f32x16{};
+  };
+  // dQ^T: lane = query, register r = head dim 32*nb + 8*(r/4) + 4*grp + r%4.
+  auto store_dq = [&](int qw) {
+    const int t = qw + col;
+    T* dqr = (T*)p.dqkv + ((int64_t)b * p.Np + t) * p.W + (int64_t)i * D;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int c = nb * 32 + 8 * rq + 4 * grp;
+        const f32x16& a = dq[nb];
+        *reinterpret_cast<bf16x4*>(dqr + c) =
+            bf16x4{(bf16)(a[4 * rq] * p.scale), (bf16)(a[4 * rq + 1] * p.scale),
+                   (bf16)(a[4 * rq + 2] * p.scale), (bf16)(a[4 * rq + 3] * p.scale)};
+      }
+  };
+
+  // Prologue: items 0..NBUF-2 in flight, then the first query tile's
+  // fragments; the K^T tile of the last slot starts as zeros (a pipelined run
+  // from item 0 reads it as its absent previous item's and multiplies it by
+  // zeros, which must not meet an Inf or NaN).
+  int qw = qt0 * 256 + 32 * wave;   // this wave's first query
+  while (next_issue < min(NBUF - 1, n_items)) issue_next();
+  load_q(qw);
+  for (int x = tid; x < TE * 2 / 16; x += WAVES * 64)
+    reinterpret_cast<f32x4*>(smem + (2 * NBUF + NBUF - 1) * TE)[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  // Items [t0, t1) that need a mask, one 32-key block at a time.
+  auto run_masked = [&](int t0, int t1) {
+    for (int t = t0; t < t1; ++t) {
+      sync(t, t);   // item t visible; every wave done with the items before it
+      const int sw = t % NBUF;
+      const int k0 = item_tile(t) * BT;
+#pragma unroll
+      for (int jb = 0; jb < BT / 32; ++jb) {
+        const int kb = k0 + 32 * jb;
+        if (kb >= p.N || (p.causal && kb > qw + 31)) continue;   // wave-uniform
+        f32x16 s = s_init, dp = d_init;
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+          s = MF::run(row_frag<T, D>(tile(0, sw), 32 * jb + col, st, grp), qf[st], s);
+          dp = MF::run(row_frag<T, D>(tile(1, sw), 32 * jb + col, st, grp), of[st], dp);
+        }
+        // register r: key kb + 4*grp + o_r, o_r = 8*(r/4) + r%4; visible iff
+        // o_r < lim (lim = N - kb - 4*grp, and for causal also <= q - kb - 4*grp)
+        const int base = kb + 4 * grp;
+        const int lim = p.causal ? min(p.N - base, qw + col - base + 1) : p.N - base;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pv = __builtin_amdgcn_exp2f(s[r] * p.c);
+          s[r] = 8 * (r / 4) + r % 4 < lim ? pv * dp[r] : 0.f;   // dS^T
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            dq[nb] = MF::run(line_frag<T>(tile(2, sw), nb * 32 + col, 32 * jb, h, grp), frag_regs<T>(s, h), dq[nb]);
+      }
+    }
+  };
+
+  // Items [t0, t1) without a mask, pipelined.
+  auto run_clear = [&](int t0, int t1) {
+    if (t0 >= t1) return;
+    constexpr int NGG = 2 * NB;      // dQ MFMAs of a block
+    constexpr int NGS = 2 * NS;      // S^T/dP^T MFMAs of a block
+    constexpr int NGP = NGG + NGS;   // MFMAs (groups) of a phase
+    constexpr int FA = 3;            // fragment reads ahead
+    static_assert(FA <= NGS, "groups");
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    f32x16 sA, dA, sB, dB;           // S^T and dP^T - D of block 0 (A) and block 1 (B)
+    u32x4 pA[2], pB[2];              // dS^T as bf16 pairs, per k-step: B operands of dQ
+    Frag fr[2 * NGP];                // the fragment of each MFMA of an iteration
+    // The fragment of MFMA u of the iteration over the ring slots of items
+    // t-1 (prev), t (cur) and t+1 (next). A phase's score MFMAs come first,
+    // its dQ MFMAs last: the softmax work of the next phase then reads scores
+    // whose MFMAs ended NGG groups before.
+    auto fetch = [&](auto uc, int prev, int cur, int next) __attribute__((always_inline)) {
+      constexpr int u = decltype(uc)::value, ph = u / NGP, k = u % NGP;
+      if constexpr (k < NGS) {
+        constexpr int st = k / 2, which = k % 2;   // 0: S^T (K), 1: dP^T (V)
+        fr[u] = row_frag<T, D>(tile(which, ph == 0 ? cur : next), (ph == 0 ? 32 : 0) + col, st, grp);
+      } else {
+        constexpr int h = (k - NGS) / NB, nb = (k - NGS) % NB;
+        fr[u] = line_frag<T>(tile(2, ph == 0 ? prev : cur), nb * 32 + col, ph == 0 ? 32 : 0, h, grp);
+      }
+    };
+    // dQ MFMA k (< NGG) of a block with packed dS^T pk
+    auto grad_mfma = [&](auto kc, const Frag& a, const u32x4 (&pk)[2]) __attribute__((always_inline)) {
+      constexpr int k = decltype(kc)::value, h = k / NB, nb = k % NB;
+      dq[nb] = MF::run(a, __builtin_bit_cast(Frag, pk[h]), dq[nb]);
+    };
+    // the scores [lo(k), lo(k+1)) of a phase go with its group k
+    auto lo = [](int k) constexpr { return 16 * k / NGP; };
+    float ex[16];
+    auto group = [&](auto uc, int prev, int cur, int next) __attribute__((always_inline)) {
+      constexpr int u = decltype(uc)::value, ph = u / NGP, k = u % NGP;
+      f32x16& s_sc = ph == 0 ? sB : sA;   // scored in this phase
+      f32x16& d_sc = ph == 0 ? dB : dA;
+      const f32x16& s_sm = ph == 0 ? sA : sB;   // softmax gradient in this phase
+      const f32x16& d_sm = ph == 0 ? dA : dB;
+      u32x4 (&p_sm)[2] = ph == 0 ? pA : pB;
+      // the fragment FA groups ahead; past the iteration's end, the first
+      // groups of the next one (scores of block 1 of item t+1: tile next)
+      if constexpr (u + FA < 2 * NGP) fetch(std::integral_constant<int, u + FA>{}, prev, cur, next);
+      else fetch(std::integral_constant<int, u + FA - 2 * NGP>{}, cur, next, next);
+      if constexpr (k < NGS) {
+        constexpr int st = k / 2, which = k % 2;
+        if constexpr (which == 0) s_sc = MF::run(fr[u], qf[st], st == 0 ? s_init : s_sc);
+        else d_sc = MF::run(fr[u], of[st], st == 0 ? d_init : d_sc);
+      } else {
+        grad_mfma(std::integral_constant<int, k - NGS>{}, fr[u], ph == 0 ? pB : pA);
+      }
+      // softmax gradient of this group's scores; exponentials one group ahead
+      constexpr int r0 = lo(k), r1 = lo(k + 1), r2 = k + 1 < NGP ? lo(k + 2) : 16;
+      if constexpr (k == 0) {
+#pragma unroll
+        for (int r = r0; r < r1; ++r) ex[r] = __builtin_amdgcn_exp2f(s_sm[r] * p.c);
+      }
+#pragma unroll
+      for (int r = r1; r < r2; ++r) ex[r] = __builtin_amdgcn_exp2f(s_sm[r] * p.c);
+#pragma unroll
+      for (int r = r0; r < r1; ++r) {
+        ex[r] = ex[r] * d_sm[r];   // dS^T = P (dP - D)
+        if (r % 2 == 1)
+          p_sm[r / 8][(r % 8) / 2] = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{ex[r - 1], ex[r]}, bf16x2));
+      }
+      // within the group: the MFMA, the fragment read, then the VALU work, so
+      // that the MFMAs of consecutive groups never issue back to back
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Prologue: tile t0 visible; scores of its block 0. The dS of block "1 of
+    // item t0-1" is zeros, so the first phase's dQ MFMAs add exact zeros:
+    // their other operand, the K^T tile in the slot before t0's, holds item
+    // t0-1 (finite) or, before item 0, zeros. Then the first FA fragments of
+    // the first iteration (scores of block 1 of tile t0).
+    sync(t0, t0);
+    {
+      const int s0 = t0 % NBUF;
+      sA = s_init; dA = d_init;
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        sA = MF::run(row_frag<T, D>(tile(0, s0), col, st, grp), qf[st], sA);
+        dA = MF::run(row_frag<T, D>(tile(1, s0), col, st, grp), of[st], dA);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) pB[h] = u32x4{0u, 0u, 0u, 0u};
+      static_for<0, FA>([&](auto uc) { fetch(uc, (s0 + NBUF - 1) % NBUF, s0, s0); });
+    }
+    // Iteration t reads the slots of items t-1 (prev), t (cur) and t+1
+    // (next; past the loop's end, item t+1's scores are computed and
+    // dropped, and its first fragments read and dropped). There is one copy
+    // of it per slot of t.
+    for (int t = t0; t < t1; ++t) {
+      sync(t + 1, t - 1);   // items t and t+1 visible; every wave done with the items before t-1
+      const int m = t % NBUF;
+      static_for<0, NBUF>([&](auto mc) {
+        constexpr int c = decltype(mc)::value;
+        if (m == c) static_for<0, 2 * NGP>([&](auto uc) { group(uc, (c + NBUF - 1) % NBUF, c, (c + 1) % NBUF); });
+      });
+    }
+    // Epilogue: dQ of block 1 of the last item.
+    const int lt = (t1 - 1) % NBUF;
+    static_for<0, NGG>([&](auto kc) { fetch(std::integral_constant<int, NGS + decltype(kc)::value>{}, lt, lt, lt); });
+    static_for<0, NGG>([&](auto kc) { grad_mfma(kc, fr[NGS + decltype(kc)::value], pB); });
+  };
+
+  // Key tiles [0, clear) are fully visible to every query of query tile qt.
+  auto clear_tiles = [&](int qt) { return min(p.causal ? qt * 256 / BT : p.N / BT, p.N / BT); };
+  // Phase 0 walks key tiles upward: the clear ones first.
+  const int d0 = min(clear_tiles(qt0), n0);
+  run_clear(0, d0);
+  run_masked(d0, n0);
+  if (n_items > n0) {   // second query tile: store the first one's dQ
+    store_dq(qw);
+    qw = qt1 * 256 + 32 * wave;
+    load_q(qw);
+    wait_vmcnt<0>();
+    // Phase 1 walks key tiles downward: the clear ones last.
+    const int m1 = n0 + max(0, nt1 - clear_tiles(qt1));
+    run_masked(n0, m1);
+    run_clear(m1, n_items);
+  }
+  store_dq(qw);
+}
+
 template <typename T, bool PERM = false>
 hipError_t transpose(const void* src, int64_t src_bs, int64_t src_ld, int64_t r_valid,
                      int64_t r_total, void* dst, int64_t dst_bs, int64_t dst_ld, int64_t C,
@@ -1056,7 +1382,9 @@ hipError_t backward_impl(const void* x, const void* wq, const void* wk, const vo
   SQA_CK(hipGetLastError());
   // causal: workgroups take pairs of 256-query tiles (qt, n_qt-1-qt)
   const int64_t n_qt = Np / 256;
-  bwd_dq<T, D><<<(unsigned)((causal ? (n_qt + 1) / 2 : n_qt) * B * H_q), 256, 0, stream>>>(p);
+  const unsigned dq_grid = (unsigned)((causal ? (n_qt + 1) / 2 : n_qt) * B * H_q);
+  if constexpr (std::is_same_v<T, bf16> && D == 64) bwd_dq_pipe<D><<<dq_grid, 512, 0, stream>>>(p);
+  else bwd_dq<T, D><<<dq_grid, 256, 0, stream>>>(p);
   SQA_CK(hipGetLastError());
   // dX = [dQ | dK | dV] [Wq | Wk | Wv]^T
   concat_weights<T><<<(unsigned)((d_model * W + 255) / 256), 256, 0, stream>>>(
