@@ -221,35 +221,47 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_kernel(Rows rows, const T* w
   const int n0 = ct * BN;
   const int k_begin = blockIdx.y * k_split;
 
-  // Per-thread sources of its direct loads (fixed rows, chunk swizzled per row).
-  const T* a_src[C::A_INS];
-  const T* b_src[C::B_INS];
+  // Direct loads as buffer loads: unlike global_load_lds they count only in
+  // vmcnt, so the compiler's waits for the fragment reads in flight stay
+  // exact (with a global_load_lds in flight it waits for every LDS read).
+  // Load i of a wave covers 64 chunks of the tile rows r0 .. r0 + 64/CPR - 1;
+  // its buffer starts at row r0 (a row at or after it: clamped rows repeat a
+  // later one), and each lane's byte offset in it (its row, its chunk
+  // swizzled per row) is fixed, below 2^32 for these few rows of K elements.
+  // Stage kt moves the scalar offset only.
+  const T* a_base[C::A_INS];
+  const T* b_base[C::B_INS];
+  uint32_t a_off[C::A_INS], b_off[C::B_INS];
 #pragma unroll
   for (int i = 0; i < C::A_INS; ++i) {
     const int pos = (wave * C::A_INS + i) * 64 + lane;
-    const int r = pos / C::CPR, slot = pos % C::CPR;
-    a_src[i] = rows.row(m0 + r) + k_begin + (slot ^ swz<C::CPR>(r)) * C::EPC;
+    const int r = pos / C::CPR, slot = pos % C::CPR, r0 = (wave * C::A_INS + i) * 64 / C::CPR;
+    a_base[i] = rows.row(m0 + r0) + k_begin;
+    a_off[i] = (uint32_t)((rows.row(m0 + r) + k_begin + (slot ^ swz<C::CPR>(r)) * C::EPC - a_base[i]) * (int64_t)sizeof(T));
   }
 #pragma unroll
   for (int i = 0; i < C::B_INS; ++i) {
     const int pos = (wave * C::B_INS + i) * 64 + lane;
-    const int r = pos / C::CPR, slot = pos % C::CPR;
-    const int n = min(n0 + r, ncols - 1);
-    b_src[i] = wt + (int64_t)n * K + k_begin + (slot ^ swz<C::CPR>(r)) * C::EPC;
+    const int r = pos / C::CPR, slot = pos % C::CPR, r0 = (wave * C::B_INS + i) * 64 / C::CPR;
+    const int nb0 = min(n0 + r0, ncols - 1), n = min(n0 + r, ncols - 1);
+    b_base[i] = wt + (int64_t)nb0 * K + k_begin;
+    b_off[i] = (uint32_t)(((int64_t)(n - nb0) * K + (slot ^ swz<C::CPR>(r)) * C::EPC) * (int64_t)sizeof(T));
   }
   const int nk = (min(K, k_begin + k_split) - k_begin) / BK;
   auto issue = [&](int kt) {
     if (kt >= nk) return;
     T* st = smem + (kt % NST) * C::STAGE;
+    const int koff = kt * BK * (int)sizeof(T);
 #pragma unroll
     for (int i = 0; i < C::A_INS; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(a_src[i] + kt * BK),
-                                       (lds_ptr)(st + (wave * C::A_INS + i) * 64 * C::EPC), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(__builtin_amdgcn_make_buffer_rsrc((void*)a_base[i], (short)0, -1, 0x00020000),
+                                               (lds_ptr)(st + (wave * C::A_INS + i) * 64 * C::EPC), 16,
+                                               (int)a_off[i], koff, 0, 0);
 #pragma unroll
     for (int i = 0; i < C::B_INS; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(b_src[i] + kt * BK),
-                                       (lds_ptr)(st + C::A_ELEMS + (wave * C::B_INS + i) * 64 * C::EPC),
-                                       16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(__builtin_amdgcn_make_buffer_rsrc((void*)b_base[i], (short)0, -1, 0x00020000),
+                                               (lds_ptr)(st + C::A_ELEMS + (wave * C::B_INS + i) * 64 * C::EPC),
+                                               16, (int)b_off[i], koff, 0, 0);
   };
   // MFMA fragment of tile row r (A or B part of a stage), k-step s.
   auto frag = [&](const T* part, int r, int s) -> Frag {
@@ -289,35 +301,45 @@ __global__ __launch_bounds__(TL::THREADS) void gemm_kernel(Rows rows, const T* w
 #pragma unroll
     for (int s = 0; s < NST; ++s) issue(s);
     wait_vmcnt_tiles<C::VM, NST - 1>(min(NST - 1, nk - 1));
-    __syncthreads();
-    Frag ca[MI], cb[NJ];
-    read(0, 0, ca, cb);
-    for (int kt = 0; kt < nk; ++kt) {
+    ring_barrier();
+    // Fragments in two register sets: k-step s uses set s % 2 while the
+    // reads of k-step s + 1 fill the other (SUB is even, so a stage's first
+    // k-step always uses set 0 and no set is copied into another). The last
+    // stage runs in a copy of its own, so that no branch joins the paths
+    // before a k-step's MFMAs and their waits count the reads in flight
+    // exactly.
+    static_assert(SUB % 2 == 0, "k-steps per stage");
+    Frag fa[2][MI], fb[2][NJ];
+    read(0, 0, fa[0], fb[0]);
+    auto stage = [&](int kt, auto last) {
 #pragma unroll
       for (int s = 0; s < SUB; ++s) {
-        Frag na[MI], nb[NJ];
+        const int cur = s % 2, nxt = (s + 1) % 2;
         if (s + 1 < SUB) {
-          read(kt, s + 1, na, nb);
-        } else if (kt + 1 < nk) {
+          read(kt, s + 1, fa[nxt], fb[nxt]);
+        } else if constexpr (!decltype(last)::value) {
           // Stage kt+1 complete for this wave (later stages may be in flight),
           // then visible to all; every wave's reads of stage kt are done, so
           // its slot takes stage kt+NST.
           wait_vmcnt_tiles<C::VM, NST - 2>(min(NST - 2, max(0, nk - 2 - kt)));
-          __syncthreads();
+          ring_barrier();
           issue(kt + NST);
-          read(kt + 1, 0, na, nb);
+          read(kt + 1, 0, fa[nxt], fb[nxt]);
         }
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
           for (int j = 0; j < NJ; ++j)
-            acc[i][j] = TR ? MF::run(cb[j], ca[i], acc[i][j]) : MF::run(ca[i], cb[j], acc[i][j]);
-#pragma unroll
-        for (int i = 0; i < MI; ++i) ca[i] = na[i];
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) cb[j] = nb[j];
+            acc[i][j] = TR ? MF::run(fb[cur][j], fa[cur][i], acc[i][j]) : MF::run(fa[cur][i], fb[cur][j], acc[i][j]);
+        // the next k-step's reads before this one's MFMAs, so that their
+        // latency hides behind all of them
+        __builtin_amdgcn_sched_group_barrier(0x100, MI + NJ, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, MI * NJ, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
-    }
+    };
+    for (int kt = 0; kt + 1 < nk; ++kt) stage(kt, std::false_type{});
+    if (nk > 0) stage(nk - 1, std::true_type{});
   };
   if constexpr (Store::kDirect) {
     // register r of this lane: row 8*(r/4) + 4*grp + r%4, column col
