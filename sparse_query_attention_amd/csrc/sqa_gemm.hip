@@ -17,14 +17,15 @@
 //    Every other product (fp32, the backward pass) runs 256-thread workgroups
 //    on 128x128 tiles, four waves of 64x64 (2x2 MFMA tiles).
 //  * K advances in steps of 32 through a 4-stage LDS ring filled by direct
-//    global->LDS loads (global_load_lds_dwordx4), three stages ahead, with one
+//    loads into LDS (buffer_load_dwordx4 ... lds), three stages ahead, with one
 //    barrier per step. Each load lands lane-contiguously, so 16-byte chunks are
 //    XOR-swizzled per row against LDS bank conflicts.
 //  * Workgroups are dispatched round-robin over the 8 XCDs, each with its own
 //    L2. The 1-D grid is remapped so that every column tile of a row block
 //    runs on one XCD, and that row block of A is fetched from memory once.
 //  * LDS fragments are read one k-step of 16 ahead of the MFMAs that use them,
-//    across the stage boundary too, so LDS latency overlaps the MFMAs.
+//    across the stage boundary too, into two alternating register sets, so LDS
+//    latency overlaps the MFMAs.
 //  * Rows past the end of A are loaded from a clamped, valid row and never
 //    stored as computed: step 1 writes zeros there (the padded rows of the
 //    Q/K/V^T layouts), step 3 skips them.
