@@ -152,8 +152,10 @@ __global__ __launch_bounds__(1024) void lpt_order(AttnParams p, int grid, int n_
   for (int i = threadIdx.x; i < grid; i += 1024) order[i] = val[i];
 }
 
+// Two waves per SIMD, except fp32 at d_head 64, whose operand fragments and
+// accumulators take more than the 256 registers a wave has at that occupancy.
 template <typename T, int D, int WAVES>
-__global__ __launch_bounds__(64 * WAVES, 2) void attn_kernel(AttnParams p) {
+__global__ __launch_bounds__(64 * WAVES, sizeof(T) == 2 || D < 64 ? 2 : 1) void attn_kernel(AttnParams p) {
   using MF = Mfma<T>;
   using Frag = typename MF::Frag;
   constexpr int EPC = 16 / sizeof(T);          // elements per 16-byte chunk

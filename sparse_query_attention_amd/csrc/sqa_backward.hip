@@ -710,8 +710,9 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
 // workgroup has the same number of items, and at each step all workgroups in
 // the same half read the same key tile. Without a mask every workgroup walks
 // all key tiles upward.
+// (one wave per SIMD for fp32 at d_head 64: its fragments take more registers than two waves have)
 template <typename T, int D>
-__global__ __launch_bounds__(256, 2) void bwd_dq(BwdParams p) {
+__global__ __launch_bounds__(256, sizeof(T) == 2 || D < 64 ? 2 : 1) void bwd_dq(BwdParams p) {
   using MF = Mfma<T>;
   using Frag = typename MF::Frag;
   constexpr int WAVES = 4;
