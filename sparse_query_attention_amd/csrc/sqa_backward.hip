@@ -290,12 +290,11 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
   const int n0 = max(0, qt_end - first0) * p.g;
   const int n_work = n0 + (p.causal && kt1 != kt0 ? max(0, qt_end - first1) * p.g : 0);
 
-  // item -> (query tile, head within the group)
+  // item -> query tile (the head within the group: (w < n0 ? w : w - n0) % g)
   auto item_tile = [&](int w) {
     if (w < n0) return p.causal ? qt_end - 1 - w / p.g : w / p.g;
     return first1 + (w - n0) / p.g;
   };
-  auto item_head = [&](int w) { return (w < n0 ? w : w - n0) % p.g; };
 
   const T* Kh = (const T*)p.k + ((int64_t)b * p.H_kv + j) * (int64_t)p.Np * D;
   const T* Vh = (const T*)p.v + ((int64_t)b * p.H_kv + j) * (int64_t)p.Np * D;
@@ -323,7 +322,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
   const T* arr_base = (const T*)(arr == 0 ? p.q : arr == 1 ? p.dO : arr == 2 ? p.qt : p.dOt);
   const int which = wave >> 2, part = wave & 3;   // row statistics: -lse/c (waves 0-3), -D (4-7)
   // Items are issued in order, so the next one's query tile and head are
-  // stepped along instead of divided out of its index (item_tile, item_head):
+  // stepped along instead of divided out of its index (item_tile, and the head):
   // the scalar work per item shrinks. it_soff = (b*H_q + head) * Np, the head's
   // offset in the row statistics; times D it is the head's element offset in
   // Q, dO ([.., Np, D]) and in Q^T, dO^T ([.., D, Np]) alike.
@@ -355,7 +354,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
     const __amdgpu_buffer_rsrc_t rss = __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, 64, 0x00020000);
     float* dst = reinterpret_cast<float*>(smem + 4 * NBUF * TE + (w % NBUF) * SE) + which * BT + part * 16;
     if (lane < 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(rss, (lds_ptr)dst, 4, lane * 4, 0, 0, 0);
-    // step to item w + 1 (item_tile / item_head of it)
+    // step to item w + 1 (its query tile and head)
     if (w + 1 == n0) {
       it_tile = first1; it_head = 0; it_soff = it_soff0;
     } else if (++it_head == p.g) {
