@@ -226,7 +226,7 @@ template <typename T> constexpr int kHalves = sizeof(T) == 2 ? 2 : 16;   // k-st
 // dK, dV: workgroup = (key tiles of 256 keys, KV head j, batch b); 8 waves x
 // 32 keys. The query-side operand tiles (Q, dO, Q^T, dO^T and the rows' lse
 // and D) of each 64-query tile go straight from global memory into a ring of
-// LDS slots (global_load_lds), NBUF-1 tiles ahead of the one in use; no
+// LDS slots (buffer loads into LDS), NBUF-1 tiles ahead of the one in use; no
 // registers hold them in transit. Row-major tiles [64][D] and transposed tiles
 // [D][64] keep their 16-byte chunks XOR-swizzled per row, so the MFMA operand
 // reads are free of bank conflicts.
@@ -698,10 +698,11 @@ __global__ __launch_bounds__(512, 2) void bwd_dkdv(BwdParams p) {
   }
 }
 
-// dQ: workgroup = (query tiles of 256 queries, head i, batch b); 4 waves x 64
+// dQ (fp32, and bf16 at d_head 32; bwd_dq_pipe below serves bf16 at d_head
+// 64): workgroup = (query tiles of 256 queries, head i, batch b); 4 waves x 64
 // queries. The key-side tiles (K, V and K^T, 64 keys each) go straight from
-// global memory into a ring of LDS slots (global_load_lds), NBUF-1 tiles ahead
-// of the one in use, XOR-swizzled per row as in bwd_dkdv.
+// global memory into a ring of LDS slots (buffer loads into LDS), NBUF-1 tiles
+// ahead of the one in use, XOR-swizzled per row as in bwd_dkdv.
 //
 // Order of the work, for L2 reuse as in bwd_dkdv: causal workgroup pr takes
 // query tile pr, walking its key tiles upward from the first, then query tile
