@@ -641,7 +641,7 @@ sqa_status sqa_decode_step(const void* x_new, const void* Wq, const void* Wk, co
   // Workspace: q and a [B, H_q*d_head], then the decode attention's fp32
   // partial states of its key chunks.
   const int64_t qa_b = B * H_q * d_head * (int64_t)es;
-  const int64_t scratch_b = (int64_t)sqa::decode_partial_bytes(B, H_q, H_kv, N_max, d_head);
+  const int64_t scratch_b = (int64_t)sqa::decode_partial_bytes(dtype, B, H_q, H_kv, N_max, d_head);
   const int64_t off_a = round256(qa_b), off_p = off_a + round256(qa_b);
   const int64_t total = off_p + round256(scratch_b);
   Workspace ws;
@@ -653,7 +653,7 @@ sqa_status sqa_decode_step(const void* x_new, const void* Wq, const void* Wk, co
                              H_kv, d_head, N_max, stream);
   // The merge of the attention's key chunks runs inside the output
   // projection where its LDS row fits, else as a launch of its own.
-  const bool fused = sqa::decode_merge_out_fits(B, N_max, H_q, H_kv, d_head, d_model);
+  const bool fused = sqa::decode_merge_out_fits(dtype, B, N_max, H_q, H_kv, d_head, d_model);
   if (e == hipSuccess)
     e = sqa::launch_decode_attention(dtype, q, k_cache, v_cache, pos, fused ? nullptr : a, part, B,
                                      N_max, H_q, H_kv, d_head, stream);

@@ -25,6 +25,7 @@
 //  * The four waves' partial states, then the chunks' partial states (a second
 //    kernel), are merged with the usual max/rescale rule.
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
 #include <type_traits>
 
@@ -359,17 +360,58 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_partial(DecParams p) {
     return;
   }
 
-  const T* Q = (const T*)p.q;
-  for (int i = tid; i < G * D; i += DEC_THREADS) {
-    const int hd = i / D, e = i % D;
-    qs[hd][e] = hd < gq ? to_f32(Q[((int64_t)b * p.H_q + i0 + hd) * D + e]) : 0.f;
-  }
-  __syncthreads();
-
   const int64_t row0 = ((int64_t)b * p.H_kv + h) * p.N_max;   // cache row of token 0
   const T* Kc = (const T*)p.kc + row0 * D;
   const T* Vc = (const T*)p.vc + row0 * D;
   const int kg = lane / CPK, dc = lane % CPK;
+
+  // Each wave streams its 64-key blocks with the next block's loads in flight
+  // while the current one is computed: its key rows are requested as soon as
+  // phase 1 has consumed the current ones, its value chunks as soon as phase 2
+  // has. Rows past the chunk are clamped to its first row (one cache line for
+  // the whole wave), so no load sits behind a branch; the loads issued in a
+  // wave's last step are drained after the loop.
+  constexpr int KSTEP = DEC_WAVES * KB;
+  Chunk kraw[CPK], vraw[CPK];
+  auto load_k = [&](int kb) {
+    const int j = kb + lane;
+    const T* krow = Kc + (int64_t)(j < k_end ? j : k_begin) * D;
+#pragma unroll
+    for (int ck = 0; ck < CPK; ++ck) kraw[ck] = *reinterpret_cast<const Chunk*>(krow + ck * EPC);
+  };
+  auto load_v = [&](int kb) {
+#pragma unroll
+    for (int r = 0; r < CPK; ++r) {
+      const int jv = kb + r * KGS + kg;
+      vraw[r] = *reinterpret_cast<const Chunk*>(Vc + (int64_t)(jv < k_end ? jv : k_begin) * D + dc * EPC);
+    }
+  };
+
+  // The queries go to LDS as fp32. Their loads are issued first and the first
+  // block's keys and values right behind them, so the staging waits for the
+  // queries alone and phase 1 for the keys alone.
+  constexpr int QPT = (G * D + DEC_THREADS - 1) / DEC_THREADS;
+  const T* Q = (const T*)p.q;
+  float qv[QPT];
+#pragma unroll
+  for (int u = 0; u < QPT; ++u) {
+    const int i = tid + u * DEC_THREADS;
+    const bool ok = i < G * D && i / D < gq;
+    const int ic = ok ? i : 0;   // a valid element, so the load needs no branch
+    const float v = to_f32(Q[((int64_t)b * p.H_q + i0 + ic / D) * D + ic % D]);
+    qv[u] = ok ? v : 0.f;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  load_k(k_begin + wave * KB);
+  __builtin_amdgcn_sched_barrier(0);
+  load_v(k_begin + wave * KB);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int u = 0; u < QPT; ++u) {
+    const int i = tid + u * DEC_THREADS;
+    if (i < G * D) qs[i / D][i % D] = qv[u];
+  }
+  __syncthreads();
 
   float m[G], l[G], o[G][EPC];
 #pragma unroll
@@ -380,24 +422,13 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_partial(DecParams p) {
     for (int e = 0; e < EPC; ++e) o[i][e] = 0.f;
   }
 
-  for (int kb = k_begin + wave * KB; kb < k_end; kb += DEC_WAVES * KB) {
+  for (int kb = k_begin + wave * KB; kb < k_end; kb += KSTEP) {
     // phase 1: lane = key
     const int j = kb + lane;
     const bool valid = j < k_end;
-    const T* krow = Kc + (int64_t)(valid ? j : k_begin) * D;
     float s[G];
 #pragma unroll
     for (int i = 0; i < G; ++i) s[i] = 0.f;
-    Chunk kraw[CPK];   // the whole key row in flight before any use
-#pragma unroll
-    for (int ck = 0; ck < CPK; ++ck) kraw[ck] = *reinterpret_cast<const Chunk*>(krow + ck * EPC);
-    // value chunks of this block for phase 2, also issued now
-    Chunk vraw[CPK];
-#pragma unroll
-    for (int r = 0; r < CPK; ++r) {
-      const int jv = kb + r * KGS + kg;
-      vraw[r] = *reinterpret_cast<const Chunk*>(Vc + (int64_t)(jv < k_end ? jv : k_begin) * D + dc * EPC);
-    }
     // The queries are read from LDS in the loop: an opaque zero offset keeps
     // the compiler from hoisting G*D of them into registers, which at G >= 2
     // cost more occupancy than the broadcast reads cost time.
@@ -419,6 +450,12 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_partial(DecParams p) {
         }
       }
     }
+    // The scheduler would otherwise move the next block's loads next to their
+    // first use and pull the value conversions into phase 1, which then waits
+    // for the values; the barriers keep each block's loads where they are.
+    __builtin_amdgcn_sched_barrier(0);
+    load_k(kb + KSTEP);   // phase 1 is done with kraw
+    __builtin_amdgcn_sched_barrier(0);
     float alpha[G];
 #pragma unroll
     for (int i = 0; i < G; ++i) {
@@ -451,7 +488,11 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_partial(DecParams p) {
         for (int e = 0; e < EPC; ++e) o[i][e] = fmaf(pj, vf[e], o[i][e]);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    load_v(kb + KSTEP);   // phase 2 is done with vraw
+    __builtin_amdgcn_sched_barrier(0);
   }
+  wait_vmcnt<0>();   // the last step's loads, never used
 
   // This wave's state: o summed over the key groups (lanes with the same dc).
 #pragma unroll
@@ -711,18 +752,53 @@ __global__ __launch_bounds__(256) void decode_merge_out(const float* part, const
   }
 }
 
-// Chunking of a decode step: enough workgroups for the chip, chunks a multiple of KB.
+// Workgroups of decode_partial<T, D, G> the current device holds at once: the
+// kernel's occupancy per CU times the CUs (cached per device).
+template <typename T, int D, int G> int64_t partial_slots() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_partial<T, D, G>, DEC_THREADS, 0) !=
+            hipSuccess || per_cu <= 0)
+      per_cu = 1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    n = per_cu * cus;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+template <typename T, int D> int64_t partial_slots_for(int G) {
+  switch (G) {
+    case 1: return partial_slots<T, D, 1>();
+    case 2: return partial_slots<T, D, 2>();
+    case 4: return partial_slots<T, D, 4>();
+    default: return partial_slots<T, D, 8>();
+  }
+}
+
+// Chunking of a decode step: as many workgroups as the device holds at once
+// (a second, partly filled round of them cost about a quarter of the step),
+// chunks a multiple of KB.
 struct DecodePlan { int G, n_hg, n_chunks, chunk; };
 
-DecodePlan decode_plan(int64_t B, int64_t H_q, int64_t H_kv, int64_t N_max) {
+DecodePlan decode_plan(sqa_dtype dt, int64_t d_head, int64_t B, int64_t H_q, int64_t H_kv,
+                       int64_t N_max) {
   const int g = (int)(H_q / H_kv);
   DecodePlan pl;
   pl.G = 1;
   while (pl.G < g && pl.G < 8) pl.G *= 2;   // 16 heads' accumulators would spill
   pl.n_hg = (g + pl.G - 1) / pl.G;
+  const int64_t slots = dt == SQA_DTYPE_BF16
+      ? (d_head == 64 ? partial_slots_for<bf16, 64>(pl.G) : partial_slots_for<bf16, 32>(pl.G))
+      : (d_head == 64 ? partial_slots_for<float, 64>(pl.G) : partial_slots_for<float, 32>(pl.G));
   const int64_t units = B * H_kv * pl.n_hg;
   const int64_t max_chunks = (N_max + KB - 1) / KB;
-  const int64_t want = std::max<int64_t>(1, std::min<int64_t>(max_chunks, (1024 + units - 1) / units));
+  const int64_t want = std::max<int64_t>(1, std::min<int64_t>(max_chunks, slots / units));
   const int64_t per = (N_max + want - 1) / want;
   pl.chunk = (int)((per + KB - 1) / KB * KB);
   pl.n_chunks = (int)((N_max + pl.chunk - 1) / pl.chunk);
@@ -751,7 +827,8 @@ template <typename T, int D>
 hipError_t decode_impl(const void* q, const void* kc, const void* vc, const int32_t* pos, void* a,
                        float* part, int64_t B, int64_t N_max, int64_t H_q, int64_t H_kv,
                        hipStream_t stream) {
-  const DecodePlan pl = decode_plan(B, H_q, H_kv, N_max);
+  const DecodePlan pl =
+      decode_plan(sizeof(T) == 2 ? SQA_DTYPE_BF16 : SQA_DTYPE_FP32, D, B, H_q, H_kv, N_max);
   DecParams p;
   p.q = q; p.kc = kc; p.vc = vc; p.pos = pos; p.part = part;
   p.N_max = N_max;
@@ -768,8 +845,9 @@ hipError_t decode_impl(const void* q, const void* kc, const void* vc, const int3
 
 }  // namespace
 
-size_t decode_partial_bytes(int64_t B, int64_t H_q, int64_t H_kv, int64_t N_max, int64_t d_head) {
-  const DecodePlan pl = decode_plan(B, H_q, H_kv, N_max);
+size_t decode_partial_bytes(sqa_dtype dt, int64_t B, int64_t H_q, int64_t H_kv, int64_t N_max,
+                            int64_t d_head) {
+  const DecodePlan pl = decode_plan(dt, d_head, B, H_q, H_kv, N_max);
   return (size_t)(B * H_q * pl.n_chunks * (d_head + 2)) * sizeof(float);
 }
 
@@ -850,18 +928,19 @@ hipError_t launch_decode_out(sqa_dtype dt, const void* a, const void* wo, void* 
                               : decode_out<float>(a, wo, out, B, K, d_model, stream);
 }
 
-bool decode_merge_out_fits(int64_t B, int64_t N_max, int64_t H_q, int64_t H_kv, int64_t d_head,
-                           int64_t d_model) {
+bool decode_merge_out_fits(sqa_dtype dt, int64_t B, int64_t N_max, int64_t H_q, int64_t H_kv,
+                           int64_t d_head, int64_t d_model) {
   return H_q * d_head <= 8192 && d_model % MC == 0 && d_model / MC <= 0x7FFFFFFF && B <= 65535 &&
-         H_q * decode_plan(B, H_q, H_kv, N_max).n_chunks <= MERGE_MAX_W;
+         H_q * decode_plan(dt, d_head, B, H_q, H_kv, N_max).n_chunks <= MERGE_MAX_W;
 }
 
 hipError_t launch_decode_merge_out(sqa_dtype dt, const void* part, const int32_t* pos,
                                    const void* wo, void* out, int64_t B, int64_t N_max,
                                    int64_t H_q, int64_t H_kv, int64_t d_head, int64_t d_model,
                                    hipStream_t stream) {
-  if (!decode_merge_out_fits(B, N_max, H_q, H_kv, d_head, d_model)) return hipErrorInvalidConfiguration;
-  const DecodePlan pl = decode_plan(B, H_q, H_kv, N_max);
+  if (!decode_merge_out_fits(dt, B, N_max, H_q, H_kv, d_head, d_model))
+    return hipErrorInvalidConfiguration;
+  const DecodePlan pl = decode_plan(dt, d_head, B, H_q, H_kv, N_max);
   const int tpr = MC / (dt == SQA_DTYPE_BF16 ? 8 : 4);
   const size_t lds =
       (size_t)(H_q * d_head + H_q * pl.n_chunks + H_q + (256 / tpr) * MC + 8 * MC) * sizeof(float);

@@ -101,15 +101,16 @@ hipError_t launch_decode_qkv(sqa_dtype dt, const void* x_new, const void* wq, co
                              const void* wv, const int32_t* pos, void* q, void* kc, void* vc,
                              int64_t B, int64_t d_model, int64_t H_q, int64_t H_kv, int64_t d_head,
                              int64_t N_max, hipStream_t stream);
-size_t decode_partial_bytes(int64_t B, int64_t H_q, int64_t H_kv, int64_t N_max, int64_t d_head);
+size_t decode_partial_bytes(sqa_dtype dt, int64_t B, int64_t H_q, int64_t H_kv, int64_t N_max,
+                            int64_t d_head);
 hipError_t launch_decode_attention(sqa_dtype dt, const void* q, const void* kc, const void* vc,
                                    const int32_t* pos, void* a, void* part, int64_t B,
                                    int64_t N_max, int64_t H_q, int64_t H_kv, int64_t d_head,
                                    hipStream_t stream);
 hipError_t launch_decode_out(sqa_dtype dt, const void* a, const void* wo, void* out, int64_t B,
                              int64_t K, int64_t d_model, hipStream_t stream);
-bool decode_merge_out_fits(int64_t B, int64_t N_max, int64_t H_q, int64_t H_kv, int64_t d_head,
-                           int64_t d_model);
+bool decode_merge_out_fits(sqa_dtype dt, int64_t B, int64_t N_max, int64_t H_q, int64_t H_kv,
+                           int64_t d_head, int64_t d_model);
 hipError_t launch_decode_merge_out(sqa_dtype dt, const void* part, const int32_t* pos,
                                    const void* wo, void* out, int64_t B, int64_t N_max,
                                    int64_t H_q, int64_t H_kv, int64_t d_head, int64_t d_model,
