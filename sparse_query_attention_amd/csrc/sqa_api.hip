@@ -318,7 +318,10 @@ sqa_status forward_impl(const void* x, const void* Wq, const void* Wk, const voi
   const int64_t off_a = off_v + act * round256(z.kv), off_w1 = off_a + act * round256(z.a);
   const int64_t off_w3 = off_w1 + round256((int64_t)sqa::qkv_wt_bytes(dtype, d_model, H_q, H_kv, d_head));
   const int64_t off_ord = off_w3 + round256((int64_t)sqa::out_wt_bytes(dtype, H_q * d_head, d_model));
-  const int64_t total = off_ord + (lens ? round256((int64_t)sqa::attention_order_bytes(B, N, H_q)) : 0);
+  const int64_t off_split = off_ord + (lens ? round256((int64_t)sqa::attention_order_bytes(B, N, H_q)) : 0);
+  const int64_t split_b = (int64_t)sqa::attention_split_bytes(dtype, B, N, H_q, H_kv, d_head, causal != 0,
+                                                              lens != nullptr, stream);
+  const int64_t total = off_split + round256(split_b);
   void* ws = nullptr;
   Workspace wsp;
   hipError_t e = hipSuccess;
@@ -338,6 +341,7 @@ sqa_status forward_impl(const void* x, const void* Wq, const void* Wk, const voi
   void *q = base, *k = base + off_k, *vt = base + off_v, *a = base + off_a;
   void *w1 = base + off_w1, *w3 = base + off_w3;
   int32_t* order = lens ? (int32_t*)(base + off_ord) : nullptr;
+  float* split_ws = split_b > 0 ? (float*)(base + off_split) : nullptr;
   float* lse = nullptr;
   float* o32 = nullptr;
   if (saved) {
@@ -354,7 +358,7 @@ sqa_status forward_impl(const void* x, const void* Wq, const void* Wk, const voi
     e = sqa::launch_fill_cache(dtype, k, vt, kc, vc, B, H_kv, N, z.Np, N_max, d_head, stream);
   if (e == hipSuccess)
     e = sqa::launch_attention(dtype, q, k, vt, a, B, N, z.Np, H_q, H_kv, d_head, causal != 0, lens,
-                              stream, lse, order, o32);
+                              stream, lse, order, o32, split_ws);
   if (e == hipSuccess)
     e = sqa::launch_output_projection(dtype, a, Wo, w3, out, B * N, H_q * d_head, d_model, lens, N,
                                       stream);
@@ -412,7 +416,7 @@ sqa_status backward_impl(const void* x, const void* Wq, const void* Wk, const vo
   if (saved) SQA_TRY(check_saved(saved, saved_bytes, s, dtype, outs, outb, 5));
   Workspace ws;
   SQA_TRY(ws.acquire(sqa::backward_workspace_bytes(dtype, B, N, z.Np, d_model, H_q, H_kv, d_head,
-                                                   saved != nullptr),
+                                                   saved != nullptr, causal != 0),
                      stream));
   const hipError_t e = sqa::launch_backward(dtype, x, Wq, Wk, Wv, Wo, dy, saved, dx, dWq, dWk, dWv, dWo,
                                             B, N, z.Np, d_model, H_q, H_kv, d_head, causal != 0,
@@ -500,9 +504,16 @@ sqa_status sqa_attention(const void* q, const void* k, const void* vt, void* a, 
   SQA_TRY(sizes_for(s, dtype, &z));
   if (overlap(a, z.a, q, z.q) || overlap(a, z.a, k, z.kv) || overlap(a, z.a, vt, z.kv))
     return fail(SQA_ERR_INVALID_ARG, "a overlaps q, k or vt");
+  Workspace ws;   // the key-split parts of a partial last round, if any
+  const size_t split_b =
+      sqa::attention_split_bytes(dtype, B, N, H_q, H_kv, d_head, causal != 0, false, stream);
+  if (split_b > 0) SQA_TRY(ws.acquire(split_b, stream));
   hipError_t e = sqa::launch_attention(dtype, q, k, vt, a, B, N, z.Np, H_q, H_kv, d_head,
-                                       causal != 0, nullptr, stream);
+                                       causal != 0, nullptr, stream, nullptr, nullptr, nullptr,
+                                       (float*)ws.ptr);
+  const hipError_t ef = ws.release();
   if (e != hipSuccess) return fail_hip(e, "attention launch");
+  if (ef != hipSuccess) return fail_hip(ef, "workspace release");
   return ok();
 }
 

@@ -84,6 +84,12 @@ struct AttnParams {
   float* o32;            // null, or [B*N, H_q*d]: the output before its rounding to T (fp32)
   int N, Np, H_q, H_kv, g, G, n_sub, q_per_wg, n_qt, causal;
   int chunk, remap_end;   // XCD-aware workgroup order (see the kernel's block decode)
+  // Key-split tail (non-causal): work items from split_begin on run as n_split
+  // workgroups each, part k taking keys [k*split_keys, (k+1)*split_keys), and
+  // leave their unnormalised state (O rows in part, m_ref and l in part_ml)
+  // for split_merge. split_begin is INT_MAX when nothing is split.
+  int split_begin, n_split, split_keys;
+  float* part; float* part_ml;
   float c;  // log2(e) / sqrt(d_head)
 };
 
@@ -183,9 +189,13 @@ __global__ __launch_bounds__(64 * WAVES, sizeof(T) == 2 || D < 64 ? 2 : 1) void 
   // causal work falling linearly along the chunks this gives every XCD the same
   // total. Blocks from remap_end on keep their index.
   // A ragged launch may instead take its work items in a precomputed order.
-  int blk = blockIdx.x;
+  int blk = blockIdx.x, kpart = -1;
   if (p.order) {
     blk = p.order[blk];
+  } else if (blk >= p.split_begin) {   // part kpart of a split work item
+    const int sidx = blk - p.split_begin;
+    blk = p.split_begin + sidx / p.n_split;
+    kpart = sidx % p.n_split;
   } else if (blk < p.remap_end) {
     const int xcd = blk % XCDS, s = blk / XCDS, r = s / p.chunk;
     blk = (r * XCDS + ((r & 1) ? XCDS - 1 - xcd : xcd)) * p.chunk + s % p.chunk;
@@ -203,6 +213,10 @@ __global__ __launch_bounds__(64 * WAVES, sizeof(T) == 2 || D < 64 ? 2 : 1) void 
   // Tokens of this sequence: N, or its own length in a padded batch. Its keys
   // end there, and its rows from there on are zero.
   const int L = p.lens ? min(max(p.lens[b], 0), p.N) : p.N;
+  // First key of this workgroup's range (0 unless it is part of a split item);
+  // key indexes below count from it, and the sequence ends Lk keys after it.
+  const int kb0 = kpart >= 0 ? kpart * p.split_keys : 0;
+  const int Lk = L - kb0;
 
   // A query tile wholly in the padding: zero rows, no keys (uniform per workgroup).
   if (q0 >= L) {
@@ -229,8 +243,8 @@ __global__ __launch_bounds__(64 * WAVES, sizeof(T) == 2 || D < 64 ? 2 : 1) void 
   }
 
   const T* Qh = (const T*)p.q + ((int64_t)b * p.H_q + head) * (int64_t)p.Np * D;
-  const T* Kh = (const T*)p.k + ((int64_t)b * p.H_kv + h) * (int64_t)p.Np * D;
-  const T* Vh = (const T*)p.vt + ((int64_t)b * p.H_kv + h) * (int64_t)D * p.Np;
+  const T* Kh = (const T*)p.k + ((int64_t)b * p.H_kv + h) * (int64_t)p.Np * D + (int64_t)kb0 * D;
+  const T* Vh = (const T*)p.vt + ((int64_t)b * p.H_kv + h) * (int64_t)D * p.Np + kb0;
 
   // Q as the B operand of S^T = K Q^T: lane -> query qw + 32*qb + col, k-group grp.
   // A query tile may reach past Np (tiles of 512 rows, Np a multiple of 256):
@@ -246,7 +260,7 @@ __global__ __launch_bounds__(64 * WAVES, sizeof(T) == 2 || D < 64 ? 2 : 1) void 
   // The workgroup stages the keys of its last query; this wave computes the
   // blocks up to its own last query (nblk_w) and only keeps pace with the
   // tile ring for the rest.
-  const int kv_len = p.causal ? min(L, q0 + p.q_per_wg) : L;
+  const int kv_len = p.causal ? min(L, q0 + p.q_per_wg) : kpart >= 0 ? min(Lk, p.split_keys) : L;
   const int nblk = (kv_len + 31) / 32;
   const int nblk_w = p.causal ? (min(kv_len, qw + QW) + 31) / 32 : nblk;
   const int n_tiles = (kv_len + KT - 1) / KT;
@@ -447,7 +461,7 @@ __global__ __launch_bounds__(64 * WAVES, sizeof(T) == 2 || D < 64 ? 2 : 1) void 
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = k0b + 16 * (r >> 3) + 8 * grp + (r & 7);
-        if (key >= L || (p.causal && key > qi)) s[qb][r] = -INFINITY;
+        if (key >= Lk || (p.causal && key > qi)) s[qb][r] = -INFINITY;
       }
     }
   };
@@ -612,7 +626,7 @@ __global__ __launch_bounds__(64 * WAVES, sizeof(T) == 2 || D < 64 ? 2 : 1) void 
   auto run_step = [&](int j, f32x16 (&s_cur)[QB], f32x16 (&s_next)[QB], auto mask_on,
                       float (&bsum)[QB], auto jm) __attribute__((always_inline)) {
     const bool masked =
-        decltype(mask_on)::value && (j * 32 + 32 > L || (p.causal && j * 32 + 31 > qw));
+        decltype(mask_on)::value && (j * 32 + 32 > Lk || (p.causal && j * 32 + 31 > qw));
     if (masked) mask(s_cur, j);
     float bcur[QB];
     if constexpr (sizeof(T) == 2) {
@@ -672,7 +686,7 @@ __global__ __launch_bounds__(64 * WAVES, sizeof(T) == 2 || D < 64 ? 2 : 1) void 
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) sB[qb] = f32x16{};   // P(-1) = 0
   qk(0, sA);
-  if (32 > L || (p.causal && 31 > qw)) mask(sA, 0);
+  if (32 > Lk || (p.causal && 31 > qw)) mask(sA, 0);
   {
     float m0[QB];
     block_max(sA, m0);
@@ -697,7 +711,7 @@ __global__ __launch_bounds__(64 * WAVES, sizeof(T) == 2 || D < 64 ? 2 : 1) void 
   // same blocks, whichever loop it is in, and steps only up to nblk_w
   // (jc <= nblk_w). A wave's last block is finished right after its step: the
   // next advance() but one recycles that block's tile.
-  const int jc = min(nblk, min(L / 32, p.causal ? qw / 32 : nblk)) & ~1;
+  const int jc = min(nblk, min(Lk / 32, p.causal ? qw / 32 : nblk)) & ~1;
   // The mask-free loop runs its first 2*NBUF blocks with the slot from j (block
   // 0's step reads block 0 for its padding PV), then NBUF tiles per iteration
   // with every slot known at compile time, then the rest with the slot from j.
@@ -737,6 +751,25 @@ __global__ __launch_bounds__(64 * WAVES, sizeof(T) == 2 || D < 64 ? 2 : 1) void 
   }
   if (jc == nblk_w) finish(nblk_w - 1, sB, bsum);   // every block in the first loop (nblk_w even)
 
+  if (kpart >= 0) {   // a part of a split item: its unnormalised state
+    const int64_t rows_item = (int64_t)p.G * p.q_per_wg;
+    const int64_t prow0 = (int64_t)((blk - p.split_begin) * p.n_split + kpart) * rows_item +
+                          (int64_t)(slot / waves_per_head) * p.q_per_wg + (qw - q0);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int64_t prow = prow0 + 32 * qb + col;
+      const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32);
+      float* po = p.part + prow * D;
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq)
+          *reinterpret_cast<f32x4*>(po + nb * 32 + 8 * rq + 4 * grp) =
+              f32x4{o[qb][nb][4 * rq], o[qb][nb][4 * rq + 1], o[qb][nb][4 * rq + 2], o[qb][nb][4 * rq + 3]};
+      if (grp == 0) *reinterpret_cast<float2*>(p.part_ml + 2 * prow) = float2{m_ref[qb], l_tot};
+    }
+    return;
+  }
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int t = qw + 32 * qb + col;
@@ -772,6 +805,47 @@ __global__ __launch_bounds__(64 * WAVES, sizeof(T) == 2 || D < 64 ? 2 : 1) void 
   }
 }
 
+// The parts of each split work item combined into its rows of A (and lse, o32):
+// with part k's reference m_k, sum l_k and unnormalised O_k, and M the largest
+// m_k, O = sum_k 2^(m_k - M) O_k / sum_k 2^(m_k - M) l_k, and the row's
+// log-sum-exp is M + log2 of that denominator. A thread takes four head dims of
+// one row; rows past N are not stored (their lse is +inf, as in attn_kernel).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void split_merge(AttnParams p, int n_items) {
+  constexpr int GPR = D / 4, RPW = 256 / GPR;   // threads per row, rows per workgroup
+  const int rows_item = p.G * p.q_per_wg;
+  const int64_t row = (int64_t)blockIdx.x * RPW + threadIdx.x / GPR;
+  if (row >= (int64_t)n_items * rows_item) return;
+  const int dg = threadIdx.x % GPR;
+  const int si = (int)(row / rows_item), rr = (int)(row % rows_item);
+  const WorkItem it = decode_item(p, p.split_begin + si);
+  const int head = it.h * p.g + it.sub * p.G + rr / p.q_per_wg;
+  const int t = it.qt * p.q_per_wg + rr % p.q_per_wg;
+  const int64_t prow0 = (int64_t)si * p.n_split * rows_item + rr;   // part k: prow0 + k * rows_item
+  float M = -INFINITY;
+  for (int k = 0; k < p.n_split; ++k) M = fmaxf(M, p.part_ml[2 * (prow0 + (int64_t)k * rows_item)]);
+  float l = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+  for (int k = 0; k < p.n_split; ++k) {
+    const int64_t pr = prow0 + (int64_t)k * rows_item;
+    const float2 ml = *reinterpret_cast<const float2*>(p.part_ml + 2 * pr);
+    const f32x4 ov = *reinterpret_cast<const f32x4*>(p.part + pr * D + 4 * dg);
+    const float w = __builtin_amdgcn_exp2f(ml.x - M);
+    l = fmaf(w, ml.y, l);
+    o0 = fmaf(w, ov[0], o0); o1 = fmaf(w, ov[1], o1); o2 = fmaf(w, ov[2], o2); o3 = fmaf(w, ov[3], o3);
+  }
+  const bool pad = t >= p.N;
+  if (p.lse && dg == 0 && t < p.Np)
+    p.lse[((int64_t)it.b * p.H_q + head) * p.Np + t] = pad ? INFINITY : M + log2f(l);
+  if (pad) return;
+  const float inv = 1.f / l;
+  const float v0 = o0 * inv, v1 = o1 * inv, v2 = o2 * inv, v3 = o3 * inv;
+  const int64_t off = ((int64_t)it.b * p.N + t) * ((int64_t)p.H_q * D) + head * D + 4 * dg;
+  T* dst = (T*)p.a + off;
+  if constexpr (sizeof(T) == 2) *reinterpret_cast<bf16x4*>(dst) = bf16x4{from_f32<T>(v0), from_f32<T>(v1), from_f32<T>(v2), from_f32<T>(v3)};
+  else *reinterpret_cast<f32x4*>(dst) = f32x4{v0, v1, v2, v3};
+  if (p.o32) *reinterpret_cast<f32x4*>(p.o32 + off) = f32x4{v0, v1, v2, v3};
+}
+
 template <typename T, int D, int WAVES>
 hipError_t run(const AttnParams& p, unsigned grid, hipStream_t stream) {
   attn_kernel<T, D, WAVES><<<grid, 64 * WAVES, 0, stream>>>(p);
@@ -792,7 +866,7 @@ int64_t plan(AttnParams& p, int64_t B, int64_t H_kv) {
 // (two waves per SIMD: 8 / WAVES workgroups per CU). No renumbering when the
 // CU count does not split evenly over the XCDs.
 template <int WAVES>
-void plan_order(AttnParams& p, int64_t grid, int64_t cus) {
+void plan_order(AttnParams& p, int64_t grid, int64_t cus) {   // grid: the items to renumber
   p.chunk = (int)(cus / XCDS) * (8 / WAVES);
   p.remap_end = 0;
   if (cus % XCDS == 0 && p.chunk > 0)
@@ -801,9 +875,9 @@ void plan_order(AttnParams& p, int64_t grid, int64_t cus) {
 
 template <int WAVES>
 hipError_t dispatch(sqa_dtype dt, int64_t d_head, AttnParams& p, int64_t grid, int64_t cus,
-                    int32_t* order_ws, hipStream_t stream) {
+                    int32_t* order_ws, hipStream_t stream, int64_t remap_items = -1) {
   if (grid <= 0 || grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  plan_order<WAVES>(p, grid, cus);
+  plan_order<WAVES>(p, remap_items < 0 ? grid : remap_items, cus);
   // Sequences of different lengths break the chunk order's premise (equal
   // streams whose work falls linearly), and its static XCD assignment then
   // unbalances the XCDs (5.5 against 4.8 ms for plain round-robin on a batch of
@@ -858,25 +932,81 @@ int cu_count(hipStream_t stream) {
 // fill their tail with short workgroups. fp32 at d_head 64 always runs with
 // 4-wave workgroups: its 8-wave form needs more than the 256 registers that
 // two waves per SIMD leave.
+// Key-split tail of a non-causal grid. Every non-causal work item streams all
+// of its sequence's keys, so a grid of R full dispatch rounds and a partial
+// one takes R + 1 round times (the 200k-token xSMQA workload: 1563 items on
+// 256 CUs, 6.1 rounds run in 7). The items of the partial round are split
+// over their keys into up to cus / tail parts of at least SPLIT_MIN_KEYS keys,
+// so that round shrinks to about 1 / n_split of a round, and split_merge
+// combines the parts. At most SPLIT_MAX_WGS workgroups are split parts.
+constexpr int64_t SPLIT_MIN_KEYS = 2048, SPLIT_MAX_WGS = 256;
+struct SplitPlan { int64_t full = 0, tail = 0, n_split = 1, keys = 0, bytes = 0; };
+
+SplitPlan split_plan(sqa_dtype dt, int64_t B, int64_t N, int64_t H_q, int64_t H_kv, int64_t d_head,
+                     bool causal, bool varlen, int64_t cus) {
+  SplitPlan sp;
+  if (causal || varlen || dt != SQA_DTYPE_BF16 || B * N == 0) return sp;
+  AttnParams p{};
+  p.N = (int)N; p.g = (int)(H_q / H_kv);
+  const int64_t grid = plan<8>(p, B, H_kv);
+  const int64_t tail = grid % cus;
+  if (grid < cus || tail == 0) return sp;
+  int64_t n = std::min(std::min(cus, SPLIT_MAX_WGS) / tail, N / SPLIT_MIN_KEYS);
+  if (n < 2) return sp;
+  const int64_t keys = ((N + n - 1) / n + KT - 1) / KT * KT;
+  n = (N + keys - 1) / keys;   // every part holds keys
+  if (n < 2) return sp;
+  sp.full = grid - tail; sp.tail = tail; sp.n_split = n; sp.keys = keys;
+  sp.bytes = tail * n * p.G * p.q_per_wg * (d_head + 2) * (int64_t)sizeof(float);
+  return sp;
+}
+
 size_t attention_order_bytes(int64_t B, int64_t N, int64_t H_q) {
   // a bound on the grid: query tiles of at least 64 rows, at most H_q head groups
   return (size_t)(B * ((N + 63) / 64) * H_q) * sizeof(int32_t);
 }
 
+size_t attention_split_bytes(sqa_dtype dt, int64_t B, int64_t N, int64_t H_q, int64_t H_kv,
+                             int64_t d_head, bool causal, bool varlen, hipStream_t stream) {
+  return (size_t)split_plan(dt, B, N, H_q, H_kv, d_head, causal, varlen, cu_count(stream)).bytes;
+}
+
+size_t attention_split_bound(int64_t d_head) {
+  return (size_t)(SPLIT_MAX_WGS * 8 * QW * (d_head + 2) * (int64_t)sizeof(float));
+}
+
 hipError_t launch_attention(sqa_dtype dt, const void* q, const void* k, const void* vt, void* a,
                             int64_t B, int64_t N, int64_t Np, int64_t H_q, int64_t H_kv,
                             int64_t d_head, bool causal, const int32_t* lens, hipStream_t stream,
-                            float* lse, int32_t* order_ws, float* o32) {
+                            float* lse, int32_t* order_ws, float* o32, float* split_ws) {
   AttnParams p;
   p.q = q; p.k = k; p.vt = vt; p.a = a; p.lens = lens; p.lse = lse; p.o32 = o32;
   p.N = (int)N; p.Np = (int)Np; p.H_q = (int)H_q; p.H_kv = (int)H_kv;
   p.g = (int)(H_q / H_kv);
   p.causal = causal ? 1 : 0;
   p.c = (float)(1.4426950408889634 / sqrt((double)d_head));
+  p.split_begin = 0x7FFFFFFF; p.n_split = 1; p.split_keys = 0;
+  p.part = nullptr; p.part_ml = nullptr;
   AttnParams p8 = p;
   const int64_t grid8 = plan<8>(p8, B, H_kv);
   const int64_t cus = cu_count(stream);
   const int64_t tail = grid8 % cus;
+  const SplitPlan sp = split_ws ? split_plan(dt, B, N, H_q, H_kv, d_head, causal, lens != nullptr, cus)
+                                : SplitPlan{};
+  if (sp.n_split >= 2) {
+    const int64_t grid = sp.full + sp.tail * sp.n_split, rows = grid - sp.full;
+    p8.split_begin = (int)sp.full; p8.n_split = (int)sp.n_split; p8.split_keys = (int)sp.keys;
+    p8.part = split_ws;
+    p8.part_ml = split_ws + rows * p8.G * p8.q_per_wg * d_head;
+    hipError_t e = dispatch<8>(dt, d_head, p8, grid, cus, nullptr, stream, sp.full);
+    if (e != hipSuccess) return e;
+    const int rpw = 256 / (int)(d_head / 4);
+    const int64_t merge_rows = sp.tail * p8.G * p8.q_per_wg;
+    const unsigned mgrid = (unsigned)((merge_rows + rpw - 1) / rpw);
+    if (d_head == 64) split_merge<bf16, 64><<<mgrid, 256, 0, stream>>>(p8, (int)sp.tail);
+    else split_merge<bf16, 32><<<mgrid, 256, 0, stream>>>(p8, (int)sp.tail);
+    return hipGetLastError();
+  }
   if ((!causal && tail != 0 && 2 * tail <= cus) || (dt == SQA_DTYPE_FP32 && d_head == 64)) {
     const int64_t grid4 = plan<4>(p, B, H_kv);
     return dispatch<4>(dt, d_head, p, grid4, cus, order_ws, stream);

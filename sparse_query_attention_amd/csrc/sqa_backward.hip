@@ -1292,10 +1292,13 @@ inline int64_t r256(int64_t x) { return (x + 255) / 256 * 256; }
 // training forward in the caller's buffer, and those regions (and the weight
 // transpose that recomputing them needs) take no workspace.
 BwdLayout bwd_layout(int64_t es, int64_t B, int64_t N, int64_t Np, int64_t d_model, int64_t H_q,
-                     int64_t H_kv, int64_t d, bool saved) {
+                     int64_t H_kv, int64_t d, bool saved, bool causal) {
   const int64_t W = (H_q + 2 * H_kv) * d, T = B * Np;
   const SplitK s1 = splitk_plan(d_model, T, W), s2 = splitk_plan(H_q * d, T, d_model);
-  const int64_t part = std::max(s1.n_split * d_model * W, s2.n_split * H_q * d * d_model) * 4;
+  // The region also holds the key-split parts of a recomputed non-causal
+  // attention (bf16) before the weight gradients use it.
+  const int64_t att = !saved && !causal && es == 2 ? (int64_t)attention_split_bound(d) : 0;
+  const int64_t part = std::max(std::max(s1.n_split * d_model * W, s2.n_split * H_q * d * d_model) * 4, att);
   const int64_t f = saved ? 0 : 1;
   const int64_t sizes[] = {
       f * es * B * H_q * Np * d, f * es * B * H_kv * Np * d, f * es * B * H_kv * Np * d,
@@ -1324,7 +1327,7 @@ hipError_t backward_impl(const void* x, const void* wq, const void* wk, const vo
                          int64_t d_model, int64_t H_q, int64_t H_kv, bool causal, char* ws,
                          hipStream_t stream) {
   const sqa_dtype dt = sizeof(T) == 2 ? SQA_DTYPE_BF16 : SQA_DTYPE_FP32;
-  const BwdLayout L = bwd_layout(sizeof(T), B, N, Np, d_model, H_q, H_kv, D, saved != nullptr);
+  const BwdLayout L = bwd_layout(sizeof(T), B, N, Np, d_model, H_q, H_kv, D, saved != nullptr, causal);
   const int64_t wq_w = H_q * D, wkv_w = H_kv * D, W = wq_w + 2 * wkv_w, TT = B * Np;
   void *q = ws + L.q, *k = ws + L.k, *vt = ws + L.vt, *a = ws + L.a, *wt = ws + L.wt;
   float* lse = (float*)(ws + L.lse);
@@ -1349,7 +1352,7 @@ hipError_t backward_impl(const void* x, const void* wq, const void* wk, const vo
     SQA_CK(launch_qkv_projection(dt, x, wq, wk, wv, wt, q, k, vt, B, N, Np, d_model, H_q, H_kv, D,
                                  nullptr, stream));
     SQA_CK(launch_attention(dt, q, k, vt, a, B, N, Np, H_q, H_kv, D, causal, nullptr, stream, lse,
-                            nullptr, o32));
+                            nullptr, o32, (float*)(ws + L.part)));
   }
   // dO = dY Wo^T in the head layout of q (Wo [H_q*d, d_model] is W^T of that product)
   SQA_CK(launch_gemm_heads(dt, dy, wo, dO, B, N, Np, d_model, wq_w, D, stream));
@@ -1420,9 +1423,9 @@ hipError_t backward_impl(const void* x, const void* wq, const void* wk, const vo
 }  // namespace
 
 size_t backward_workspace_bytes(sqa_dtype dt, int64_t B, int64_t N, int64_t Np, int64_t d_model,
-                                int64_t H_q, int64_t H_kv, int64_t d_head, bool saved) {
+                                int64_t H_q, int64_t H_kv, int64_t d_head, bool saved, bool causal) {
   return (size_t)bwd_layout(dt == SQA_DTYPE_BF16 ? 2 : 4, B, N, Np, d_model, H_q, H_kv, d_head,
-                            saved).total;
+                            saved, causal).total;
 }
 
 hipError_t launch_backward(sqa_dtype dt, const void* x, const void* wq, const void* wk,

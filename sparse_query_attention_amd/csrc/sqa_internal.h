@@ -33,12 +33,18 @@ hipError_t launch_qkv_projection(sqa_dtype dt, const void* x, const void* wq, co
 // with o32, also the output before its rounding, [B*N, H_q*d] fp32.
 // With lens and order_ws (device scratch of attention_order_bytes()), the
 // workgroups take the work items longest first.
+// With split_ws (device scratch of attention_split_bytes(), at most
+// attention_split_bound()), a non-causal bf16 grid whose last dispatch round is
+// partial splits that round's work items over their keys and merges the parts.
 size_t attention_order_bytes(int64_t B, int64_t N, int64_t H_q);
+size_t attention_split_bytes(sqa_dtype dt, int64_t B, int64_t N, int64_t H_q, int64_t H_kv,
+                             int64_t d_head, bool causal, bool varlen, hipStream_t stream);
+size_t attention_split_bound(int64_t d_head);
 hipError_t launch_attention(sqa_dtype dt, const void* q, const void* k, const void* vt, void* a,
                             int64_t B, int64_t N, int64_t Np, int64_t H_q, int64_t H_kv,
                             int64_t d_head, bool causal, const int32_t* lens, hipStream_t stream,
                             float* lse = nullptr, int32_t* order_ws = nullptr,
-                            float* o32 = nullptr);
+                            float* o32 = nullptr, float* split_ws = nullptr);
 
 // Step 3: out [M, d_model] = a [M, K] * wo [K, d_model]. wt is device scratch of
 // out_wt_bytes() for the transposed weights. With lens, row m is token m % seq_n
@@ -77,7 +83,7 @@ SavedLayout saved_layout(int64_t es, int64_t B, int64_t N, int64_t Np, int64_t H
 // from `saved` (saved_layout) or, if it is null, are recomputed. ws is device
 // scratch of backward_workspace_bytes(..., saved != null).
 size_t backward_workspace_bytes(sqa_dtype dt, int64_t B, int64_t N, int64_t Np, int64_t d_model,
-                                int64_t H_q, int64_t H_kv, int64_t d_head, bool saved);
+                                int64_t H_q, int64_t H_kv, int64_t d_head, bool saved, bool causal);
 hipError_t launch_backward(sqa_dtype dt, const void* x, const void* wq, const void* wk,
                            const void* wv, const void* wo, const void* dy, const void* saved,
                            void* dx, void* dwq, void* dwk, void* dwv, void* dwo, int64_t B,

@@ -202,6 +202,45 @@ def test_backward_at_full_size_with_dy_on_two_windows_all_gradients(dev):
     assert not bad, bad
 
 
+def test_backward_non_causal_key_split_tail_all_gradients(dev):
+    """20000 tokens, non-causal, 8 KV heads: the forward's partial last round of
+    work items runs split over the keys and merged (output and log-sum-exp),
+    both in forward_train and in the backward that recomputes them. The two
+    give bitwise the same gradients, and with dY on two windows of rows all
+    five gradients match the oracle at every position."""
+    w = wl.Workload("key_split_bwd", B=1, N=20000, d_model=1024, H=16, H_q=8, H_kv=8,
+                    causal=False, dtype="bf16", seed=3302)
+    rows = np.r_[np.arange(9000, 9512), np.arange(w.N - 300, w.N)]
+    log(f"case backward key split {w.name}, dY on {rows.size} rows")
+    arrays = wl.draw(w)
+    dy = np.zeros_like(wl.draw_upstream_grad(w))
+    dy[0, rows] = wl.draw_upstream_grad(w)[0, rows]
+    arrays["dY"] = dy
+    host = wl.to_device_dtype(arrays, w.dtype)
+    d = {k: v.to(dev) for k, v in host.items()}
+    kw = dict(H=w.H, H_q=w.H_q, H_kv=w.H_kv, causal=False)
+    y = sqa.forward(d["X"], d["Wq"], d["Wk"], d["Wv"], d["Wo"], **kw)
+    y2, saved = sqa.forward_train(d["X"], d["Wq"], d["Wk"], d["Wv"], d["Wo"], **kw)
+    g_saved = sqa.backward(d["X"], d["Wq"], d["Wk"], d["Wv"], d["Wo"], d["dY"], saved=saved, **kw)
+    g_re = _run(w, d)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    for k, x, z in zip(GRADS, g_saved, g_re):
+        assert torch.equal(x, z), k
+    got = [g.cpu() for g in g_re]
+    del d, saved, g_saved
+    o = {k: wl.widen(v) for k, v in host.items()}
+    ref = oracle.sqa_backward_dy_rows(o["X"], o["Wq"], o["Wk"], o["Wv"], o["Wo"], o["dY"], w.H_q,
+                                      w.H_kv, w.d_head, False, True, rows)
+    bad = []
+    for k, g in zip(GRADS, got):
+        rep = compare(wl.widen(g), ref[k], w.dtype)
+        log(f"  {k}: {rep}")
+        if not rep.ok:
+            bad.append(k)
+    assert not bad, bad
+
+
 @pytest.mark.parametrize("causal,dtype,dh", [(True, "bf16", 64), (False, "bf16", 32), (True, "fp32", 32)])
 def test_saved_activations_give_the_same_results(dev, causal, dtype, dh):
     """forward_train is bitwise forward, and backward from its saved activations

@@ -191,6 +191,39 @@ def test_long_workloads_write_every_element(dev, w):
     assert not bool(q[:, :, w.N:].any()) and not bool(vt[..., w.N:].any()), "padding rows not zero"
 
 
+# A non-causal grid of 8 KV heads x 40 query tiles = 320 work items on 256 CUs: the 64 items
+# of the partial last round are split into 4 key ranges of 5056 keys (the last one ragged,
+# 4832 keys) and merged. Heads 6 and 7 hold the split items.
+KEY_SPLIT = wl.Workload("key_split_bf16_n20000", B=1, N=20000, d_model=1024, H=16, H_q=8, H_kv=8,
+                        causal=False, dtype="bf16", seed=3301)
+
+
+def test_key_split_tail_on_sampled_rows(dev):
+    w = KEY_SPLIT
+    log(f"case {w.name}: B={w.B} N={w.N} H_q={w.H_q} H_kv={w.H_kv} causal={w.causal}")
+    host, d = device_inputs(w, dev)
+    y = run_forward(w, d)
+    q, k, vt = sqa.qkv_projection(d["X"], d["Wq"], d["Wk"], d["Wv"], H=w.H, H_q=w.H_q, H_kv=w.H_kv)
+    a = sqa.attention(q, k, vt, N=w.N, causal=w.causal)
+    torch.cuda.synchronize()
+    rows = np.unique(np.r_[sample_rows(w, n_random=96), np.arange(w.N - 70, w.N)])
+    idx = torch.from_numpy(rows).to(dev)
+    ag = wl.widen(a.reshape(-1, w.H_q * w.d_head)[idx].cpu())
+    yg = wl.widen(y.reshape(-1, w.d_model)[idx].cpu())
+    o = oracle_inputs(host)
+    ref = oracle.sqa_forward_rows(o["X"], o["Wq"], o["Wk"], o["Wv"], o["Wo"], w.H_q, w.H_kv,
+                                  w.d_head, w.causal, bf16=True, rows=rows)
+    for name, got, r in (("A", ag, ref["A_rows"]), ("Y", yg, ref["Y_rows"])):
+        rep = compare(got, r, w.dtype)
+        log(f"  {name} on {rows.size} rows: {rep}")
+        assert rep.ok, f"{w.name} {name}: {rep}"
+    # the split heads (6 and 7) on their own
+    split_cols = slice(6 * w.d_head, 8 * w.d_head)
+    rep = compare(ag[:, split_cols], ref["A_rows"][:, split_cols], w.dtype)
+    log(f"  A of heads 6-7: {rep}")
+    assert rep.ok, rep
+
+
 # ----------------------------------------------------------------------------------------------
 # determinism and edge cases
 
