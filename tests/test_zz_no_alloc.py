@@ -62,6 +62,19 @@ def test_noalloc_matches_forward_on_two_calls_the_second_smaller(dev):
             assert rep.ok, rep
 
 
+def test_noalloc_key_split_tail(dev):
+    """A non-causal grid of 320 work items on 256 CUs, whose partial last round
+    runs split over the keys: the split states sit in the fixed array too
+    (about 120 MB of workspace in all), and the result is bitwise sqa_forward's."""
+    w = wl.Workload("noalloc_split", B=1, N=20000, d_model=1024, H=16, H_q=8, H_kv=8,
+                    causal=False, dtype="bf16", seed=2204)
+    log(f"case noalloc {w.name}: B={w.B} N={w.N} H_q={w.H_q} H_kv={w.H_kv} causal={w.causal}")
+    _, d = _inputs(w, dev)
+    for _ in range(2):
+        y, y_ref = _both(w, d)
+        assert torch.equal(y, y_ref)
+
+
 def test_noalloc_fp32_and_repeat(dev):
     w = wl.TINY_SQA_FP32
     _, d = _inputs(w, dev)
