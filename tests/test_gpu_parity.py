@@ -224,6 +224,32 @@ def test_key_split_tail_on_sampled_rows(dev):
     assert rep.ok, rep
 
 
+def test_key_split_tail_two_sequences_head_pairs_d32(dev):
+    """2 sequences x 4 KV heads x 40 query tiles of 256 rows (2 query heads per
+    KV head, d_head 32) = 320 items: the 64 split items all lie in the second
+    sequence (heads 4-7 of it), 4 parts of 2560 keys, the last 2320. Every row
+    of that sequence against the oracle, and sampled rows of the first."""
+    w = wl.Workload("key_split_bf16_b2_n10000_d32", B=2, N=10000, d_model=512, H=16, H_q=8,
+                    H_kv=4, causal=False, dtype="bf16", seed=3303)
+    log(f"case {w.name}: B={w.B} N={w.N} H_q={w.H_q} H_kv={w.H_kv} d_head={w.d_head}")
+    host, d = device_inputs(w, dev)
+    q, k, vt = sqa.qkv_projection(d["X"], d["Wq"], d["Wk"], d["Wv"], H=w.H, H_q=w.H_q, H_kv=w.H_kv)
+    a = sqa.attention(q, k, vt, N=w.N, causal=w.causal)
+    y = run_forward(w, d)
+    torch.cuda.synchronize()
+    rows = np.r_[np.arange(0, w.N, 97), np.arange(w.N, 2 * w.N)]
+    idx = torch.from_numpy(rows).to(dev)
+    ag = wl.widen(a.reshape(-1, w.H_q * w.d_head)[idx].cpu())
+    yg = wl.widen(y.reshape(-1, w.d_model)[idx].cpu())
+    o = oracle_inputs(host)
+    ref = oracle.sqa_forward_rows(o["X"], o["Wq"], o["Wk"], o["Wv"], o["Wo"], w.H_q, w.H_kv,
+                                  w.d_head, w.causal, bf16=True, rows=rows)
+    for name, got, r in (("A", ag, ref["A_rows"]), ("Y", yg, ref["Y_rows"])):
+        rep = compare(got, r, w.dtype)
+        log(f"  {name} on {rows.size} rows: {rep}")
+        assert rep.ok, f"{w.name} {name}: {rep}"
+
+
 # ----------------------------------------------------------------------------------------------
 # determinism and edge cases
 
