@@ -125,22 +125,35 @@ __global__ __launch_bounds__(256) void concat_weights(const T* wq, const T* wk, 
 // nlse[b, i, t] = -lse / c (lse the base-2 log-sum-exp of the scaled scores,
 // c = log2(e) / sqrt(d)), -inf on padding rows: the dK/dV kernel starts its
 // S accumulation from it, so that a probability is exp2(c * acc).
+// Eight lanes share a row, each with D/8 consecutive elements of it, so that a
+// wave reads eight whole rows of dO and of O with vector loads (one row per
+// thread had made every load instruction touch 64 lines: 1.6 TB/s). The eight
+// partial sums meet in a fixed butterfly.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void dvec_kernel(const T* dO, const float* a, const float* lse,
                                                    float c, float* dvec, float* nlse, int N,
                                                    int64_t Np, int H_q, int64_t rows) {
-  const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (x >= rows) return;
-  const int64_t t = x % Np, bi = x / Np, i = bi % H_q, b = bi / H_q;
+  constexpr int EPL = D / 8;   // elements per lane
+  struct alignas(EPL * sizeof(T)) TV { T v[EPL]; };
+  struct alignas(EPL * 4 >= 16 ? 16 : EPL * 4) FV { float v[EPL]; };
+  const int64_t x = (int64_t)blockIdx.x * 32 + threadIdx.x / 8;
+  const int sub = threadIdx.x % 8;
+  const int64_t xr = x < rows ? x : rows - 1;   // every lane of the wave takes part in the butterfly
+  const int64_t t = xr % Np, bi = xr / Np, i = bi % H_q, b = bi / H_q;
   float s = 0.f;
   if (t < N) {
-    const T* o = dO + x * D;
-    const float* av = a + ((b * N + t) * H_q + i) * D;
-#pragma unroll 8
-    for (int k = 0; k < D; ++k) s = fmaf(f32_of(o[k]), f32_of(av[k]), s);
+    const TV o = *reinterpret_cast<const TV*>(dO + xr * D + sub * EPL);
+    const FV av = *reinterpret_cast<const FV*>(a + ((b * N + t) * H_q + i) * D + sub * EPL);
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) s = fmaf(f32_of(o.v[k]), av.v[k], s);
   }
-  dvec[x] = -s;
-  nlse[x] = t < N ? -lse[x] / c : -INFINITY;
+  s += __shfl_xor(s, 1);
+  s += __shfl_xor(s, 2);
+  s += __shfl_xor(s, 4);
+  if (sub == 0 && x < rows) {
+    dvec[x] = -s;
+    nlse[x] = t < N ? -lse[x] / c : -INFINITY;
+  }
 }
 
 // out segments [M, w0 | w1 | w2] = sum over the n_split partials, rounded once.
@@ -1358,7 +1371,7 @@ hipError_t backward_impl(const void* x, const void* wq, const void* wk, const vo
   SQA_CK(launch_gemm_heads(dt, dy, wo, dO, B, N, Np, d_model, wq_w, D, stream));
   {
     const int64_t rows = B * H_q * Np;
-    dvec_kernel<T, D><<<(unsigned)((rows + 255) / 256), 256, 0, stream>>>(
+    dvec_kernel<T, D><<<(unsigned)((rows + 31) / 32), 256, 0, stream>>>(
         (const T*)dO, o32, lse, (float)(1.4426950408889634 / sqrt((double)D)), dvec, nlse, (int)N, Np,
         (int)H_q, rows);
     SQA_CK(hipGetLastError());
