@@ -33,7 +33,9 @@
 //    loads). The two waves that share a SIMD take complementary query rows, so
 //    every SIMD carries the same causal work. Only blocks that cross the
 //    diagonal or the sequence end are masked. The heaviest query tiles are
-//    dispatched first.
+//    dispatched first; a grid that fits one dispatch round instead runs as
+//    4-wave workgroups, two per CU, each CU pairing a heavy tile with its
+//    complement.
 #include <math.h>
 
 #include <atomic>
@@ -90,6 +92,10 @@ struct AttnParams {
   // for split_merge. split_begin is INT_MAX when nothing is split.
   int split_begin, n_split, split_keys;
   float* part; float* part_ml;
+  // Paired order (causal, 4-wave workgroups, one dispatch round): blocks b and
+  // b + pair_stride of each group of 2*pair_stride take a heavy query tile and
+  // its complement in the same stream; 0 when off.
+  int pair_stride;
   float c;  // log2(e) / sqrt(d_head)
 };
 
@@ -190,8 +196,15 @@ __global__ __launch_bounds__(64 * WAVES, sizeof(T) == 2 || D < 64 ? 2 : 1) void 
   // total. Blocks from remap_end on keep their index.
   // A ragged launch may instead take its work items in a precomputed order.
   int blk = blockIdx.x, kpart = -1;
+  bool light = false;   // the lighter tile of a pair: its waves take the slots in reverse
   if (p.order) {
     blk = p.order[blk];
+  } else if (p.pair_stride) {
+    const int ps = p.pair_stride, within = blk % (2 * ps);
+    const int pi = blk / (2 * ps) * ps + within % ps, hn = p.n_qt / 2;
+    light = within >= ps;
+    const int r = pi % hn;   // 0: the stream's heaviest tile (decode_item reverses causal tiles)
+    blk = pi / hn * p.n_qt + (light ? p.n_qt - 1 - r : r);
   } else if (blk >= p.split_begin) {   // part kpart of a split work item
     const int sidx = blk - p.split_begin;
     blk = p.split_begin + sidx / p.n_split;
@@ -206,7 +219,7 @@ __global__ __launch_bounds__(64 * WAVES, sizeof(T) == 2 || D < 64 ? 2 : 1) void 
   // Waves w and w+4 of an 8-wave workgroup share a SIMD. The second four take
   // the (head, row block) slots in reverse order, so each SIMD pairs a low
   // row block with a high one and carries the same causal work.
-  const int slot = (WAVES == 8 && wave >= 4) ? 11 - wave : wave;
+  const int slot = (WAVES == 8 && wave >= 4) ? 11 - wave : light ? WAVES - 1 - wave : wave;
   const int head = h * p.g + sub * p.G + slot / waves_per_head;
   const int q0 = qt * p.q_per_wg;
   const int qw = q0 + (slot % waves_per_head) * QW;   // first query row of this wave
@@ -929,9 +942,10 @@ int cu_count(hipStream_t stream) {
 // under half full runs with 4-wave workgroups instead (two per CU): every
 // workgroup of a non-causal grid costs the same, and the smaller ones pack
 // that tail round over more CUs. Causal grids, dispatched heaviest first,
-// fill their tail with short workgroups. fp32 at d_head 64 always runs with
-// 4-wave workgroups: its 8-wave form needs more than the 256 registers that
-// two waves per SIMD leave.
+// fill their tail with short workgroups; one that fits a single round of
+// 8-wave workgroups pairs its heavy and light tiles on each CU instead. fp32
+// at d_head 64 always runs with 4-wave workgroups: its 8-wave form needs more
+// than the 256 registers that two waves per SIMD leave.
 // Key-split tail of a non-causal grid. Every non-causal work item streams all
 // of its sequence's keys, so a grid of R full dispatch rounds and a partial
 // one takes R + 1 round times (the 200k-token xSMQA workload: 1563 items on
@@ -986,11 +1000,28 @@ hipError_t launch_attention(sqa_dtype dt, const void* q, const void* k, const vo
   p.causal = causal ? 1 : 0;
   p.c = (float)(1.4426950408889634 / sqrt((double)d_head));
   p.split_begin = 0x7FFFFFFF; p.n_split = 1; p.split_keys = 0;
-  p.part = nullptr; p.part_ml = nullptr;
+  p.part = nullptr; p.part_ml = nullptr; p.pair_stride = 0;
   AttnParams p8 = p;
   const int64_t grid8 = plan<8>(p8, B, H_kv);
   const int64_t cus = cu_count(stream);
   const int64_t tail = grid8 % cus;
+  // A causal grid that fits one round of 8-wave workgroups ends when its
+  // heaviest tiles do, while CUs holding light tiles idle. Run it as 4-wave
+  // workgroups, two per CU, each CU pairing a heavy tile with its complement
+  // in the same stream (slots reversed in the light one), so every SIMD carries
+  // about the same number of block steps.
+  if (causal && dt == SQA_DTYPE_BF16 && !lens && grid8 <= cus) {
+    AttnParams p4 = p;
+    const int64_t grid4 = plan<4>(p4, B, H_kv);
+    if (grid4 <= 2 * cus && p4.n_qt % 2 == 0) {   // grid4 = streams * n_qt: even
+      // The dispatcher puts blocks b and b + grid/2 of a one-round grid on one
+      // CU: the first half takes the heavy tiles, the second their complements
+      // (measured: pairs of neighbouring blocks, or blocks 8 apart, ran 33-34
+      // against 25 us on the 16x1024 sSQA workload; unpaired 8-wave 31.5 us).
+      p4.pair_stride = (int)(grid4 / 2);
+      return dispatch<4>(dt, d_head, p4, grid4, cus, nullptr, stream, 0);
+    }
+  }
   const SplitPlan sp = split_ws ? split_plan(dt, B, N, H_q, H_kv, d_head, causal, lens != nullptr, cus)
                                 : SplitPlan{};
   if (sp.n_split >= 2) {
